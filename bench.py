@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of paged-KV decode attention on one MI355X.
+
+A step is one pad_decode_attn call (the whole hot path: plan, page gather,
+QK^T, mask, online softmax, PV, split partials and in-kernel merge) over one
+batch of seeded synthetic inputs.  The default workload is benchmark
+configuration 2 -- batch 1, bf16, head size 128, 32 q heads / 8 kv heads,
+page size 16, HND, shuffled block table -- at its longest context (32768)
+and largest query count (M = 4), with the K/V pool at 512 MiB so the
+rotating instances stay out of the 256 MiB last-level cache.
+
+The metric is effective HBM bandwidth: bytes of the distinct K/V rows the
+call must read, plus Q and O, per second; and its fraction of the 8 TB/s
+HBM peak.  One JSON line is printed.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+POOL_BYTES = 512 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_config2.json")
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_decode_block_amd", "csrc", "decode_mfma.hip")
+
+
+def effective_bytes(case) -> int:
+    """Distinct K/V bytes the call must read plus Q and O bytes.
+
+    A sequence of length L reads L keys, or min(L, W + M - 1) keys when a
+    window W limits the M query tokens; each key costs 2 * D elements per kv
+    head.  Padded sequences (L = 0) move nothing.
+    """
+    spec = case.spec
+    eb = case.q.element_size()
+    M = case.query_len
+    W = case.window
+    total = 0
+    for L in case.seq_lens.tolist():
+        if L <= 0:
+            continue
+        keys = min(L, W + M - 1) if W > 0 else L
+        total += keys * spec.num_kv_heads * 2 * spec.head_size * eb
+        total += 2 * M * spec.num_q_heads * spec.head_size * eb  # Q in, O out
+    return total
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def time_calls(case, n_warm: int, n_timed: int, **kw):
+    """Average ms per call over n_timed calls rotating through the instances,
+    timed with HIP events on the stream the kernel is launched on."""
+    import torch
+
+    import paged_kv_decode_block_amd as pad
+
+    out = torch.empty_like(case.q)
+    shape = pad.make_shape(case.q, case.kv_cache, case.block_tables[0], case.layout, **kw)
+    ws = pad.Workspace(case.q.device).get(shape)
+    n_inst = len(case.block_tables)
+
+    def call(i):
+        pad.pad_decode_attn(case.q, case.kv_cache, case.block_tables[i % n_inst], case.seq_lens, case.scale,
+                            case.window, out, layout=case.layout, workspace=ws, **kw)
+
+    for i in range(n_warm):
+        call(i)
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(n_timed):
+        call(n_warm + i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / n_timed, pad.pad_decode_attn_plan(shape, case.window)
+
+
+def cpu_baseline(cfg: int, context: int, M: int, budget_s: float = 12.0) -> dict:
+    """The fp64 oracle on the host, on a bounded sample of the workload."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+
+    case = wl.config_case(cfg, context, M, device="cpu")
+    kv64, table, lens = wl.compact(case)
+    q64 = wl.as_f64(case.q)
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_attention(q64, kv64, table, lens, case.scale, case.window, case.layout)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or calls >= 50:
+            break
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    gbs = effective_bytes(case) * calls / el / 1e9
+    return {
+        "value": round(gbs, 4),
+        "unit": "GB/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{calls} full call(s) of the config {cfg} workload at context {context}, M={M} "
+                  f"(one sequence, all kv heads), {el:.1f} s of host time; BLAS threads as reported",
+    }
+
+
+def traffic_entry():
+    """Measured HBM bytes per launch from the committed counter runs, if
+    they were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--context", type=int, default=None)
+    ap.add_argument("--queries", type=int, default=None)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the per-(context, M) sweep of the config")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the decode-attention path has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads as wl
+
+    cfg = args.config
+    pts = wl.CONFIG_POINTS[cfg]
+    context = args.context or max(pts["contexts"])
+    M = args.queries or max(pts["queries"])
+    spec = wl.CONFIGS[cfg]
+
+    def build_case(ctx, m):
+        per_inst = spec.block_bytes * (-(-ctx // spec.page_size))
+        inst = max(1, POOL_BYTES // per_inst) if cfg != 5 else 1
+        return wl.config_case(cfg, ctx, m, device="cuda", instances=inst, pool_bytes=POOL_BYTES)
+
+    print(f"[bench] config {cfg}: context {context}, M={M}: building inputs", file=sys.stderr, flush=True)
+    case = build_case(context, M)
+    nbytes = effective_bytes(case)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms, plan = time_calls(case, args.warmup, args.steps)
+    wall = time.perf_counter() - t0
+    print(f"[bench] timed {args.steps} steps: {ms * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+
+    sweep = []
+    if not args.no_sweep:
+        for ctx in pts["contexts"]:
+            for m in pts["queries"]:
+                c = build_case(ctx, m)
+                t, p = time_calls(c, 20, 100)
+                b = effective_bytes(c)
+                sweep.append({"context": ctx, "M": m, "us": round(t * 1e3, 3), "GB/s": round(b / (t * 1e-3) / 1e9, 1),
+                              "frac": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "segments": p["num_segments"]})
+                del c
+        print(f"[bench] sweep done ({len(sweep)} points)", file=sys.stderr, flush=True)
+
+    cpu = None if args.no_cpu else cpu_baseline(cfg, context, M)
+    line = {
+        "metric": "decode-attention effective HBM GB/s (K+V rows read + Q + O) and fraction of 8 TB/s",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"config {cfg}: batch {case.num_seqs}, {spec.dtype}, D={spec.head_size}, "
+                        f"{spec.num_q_heads}/{spec.num_kv_heads} heads, page {spec.page_size}, "
+                        f"{'HND' if spec.layout == wl.HND else 'NHD'}, window {case.window}",
+            "context": context,
+            "query_len": M,
+            "pool_bytes": POOL_BYTES,
+            "instances": len(case.block_tables),
+            "bytes_per_step": nbytes,
+            "plan": plan,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic_entry(),
+        },
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

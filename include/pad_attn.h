@@ -1,0 +1,166 @@
+/*
+ * pad_attn.h -- C ABI of the paged-KV decode / speculative-verify attention
+ * library (libpad_attn.so, HIP kernels for gfx950 / CDNA4).
+ *
+ * What it computes.  For every sequence s of a batch, every one of its M
+ * newest query tokens m (M <= 8) and every query head h, with L the
+ * sequence's length (which already counts the M new tokens) and
+ * qpos = L - M + m:
+ *
+ *     out[s,m,h,:] = sum_t softmax_t(scale * q[s,m,h,:] . K_t) * V_t
+ *
+ * over the keys t with lo <= t <= qpos, where lo = 0 without a window and
+ * lo = max(0, qpos - window + 1) with one.  K_t and V_t are the two halves
+ * of the packed K+V slot of token t of kv head h / (Hq / Hkv), found in
+ * physical block block_table[s][t / page_size] at offset t % page_size.
+ * A row with no visible key (L == 0 padding, or qpos < 0) is written as 0.
+ *
+ * Sources (page titles and sections):
+ *   - ROCm/vllm pull request 1330, "Summary": decode and speculative decode
+ *     attention over M <= 8 query tokens per sequence; all query rows of a
+ *     kv head share one read of its K/V; split-KV segments with an
+ *     in-kernel merge; sliding windows; batched decode; head sizes
+ *     64/128/256/512.
+ *   - vllm.v1.attention.ops.rocm_rdna_hip docs page: `KernelVariant`
+ *     (layout codes 0 = NHD, 1 = HND; dtype flag 1 = bf16; window 0 = full
+ *     causal), `expected_kv_cache_strides` (HND packed 2*D row strides),
+ *     `KernelVariant.scratch_shapes` / `make_scratch` / `scratch_bytes`
+ *     (fp32 split partials acc, m, l plus int32 counters that are zeroed
+ *     once and left zeroed by every launch).
+ *   - vllm.v1.attention.backends.rocm_octave_attn docs page:
+ *     `RocmOctaveMetadataBuilder._fill_query_maps` (K length
+ *     seq_len - q_len + i + 1, padding gets K length 0),
+ *     `supported_kv_cache_layouts` (HND and NHD), `customize_spec` (one
+ *     packed K+V slot per token and kv head), `RocmOctaveAttentionImpl`
+ *     (`accept_output_buffer`: the caller owns the output; block sizes are
+ *     multiples of 16).
+ *
+ * Layouts (all tensors dense, row-major, element type fp16 or bf16):
+ *   q, out        [num_seqs, query_len, num_q_heads, head_size]
+ *   kv_cache HND  [num_blocks, num_kv_heads, page_size, 2, head_size]
+ *   kv_cache NHD  [num_blocks, page_size, num_kv_heads, 2, head_size]
+ *                 (index 0 of the "2" axis is K, index 1 is V)
+ *   block_table   int32 [num_seqs, max_blocks_per_seq]
+ *   seq_lens      int32 [num_seqs]
+ * Query head h uses kv head h / (num_q_heads / num_kv_heads).
+ *
+ * Ownership and threading.  Every pointer is a device pointer owned by the
+ * caller; the library never allocates, frees or synchronises.  Each
+ * pad_decode_attn call enqueues exactly one kernel on `stream` (a
+ * hipStream_t, NULL = the null stream), so calls may be captured into a
+ * HIP graph.  A workspace serves one in-flight call at a time; calls that
+ * overlap on the same workspace race.  Calls made one after another on a
+ * stream may share a workspace whatever their shapes.
+ *
+ * Errors.  Functions return a pad_status and never abort.  Only facts
+ * visible on the host are validated (shape fields, pointer presence and
+ * alignment, workspace size).  Device contents are the caller's contract:
+ * block ids in the block table must address existing blocks for every page
+ * a sequence's visible keys touch, and seq_lens[s] <= max_blocks_per_seq *
+ * page_size; violating it is undefined behaviour.  Table entries of pages
+ * no visible key touches (before a window, past a sequence's end, the rows
+ * of length-0 sequences) are never read.
+ */
+#ifndef PAD_ATTN_H
+#define PAD_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PAD_ABI_VERSION 1
+
+typedef enum pad_status {
+  PAD_OK = 0,
+  PAD_EINVAL = 1,        /* a shape field, pointer or alignment is invalid   */
+  PAD_EUNSUPPORTED = 2,  /* valid but not built (e.g. head size 96)          */
+  PAD_EWORKSPACE = 3,    /* workspace missing, misaligned or too small       */
+  PAD_EHIP = 4           /* the HIP runtime reported an error at launch      */
+} pad_status;
+
+/* Element type of q, kv_cache and out (same 0/1 flag as KernelVariant's
+ * dtype field on the rocm_rdna_hip page). */
+typedef enum pad_dtype { PAD_F16 = 0, PAD_BF16 = 1 } pad_dtype;
+
+/* Cache layout codes of KernelVariant.layout (rocm_rdna_hip page). */
+typedef enum pad_layout { PAD_NHD = 0, PAD_HND = 1 } pad_layout;
+
+/* Which kernel family serves a call.  AUTO lets the planner choose; the
+ * others force a family (tuning and tests). */
+typedef enum pad_path { PAD_PATH_AUTO = 0, PAD_PATH_MFMA = 1, PAD_PATH_DOT = 2 } pad_path;
+
+/* Shape of one call.  Every field is host data. */
+typedef struct pad_shape {
+  int32_t num_seqs;           /* S >= 0 (0: the call does nothing)                 */
+  int32_t query_len;          /* M, 1..8 query tokens per sequence               */
+  int32_t num_q_heads;        /* Hq >= 1                                         */
+  int32_t num_kv_heads;       /* Hkv >= 1, divides Hq                            */
+  int32_t head_size;          /* D in {64, 128, 256, 512}                        */
+  int32_t page_size;          /* P >= 16, a multiple of 16                       */
+  int32_t max_blocks_per_seq; /* row stride of block_table, >= 1                 */
+  int32_t max_seq_len;        /* host bound on seq_lens used to plan segments;
+                                 0 = max_blocks_per_seq * page_size. A larger
+                                 device length is still computed correctly.     */
+  int32_t dtype;              /* pad_dtype                                       */
+  int32_t layout;             /* pad_layout                                      */
+  int32_t num_segments;       /* 0 = planner's choice; > 0 forces the split-KV
+                                 segment count per (sequence, kv head)           */
+  int32_t path;               /* pad_path                                        */
+} pad_shape;
+
+/* The launch the planner chose (introspection, tests and tuning). */
+typedef struct pad_plan {
+  int32_t path;              /* PAD_PATH_MFMA or PAD_PATH_DOT                     */
+  int32_t rows;              /* query rows per (sequence, kv head) = G * M        */
+  int32_t row_tiles;         /* rows of one workgroup in 16-row tiles             */
+  int32_t row_groups;        /* workgroups splitting a kv head's rows             */
+  int32_t waves;             /* waves (64 lanes) per workgroup                    */
+  int32_t num_segments;      /* split-KV segments per (sequence, kv head, group)  */
+  int32_t segment_tiles;     /* 16-key tiles per segment (planned)                */
+  int32_t grid_x, grid_y;    /* launch grid                                       */
+  int32_t reserved;
+  uint64_t workspace_bytes;  /* bytes pad_decode_attn needs for this call         */
+} pad_plan;
+
+/* Version of this header the library was built from (PAD_ABI_VERSION). */
+int32_t pad_abi_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* pad_status_string(pad_status status);
+
+/* Plan a call for a device with `num_cus` compute units (> 0).  Pure host
+ * computation; no GPU needed.  `window` >= 0 as in pad_decode_attn. */
+pad_status pad_decode_attn_plan(const pad_shape* shape, int32_t window, int32_t num_cus,
+                                pad_plan* plan);
+
+/* Workspace bytes that serve every call of this shape (any window) on the
+ * current device.  0 means no workspace is needed (a single segment). The
+ * split partials are fp32 (acc[rows][D], m, l per row and segment) plus
+ * one int32 arrival counter per (sequence, kv head, row group), as in
+ * KernelVariant.scratch_shapes. */
+pad_status pad_decode_attn_workspace_size(const pad_shape* shape, size_t* bytes);
+
+/* Zero a workspace of `bytes` bytes (device pointer, 256-byte aligned) on
+ * `stream`.  Needed once after allocation: every pad_decode_attn call
+ * leaves the arrival counters zero again. */
+pad_status pad_decode_attn_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/* Paged-KV decode attention (see the top of this file).  `scale` multiplies
+ * q.k before the softmax (finite); `window` is the sliding window in keys,
+ * 0 for full causal attention.  q, kv_cache and out must be 16-byte
+ * aligned, block_table and seq_lens 4-byte aligned, the workspace 256-byte
+ * aligned with at least pad_decode_attn_workspace_size bytes (it may be
+ * NULL when that size is 0).  out may not alias q or kv_cache. */
+pad_status pad_decode_attn(const pad_shape* shape, const void* q, const void* kv_cache,
+                           const int32_t* block_table, const int32_t* seq_lens, float scale,
+                           int32_t window, void* out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAD_ATTN_H */

@@ -1,0 +1,255 @@
+"""Python binding of libpad_attn.so: paged-KV decode attention on gfx950.
+
+Thin ctypes marshalling over the C ABI declared in ``include/pad_attn.h``;
+the functions keep the C names.  PyTorch supplies device memory and the
+current stream; every step of the computation runs in the library's HIP
+kernels.  Importing this package fails if the library has not been built
+(``python -m paged_kv_decode_block_amd.build``): there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "PAD_OK", "PAD_EINVAL", "PAD_EUNSUPPORTED", "PAD_EWORKSPACE", "PAD_EHIP",
+    "PAD_F16", "PAD_BF16", "PAD_NHD", "PAD_HND",
+    "PAD_PATH_AUTO", "PAD_PATH_MFMA", "PAD_PATH_DOT",
+    "PadError", "pad_shape", "pad_plan", "lib", "LIB_PATH",
+    "pad_abi_version", "pad_status_string", "pad_decode_attn_plan",
+    "pad_decode_attn_workspace_size", "pad_decode_attn_workspace_init", "pad_decode_attn",
+    "make_shape", "Workspace",
+]
+
+PAD_OK, PAD_EINVAL, PAD_EUNSUPPORTED, PAD_EWORKSPACE, PAD_EHIP = 0, 1, 2, 3, 4
+PAD_F16, PAD_BF16 = 0, 1
+PAD_NHD, PAD_HND = 0, 1
+PAD_PATH_AUTO, PAD_PATH_MFMA, PAD_PATH_DOT = 0, 1, 2
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpad_attn.so")
+
+
+class pad_shape(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("query_len", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_size", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
+        ("num_segments", ctypes.c_int32),
+        ("path", ctypes.c_int32),
+    ]
+
+
+class pad_plan(ctypes.Structure):
+    _fields_ = [
+        ("path", ctypes.c_int32),
+        ("rows", ctypes.c_int32),
+        ("row_tiles", ctypes.c_int32),
+        ("row_groups", ctypes.c_int32),
+        ("waves", ctypes.c_int32),
+        ("num_segments", ctypes.c_int32),
+        ("segment_tiles", ctypes.c_int32),
+        ("grid_x", ctypes.c_int32),
+        ("grid_y", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_uint64),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m paged_kv_decode_block_amd.build` "
+            "(the decode-attention path has no non-HIP fallback)"
+        )
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    L.pad_abi_version.restype = ctypes.c_int32
+    L.pad_abi_version.argtypes = []
+    L.pad_status_string.restype = ctypes.c_char_p
+    L.pad_status_string.argtypes = [ctypes.c_int]
+    L.pad_decode_attn_plan.restype = ctypes.c_int
+    L.pad_decode_attn_plan.argtypes = [P(pad_shape), ctypes.c_int32, ctypes.c_int32, P(pad_plan)]
+    L.pad_decode_attn_workspace_size.restype = ctypes.c_int
+    L.pad_decode_attn_workspace_size.argtypes = [P(pad_shape), P(ctypes.c_size_t)]
+    L.pad_decode_attn_workspace_init.restype = ctypes.c_int
+    L.pad_decode_attn_workspace_init.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.pad_decode_attn.restype = ctypes.c_int
+    L.pad_decode_attn.argtypes = [
+        P(pad_shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+    ]
+    return L
+
+
+lib = _load()
+
+
+class PadError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {pad_status_string(status)} (status {status})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != PAD_OK:
+        raise PadError(status, where)
+
+
+def pad_abi_version() -> int:
+    return int(lib.pad_abi_version())
+
+
+def pad_status_string(status: int) -> str:
+    return lib.pad_status_string(int(status)).decode()
+
+
+_DTYPE_CODE = {torch.float16: PAD_F16, torch.bfloat16: PAD_BF16}
+
+
+def make_shape(
+    q: torch.Tensor,
+    kv_cache: torch.Tensor,
+    block_table: torch.Tensor,
+    layout: int,
+    *,
+    max_seq_len: int = 0,
+    num_segments: int = 0,
+    path: int = PAD_PATH_AUTO,
+) -> pad_shape:
+    """The ``pad_shape`` of a call, read off the tensors' sizes."""
+    if q.dim() != 4 or kv_cache.dim() != 5 or block_table.dim() != 2:
+        raise ValueError("expected q [S,M,Hq,D], kv_cache 5-d, block_table [S,max_blocks]")
+    S, M, Hq, D = q.shape
+    if layout == PAD_HND:
+        _, Hkv, P, two, Dk = kv_cache.shape
+    elif layout == PAD_NHD:
+        _, P, Hkv, two, Dk = kv_cache.shape
+    else:
+        raise ValueError(f"unknown layout {layout}")
+    if two != 2 or Dk != D:
+        raise ValueError("kv_cache must hold packed (K, V) slots of the query head size")
+    if q.dtype not in _DTYPE_CODE or kv_cache.dtype != q.dtype:
+        raise ValueError("q and kv_cache must share dtype float16 or bfloat16")
+    if block_table.shape[0] != S:
+        raise ValueError("block_table must have one row per sequence")
+    return pad_shape(
+        num_seqs=S, query_len=M, num_q_heads=Hq, num_kv_heads=Hkv, head_size=D, page_size=P,
+        max_blocks_per_seq=block_table.shape[1], max_seq_len=max_seq_len, dtype=_DTYPE_CODE[q.dtype],
+        layout=layout, num_segments=num_segments, path=path,
+    )
+
+
+def pad_decode_attn_plan(shape: pad_shape, window: int = 0, num_cus: int | None = None) -> dict:
+    """The planner's choice for ``shape`` (pure host computation)."""
+    if num_cus is None:
+        num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    plan = pad_plan()
+    _check(lib.pad_decode_attn_plan(ctypes.byref(shape), int(window), int(num_cus), ctypes.byref(plan)),
+           "pad_decode_attn_plan")
+    return {name: getattr(plan, name) for name, _ in pad_plan._fields_ if name != "reserved"}
+
+
+def pad_decode_attn_workspace_size(shape: pad_shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.pad_decode_attn_workspace_size(ctypes.byref(shape), ctypes.byref(n)),
+           "pad_decode_attn_workspace_size")
+    return int(n.value)
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def pad_decode_attn_workspace_init(workspace: torch.Tensor, stream=None) -> None:
+    _check(lib.pad_decode_attn_workspace_init(
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+        ctypes.c_void_p(_stream_ptr(stream))), "pad_decode_attn_workspace_init")
+
+
+class Workspace:
+    """A zero-initialised device workspace (allocate it outside graph capture).
+
+    ``get(shape)`` returns a buffer of at least the bytes ``shape`` needs,
+    growing (and re-zeroing) it when a larger shape comes along.
+    """
+
+    def __init__(self, device=None):
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        self.buf: torch.Tensor | None = None
+
+    def get(self, shape: pad_shape) -> torch.Tensor | None:
+        need = pad_decode_attn_workspace_size(shape)
+        if need == 0:
+            return self.buf
+        if self.buf is None or self.buf.numel() < need:
+            self.buf = torch.empty(need, dtype=torch.uint8, device=self.device)
+            pad_decode_attn_workspace_init(self.buf)
+        return self.buf
+
+
+_default_ws: dict[int, Workspace] = {}
+
+
+def pad_decode_attn(
+    q: torch.Tensor,
+    kv_cache: torch.Tensor,
+    block_table: torch.Tensor,
+    seq_lens: torch.Tensor,
+    scale: float,
+    window: int,
+    out: torch.Tensor,
+    *,
+    layout: int = PAD_HND,
+    workspace: torch.Tensor | None = None,
+    max_seq_len: int = 0,
+    num_segments: int = 0,
+    path: int = PAD_PATH_AUTO,
+    stream=None,
+) -> torch.Tensor:
+    """Paged-KV decode attention into ``out`` (see include/pad_attn.h).
+
+    ``workspace`` must be a zero-initialised device buffer of at least
+    ``pad_decode_attn_workspace_size`` bytes; when omitted, a per-device
+    buffer is kept by this module (allocated on first use, so make one call
+    before capturing a graph).
+    """
+    for name, t in (("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
+                    ("seq_lens", seq_lens), ("out", out)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q's shape and dtype")
+    if seq_lens.shape != (q.shape[0],):
+        raise ValueError("seq_lens must have one entry per sequence")
+    shape = make_shape(q, kv_cache, block_table, layout, max_seq_len=max_seq_len,
+                       num_segments=num_segments, path=path)
+    if workspace is None:
+        dev = q.device.index
+        ws = _default_ws.setdefault(dev, Workspace(q.device)).get(shape)
+    else:
+        ws = workspace
+    ws_ptr = ws.data_ptr() if ws is not None else 0
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib.pad_decode_attn(
+        ctypes.byref(shape), ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kv_cache.data_ptr()),
+        ctypes.c_void_p(block_table.data_ptr()), ctypes.c_void_p(seq_lens.data_ptr()),
+        ctypes.c_float(scale), ctypes.c_int32(window), ctypes.c_void_p(out.data_ptr()),
+        ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(_stream_ptr(stream)),
+    ), "pad_decode_attn")
+    return out

@@ -1,0 +1,61 @@
+"""Build libpad_attn.so (HIP kernels for gfx950 plus the C ABI) in-tree.
+
+Run as ``python -m paged_kv_decode_block_amd.build`` or through
+``__graft_entry__.build()``.  hipcc cross-compiles for gfx950 without a GPU.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libpad_attn.so")
+SOURCES = ["decode_mfma.hip", "plan.cpp", "api.cpp"]
+
+# Packed fp32 VALU ops are turned off for every HIP source (the host pass
+# reports the feature as unknown; that warning is harmless).
+HIP_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libpad_attn.so)")
+
+
+def build(verbose: bool = False) -> str:
+    cc = hipcc()
+    tmp = LIB + ".tmp"
+    cmd = [cc, *HIP_FLAGS, "-shared", "-o", tmp]
+    for src in SOURCES:
+        path = os.path.join(CSRC, src)
+        # .cpp files hold host code only; compile them as HIP too so one
+        # hipcc line links everything against the HIP runtime.
+        cmd += (["-x", "hip"] if src.endswith(".cpp") else []) + [path]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    errs = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
+    if errs.strip() and verbose:
+        print(errs, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

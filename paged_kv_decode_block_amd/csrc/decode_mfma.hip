@@ -1,0 +1,467 @@
+// Paged-KV decode / speculative-verify attention for gfx950 (CDNA4).
+//
+// One workgroup serves one (sequence, kv head, row group, KV segment): it
+// packs the G*M query rows of the kv head into 16-row MFMA tiles so the
+// kv head's K/V pages are read once for all of them, walks its segment's
+// 16-key tiles, and either writes the output directly (one segment) or
+// writes a partial (acc, m, l) that the last segment to arrive merges
+// (ROCm/vllm pull request 1330, "Summary"; split partials and counters as
+// in KernelVariant.scratch_shapes / make_scratch on the rocm_rdna_hip
+// page).
+//
+// Inside a workgroup the four waves take interleaved tiles of the
+// segment, each with its own online-softmax state over all rows, and are
+// combined through LDS at the end.  Per 16-key tile a wave:
+//   * loads the K and V rows of the tile straight into registers with
+//     16-byte loads (lane = key c, 8 consecutive head-dim elements);
+//   * computes S^T = K Q^T with v_mfma_f32_16x16x32_{bf16,f16}: K is the
+//     A operand as loaded, the query tile is the B operand, and the result
+//     leaves each lane with 4 keys of one query row (row = lane % 16), so
+//     row max and sum need only the 4 lane groups (two cross-lane steps);
+//   * stages V in LDS and reads it back transposed (4 keys of one head-dim
+//     column per lane) as the A operand of v_mfma_f32_16x16x16 for
+//     O^T += V^T P^T, whose B operand (P in the input dtype) is exactly the
+//     softmax lane layout -- no shuffle of P is needed.
+// Logits live in the exp2 domain (scale * log2 e folded in).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+
+namespace pad {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<__bf16> {
+  typedef __bf16 x8 __attribute__((ext_vector_type(8)));
+  typedef short x4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f32x4 qk(i32x4 a, i32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(x8, a), __builtin_bit_cast(x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(uint64_t a, uint64_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(x4, a), __builtin_bit_cast(x4, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint16_t bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x)); }
+};
+
+template <>
+struct Mfma<_Float16> {
+  typedef _Float16 x8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 x4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f32x4 qk(i32x4 a, i32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(x8, a), __builtin_bit_cast(x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(uint64_t a, uint64_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(x4, a), __builtin_bit_cast(x4, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint16_t bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); }
+};
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kNW = kWaves;
+constexpr int kThreads = kNW * 64;
+// Cross-segment merge weights held in LDS (segments x rows of a workgroup).
+constexpr int kMergeWeights = kMaxMergeWeights;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint64_t pack4(uint16_t a, uint16_t b, uint16_t c, uint16_t d) {
+  return uint64_t(a) | (uint64_t(b) << 16) | (uint64_t(c) << 32) | (uint64_t(d) << 48);
+}
+
+template <int D, int RT>
+struct Lds {
+  static constexpr int kVStride = D + 8;  // bf16/f16 elements per staged V row (16-byte padded)
+  static constexpr int kAccStride = D + 4;  // floats per merged accumulator row
+  static constexpr int kVBytes = kNW * 16 * kVStride * 2;
+  static constexpr int kMergeBytes = (2 * kNW * RT * 16 + 2 * RT * 16) * 4 + RT * 16 * kAccStride * 4;
+  static constexpr int kFinalBytes = (kMergeWeights + RT * 16) * 4;
+  static constexpr int kBytes0 = kVBytes > kMergeBytes ? kVBytes : kMergeBytes;
+  static constexpr int kBytes = (kBytes0 > kFinalBytes ? kBytes0 : kFinalBytes) + 16;
+};
+
+// Write zeros to the output rows [row0, row0 + nrows) of (s, kvh).
+template <typename T, int D>
+__device__ void zero_rows(const Params& p, int s, int kvh, int row0, int nrows) {
+  T* out = static_cast<T*>(p.out);
+  const int items = nrows * (D / 8);
+  for (int it = threadIdx.x; it < items; it += kThreads) {
+    const int r = it / (D / 8), d8 = it % (D / 8);
+    const int ru = row0 + r, m = ru / p.group, gq = ru % p.group;
+    T* dst = out + ((int64_t(s) * p.query_len + m) * p.num_q_heads + kvh * p.group + gq) * D + 8 * d8;
+    *reinterpret_cast<i32x4*>(dst) = i32x4{0, 0, 0, 0};
+  }
+}
+
+template <typename T, int D, int RT>
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p) {
+  using MF = Mfma<T>;
+  using LD = Lds<D, RT>;
+  constexpr int KC = D / 32;  // 32-wide head-dim chunks (QK^T MFMA steps)
+  constexpr int DT = D / 16;  // 16-wide head-dim tiles of the output
+  constexpr bool kPrefetch = D <= 256;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[LD::kBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int s = blockIdx.y;
+  const int units = p.num_kv_heads * p.row_groups;
+  const int unit = blockIdx.x % units;
+  const int seg = blockIdx.x / units;
+  const int kvh = unit % p.num_kv_heads;
+  const int rg = unit / p.num_kv_heads;
+  const int row0 = rg * RT * 16;
+  const int wg_rows = min(RT * 16, p.rows - row0);
+  const int M = p.query_len;
+
+  const int L = p.seq_lens[s];
+  if (L <= 0) {
+    if (seg == 0) zero_rows<T, D>(p, s, kvh, row0, wg_rows);
+    return;
+  }
+  const int k_lo = p.window > 0 ? max(0, L - M - p.window + 1) : 0;
+  const int t_lo = k_lo >> 4, t_hi = (L + 15) >> 4;
+  const int n_tiles = t_hi - t_lo;
+  const int seg_tiles = max(p.seg_tiles, (n_tiles + p.nseg - 1) / p.nseg);
+  const int n_live = (n_tiles + seg_tiles - 1) / seg_tiles;
+  if (seg >= n_live) return;
+  const int ts = t_lo + seg * seg_tiles, te = min(ts + seg_tiles, t_hi);
+  // Tiles needing no mask: every key visible to every row.
+  const int lo_last = p.window > 0 ? max(0, L - p.window) : 0;
+  const int qpos_first = L - M;
+
+  // Per-lane query row (row = lane % 16 of each row tile): position and
+  // window start; rows past G*M see nothing.
+  int qpos_r[RT], lo_r[RT];
+  i32x4 qop[RT][KC];
+  const T* Q = static_cast<const T*>(p.q);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int ru = row0 + rt * 16 + c;
+    if (ru < p.rows) {
+      const int m = ru / p.group, gq = ru % p.group;
+      qpos_r[rt] = L - M + m;
+      lo_r[rt] = p.window > 0 ? max(0, qpos_r[rt] - p.window + 1) : 0;
+      const T* qrow = Q + ((int64_t(s) * M + m) * p.num_q_heads + kvh * p.group + gq) * D;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) qop[rt][kc] = *reinterpret_cast<const i32x4*>(qrow + 32 * kc + 8 * g);
+    } else {
+      qpos_r[rt] = -1;
+      lo_r[rt] = 0;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) qop[rt][kc] = i32x4{0, 0, 0, 0};
+    }
+  }
+
+  float m_run[RT], l_run[RT];
+  f32x4 acc[RT][DT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m_run[rt] = kNegInf;
+    l_run[rt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const T* KV = static_cast<const T*>(p.kv);
+  const int32_t* table = p.block_table + int64_t(s) * p.max_blocks;
+  const int64_t head_off = int64_t(kvh) * p.head_stride;
+  uint16_t* vs = reinterpret_cast<uint16_t*>(lds) + wave * 16 * LD::kVStride;
+
+  struct Tile {
+    i32x4 k[KC];
+    i32x4 v[KC];
+  };
+
+  auto load_tile = [&](Tile& tl, int t) {
+    const int key0 = t * 16;
+    const int blk = table[key0 / p.page_size];
+    const T* row = KV + int64_t(blk) * p.block_stride + head_off + int64_t(key0 % p.page_size + c) * p.token_stride;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) tl.k[kc] = *reinterpret_cast<const i32x4*>(row + 32 * kc + 8 * g);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) tl.v[kc] = *reinterpret_cast<const i32x4*>(row + D + 32 * kc + 8 * g);
+  };
+
+  auto compute_tile = [&](Tile& tl, int t) {
+    const int key0 = t * 16;
+    const bool edge = !(key0 >= lo_last && key0 + 15 <= qpos_first);
+    if (edge) {
+      // Keys outside [k_lo, L) may hold anything (even NaN); they must not
+      // reach the PV product, where 0 * NaN would poison the sum.
+      const int key = key0 + c;
+      if (key < k_lo || key >= L) {
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) tl.v[kc] = i32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      *reinterpret_cast<i32x4*>(vs + c * LD::kVStride + 32 * kc + 8 * g) = tl.v[kc];
+
+    uint64_t pb[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) sc = MF::qk(tl.k[kc], qop[rt][kc], sc);
+      float x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = sc[j] * p.scale_log2;
+        if (edge) {
+          const int key = key0 + 4 * g + j;
+          if (key < lo_r[rt] || key > qpos_r[rt]) x[j] = kNegInf;
+        }
+      }
+      float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run[rt], tmax);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[rt] - m_use);
+      float pj[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pj[j] = fast_exp2(x[j] - m_use);
+      l_run[rt] = l_run[rt] * alpha + ((pj[0] + pj[1]) + (pj[2] + pj[3]));
+      m_run[rt] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
+      pb[rt] = pack4(MF::bits(pj[0]), MF::bits(pj[1]), MF::bits(pj[2]), MF::bits(pj[3]));
+    }
+
+    // The staged V rows were written by other lanes of this wave; LDS
+    // operations of a wave complete in order, the fences keep the compiler
+    // from moving the reads above the writes.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint16_t* col = vs + 4 * g * LD::kVStride + 16 * dt + c;
+      const uint64_t va = pack4(col[0], col[LD::kVStride], col[2 * LD::kVStride], col[3 * LD::kVStride]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt][dt] = MF::pv(va, pb[rt], acc[rt][dt]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // Interleaved tiles per wave; the next tile's loads are issued before the
+  // current tile is computed.
+  int t = ts + wave;
+  if constexpr (kPrefetch) {
+    Tile ta, tb;
+    if (t < te) load_tile(ta, t);
+    while (t < te) {
+      if (t + kNW < te) load_tile(tb, t + kNW);
+      compute_tile(ta, t);
+      t += kNW;
+      if (t >= te) break;
+      if (t + kNW < te) load_tile(ta, t + kNW);
+      compute_tile(tb, t);
+      t += kNW;
+    }
+  } else {
+    Tile ta;
+    for (; t < te; t += kNW) {
+      load_tile(ta, t);
+      compute_tile(ta, t);
+    }
+  }
+
+  // ---- combine the four waves (fixed order: bitwise deterministic) ----
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    l_run[rt] += __shfl_xor(l_run[rt], 16);
+    l_run[rt] += __shfl_xor(l_run[rt], 32);
+  }
+  __syncthreads();  // V staging area is reused below
+  float* sm_m = reinterpret_cast<float*>(lds);   // [NW][RT*16]
+  float* sm_l = sm_m + kNW * RT * 16;            // [NW][RT*16]
+  float* sm_ms = sm_l + kNW * RT * 16;           // [RT*16] merged max
+  float* sm_ls = sm_ms + RT * 16;                // [RT*16] merged sum
+  float* sm_acc = sm_ls + RT * 16;               // [RT*16][kAccStride]
+  if (g == 0) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      sm_m[wave * RT * 16 + rt * 16 + c] = m_run[rt];
+      sm_l[wave * RT * 16 + rt * 16 + c] = l_run[rt];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = rt * 16 + c;
+    float ms = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) ms = fmaxf(ms, sm_m[w * RT * 16 + r]);
+    const float mu = ms == kNegInf ? 0.f : ms;
+    float ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) ls += sm_l[w * RT * 16 + r] * fast_exp2(sm_m[w * RT * 16 + r] - mu);
+    const float f = fast_exp2(m_run[rt] - mu);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= f;
+    if (wave == 0 && g == 0) {
+      sm_ms[r] = ms;
+      sm_ls[r] = ls;
+    }
+  }
+#pragma unroll
+  for (int w = 0; w < kNW; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          f32x4* dst = reinterpret_cast<f32x4*>(sm_acc + (rt * 16 + c) * LD::kAccStride + 16 * dt + 4 * g);
+          if (w == 0)
+            *dst = acc[rt][dt];
+          else
+            *dst += acc[rt][dt];
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  T* out = static_cast<T*>(p.out);
+  auto out_row = [&](int ru) {
+    const int m = ru / p.group, gq = ru % p.group;
+    return out + ((int64_t(s) * M + m) * p.num_q_heads + kvh * p.group + gq) * D;
+  };
+
+  if (n_live == 1) {
+    for (int it = tid; it < wg_rows * (D / 8); it += kThreads) {
+      const int r = it / (D / 8), d8 = it % (D / 8);
+      const float ls = sm_ls[r];
+      const float inv = ls > 0.f ? 1.f / ls : 0.f;
+      const float* a = sm_acc + r * LD::kAccStride + 8 * d8;
+      uint16_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = MF::bits(a[e] * inv);
+      i32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = int(uint32_t(h[2 * e]) | (uint32_t(h[2 * e + 1]) << 16));
+      *reinterpret_cast<i32x4*>(out_row(row0 + r) + 8 * d8) = v;
+    }
+    return;
+  }
+
+  // ---- split-KV partial and arrival ----
+  const int64_t slot0 = (int64_t(s) * p.num_kv_heads + kvh) * p.nseg;
+  {
+    const int64_t base = (slot0 + seg) * p.rows + row0;
+    for (int it = tid; it < wg_rows * (D / 4); it += kThreads) {
+      const int r = it / (D / 4), d4 = it % (D / 4);
+      *reinterpret_cast<f32x4*>(p.ws_acc + (base + r) * D + 4 * d4) =
+          *reinterpret_cast<const f32x4*>(sm_acc + r * LD::kAccStride + 4 * d4);
+    }
+    for (int r = tid; r < wg_rows; r += kThreads) {
+      p.ws_ml[(base + r) * 2 + 0] = sm_ms[r];
+      p.ws_ml[(base + r) * 2 + 1] = sm_ls[r];
+    }
+  }
+  int* counter = p.ws_cnt + (int64_t(s) * p.num_kv_heads + kvh) * p.row_groups + rg;
+  __threadfence();  // release this thread's partial writes at device scope
+  __syncthreads();
+  int* sm_flag = reinterpret_cast<int*>(lds + LD::kBytes - 16);
+  if (tid == 0) *sm_flag = atomicAdd(counter, 1) == n_live - 1;
+  __syncthreads();
+  if (!*sm_flag) return;
+  __threadfence();  // acquire the other segments' partials
+
+  // ---- last arriver: log-sum-exp merge of all live segments ----
+  float* sm_w = reinterpret_cast<float*>(lds);       // [n_live][wg_rows]
+  float* sm_lt = sm_w + kMergeWeights;                 // [wg_rows]
+  for (int r = tid; r < wg_rows; r += kThreads) {
+    float ms = kNegInf;
+    for (int j = 0; j < n_live; ++j) ms = fmaxf(ms, p.ws_ml[((slot0 + j) * p.rows + row0 + r) * 2]);
+    const float mu = ms == kNegInf ? 0.f : ms;
+    float ls = 0.f;
+    for (int j = 0; j < n_live; ++j) {
+      const float* ml = p.ws_ml + ((slot0 + j) * p.rows + row0 + r) * 2;
+      const float w = fast_exp2(ml[0] - mu);
+      sm_w[j * wg_rows + r] = w;
+      ls += w * ml[1];
+    }
+    sm_lt[r] = ls;
+  }
+  __syncthreads();
+  for (int it = tid; it < wg_rows * (D / 4); it += kThreads) {
+    const int r = it / (D / 4), d4 = it % (D / 4);
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    const float* src = p.ws_acc + ((slot0)*p.rows + row0 + r) * D + 4 * d4;
+    const int64_t jstride = int64_t(p.rows) * D;
+    for (int j = 0; j < n_live; ++j) a += sm_w[j * wg_rows + r] * *reinterpret_cast<const f32x4*>(src + j * jstride);
+    const float ls = sm_lt[r];
+    const float inv = ls > 0.f ? 1.f / ls : 0.f;
+    uint2 v;
+    v.x = uint32_t(MF::bits(a[0] * inv)) | (uint32_t(MF::bits(a[1] * inv)) << 16);
+    v.y = uint32_t(MF::bits(a[2] * inv)) | (uint32_t(MF::bits(a[3] * inv)) << 16);
+    *reinterpret_cast<uint2*>(out_row(row0 + r) + 4 * d4) = v;
+  }
+  if (tid == 0) *counter = 0;  // leave the counter zeroed for the next launch
+}
+
+__global__ void zero_kernel(uint32_t* p, size_t n) {
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
+template <typename T, int D, int RT>
+int launch_t(const Plan& pl, const Params& pr, hipStream_t st) {
+  hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT>), dim3(pl.grid_x, pl.grid_y), dim3(kThreads), 0, st, pr);
+  return int(hipGetLastError());
+}
+
+template <typename T, int D>
+int launch_d(const Plan& pl, const Params& pr, hipStream_t st) {
+  switch (pl.row_tiles) {
+    case 1: return launch_t<T, D, 1>(pl, pr, st);
+    case 2: if constexpr (D <= 256) return launch_t<T, D, 2>(pl, pr, st); break;
+    case 3: if constexpr (D <= 128) return launch_t<T, D, 3>(pl, pr, st); break;
+    case 4: if constexpr (D <= 128) return launch_t<T, D, 4>(pl, pr, st); break;
+  }
+  return int(hipErrorInvalidValue);
+}
+
+template <typename T>
+int launch_dtype(const Plan& pl, const Params& pr, int head_size, hipStream_t st) {
+  switch (head_size) {
+    case 64: return launch_d<T, 64>(pl, pr, st);
+    case 128: return launch_d<T, 128>(pl, pr, st);
+    case 256: return launch_d<T, 256>(pl, pr, st);
+    case 512: return launch_d<T, 512>(pl, pr, st);
+  }
+  return int(hipErrorInvalidValue);
+}
+
+}  // namespace
+
+int launch_decode(const Plan& plan, const Params& params, int dtype, int head_size, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == PAD_BF16) return launch_dtype<__bf16>(plan, params, head_size, st);
+  return launch_dtype<_Float16>(plan, params, head_size, st);
+}
+
+int launch_zero(void* ptr, size_t words, void* stream) {
+  if (words == 0) return 0;
+  const size_t blocks = (words + 255) / 256;
+  const unsigned grid = unsigned(blocks < 1024 ? blocks : 1024);
+  hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<uint32_t*>(ptr), words);
+  return int(hipGetLastError());
+}
+
+}  // namespace pad

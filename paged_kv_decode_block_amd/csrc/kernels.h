@@ -1,0 +1,39 @@
+// Device-side parameters and launchers of the decode-attention kernels.
+#pragma once
+
+#include <cstdint>
+
+#include "plan.h"
+
+namespace pad {
+
+// Everything a decode-attention workgroup needs; passed by value.
+struct Params {
+  const void* q;              // [S, M, Hq, D]
+  const void* kv;             // packed K+V cache (HND or NHD)
+  const int32_t* block_table; // [S, max_blocks]
+  const int32_t* seq_lens;    // [S]
+  void* out;                  // [S, M, Hq, D]
+  int32_t* ws_cnt;            // arrival counters [S, Hkv, row_groups]
+  float* ws_ml;               // partial (m, l) [S, Hkv, nseg, rows, 2]
+  float* ws_acc;              // partial acc     [S, Hkv, nseg, rows, D]
+  int64_t block_stride;       // elements between physical blocks
+  int64_t head_stride;        // elements between kv heads of a block
+  int64_t token_stride;       // elements between tokens of a block
+  int32_t num_seqs, query_len, num_q_heads, num_kv_heads, group, page_size, max_blocks;
+  int32_t rows;               // G * M query rows per (sequence, kv head)
+  int32_t window;             // 0 = full causal
+  int32_t nseg;               // segments per (sequence, kv head, row group)
+  int32_t seg_tiles;          // planned 16-key tiles per segment
+  int32_t row_groups;         // workgroups splitting the rows
+  float scale_log2;           // scale * log2(e): logits are kept in the exp2 domain
+};
+
+// Enqueue the decode kernel the plan selects.  Returns a HIP error code
+// (0 = success).
+int launch_decode(const Plan& plan, const Params& params, int dtype, int head_size, void* stream);
+
+// Enqueue a fill of `words` 32-bit zeros at `ptr`.
+int launch_zero(void* ptr, size_t words, void* stream);
+
+}  // namespace pad

@@ -1,0 +1,105 @@
+// Host-side launch planning (see plan.h).
+#include "plan.h"
+
+#include <algorithm>
+
+namespace pad {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool known_head_size(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
+
+}  // namespace
+
+int max_row_tiles(int head_size) {
+  // The fp32 accumulator of one 16-row tile costs head_size/4 registers per
+  // lane; keep it at or below 128 per wave.
+  return std::max(1, std::min(4, 512 / head_size));
+}
+
+pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
+  if (sh.num_seqs < 0 || sh.query_len < 1 || sh.num_q_heads < 1 || sh.num_kv_heads < 1 ||
+      sh.head_size < 1 || sh.page_size < 1 || sh.max_blocks_per_seq < 1 || sh.max_seq_len < 0 ||
+      sh.num_segments < 0 || window < 0 || num_cus < 1)
+    return PAD_EINVAL;
+  if (sh.num_q_heads % sh.num_kv_heads != 0) return PAD_EINVAL;
+  if (sh.dtype != PAD_F16 && sh.dtype != PAD_BF16) return PAD_EINVAL;
+  if (sh.layout != PAD_NHD && sh.layout != PAD_HND) return PAD_EINVAL;
+  if (sh.path < PAD_PATH_AUTO || sh.path > PAD_PATH_DOT) return PAD_EINVAL;
+  const int64_t table_keys = int64_t(sh.max_blocks_per_seq) * sh.page_size;
+  if (sh.max_seq_len > table_keys) return PAD_EINVAL;
+  // Decode and speculative verify only (M <= 8); other head sizes and page
+  // sizes that are not multiples of the 16-key tile are not built.
+  if (sh.query_len > 8 || !known_head_size(sh.head_size) || sh.page_size % kTileKeys != 0)
+    return PAD_EUNSUPPORTED;
+  if (sh.num_seqs > 65535) return PAD_EUNSUPPORTED;
+  const int G = sh.num_q_heads / sh.num_kv_heads;
+  const int rows = G * sh.query_len;
+  if (rows > 1024) return PAD_EUNSUPPORTED;
+  if (sh.path == PAD_PATH_DOT) return PAD_EUNSUPPORTED;  // dot-product family not built yet
+
+  Plan p{};
+  p.path = PAD_PATH_MFMA;
+  p.rows = rows;
+  p.waves = kWaves;
+  const int tiles_total = int(ceil_div(rows, 16));
+  int rt = std::min(tiles_total, max_row_tiles(sh.head_size));
+  p.row_groups = int(ceil_div(tiles_total, rt));
+  p.row_tiles = int(ceil_div(tiles_total, p.row_groups));
+
+  // Keys one unit may have to read: the whole table bound, or the window
+  // span (window + M - 1 keys) plus one tile of alignment slack.
+  const int64_t max_len = sh.max_seq_len ? sh.max_seq_len : table_keys;
+  int64_t span = max_len;
+  int64_t span_tiles;
+  if (window > 0) {
+    span = std::min<int64_t>(max_len, int64_t(window) + sh.query_len - 1);
+    span_tiles = ceil_div(span, kTileKeys) + 1;
+  } else {
+    span_tiles = ceil_div(span, kTileKeys);
+  }
+  span_tiles = std::max<int64_t>(1, span_tiles);
+
+  const int64_t units = int64_t(sh.num_seqs) * sh.num_kv_heads * p.row_groups;
+  const int resident = (sh.head_size * p.row_tiles <= 128) ? 2 : 1;  // workgroups per CU
+  const int64_t slots = int64_t(num_cus) * resident;
+  int64_t nseg;
+  if (sh.num_segments > 0) {
+    nseg = sh.num_segments;
+  } else {
+    // One full round of workgroups for a single sequence; two rounds when a
+    // batch's lengths may differ, so short sequences leave no idle CUs.
+    const int64_t target = sh.num_seqs > 1 ? 2 * slots : slots;
+    nseg = std::max<int64_t>(1, target / std::max<int64_t>(1, units));
+    nseg = std::min<int64_t>(nseg, std::max<int64_t>(1, span_tiles / 4));  // >= 64 keys each
+  }
+  nseg = std::min<int64_t>(nseg, span_tiles);
+  nseg = std::min<int64_t>(nseg, kMaxSegments);
+  nseg = std::min<int64_t>(nseg, kMaxMergeWeights / (p.row_tiles * 16));
+  nseg = std::max<int64_t>(1, nseg);
+  p.seg_tiles = int(ceil_div(span_tiles, nseg));
+  p.nseg = int(ceil_div(span_tiles, p.seg_tiles));
+
+  p.grid_x = p.nseg * sh.num_kv_heads * p.row_groups;
+  p.grid_y = std::max(1, sh.num_seqs);
+
+  if (p.nseg > 1) {
+    const size_t S = size_t(sh.num_seqs), H = size_t(sh.num_kv_heads);
+    const size_t slots_rows = S * H * size_t(p.nseg) * size_t(rows);
+    p.ws_counters = 0;
+    p.ws_ml = align_up(S * H * size_t(p.row_groups) * sizeof(int32_t));
+    p.ws_acc = p.ws_ml + align_up(slots_rows * 2 * sizeof(float));
+    p.ws_bytes = p.ws_acc + align_up(slots_rows * size_t(sh.head_size) * sizeof(float));
+  } else {
+    p.ws_counters = p.ws_ml = p.ws_acc = p.ws_bytes = 0;
+  }
+  *pl = p;
+  return PAD_OK;
+}
+
+}  // namespace pad

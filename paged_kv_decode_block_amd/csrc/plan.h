@@ -1,0 +1,46 @@
+// Host-side launch planning for paged-KV decode attention.
+//
+// A "unit" is one (sequence, kv head) pair: all G*M query rows of the kv
+// head share one read of its K/V pages (ROCm/vllm pull request 1330,
+// "Summary": one workgroup per kv head, row group and KV segment).  The
+// key range of a unit is split into segments; each segment is one
+// workgroup whose partial (acc, m, l) is merged in-kernel by the last
+// segment to arrive.  The planner picks the row tiling (16-row MFMA tiles,
+// the rows_padded rule of KernelVariant on the rocm_rdna_hip page), the
+// number of segments (enough workgroups to fill the device, cf. the
+// split cap of 256 "to fill its CUs with one query" of _mid_o_shape on the
+// rocm_octave_attn page) and the workspace layout.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/pad_attn.h"
+
+namespace pad {
+
+constexpr int kTileKeys = 16;    // keys per MFMA tile (page sizes are multiples of 16)
+constexpr int kWaves = 4;        // waves per workgroup
+constexpr int kMaxSegments = 256;
+constexpr int kMaxMergeWeights = 4096;  // LDS floats for merge weights (segments x rows)
+
+struct Plan {
+  int path;          // PAD_PATH_MFMA / PAD_PATH_DOT
+  int rows;          // G*M rows per unit
+  int row_tiles;     // 16-row tiles handled by each workgroup (per wave)
+  int row_groups;    // workgroups splitting a unit's rows
+  int waves;         // waves per workgroup
+  int nseg;          // segments per (unit, row group)
+  int seg_tiles;     // planned tiles per segment
+  int grid_x, grid_y;
+  // Workspace layout (byte offsets; all 256-byte aligned).
+  size_t ws_counters, ws_ml, ws_acc, ws_bytes;
+};
+
+// Validates the shape fields (not pointers) and fills `plan`.
+pad_status make_plan(const pad_shape& shape, int window, int num_cus, Plan* plan);
+
+// Largest row tiles per wave that fit the accumulator budget at head size D.
+int max_row_tiles(int head_size);
+
+}  // namespace pad

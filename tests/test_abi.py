@@ -1,0 +1,188 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol,
+plans shapes and rejects invalid calls before touching a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_decode_block_amd as pad
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pad_attn.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pad_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert "pad_decode_attn" in names and "pad_decode_attn_workspace_size" in names
+    lib = ctypes.CDLL(pad.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"libpad_attn.so does not export {n}"
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define PAD_ABI_VERSION (\d+)", open(HEADER).read())
+    assert pad.pad_abi_version() == int(m.group(1))
+
+
+def test_status_strings():
+    for code in range(5):
+        assert pad.pad_status_string(code) and pad.pad_status_string(code) != "unknown status"
+    assert pad.pad_status_string(77) == "unknown status"
+
+
+def shape(**kw):
+    base = dict(num_seqs=1, query_len=4, num_q_heads=32, num_kv_heads=8, head_size=128, page_size=16,
+                max_blocks_per_seq=2048, max_seq_len=0, dtype=pad.PAD_BF16, layout=pad.PAD_HND,
+                num_segments=0, path=0)
+    base.update(kw)
+    return pad.pad_shape(**base)
+
+
+def plan(sh, window=0, cus=256):
+    return pad.pad_decode_attn_plan(sh, window, cus)
+
+
+def _align(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize(
+    "kw",
+    [
+        dict(),
+        dict(query_len=1),
+        dict(num_q_heads=4, num_kv_heads=1, head_size=64, max_blocks_per_seq=16, dtype=pad.PAD_F16),
+        dict(num_q_heads=8, num_kv_heads=2, head_size=256, page_size=32, max_blocks_per_seq=512, layout=pad.PAD_NHD),
+        dict(num_q_heads=16, num_kv_heads=2, head_size=512, page_size=32, max_blocks_per_seq=1024, query_len=8),
+        dict(num_seqs=65, num_q_heads=16, num_kv_heads=2, head_size=256, page_size=1056, max_blocks_per_seq=16),
+    ],
+)
+def test_plan_invariants(kw):
+    sh = shape(**kw)
+    p = plan(sh)
+    G = sh.num_q_heads // sh.num_kv_heads
+    rows = G * sh.query_len
+    assert p["rows"] == rows
+    # 16-row tiles per workgroup times workgroups per kv head cover the rows
+    assert p["row_tiles"] * p["row_groups"] * 16 >= rows
+    assert (p["row_tiles"] - 1) * p["row_groups"] * 16 < rows
+    keys = sh.max_blocks_per_seq * sh.page_size
+    tiles = -(-keys // 16)
+    assert p["num_segments"] * p["segment_tiles"] >= tiles
+    assert (p["num_segments"] - 1) * p["segment_tiles"] < tiles
+    assert 1 <= p["num_segments"] <= 256
+    assert p["grid_x"] == p["num_segments"] * sh.num_kv_heads * p["row_groups"]
+    assert p["grid_y"] == sh.num_seqs
+    if p["num_segments"] == 1:
+        assert p["workspace_bytes"] == 0
+    else:
+        S, H, n = sh.num_seqs, sh.num_kv_heads, p["num_segments"]
+        want = _align(S * H * p["row_groups"] * 4) + _align(S * H * n * rows * 2 * 4) + _align(
+            S * H * n * rows * sh.head_size * 4)
+        assert p["workspace_bytes"] == want
+
+
+def test_plan_fills_device():
+    # batch 1, 8 kv heads, long context: enough workgroups for every CU
+    p = plan(shape(), cus=256)
+    assert p["grid_x"] * p["grid_y"] >= 256
+
+
+def test_forced_segments():
+    for n in (1, 2, 7, 256):
+        p = plan(shape(num_segments=n, max_blocks_per_seq=64))
+        tiles = 64  # 1024 keys / 16
+        assert p["num_segments"] <= n
+        assert p["num_segments"] * p["segment_tiles"] >= tiles
+        if n <= tiles:
+            assert p["num_segments"] == -(-tiles // -(-tiles // n))
+
+
+def test_window_plan_is_smaller():
+    full = plan(shape(max_blocks_per_seq=1024))
+    win = plan(shape(max_blocks_per_seq=1024), window=512)
+    assert win["workspace_bytes"] <= full["workspace_bytes"]
+    assert win["num_segments"] * win["segment_tiles"] * 16 >= 512 + 4 - 1 + 15
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(query_len=0), pad.PAD_EINVAL),
+        (dict(query_len=9), pad.PAD_EUNSUPPORTED),
+        (dict(head_size=96), pad.PAD_EUNSUPPORTED),
+        (dict(head_size=0), pad.PAD_EINVAL),
+        (dict(page_size=8), pad.PAD_EUNSUPPORTED),
+        (dict(page_size=24), pad.PAD_EUNSUPPORTED),
+        (dict(num_q_heads=30), pad.PAD_EINVAL),
+        (dict(num_kv_heads=0), pad.PAD_EINVAL),
+        (dict(dtype=2), pad.PAD_EINVAL),
+        (dict(layout=5), pad.PAD_EINVAL),
+        (dict(max_seq_len=2048 * 16 + 1), pad.PAD_EINVAL),
+        (dict(num_segments=-1), pad.PAD_EINVAL),
+        (dict(path=3), pad.PAD_EINVAL),
+        (dict(num_seqs=-1), pad.PAD_EINVAL),
+        (dict(max_blocks_per_seq=0), pad.PAD_EINVAL),
+    ],
+)
+def test_plan_rejects(kw, status):
+    with pytest.raises(pad.PadError) as e:
+        plan(shape(**kw))
+    assert e.value.status == status
+
+
+def test_plan_rejects_bad_window_and_cus():
+    with pytest.raises(pad.PadError):
+        plan(shape(), window=-1)
+    with pytest.raises(pad.PadError):
+        plan(shape(), cus=0)
+
+
+def _call(sh, q=0x1000, kv=0x2000, bt=0x3000, sl=0x4000, out=0x5000, scale=1.0, window=0, ws=None, ws_bytes=0):
+    P = ctypes.c_void_p
+    return pad.lib.pad_decode_attn(ctypes.byref(sh) if sh is not None else None, P(q), P(kv), P(bt), P(sl),
+                                   ctypes.c_float(scale), ctypes.c_int32(window), P(out), P(ws),
+                                   ctypes.c_size_t(ws_bytes), None)
+
+
+def test_decode_validates_before_launch():
+    # None of these reaches the GPU: validation fails first (fake addresses).
+    one_seg = shape(num_segments=1)
+    assert _call(None) == pad.PAD_EINVAL
+    assert _call(one_seg, scale=float("nan")) == pad.PAD_EINVAL
+    assert _call(one_seg, scale=float("inf")) == pad.PAD_EINVAL
+    assert _call(one_seg, q=0) == pad.PAD_EINVAL
+    assert _call(one_seg, kv=0) == pad.PAD_EINVAL
+    assert _call(one_seg, bt=0) == pad.PAD_EINVAL
+    assert _call(one_seg, sl=0) == pad.PAD_EINVAL
+    assert _call(one_seg, out=0) == pad.PAD_EINVAL
+    assert _call(one_seg, q=0x1008) == pad.PAD_EINVAL  # 16-byte alignment
+    assert _call(one_seg, kv=0x2004) == pad.PAD_EINVAL
+    assert _call(one_seg, out=0x5002) == pad.PAD_EINVAL
+    assert _call(one_seg, bt=0x3002) == pad.PAD_EINVAL  # 4-byte alignment
+    assert _call(one_seg, window=-3) == pad.PAD_EINVAL
+    assert _call(shape(query_len=9)) == pad.PAD_EUNSUPPORTED
+    split = shape(num_segments=4)
+    need = plan(split)["workspace_bytes"]
+    assert need > 0
+    assert _call(split) == pad.PAD_EWORKSPACE
+    assert _call(split, ws=0x10000, ws_bytes=need - 1) == pad.PAD_EWORKSPACE
+    assert _call(split, ws=0x10010, ws_bytes=need) == pad.PAD_EWORKSPACE  # 256-byte alignment
+    # an empty batch is a successful no-op, even with no buffers
+    assert _call(shape(num_seqs=0), q=0, kv=0, bt=0, sl=0, out=0) == pad.PAD_OK
+
+
+def test_workspace_size_and_init_validation():
+    assert pad.pad_decode_attn_workspace_size(shape()) == plan(shape())["workspace_bytes"]
+    P = ctypes.c_void_p
+    assert pad.lib.pad_decode_attn_workspace_init(P(0), ctypes.c_size_t(0), None) == pad.PAD_OK
+    assert pad.lib.pad_decode_attn_workspace_init(P(0), ctypes.c_size_t(256), None) == pad.PAD_EINVAL
+    assert pad.lib.pad_decode_attn_workspace_init(P(0x1010), ctypes.c_size_t(256), None) == pad.PAD_EINVAL

@@ -1,0 +1,262 @@
+"""HIP path vs the fp64 oracle, through the C ABI, on seeded inputs.
+
+Small cases span several 16-key tiles and a ragged tail; full-size cases
+run the benchmark's sizes and launch configuration and compare whole
+sequences (or sampled sequences of the batch)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_decode_block_amd as pad
+import workloads as wl
+from gpu_check import ABS_TOL, check, errors, oracle_out, passes, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _case(spec, lens, M, seed, **kw):
+    say(f"case: D={spec.head_size} Hq={spec.num_q_heads} Hkv={spec.num_kv_heads} P={spec.page_size} "
+        f"{spec.dtype} layout={spec.layout} lens={list(lens)[:6]} M={M} seed={seed} {kw}")
+    return wl.make_case(spec, lens, M, seed=seed, device=DEV, **kw)
+
+
+# ---------------------------------------------------------------- configs
+
+
+@pytest.mark.parametrize("M", [1])
+def test_config1_exact(M):
+    c = wl.config_case(1, 256, M, device=DEV)
+    say("config 1: fp16 D64 4/1 M1 P16 L256 HND")
+    check(run_gpu(c), oracle_out(c), c.q.dtype, "config1")
+
+
+@pytest.mark.parametrize("ctx", [128, 1000, 4096])
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_config2_small(ctx, M):
+    spec = wl.CONFIGS[2]
+    c = _case(spec, [ctx], M, wl.seed_for(2, ctx, M))
+    check(run_gpu(c), oracle_out(c), c.q.dtype, f"config2 L={ctx} M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_config3_window_nhd(M):
+    c = wl.config_case(3, 16384, M, device=DEV)
+    say(f"config 3: fp16 D256 8/2 W512 P32 L16384 NHD M={M}")
+    check(run_gpu(c), oracle_out(c), c.q.dtype, f"config3 M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+def test_config4_small(M):
+    spec = wl.CONFIGS[4]
+    c = _case(spec, [1500], M, wl.seed_for(4, 1500, M))
+    check(run_gpu(c), oracle_out(c), c.q.dtype, f"config4 L=1500 M={M}")
+
+
+def test_config5_small_batch():
+    c = wl.config_case(5, 3000, 4, device=DEV)
+    say("config 5 (length mix up to 3000): 64 seqs + 1 padded, P1056")
+    out = run_gpu(c)
+    assert torch.all(out[-1] == 0), "padded sequence must be zero"
+    check(out, oracle_out(c), c.q.dtype, "config5 small")
+
+
+# ------------------------------------------------------- random shapes
+
+
+RANDOM_SHAPES = [
+    # D, Hq, Hkv, P, dtype, layout, lens, M, window
+    (64, 8, 8, 16, "fp16", wl.HND, [77, 1, 16], 1, 0),
+    (64, 16, 1, 32, "bf16", wl.NHD, [300, 45], 3, 0),
+    (128, 8, 2, 48, "fp16", wl.HND, [999], 8, 0),
+    (128, 12, 3, 16, "bf16", wl.NHD, [513, 0, 64], 2, 100),
+    (256, 4, 4, 528, "bf16", wl.HND, [1100, 17], 5, 0),
+    (256, 32, 2, 32, "fp16", wl.HND, [400], 4, 0),   # 64 rows: two row groups at D=256
+    (512, 8, 1, 16, "fp16", wl.HND, [333], 2, 0),
+    (512, 16, 1, 32, "bf16", wl.NHD, [200], 8, 0),   # 128 rows: 8 row groups at D=512
+    (128, 4, 1, 16, "bf16", wl.HND, [5, 3, 2, 1], 4, 0),  # L < M: rows with no key
+    (64, 4, 2, 16, "fp16", wl.HND, [40, 41], 3, 1),   # window 1
+    (128, 8, 4, 544, "fp16", wl.NHD, [2000], 7, 3000),  # window wider than the context
+    (256, 16, 2, 784, "bf16", wl.HND, [1600, 784, 785], 4, 0),
+]
+
+
+@pytest.mark.parametrize("shape", RANDOM_SHAPES, ids=[f"s{i}" for i in range(len(RANDOM_SHAPES))])
+def test_random_shapes(shape):
+    D, Hq, Hkv, P, dt, layout, lens, M, W = shape
+    spec = wl.Spec(dt, D, Hq, Hkv, P, layout, window=W)
+    c = _case(spec, lens, M, 4242 + D + Hq + P + M)
+    out = run_gpu(c)
+    check(out, oracle_out(c), c.q.dtype, f"random {shape}")
+
+
+# ------------------------------------------------ split-KV and the merge
+
+
+@pytest.mark.parametrize("nseg", [1, 2, 3, 17, 256])
+def test_forced_segments(nseg):
+    spec = wl.CONFIGS[2]
+    c = _case(spec, [2000], 4, 77)
+    ref = oracle_out(c)
+    out = run_gpu(c, num_segments=nseg)
+    check(out, ref, c.q.dtype, f"nseg={nseg}")
+    base = run_gpu(c, num_segments=1)
+    assert float((out.float() - base.float()).abs().max()) < 1e-2
+
+
+def test_counters_left_zero_and_nan_scratch():
+    spec = wl.CONFIGS[4]
+    c = _case(spec, [3000], 8, 11)
+    shape = pad.make_shape(c.q, c.kv_cache, c.block_tables[0], c.layout)
+    need = pad.pad_decode_attn_workspace_size(shape)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    pad.pad_decode_attn_workspace_init(ws)
+    plan = pad.pad_decode_attn_plan(shape, 0)
+    assert plan["num_segments"] > 1
+    ref = oracle_out(c)
+    ncnt = c.num_seqs * spec.num_kv_heads * plan["row_groups"]
+    for it in range(3):
+        # poison the partial area: a stale read would surface as NaN
+        ws[256:].view(torch.uint8).fill_(0xFF)
+        out = run_gpu(c, workspace=ws)
+        torch.cuda.synchronize()
+        check(out, ref, c.q.dtype, f"poisoned scratch run {it}")
+        assert int(ws[: ncnt * 4].view(torch.int32).abs().sum()) == 0, "arrival counters must be left zero"
+
+
+def test_deterministic():
+    c = _case(wl.CONFIGS[2], [5000], 4, 5)
+    a = run_gpu(c)
+    b = run_gpu(c)
+    assert torch.equal(a, b)
+
+
+def test_graph_replay():
+    c = _case(wl.CONFIGS[4], [2500], 4, 6, instances=2)
+    ref = [oracle_out(c, i) for i in range(2)]
+    ws = pad.Workspace(c.q.device)
+    shape = pad.make_shape(c.q, c.kv_cache, c.block_tables[0], c.layout)
+    buf = ws.get(shape)
+    eager = run_gpu(c, 0, workspace=buf)
+    torch.cuda.synchronize()
+    static_out = torch.zeros_like(c.q)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_gpu(c, 0, workspace=buf, out=static_out)
+    for it in range(100):
+        static_out.fill_(float("nan"))
+        g.replay()
+        if it % 10 == 0:
+            other = run_gpu(c, 1, workspace=buf)  # eager work between replays
+            torch.cuda.synchronize()
+            check(other, ref[1], c.q.dtype, f"eager between replays {it}")
+        torch.cuda.synchronize()
+        assert torch.equal(static_out, eager), f"replay {it} differs from the eager result"
+    check(static_out, ref[0], c.q.dtype, "graph replay")
+
+
+# ------------------------------------------------------ layouts, GQA
+
+
+def test_hnd_equals_nhd():
+    spec = wl.Spec("bf16", 128, 16, 4, 32, wl.HND)
+    c = _case(spec, [700, 33], 3, 9)
+    out_h = run_gpu(c)
+    kv_n = c.kv_cache.permute(0, 2, 1, 3, 4).contiguous()
+    out_n = torch.empty_like(out_h)
+    pad.pad_decode_attn(c.q, kv_n, c.block_tables[0], c.seq_lens, c.scale, 0, out_n, layout=pad.PAD_NHD)
+    assert torch.equal(out_h, out_n)
+
+
+def test_planted_keys_unit_scale():
+    """A dominant key gives unit-scale outputs, so the absolute gate bites:
+    planted inside the window it must win; one past the token (causal) or
+    one before the window it must be ignored."""
+    spec = wl.Spec("bf16", 512, 16, 2, 32, wl.HND, window=64, kv_std=0.5)
+    L, M = 1200, 4
+    c = _case(spec, [L], M, 21)
+    bt = c.block_tables[0].cpu()
+
+    def key(t, kvh):
+        return c.kv_cache[int(bt[0, t // 32]), kvh, t % 32]
+
+    for t_star, expect_win in [(L - M - 10, True), (L - M + 1, False), (L - M - 64, False)]:
+        q = c.q.clone()
+        for kvh in range(2):
+            k = key(t_star, kvh)[0].float()
+            beta = 60.0 / (k.dot(k).item() * c.scale)
+            for g in range(8):
+                q[0, 0, kvh * 8 + g] = (beta * k).to(q.dtype)
+        c2 = wl.Case(spec, q, c.kv_cache, c.block_tables, c.seq_lens, c.scale, 64, c.poison_block, c.seed)
+        out = run_gpu(c2)
+        ref = oracle_out(c2)
+        check(out, ref, q.dtype, f"planted at {t_star}")
+        v = wl.as_f64(key(t_star, 0)[1])
+        won = np.abs(ref[0, 0, 0] - v).max() < 1e-2
+        assert won == expect_win
+
+
+# ------------------------------------------------ negative controls
+
+
+def test_negative_controls_fail_the_checker():
+    spec = wl.CONFIGS[2]
+    c = _case(spec, [20000], 4, 31)
+    ref = oracle_out(c)
+    out = run_gpu(c)
+    check(out, ref, c.q.dtype, "control baseline")
+    assert not passes(torch.zeros_like(out), ref, c.q.dtype), "zero output must fail"
+    # wrong GQA map: q heads grouped modulo instead of contiguously
+    Hq, Hkv = spec.num_q_heads, spec.num_kv_heads
+    G = Hq // Hkv
+    perm = [(h % Hkv) * G + h // Hkv for h in range(Hq)]
+    wrong = run_gpu(wl.Case(spec, c.q[:, :, perm].contiguous(), c.kv_cache, c.block_tables, c.seq_lens,
+                            c.scale, 0, c.poison_block, c.seed))
+    inv = np.argsort(perm)
+    assert not passes(wrong[:, :, inv], ref, c.q.dtype), "wrong GQA map must fail"
+    # off-by-one causal mask (every row one position early), on a short
+    # context where one key carries visible weight
+    s2 = _case(spec, [60, 45], 4, 32)
+    ref2 = oracle_out(s2)
+    early = wl.Case(spec, s2.q, s2.kv_cache, s2.block_tables, s2.seq_lens - 1, s2.scale, 0, s2.poison_block,
+                    s2.seed)
+    assert not passes(run_gpu(early), ref2, s2.q.dtype), "off-by-one mask must fail"
+
+
+# ---------------------------------------------- full benchmark sizes
+
+
+POOL = 512 << 20
+
+
+@pytest.mark.parametrize("M", [1, 2, 4])
+@pytest.mark.parametrize("ctx", [4096, 32768])
+def test_config2_full(ctx, M):
+    say(f"config 2 full: L={ctx} M={M} pool=512MiB")
+    inst = max(1, (POOL // wl.CONFIGS[2].block_bytes) // (ctx // 16))
+    c = wl.config_case(2, ctx, M, device=DEV, instances=inst, pool_bytes=POOL)
+    for i in sorted({0, inst - 1}):
+        check(run_gpu(c, i), oracle_out(c, i), c.q.dtype, f"config2 L={ctx} M={M} inst={i}")
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_config4_full(M):
+    ctx = 32768
+    say(f"config 4 full: L={ctx} M={M}")
+    c = wl.config_case(4, ctx, M, device=DEV, instances=1, pool_bytes=POOL)
+    check(run_gpu(c), oracle_out(c), c.q.dtype, f"config4 L={ctx} M={M}")
+
+
+def test_config5_full_sampled():
+    say("config 5 full: 64 seqs L~U[512,16384] + padded, P1056")
+    c = wl.config_case(5, 16384, 4, device=DEV)
+    out = run_gpu(c)
+    assert torch.all(out[-1] == 0)
+    lens = c.seq_lens.tolist()
+    order = np.argsort(lens[:-1])
+    pick = [int(order[0]), int(order[len(order) // 2]), int(order[-1]), 3, 64]
+    ref = oracle_out(c, 0, seqs=pick)
+    check(out[pick], ref, c.q.dtype, f"config5 seqs {pick}")
