@@ -59,9 +59,11 @@ def kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def time_calls(case, n_warm: int, n_timed: int, **kw):
+def time_calls(case, n_warm: int, n_timed: int, graph: bool = False, **kw):
     """Average ms per call over n_timed calls rotating through the instances,
-    timed with HIP events on the stream the kernel is launched on."""
+    timed with HIP events on the stream the kernel is launched on.  With
+    ``graph`` the n_timed calls are captured once into a HIP graph and the
+    replay is timed, which removes host launch overhead between kernels."""
     import torch
 
     import paged_kv_decode_block_amd as pad
@@ -77,12 +79,24 @@ def time_calls(case, n_warm: int, n_timed: int, **kw):
 
     for i in range(n_warm):
         call(i)
+    torch.cuda.synchronize()
+    g = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n_timed):
+                call(n_warm + i)
+        g.replay()  # warm replay
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(n_timed):
-        call(n_warm + i)
+    if g is not None:
+        g.replay()
+    else:
+        for i in range(n_timed):
+            call(n_warm + i)
     stop.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / n_timed, pad.pad_decode_attn_plan(shape, case.window)
@@ -181,7 +195,7 @@ def main() -> int:
         for ctx in pts["contexts"]:
             for m in pts["queries"]:
                 c = build_case(ctx, m)
-                t, p = time_calls(c, 20, 100)
+                t, p = time_calls(c, 20, 100, graph=True)
                 b = effective_bytes(c)
                 sweep.append({"context": ctx, "M": m, "us": round(t * 1e3, 3), "GB/s": round(b / (t * 1e-3) / 1e9, 1),
                               "frac": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "segments": p["num_segments"]})

@@ -34,6 +34,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
 struct Mfma;
@@ -67,8 +68,11 @@ struct Mfma<_Float16> {
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kNW = kWaves;
 constexpr int kThreads = kNW * 64;
-// Cross-segment merge weights held in LDS (segments x rows of a workgroup).
-constexpr int kMergeWeights = kMaxMergeWeights;
+// Split-KV merge tree: segments merge in groups of kMergeGroup, then the
+// groups merge; at most kMergeSlots partials are merged at once.
+constexpr int kMergeGroup = kMergeGroupSize;
+constexpr int kMergeSlots = kMaxSegments / kMergeGroupSize;
+static_assert(kMergeSlots >= kMergeGroup, "merge staging must hold a full group");
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -82,7 +86,7 @@ struct Lds {
   static constexpr int kAccStride = D + 4;  // floats per merged accumulator row
   static constexpr int kVBytes = kNW * 16 * kVStride * 2;
   static constexpr int kMergeBytes = (2 * kNW * RT * 16 + 2 * RT * 16) * 4 + RT * 16 * kAccStride * 4;
-  static constexpr int kFinalBytes = (kMergeWeights + RT * 16) * 4;
+  static constexpr int kFinalBytes = (2 * kMergeSlots * 64 + 2 * 64) * 4;  // (m, l) staging + row scalars
   static constexpr int kBytes0 = kVBytes > kMergeBytes ? kVBytes : kMergeBytes;
   static constexpr int kBytes = (kBytes0 > kFinalBytes ? kBytes0 : kFinalBytes) + 16;
 };
@@ -100,6 +104,113 @@ __device__ void zero_rows(const Params& p, int s, int kvh, int row0, int nrows) 
   }
 }
 
+// Merge `count` split partials (slots first_slot .. first_slot + count - 1
+// of the unit) over this workgroup's rows [row0, row0 + wg_rows): the
+// log-sum-exp merge m* = max m_j, l* = sum l_j 2^(m_j - m*),
+// acc* = sum acc_j 2^(m_j - m*), in slot order (bitwise deterministic).
+// With `out_final` the normalised result acc*/l* goes to the output rows;
+// otherwise (acc*, m*, l*) becomes partial slot `dst_slot`.
+template <typename T, int D, int RT>
+__device__ void merge_slots(const Params& p, unsigned char* lds, int64_t unit_slot0, int first_slot, int count,
+                            int row0, int wg_rows, bool out_final, int dst_slot, T* out_rows_base_s, int kvh) {
+  using MF = Mfma<T>;
+  const int tid = threadIdx.x;
+  float2* sm_ml = reinterpret_cast<float2*>(lds);                  // [count][wg_rows]
+  float* sm_ms = reinterpret_cast<float*>(lds) + 2 * kMergeSlots * 64;  // [wg_rows]
+  float* sm_ls = sm_ms + 64;                                        // [wg_rows]
+  const int n = count * wg_rows;
+  // Stage every (m, l) pair with all loads in flight at once.
+  for (int base = 0; base < n; base += kThreads * 8) {
+    float2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = base + u * kThreads + tid;
+      if (idx < n) {
+        const int j = idx / wg_rows, r = idx % wg_rows;
+        v[u] = *reinterpret_cast<const float2*>(p.ws_ml + ((unit_slot0 + first_slot + j) * p.rows + row0 + r) * 2);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = base + u * kThreads + tid;
+      if (idx < n) sm_ml[idx] = v[u];
+    }
+  }
+  __syncthreads();
+  for (int r = tid; r < wg_rows; r += kThreads) {
+    float ms = kNegInf;
+    for (int j = 0; j < count; ++j) ms = fmaxf(ms, sm_ml[j * wg_rows + r].x);
+    const float mu = ms == kNegInf ? 0.f : ms;
+    float ls = 0.f;
+    for (int j = 0; j < count; ++j) {
+      const float2 ml = sm_ml[j * wg_rows + r];
+      const float w = fast_exp2(ml.x - mu);
+      sm_ml[j * wg_rows + r].x = w;  // weight of slot j for this row
+      ls += w * ml.y;
+    }
+    sm_ms[r] = ms;
+    sm_ls[r] = ls;
+  }
+  __syncthreads();
+  const int64_t jstride = int64_t(p.rows) * D;
+  const float* src0 = p.ws_acc + ((unit_slot0 + first_slot) * p.rows + row0) * D;
+  float* dst0 = p.ws_acc + ((unit_slot0 + dst_slot) * p.rows + row0) * D;
+  const int items = wg_rows * (D / 4);
+  for (int it = tid; it < items; it += kThreads) {
+    const int r = it / (D / 4), d4 = it % (D / 4);
+    const float* src = src0 + int64_t(r) * D + 4 * d4;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < count; j0 += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < count) v[u] = *reinterpret_cast<const f32x4*>(src + (j0 + u) * jstride);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < count) a += sm_ml[(j0 + u) * wg_rows + r].x * v[u];
+    }
+    if (out_final) {
+      const float ls = sm_ls[r];
+      const float inv = ls > 0.f ? 1.f / ls : 0.f;
+      const int ru = row0 + r, m = ru / p.group, gq = ru % p.group;
+      T* dst = out_rows_base_s + (int64_t(m) * p.num_q_heads + kvh * p.group + gq) * D + 4 * d4;
+      uint2 v;
+      v.x = uint32_t(MF::bits(a[0] * inv)) | (uint32_t(MF::bits(a[1] * inv)) << 16);
+      v.y = uint32_t(MF::bits(a[2] * inv)) | (uint32_t(MF::bits(a[3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(dst) = v;
+    } else {
+      *reinterpret_cast<f32x4*>(dst0 + int64_t(r) * D + 4 * d4) = a;
+    }
+  }
+  if (!out_final) {
+    for (int r = tid; r < wg_rows; r += kThreads) {
+      float* ml = p.ws_ml + ((unit_slot0 + dst_slot) * p.rows + row0 + r) * 2;
+      ml[0] = sm_ms[r];
+      ml[1] = sm_ls[r];
+    }
+  }
+}
+
+// Release this workgroup's global writes, bump `counter` and tell whether
+// this workgroup arrived last of `expected`; the last one acquires.  Each
+// wave first waits for its own stores; then one thread makes the release at
+// device scope (a single L2 write-back for the whole workgroup), does the
+// atomic and, if last, the acquire (invalidating this CU's L1 and stale L2
+// lines before the merge reads the other workgroups' partials).
+__device__ __forceinline__ bool arrive(int* counter, int expected, int* sm_flag) {
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev == expected - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *sm_flag = last;
+  }
+  __syncthreads();
+  return *sm_flag;
+}
+
 template <typename T, int D, int RT>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p) {
   using MF = Mfma<T>;
@@ -110,7 +221,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[LD::kBytes];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 4, c = lane & 15;
   const int s = blockIdx.y;
   const int units = p.num_kv_heads * p.row_groups;
@@ -171,24 +283,36 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p) {
     for (int dt = 0; dt < DT; ++dt) acc[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const T* KV = static_cast<const T*>(p.kv);
+  const unsigned char* KVh =
+      static_cast<const unsigned char*>(p.kv) + int64_t(kvh) * p.head_stride * int64_t(sizeof(T));
   const int32_t* table = p.block_table + int64_t(s) * p.max_blocks;
-  const int64_t head_off = int64_t(kvh) * p.head_stride;
+  // Byte offset of this lane's 16-byte chunk inside a tile: key row c,
+  // head-dim elements 8g..8g+7 of chunk 0 (32-bit, per lane); the tile base
+  // itself is wave-uniform, so the loads take a scalar base address.
+  const uint32_t lane_off = uint32_t(c * p.token_stride + 8 * g) * uint32_t(sizeof(T));
   uint16_t* vs = reinterpret_cast<uint16_t*>(lds) + wave * 16 * LD::kVStride;
+  // Transposed-read address of this lane: row 4g + c/4, columns 4(c%4).. of
+  // each 16-column tile (ds_read_b64_tr_b16 returns column c of the 4x16
+  // block its 16-lane group addresses, i.e. 4 keys of one head-dim column).
+  const uint16_t* vtr = vs + (4 * g + (c >> 2)) * LD::kVStride + 4 * (c & 3);
 
   struct Tile {
     i32x4 k[KC];
     i32x4 v[KC];
   };
 
-  auto load_tile = [&](Tile& tl, int t) {
+  // Physical block of tile t (a scalar load: t is wave-uniform).
+  auto block_of = [&](int t) { return table[(t * 16) / p.page_size]; };
+
+  auto issue_tile = [&](Tile& tl, int t, int blk) {
     const int key0 = t * 16;
-    const int blk = table[key0 / p.page_size];
-    const T* row = KV + int64_t(blk) * p.block_stride + head_off + int64_t(key0 % p.page_size + c) * p.token_stride;
+    const unsigned char* base =
+        KVh + (int64_t(blk) * p.block_stride + int64_t(key0 % p.page_size) * p.token_stride) * int64_t(sizeof(T));
+    const unsigned char* row = base + lane_off;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) tl.k[kc] = *reinterpret_cast<const i32x4*>(row + 32 * kc + 8 * g);
+    for (int kc = 0; kc < KC; ++kc) tl.k[kc] = *reinterpret_cast<const i32x4*>(row + 64 * kc);
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) tl.v[kc] = *reinterpret_cast<const i32x4*>(row + D + 32 * kc + 8 * g);
+    for (int kc = 0; kc < KC; ++kc) tl.v[kc] = *reinterpret_cast<const i32x4*>(row + 2 * D + 64 * kc);
   };
 
   auto compute_tile = [&](Tile& tl, int t) {
@@ -246,8 +370,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* col = vs + 4 * g * LD::kVStride + 16 * dt + c;
-      const uint64_t va = pack4(col[0], col[LD::kVStride], col[2 * LD::kVStride], col[3 * LD::kVStride]);
+      const uint64_t va = __builtin_bit_cast(
+          uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vtr + 16 * dt)));
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) acc[rt][dt] = MF::pv(va, pb[rt], acc[rt][dt]);
     }
@@ -256,26 +380,38 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // Interleaved tiles per wave; the next tile's loads are issued before the
-  // current tile is computed.
-  int t = ts + wave;
-  if constexpr (kPrefetch) {
-    Tile ta, tb;
-    if (t < te) load_tile(ta, t);
-    while (t < te) {
-      if (t + kNW < te) load_tile(tb, t + kNW);
-      compute_tile(ta, t);
-      t += kNW;
-      if (t >= te) break;
-      if (t + kNW < te) load_tile(ta, t + kNW);
-      compute_tile(tb, t);
-      t += kNW;
-    }
-  } else {
-    Tile ta;
-    for (; t < te; t += kNW) {
-      load_tile(ta, t);
-      compute_tile(ta, t);
+  // Interleaved tiles per wave: tile i of this wave is ts + wave + i * NW.
+  // A tile's loads are issued before the previous tile is computed and its
+  // block id is read one tile earlier still.  The prefetch index is clamped
+  // to the wave's last tile instead of being skipped, so every iteration
+  // has the same loads in flight and the compiler's wait counts stay exact
+  // (the clamped re-read of the last tile hits in cache).
+  const int first_t = ts + wave;
+  const int n_w = first_t < te ? (te - first_t + kNW - 1) / kNW : 0;
+  auto tile_at = [&](int i) { return first_t + min(i, n_w - 1) * kNW; };
+  if (n_w > 0) {
+    if constexpr (kPrefetch) {
+      Tile ta, tb;
+      issue_tile(ta, tile_at(0), block_of(tile_at(0)));
+      int blk_next = block_of(tile_at(1));
+      for (int i = 0;;) {
+        issue_tile(tb, tile_at(i + 1), blk_next);
+        blk_next = block_of(tile_at(i + 2));
+        compute_tile(ta, first_t + i * kNW);
+        if (++i >= n_w) break;
+        issue_tile(ta, tile_at(i + 1), blk_next);
+        blk_next = block_of(tile_at(i + 2));
+        compute_tile(tb, first_t + i * kNW);
+        if (++i >= n_w) break;
+      }
+    } else {
+      Tile ta;
+      int blk = block_of(tile_at(0));
+      for (int i = 0; i < n_w; ++i) {
+        issue_tile(ta, first_t + i * kNW, blk);
+        blk = block_of(tile_at(i + 1));
+        compute_tile(ta, first_t + i * kNW);
+      }
     }
   }
 
@@ -335,12 +471,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p) {
     __syncthreads();
   }
 
-  T* out = static_cast<T*>(p.out);
-  auto out_row = [&](int ru) {
-    const int m = ru / p.group, gq = ru % p.group;
-    return out + ((int64_t(s) * M + m) * p.num_q_heads + kvh * p.group + gq) * D;
-  };
-
+  T* out_s = static_cast<T*>(p.out) + int64_t(s) * M * p.num_q_heads * D;
   if (n_live == 1) {
     for (int it = tid; it < wg_rows * (D / 8); it += kThreads) {
       const int r = it / (D / 8), d8 = it % (D / 8);
@@ -353,15 +484,21 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p) {
       i32x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = int(uint32_t(h[2 * e]) | (uint32_t(h[2 * e + 1]) << 16));
-      *reinterpret_cast<i32x4*>(out_row(row0 + r) + 8 * d8) = v;
+      const int ru = row0 + r, m = ru / p.group, gq = ru % p.group;
+      *reinterpret_cast<i32x4*>(out_s + (int64_t(m) * p.num_q_heads + kvh * p.group + gq) * D + 8 * d8) = v;
     }
     return;
   }
 
-  // ---- split-KV partial and arrival ----
-  const int64_t slot0 = (int64_t(s) * p.num_kv_heads + kvh) * p.nseg;
+  // ---- split-KV partial, then a two-level arrival tree ----
+  // Segments form groups of kMergeGroup; the last arriver of a group merges
+  // the group's partials (into the output when there is one group, else
+  // into a group partial); the last group to finish merges the groups.
+  const int ngroups = (n_live + kMergeGroup - 1) / kMergeGroup;
+  const int nslots = p.nseg + (p.nseg + kMergeGroup - 1) / kMergeGroup;  // segment + group slots
+  const int64_t unit_slot0 = (int64_t(s) * p.num_kv_heads + kvh) * nslots;
   {
-    const int64_t base = (slot0 + seg) * p.rows + row0;
+    const int64_t base = (unit_slot0 + seg) * p.rows + row0;
     for (int it = tid; it < wg_rows * (D / 4); it += kThreads) {
       const int r = it / (D / 4), d4 = it % (D / 4);
       *reinterpret_cast<f32x4*>(p.ws_acc + (base + r) * D + 4 * d4) =
@@ -372,46 +509,22 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p) {
       p.ws_ml[(base + r) * 2 + 1] = sm_ls[r];
     }
   }
-  int* counter = p.ws_cnt + (int64_t(s) * p.num_kv_heads + kvh) * p.row_groups + rg;
-  __threadfence();  // release this thread's partial writes at device scope
-  __syncthreads();
+  const int ngmax = (p.nseg + kMergeGroup - 1) / kMergeGroup;
+  int* counters = p.ws_cnt + ((int64_t(s) * p.num_kv_heads + kvh) * p.row_groups + rg) * (1 + ngmax);
   int* sm_flag = reinterpret_cast<int*>(lds + LD::kBytes - 16);
-  if (tid == 0) *sm_flag = atomicAdd(counter, 1) == n_live - 1;
-  __syncthreads();
-  if (!*sm_flag) return;
-  __threadfence();  // acquire the other segments' partials
-
-  // ---- last arriver: log-sum-exp merge of all live segments ----
-  float* sm_w = reinterpret_cast<float*>(lds);       // [n_live][wg_rows]
-  float* sm_lt = sm_w + kMergeWeights;                 // [wg_rows]
-  for (int r = tid; r < wg_rows; r += kThreads) {
-    float ms = kNegInf;
-    for (int j = 0; j < n_live; ++j) ms = fmaxf(ms, p.ws_ml[((slot0 + j) * p.rows + row0 + r) * 2]);
-    const float mu = ms == kNegInf ? 0.f : ms;
-    float ls = 0.f;
-    for (int j = 0; j < n_live; ++j) {
-      const float* ml = p.ws_ml + ((slot0 + j) * p.rows + row0 + r) * 2;
-      const float w = fast_exp2(ml[0] - mu);
-      sm_w[j * wg_rows + r] = w;
-      ls += w * ml[1];
-    }
-    sm_lt[r] = ls;
+  const int grp = seg / kMergeGroup;
+  const int gsize = min(kMergeGroup, n_live - grp * kMergeGroup);
+  if (!arrive(counters + 1 + grp, gsize, sm_flag)) return;
+  if (tid == 0) counters[1 + grp] = 0;  // last user of this counter in the launch
+  if (ngroups == 1) {
+    merge_slots<T, D, RT>(p, lds, unit_slot0, 0, n_live, row0, wg_rows, true, 0, out_s, kvh);
+    return;
   }
-  __syncthreads();
-  for (int it = tid; it < wg_rows * (D / 4); it += kThreads) {
-    const int r = it / (D / 4), d4 = it % (D / 4);
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-    const float* src = p.ws_acc + ((slot0)*p.rows + row0 + r) * D + 4 * d4;
-    const int64_t jstride = int64_t(p.rows) * D;
-    for (int j = 0; j < n_live; ++j) a += sm_w[j * wg_rows + r] * *reinterpret_cast<const f32x4*>(src + j * jstride);
-    const float ls = sm_lt[r];
-    const float inv = ls > 0.f ? 1.f / ls : 0.f;
-    uint2 v;
-    v.x = uint32_t(MF::bits(a[0] * inv)) | (uint32_t(MF::bits(a[1] * inv)) << 16);
-    v.y = uint32_t(MF::bits(a[2] * inv)) | (uint32_t(MF::bits(a[3] * inv)) << 16);
-    *reinterpret_cast<uint2*>(out_row(row0 + r) + 4 * d4) = v;
-  }
-  if (tid == 0) *counter = 0;  // leave the counter zeroed for the next launch
+  merge_slots<T, D, RT>(p, lds, unit_slot0, grp * kMergeGroup, gsize, row0, wg_rows, false, p.nseg + grp, out_s,
+                        kvh);
+  if (!arrive(counters, ngroups, sm_flag)) return;
+  if (tid == 0) counters[0] = 0;
+  merge_slots<T, D, RT>(p, lds, unit_slot0, p.nseg, ngroups, row0, wg_rows, true, 0, out_s, kvh);
 }
 
 __global__ void zero_kernel(uint32_t* p, size_t n) {

@@ -80,7 +80,6 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   }
   nseg = std::min<int64_t>(nseg, span_tiles);
   nseg = std::min<int64_t>(nseg, kMaxSegments);
-  nseg = std::min<int64_t>(nseg, kMaxMergeWeights / (p.row_tiles * 16));
   nseg = std::max<int64_t>(1, nseg);
   p.seg_tiles = int(ceil_div(span_tiles, nseg));
   p.nseg = int(ceil_div(span_tiles, p.seg_tiles));
@@ -90,11 +89,13 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
 
   if (p.nseg > 1) {
     const size_t S = size_t(sh.num_seqs), H = size_t(sh.num_kv_heads);
-    const size_t slots_rows = S * H * size_t(p.nseg) * size_t(rows);
+    const size_t ngroups = size_t(ceil_div(p.nseg, kMergeGroupSize));
+    const size_t slot_rows = S * H * (size_t(p.nseg) + ngroups) * size_t(rows);
+    if (S * H * size_t(p.row_groups) * (1 + ngroups) * sizeof(int32_t) > kCounterBytes) return PAD_EUNSUPPORTED;
     p.ws_counters = 0;
-    p.ws_ml = align_up(S * H * size_t(p.row_groups) * sizeof(int32_t));
-    p.ws_acc = p.ws_ml + align_up(slots_rows * 2 * sizeof(float));
-    p.ws_bytes = p.ws_acc + align_up(slots_rows * size_t(sh.head_size) * sizeof(float));
+    p.ws_ml = kCounterBytes;
+    p.ws_acc = p.ws_ml + align_up(slot_rows * 2 * sizeof(float));
+    p.ws_bytes = p.ws_acc + align_up(slot_rows * size_t(sh.head_size) * sizeof(float));
   } else {
     p.ws_counters = p.ws_ml = p.ws_acc = p.ws_bytes = 0;
   }

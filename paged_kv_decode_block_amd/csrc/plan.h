@@ -22,7 +22,11 @@ namespace pad {
 constexpr int kTileKeys = 16;    // keys per MFMA tile (page sizes are multiples of 16)
 constexpr int kWaves = 4;        // waves per workgroup
 constexpr int kMaxSegments = 256;
-constexpr int kMaxMergeWeights = 4096;  // LDS floats for merge weights (segments x rows)
+constexpr int kMergeGroupSize = 8;  // segments merged per group of the two-level merge tree
+// Arrival counters live in a fixed-size prefix of the workspace, so calls of
+// different shapes can share one workspace: partials never land where any
+// shape keeps counters, and every call leaves its counters zero.
+constexpr size_t kCounterBytes = size_t(1) << 20;
 
 struct Plan {
   int path;          // PAD_PATH_MFMA / PAD_PATH_DOT
@@ -33,7 +37,10 @@ struct Plan {
   int nseg;          // segments per (unit, row group)
   int seg_tiles;     // planned tiles per segment
   int grid_x, grid_y;
-  // Workspace layout (byte offsets; all 256-byte aligned).
+  // Workspace layout (byte offsets; all 256-byte aligned): the counter
+  // prefix (kCounterBytes; per (unit, row group) one top counter plus one
+  // per merge group), then per unit nseg segment slots plus
+  // ceil(nseg / kMergeGroupSize) group slots of (m, l) and of acc.
   size_t ws_counters, ws_ml, ws_acc, ws_bytes;
 };
 

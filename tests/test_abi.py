@@ -84,9 +84,11 @@ def test_plan_invariants(kw):
     if p["num_segments"] == 1:
         assert p["workspace_bytes"] == 0
     else:
+        # a fixed 1 MiB counter prefix, then segment slots plus one slot per
+        # merge group of 8 segments
         S, H, n = sh.num_seqs, sh.num_kv_heads, p["num_segments"]
-        want = _align(S * H * p["row_groups"] * 4) + _align(S * H * n * rows * 2 * 4) + _align(
-            S * H * n * rows * sh.head_size * 4)
+        ng = -(-n // 8)
+        want = (1 << 20) + _align(S * H * (n + ng) * rows * 2 * 4) + _align(S * H * (n + ng) * rows * sh.head_size * 4)
         assert p["workspace_bytes"] == want
 
 

@@ -117,14 +117,40 @@ def test_counters_left_zero_and_nan_scratch():
     plan = pad.pad_decode_attn_plan(shape, 0)
     assert plan["num_segments"] > 1
     ref = oracle_out(c)
-    ncnt = c.num_seqs * spec.num_kv_heads * plan["row_groups"]
+    # counters occupy a fixed 1 MiB prefix of the workspace
+    cnt_bytes = 1 << 20
     for it in range(3):
         # poison the partial area: a stale read would surface as NaN
-        ws[256:].view(torch.uint8).fill_(0xFF)
+        ws[cnt_bytes:].fill_(0xFF)
         out = run_gpu(c, workspace=ws)
         torch.cuda.synchronize()
         check(out, ref, c.q.dtype, f"poisoned scratch run {it}")
-        assert int(ws[: ncnt * 4].view(torch.int32).abs().sum()) == 0, "arrival counters must be left zero"
+        assert int(ws[:cnt_bytes].view(torch.int32).abs().sum()) == 0, "arrival counters must be left zero"
+
+
+def test_workspace_shared_across_shapes():
+    """One workspace serves calls of different shapes one after another
+    (counters stay in their own region and are left zero by every call)."""
+    cases = [
+        _case(wl.CONFIGS[2], [2000], 4, 41),
+        _case(wl.CONFIGS[4], [3000], 8, 42),
+        _case(wl.CONFIGS[2], [5000], 1, 43),
+        _case(wl.Spec("bf16", 256, 16, 2, 1056, wl.HND), [9000, 3000, 0], 4, 44),
+    ]
+    need = max(
+        pad.pad_decode_attn_workspace_size(pad.make_shape(c.q, c.kv_cache, c.block_tables[0], c.layout,
+                                                          num_segments=n))
+        for c in cases for n in (0, 256, 3))
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    pad.pad_decode_attn_workspace_init(ws)
+    refs = [oracle_out(c) for c in cases]
+    for rnd in range(2):
+        for i, c in enumerate(cases):
+            for nseg in (0, 256, 3):
+                out = run_gpu(c, workspace=ws, num_segments=nseg)
+                check(out, refs[i], c.q.dtype, f"shared workspace round {rnd} case {i} nseg={nseg}")
+    torch.cuda.synchronize()
+    assert int(ws[: 1 << 20].view(torch.int32).abs().sum()) == 0
 
 
 def test_deterministic():
