@@ -18,7 +18,7 @@ __all__ = [
     "PAD_OK", "PAD_EINVAL", "PAD_EUNSUPPORTED", "PAD_EWORKSPACE", "PAD_EHIP",
     "PAD_F16", "PAD_BF16", "PAD_NHD", "PAD_HND",
     "PAD_PATH_AUTO", "PAD_PATH_MFMA", "PAD_PATH_DOT",
-    "PadError", "pad_shape", "pad_plan", "lib", "LIB_PATH",
+    "PadError", "pad_shape", "pad_plan", "lib", "LIB_PATH", "load_library",
     "pad_abi_version", "pad_status_string", "pad_decode_attn_plan",
     "pad_decode_attn_workspace_size", "pad_decode_attn_workspace_init", "pad_decode_attn",
     "make_shape", "Workspace",
@@ -65,13 +65,14 @@ class pad_plan(ctypes.Structure):
     ]
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Open a build of the library and declare its C signatures."""
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m paged_kv_decode_block_amd.build` "
+            f"{path} is missing: build it with `python -m paged_kv_decode_block_amd.build` "
             "(the decode-attention path has no non-HIP fallback)"
         )
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     P = ctypes.POINTER
     L.pad_abi_version.restype = ctypes.c_int32
     L.pad_abi_version.argtypes = []
@@ -91,7 +92,7 @@ def _load() -> ctypes.CDLL:
     return L
 
 
-lib = _load()
+lib = load_library()
 
 
 class PadError(RuntimeError):

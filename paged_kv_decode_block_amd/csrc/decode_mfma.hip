@@ -9,20 +9,27 @@
 // in KernelVariant.scratch_shapes / make_scratch on the rocm_rdna_hip
 // page).
 //
-// Inside a workgroup the four waves take interleaved tiles of the
+// Inside a workgroup the waves take interleaved 16-key tiles of the
 // segment, each with its own online-softmax state over all rows, and are
-// combined through LDS at the end.  Per 16-key tile a wave:
+// combined through LDS at the end.  Per tile a wave:
 //   * loads the K and V rows of the tile straight into registers with
-//     16-byte loads (lane = key c, 8 consecutive head-dim elements);
+//     16-byte loads (lane = key c, 8 consecutive head-dim elements), one
+//     tile ahead of the tile it computes;
 //   * computes S^T = K Q^T with v_mfma_f32_16x16x32_{bf16,f16}: K is the
 //     A operand as loaded, the query tile is the B operand, and the result
 //     leaves each lane with 4 keys of one query row (row = lane % 16), so
 //     row max and sum need only the 4 lane groups (two cross-lane steps);
-//   * stages V in LDS and reads it back transposed (4 keys of one head-dim
-//     column per lane) as the A operand of v_mfma_f32_16x16x16 for
-//     O^T += V^T P^T, whose B operand (P in the input dtype) is exactly the
-//     softmax lane layout -- no shuffle of P is needed.
+//   * stages V in LDS and reads it back transposed with ds_read_b64_tr_b16
+//     (4 keys of one head-dim column per lane) as the A operand of
+//     v_mfma_f32_16x16x16 for O^T += V^T P^T, whose B operand (P rounded to
+//     the input dtype) is exactly the softmax lane layout.
 // Logits live in the exp2 domain (scale * log2 e folded in).
+//
+// Split partials are written with device-coherent (write-through) stores,
+// so publishing them costs no L2 write-back: each wave waits for its own
+// stores, then one atomic per workgroup counts the arrival.  Only the last
+// arriver invalidates its caches and merges, with every partial load in
+// flight before the merge weights are needed.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -66,13 +73,11 @@ struct Mfma<_Float16> {
 };
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kNW = kWaves;
-constexpr int kThreads = kNW * 64;
 // Split-KV merge tree: segments merge in groups of kMergeGroup, then the
 // groups merge; at most kMergeSlots partials are merged at once.
 constexpr int kMergeGroup = kMergeGroupSize;
-constexpr int kMergeSlots = kMaxSegments / kMergeGroupSize;
-static_assert(kMergeSlots >= kMergeGroup, "merge staging must hold a full group");
+constexpr int kMergeSlots = kMergeGroup > kMaxSegments / kMergeGroup ? kMergeGroup : kMaxSegments / kMergeGroup;
+constexpr int kMaxWgRows = 64;  // rows of one workgroup (row tiles x 16)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -80,28 +85,48 @@ __device__ __forceinline__ uint64_t pack4(uint16_t a, uint16_t b, uint16_t c, ui
   return uint64_t(a) | (uint64_t(b) << 16) | (uint64_t(c) << 32) | (uint64_t(d) << 48);
 }
 
+// Device-coherent store of 16 bytes (two 8-byte write-through stores).
+__device__ __forceinline__ void store_coherent(float* dst, f32x4 v) {
+  uint64_t* d = reinterpret_cast<uint64_t*>(dst);
+  __hip_atomic_store(d, __builtin_bit_cast(uint64_t, __builtin_shufflevector(v, v, 0, 1)), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(d + 1, __builtin_bit_cast(uint64_t, __builtin_shufflevector(v, v, 2, 3)), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_coherent2(float* dst, float a, float b) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(dst),
+                     uint64_t(__builtin_bit_cast(uint32_t, a)) | (uint64_t(__builtin_bit_cast(uint32_t, b)) << 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup shape (waves per workgroup from waves_for) and LDS layout.
 template <int D, int RT>
-struct Lds {
-  static constexpr int kVStride = D + 8;  // bf16/f16 elements per staged V row (16-byte padded)
-  static constexpr int kAccStride = D + 4;  // floats per merged accumulator row
-  static constexpr int kVBytes = kNW * 16 * kVStride * 2;
-  static constexpr int kMergeBytes = (2 * kNW * RT * 16 + 2 * RT * 16) * 4 + RT * 16 * kAccStride * 4;
-  static constexpr int kFinalBytes = (2 * kMergeSlots * 64 + 2 * 64) * 4;  // (m, l) staging + row scalars
-  static constexpr int kBytes0 = kVBytes > kMergeBytes ? kVBytes : kMergeBytes;
-  static constexpr int kBytes = (kBytes0 > kFinalBytes ? kBytes0 : kFinalBytes) + 16;
+struct Shape {
+  static constexpr int NW = waves_for(D, RT);
+  static constexpr int kThreads = NW * 64;
+  static constexpr int KC = D / 32;  // 32-wide head-dim chunks (QK^T MFMA steps)
+  static constexpr int DT = D / 16;  // 16-wide head-dim tiles of the output
+  static constexpr int kVStride = D + 8;    // elements per staged V row (16-byte padded)
+  static constexpr int kAccStride = D + 4;  // floats per accumulator row in LDS
+  static constexpr int kRows = RT * 16;
+  // LDS: V staging during the tile loop; afterwards the wave-combine area,
+  // then the merge staging.  The last 16 bytes hold the arrival flag.
+  static constexpr int kVBytes = NW * 16 * kVStride * 2;
+  static constexpr int kCombineBytes = (2 * NW * kRows) * 4 + (NW / 2) * kRows * kAccStride * 4;
+  static constexpr int kMergeBytes = (2 * kMergeSlots * kMaxWgRows + 2 * kMaxWgRows) * 4;
+  static constexpr int kMax0 = kVBytes > kCombineBytes ? kVBytes : kCombineBytes;
+  static constexpr int kBytes = (kMax0 > kMergeBytes ? kMax0 : kMergeBytes) + 16;
+  // Merge load batch: IB output items x JC partial slots per thread.
+  static constexpr int kItemsPerThread = (kRows * (D / 4) + kThreads - 1) / kThreads;
+  static constexpr int IB = kItemsPerThread < 1 ? 1 : (kItemsPerThread > 4 ? 4 : kItemsPerThread);
+  static constexpr int JC = (NW == 8 ? 16 : 32) / IB;
 };
 
-// Write zeros to the output rows [row0, row0 + nrows) of (s, kvh).
-template <typename T, int D>
-__device__ void zero_rows(const Params& p, int s, int kvh, int row0, int nrows) {
-  T* out = static_cast<T*>(p.out);
-  const int items = nrows * (D / 8);
-  for (int it = threadIdx.x; it < items; it += kThreads) {
-    const int r = it / (D / 8), d8 = it % (D / 8);
-    const int ru = row0 + r, m = ru / p.group, gq = ru % p.group;
-    T* dst = out + ((int64_t(s) * p.query_len + m) * p.num_q_heads + kvh * p.group + gq) * D + 8 * d8;
-    *reinterpret_cast<i32x4*>(dst) = i32x4{0, 0, 0, 0};
-  }
+template <typename T>
+__device__ __forceinline__ T* out_row(const Params& p, T* out_s, int kvh, int ru, int D) {
+  const int m = ru / p.group, gq = ru % p.group;
+  return out_s + (int64_t(m) * p.num_q_heads + kvh * p.group + gq) * D;
 }
 
 // Merge `count` split partials (slots first_slot .. first_slot + count - 1
@@ -109,35 +134,55 @@ __device__ void zero_rows(const Params& p, int s, int kvh, int row0, int nrows) 
 // log-sum-exp merge m* = max m_j, l* = sum l_j 2^(m_j - m*),
 // acc* = sum acc_j 2^(m_j - m*), in slot order (bitwise deterministic).
 // With `out_final` the normalised result acc*/l* goes to the output rows;
-// otherwise (acc*, m*, l*) becomes partial slot `dst_slot`.
+// otherwise (acc*, m*, l*) becomes partial slot `dst_slot` (coherent
+// stores).  The caller has acquired the partials.
 template <typename T, int D, int RT>
 __device__ void merge_slots(const Params& p, unsigned char* lds, int64_t unit_slot0, int first_slot, int count,
-                            int row0, int wg_rows, bool out_final, int dst_slot, T* out_rows_base_s, int kvh) {
+                            int row0, int wg_rows, bool out_final, int dst_slot, T* out_s, int kvh) {
+  using SH = Shape<D, RT>;
   using MF = Mfma<T>;
+  constexpr int IB = SH::IB, JC = SH::JC, NT = SH::kThreads;
+  constexpr int kMlPerThread = (kMergeSlots * kMaxWgRows + NT - 1) / NT;
   const int tid = threadIdx.x;
-  float2* sm_ml = reinterpret_cast<float2*>(lds);                  // [count][wg_rows]
-  float* sm_ms = reinterpret_cast<float*>(lds) + 2 * kMergeSlots * 64;  // [wg_rows]
-  float* sm_ls = sm_ms + 64;                                        // [wg_rows]
+  float2* sm_ml = reinterpret_cast<float2*>(lds);                               // [count][wg_rows]
+  float* sm_ms = reinterpret_cast<float*>(lds) + 2 * kMergeSlots * kMaxWgRows;  // [wg_rows]
+  float* sm_ls = sm_ms + kMaxWgRows;                                            // [wg_rows]
+  const int64_t jstride = int64_t(p.rows) * D;
+  const float* src0 = p.ws_acc + ((unit_slot0 + first_slot) * p.rows + row0) * D;
+  const int items = wg_rows * (D / 4);
+
+  // All (m, l) loads, then the first batch of partial-acc loads, go out
+  // before anything waits.
   const int n = count * wg_rows;
-  // Stage every (m, l) pair with all loads in flight at once.
-  for (int base = 0; base < n; base += kThreads * 8) {
-    float2 v[8];
+  float2 mlv[kMlPerThread];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int idx = base + u * kThreads + tid;
-      if (idx < n) {
-        const int j = idx / wg_rows, r = idx % wg_rows;
-        v[u] = *reinterpret_cast<const float2*>(p.ws_ml + ((unit_slot0 + first_slot + j) * p.rows + row0 + r) * 2);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int idx = base + u * kThreads + tid;
-      if (idx < n) sm_ml[idx] = v[u];
+  for (int u = 0; u < kMlPerThread; ++u) {
+    const int idx = u * NT + tid;
+    if (idx < n) {
+      const int j = idx / wg_rows, r = idx % wg_rows;
+      mlv[u] = *reinterpret_cast<const float2*>(p.ws_ml + ((unit_slot0 + first_slot + j) * p.rows + row0 + r) * 2);
     }
   }
+  f32x4 v[IB][JC];
+  auto load_batch = [&](int it0, int j0) {
+#pragma unroll
+    for (int b = 0; b < IB; ++b) {
+      const int it = it0 + b * NT;
+      const int r = it / (D / 4), d4 = it % (D / 4);
+      const float* src = src0 + int64_t(r) * D + 4 * d4;
+#pragma unroll
+      for (int u = 0; u < JC; ++u)
+        if (it < items && j0 + u < count) v[b][u] = *reinterpret_cast<const f32x4*>(src + (j0 + u) * jstride);
+    }
+  };
+  load_batch(tid, 0);
+#pragma unroll
+  for (int u = 0; u < kMlPerThread; ++u) {
+    const int idx = u * NT + tid;
+    if (idx < n) sm_ml[idx] = mlv[u];
+  }
   __syncthreads();
-  for (int r = tid; r < wg_rows; r += kThreads) {
+  for (int r = tid; r < wg_rows; r += NT) {
     float ms = kNegInf;
     for (int j = 0; j < count; ++j) ms = fmaxf(ms, sm_ml[j * wg_rows + r].x);
     const float mu = ms == kNegInf ? 0.f : ms;
@@ -152,56 +197,53 @@ __device__ void merge_slots(const Params& p, unsigned char* lds, int64_t unit_sl
     sm_ls[r] = ls;
   }
   __syncthreads();
-  const int64_t jstride = int64_t(p.rows) * D;
-  const float* src0 = p.ws_acc + ((unit_slot0 + first_slot) * p.rows + row0) * D;
-  float* dst0 = p.ws_acc + ((unit_slot0 + dst_slot) * p.rows + row0) * D;
-  const int items = wg_rows * (D / 4);
-  for (int it = tid; it < items; it += kThreads) {
-    const int r = it / (D / 4), d4 = it % (D / 4);
-    const float* src = src0 + int64_t(r) * D + 4 * d4;
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < count; j0 += 8) {
-      f32x4 v[8];
+
+  for (int it0 = tid; it0 < items; it0 += IB * NT) {
+    f32x4 a[IB];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (j0 + u < count) v[u] = *reinterpret_cast<const f32x4*>(src + (j0 + u) * jstride);
+    for (int b = 0; b < IB; ++b) a[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < count; j0 += JC) {
+      if (j0 > 0 || it0 != tid) load_batch(it0, j0);
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (j0 + u < count) a += sm_ml[(j0 + u) * wg_rows + r].x * v[u];
+      for (int b = 0; b < IB; ++b) {
+        const int it = it0 + b * NT;
+        const int r = it / (D / 4);
+#pragma unroll
+        for (int u = 0; u < JC; ++u)
+          if (it < items && j0 + u < count) a[b] += sm_ml[(j0 + u) * wg_rows + r].x * v[b][u];
+      }
     }
-    if (out_final) {
-      const float ls = sm_ls[r];
-      const float inv = ls > 0.f ? 1.f / ls : 0.f;
-      const int ru = row0 + r, m = ru / p.group, gq = ru % p.group;
-      T* dst = out_rows_base_s + (int64_t(m) * p.num_q_heads + kvh * p.group + gq) * D + 4 * d4;
-      uint2 v;
-      v.x = uint32_t(MF::bits(a[0] * inv)) | (uint32_t(MF::bits(a[1] * inv)) << 16);
-      v.y = uint32_t(MF::bits(a[2] * inv)) | (uint32_t(MF::bits(a[3] * inv)) << 16);
-      *reinterpret_cast<uint2*>(dst) = v;
-    } else {
-      *reinterpret_cast<f32x4*>(dst0 + int64_t(r) * D + 4 * d4) = a;
+#pragma unroll
+    for (int b = 0; b < IB; ++b) {
+      const int it = it0 + b * NT;
+      if (it >= items) continue;
+      const int r = it / (D / 4), d4 = it % (D / 4);
+      if (out_final) {
+        const float ls = sm_ls[r];
+        const float inv = ls > 0.f ? 1.f / ls : 0.f;
+        uint2 o;
+        o.x = uint32_t(MF::bits(a[b][0] * inv)) | (uint32_t(MF::bits(a[b][1] * inv)) << 16);
+        o.y = uint32_t(MF::bits(a[b][2] * inv)) | (uint32_t(MF::bits(a[b][3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(out_row(p, out_s, kvh, row0 + r, D) + 4 * d4) = o;
+      } else {
+        store_coherent(p.ws_acc + ((unit_slot0 + dst_slot) * p.rows + row0 + r) * D + 4 * d4, a[b]);
+      }
     }
   }
   if (!out_final) {
-    for (int r = tid; r < wg_rows; r += kThreads) {
-      float* ml = p.ws_ml + ((unit_slot0 + dst_slot) * p.rows + row0 + r) * 2;
-      ml[0] = sm_ms[r];
-      ml[1] = sm_ls[r];
-    }
+    for (int r = tid; r < wg_rows; r += NT)
+      store_coherent2(p.ws_ml + ((unit_slot0 + dst_slot) * p.rows + row0 + r) * 2, sm_ms[r], sm_ls[r]);
   }
 }
 
-// Release this workgroup's global writes, bump `counter` and tell whether
-// this workgroup arrived last of `expected`; the last one acquires.  Each
-// wave first waits for its own stores; then one thread makes the release at
-// device scope (a single L2 write-back for the whole workgroup), does the
-// atomic and, if last, the acquire (invalidating this CU's L1 and stale L2
-// lines before the merge reads the other workgroups' partials).
+// Count this workgroup's arrival on `counter` once every wave's partial
+// stores (device-coherent) have completed; returns whether it arrived last
+// of `expected`.  The last arriver invalidates stale cache lines (acquire)
+// before it reads the other workgroups' partials.
 __device__ __forceinline__ bool arrive(int* counter, int expected, int* sm_flag) {
   __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
   __syncthreads();
   if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = prev == expected - 1;
     if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -211,14 +253,23 @@ __device__ __forceinline__ bool arrive(int* counter, int expected, int* sm_flag)
   return *sm_flag;
 }
 
+template <typename T, int D>
+__device__ void zero_rows(const Params& p, int s, int kvh, int row0, int nrows, int nthreads) {
+  T* out_s = static_cast<T*>(p.out) + int64_t(s) * p.query_len * p.num_q_heads * D;
+  const int items = nrows * (D / 8);
+  for (int it = threadIdx.x; it < items; it += nthreads) {
+    const int r = it / (D / 8), d8 = it % (D / 8);
+    *reinterpret_cast<i32x4*>(out_row(p, out_s, kvh, row0 + r, D) + 8 * d8) = i32x4{0, 0, 0, 0};
+  }
+}
+
 template <typename T, int D, int RT>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p) {
+__global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(Params p) {
   using MF = Mfma<T>;
-  using LD = Lds<D, RT>;
-  constexpr int KC = D / 32;  // 32-wide head-dim chunks (QK^T MFMA steps)
-  constexpr int DT = D / 16;  // 16-wide head-dim tiles of the output
+  using SH = Shape<D, RT>;
+  constexpr int NW = SH::NW, KC = SH::KC, DT = SH::DT;
   constexpr bool kPrefetch = D <= 256;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[LD::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[SH::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -236,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p) {
 
   const int L = p.seq_lens[s];
   if (L <= 0) {
-    if (seg == 0) zero_rows<T, D>(p, s, kvh, row0, wg_rows);
+    if (seg == 0) zero_rows<T, D>(p, s, kvh, row0, wg_rows, SH::kThreads);
     return;
   }
   const int k_lo = p.window > 0 ? max(0, L - M - p.window + 1) : 0;
@@ -290,11 +341,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p) {
   // head-dim elements 8g..8g+7 of chunk 0 (32-bit, per lane); the tile base
   // itself is wave-uniform, so the loads take a scalar base address.
   const uint32_t lane_off = uint32_t(c * p.token_stride + 8 * g) * uint32_t(sizeof(T));
-  uint16_t* vs = reinterpret_cast<uint16_t*>(lds) + wave * 16 * LD::kVStride;
+  uint16_t* vs = reinterpret_cast<uint16_t*>(lds) + wave * 16 * SH::kVStride;
   // Transposed-read address of this lane: row 4g + c/4, columns 4(c%4).. of
   // each 16-column tile (ds_read_b64_tr_b16 returns column c of the 4x16
   // block its 16-lane group addresses, i.e. 4 keys of one head-dim column).
-  const uint16_t* vtr = vs + (4 * g + (c >> 2)) * LD::kVStride + 4 * (c & 3);
+  const uint16_t* vtr = vs + (4 * g + (c >> 2)) * SH::kVStride + 4 * (c & 3);
 
   struct Tile {
     i32x4 k[KC];
@@ -329,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p) {
     }
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
-      *reinterpret_cast<i32x4*>(vs + c * LD::kVStride + 32 * kc + 8 * g) = tl.v[kc];
+      *reinterpret_cast<i32x4*>(vs + c * SH::kVStride + 32 * kc + 8 * g) = tl.v[kc];
 
     uint64_t pb[RT];
 #pragma unroll
@@ -387,8 +438,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p) {
   // has the same loads in flight and the compiler's wait counts stay exact
   // (the clamped re-read of the last tile hits in cache).
   const int first_t = ts + wave;
-  const int n_w = first_t < te ? (te - first_t + kNW - 1) / kNW : 0;
-  auto tile_at = [&](int i) { return first_t + min(i, n_w - 1) * kNW; };
+  const int n_w = first_t < te ? (te - first_t + NW - 1) / NW : 0;
+  auto tile_at = [&](int i) { return first_t + min(i, n_w - 1) * NW; };
   if (n_w > 0) {
     if constexpr (kPrefetch) {
       Tile ta, tb;
@@ -397,121 +448,123 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p) {
       for (int i = 0;;) {
         issue_tile(tb, tile_at(i + 1), blk_next);
         blk_next = block_of(tile_at(i + 2));
-        compute_tile(ta, first_t + i * kNW);
+        compute_tile(ta, first_t + i * NW);
         if (++i >= n_w) break;
         issue_tile(ta, tile_at(i + 1), blk_next);
         blk_next = block_of(tile_at(i + 2));
-        compute_tile(tb, first_t + i * kNW);
+        compute_tile(tb, first_t + i * NW);
         if (++i >= n_w) break;
       }
     } else {
       Tile ta;
       int blk = block_of(tile_at(0));
       for (int i = 0; i < n_w; ++i) {
-        issue_tile(ta, first_t + i * kNW, blk);
+        issue_tile(ta, first_t + i * NW, blk);
         blk = block_of(tile_at(i + 1));
-        compute_tile(ta, first_t + i * kNW);
+        compute_tile(ta, first_t + i * NW);
       }
     }
   }
 
-  // ---- combine the four waves (fixed order: bitwise deterministic) ----
+  // ---- combine the waves: pairwise halving, fixed order (deterministic) ----
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     l_run[rt] += __shfl_xor(l_run[rt], 16);
     l_run[rt] += __shfl_xor(l_run[rt], 32);
   }
   __syncthreads();  // V staging area is reused below
-  float* sm_m = reinterpret_cast<float*>(lds);   // [NW][RT*16]
-  float* sm_l = sm_m + kNW * RT * 16;            // [NW][RT*16]
-  float* sm_ms = sm_l + kNW * RT * 16;           // [RT*16] merged max
-  float* sm_ls = sm_ms + RT * 16;                // [RT*16] merged sum
-  float* sm_acc = sm_ls + RT * 16;               // [RT*16][kAccStride]
+  float* sm_m = reinterpret_cast<float*>(lds);  // [NW][kRows]
+  float* sm_l = sm_m + NW * SH::kRows;           // [NW][kRows]
+  float* sm_acc = sm_l + NW * SH::kRows;         // [NW/2][kRows][kAccStride]
   if (g == 0) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      sm_m[wave * RT * 16 + rt * 16 + c] = m_run[rt];
-      sm_l[wave * RT * 16 + rt * 16 + c] = l_run[rt];
+      sm_m[wave * SH::kRows + rt * 16 + c] = m_run[rt];
+      sm_l[wave * SH::kRows + rt * 16 + c] = l_run[rt];
     }
   }
   __syncthreads();
+  float ms_r[RT], ls_r[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int r = rt * 16 + c;
     float ms = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) ms = fmaxf(ms, sm_m[w * RT * 16 + r]);
+    for (int w = 0; w < NW; ++w) ms = fmaxf(ms, sm_m[w * SH::kRows + r]);
     const float mu = ms == kNegInf ? 0.f : ms;
     float ls = 0.f;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) ls += sm_l[w * RT * 16 + r] * fast_exp2(sm_m[w * RT * 16 + r] - mu);
+    for (int w = 0; w < NW; ++w) ls += sm_l[w * SH::kRows + r] * fast_exp2(sm_m[w * SH::kRows + r] - mu);
     const float f = fast_exp2(m_run[rt] - mu);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= f;
-    if (wave == 0 && g == 0) {
-      sm_ms[r] = ms;
-      sm_ls[r] = ls;
-    }
+    ms_r[rt] = ms;
+    ls_r[rt] = ls;
   }
 #pragma unroll
-  for (int w = 0; w < kNW; ++w) {
-    if (wave == w) {
+  for (int half = NW / 2; half >= 1; half /= 2) {
+    if (wave >= half && wave < 2 * half) {
+      float* slot = sm_acc + (wave - half) * SH::kRows * SH::kAccStride;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          f32x4* dst = reinterpret_cast<f32x4*>(sm_acc + (rt * 16 + c) * LD::kAccStride + 16 * dt + 4 * g);
-          if (w == 0)
-            *dst = acc[rt][dt];
-          else
-            *dst += acc[rt][dt];
-        }
-      }
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<f32x4*>(slot + (rt * 16 + c) * SH::kAccStride + 16 * dt + 4 * g) = acc[rt][dt];
+    }
+    __syncthreads();
+    if (wave < half) {
+      const float* slot = sm_acc + wave * SH::kRows * SH::kAccStride;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          acc[rt][dt] += *reinterpret_cast<const f32x4*>(slot + (rt * 16 + c) * SH::kAccStride + 16 * dt + 4 * g);
     }
     __syncthreads();
   }
+  // Wave 0 now holds the workgroup's (acc, m, l) for its rows.
 
   T* out_s = static_cast<T*>(p.out) + int64_t(s) * M * p.num_q_heads * D;
   if (n_live == 1) {
-    for (int it = tid; it < wg_rows * (D / 8); it += kThreads) {
-      const int r = it / (D / 8), d8 = it % (D / 8);
-      const float ls = sm_ls[r];
-      const float inv = ls > 0.f ? 1.f / ls : 0.f;
-      const float* a = sm_acc + r * LD::kAccStride + 8 * d8;
-      uint16_t h[8];
+    if (wave == 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = MF::bits(a[e] * inv);
-      i32x4 v;
+      for (int rt = 0; rt < RT; ++rt) {
+        const int r = rt * 16 + c;
+        if (r >= wg_rows) continue;
+        const float inv = ls_r[rt] > 0.f ? 1.f / ls_r[rt] : 0.f;
+        T* dst = out_row(p, out_s, kvh, row0 + r, D) + 4 * g;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = int(uint32_t(h[2 * e]) | (uint32_t(h[2 * e + 1]) << 16));
-      const int ru = row0 + r, m = ru / p.group, gq = ru % p.group;
-      *reinterpret_cast<i32x4*>(out_s + (int64_t(m) * p.num_q_heads + kvh * p.group + gq) * D + 8 * d8) = v;
+        for (int dt = 0; dt < DT; ++dt) {
+          uint2 o;
+          o.x = uint32_t(MF::bits(acc[rt][dt][0] * inv)) | (uint32_t(MF::bits(acc[rt][dt][1] * inv)) << 16);
+          o.y = uint32_t(MF::bits(acc[rt][dt][2] * inv)) | (uint32_t(MF::bits(acc[rt][dt][3] * inv)) << 16);
+          *reinterpret_cast<uint2*>(dst + 16 * dt) = o;
+        }
+      }
     }
     return;
   }
 
-  // ---- split-KV partial, then a two-level arrival tree ----
+  // ---- split-KV partial, then the arrival tree ----
   // Segments form groups of kMergeGroup; the last arriver of a group merges
   // the group's partials (into the output when there is one group, else
   // into a group partial); the last group to finish merges the groups.
   const int ngroups = (n_live + kMergeGroup - 1) / kMergeGroup;
-  const int nslots = p.nseg + (p.nseg + kMergeGroup - 1) / kMergeGroup;  // segment + group slots
-  const int64_t unit_slot0 = (int64_t(s) * p.num_kv_heads + kvh) * nslots;
-  {
+  const int ngmax = (p.nseg + kMergeGroup - 1) / kMergeGroup;
+  const int64_t unit_slot0 = (int64_t(s) * p.num_kv_heads + kvh) * (p.nseg + ngmax);
+  if (wave == 0) {
     const int64_t base = (unit_slot0 + seg) * p.rows + row0;
-    for (int it = tid; it < wg_rows * (D / 4); it += kThreads) {
-      const int r = it / (D / 4), d4 = it % (D / 4);
-      *reinterpret_cast<f32x4*>(p.ws_acc + (base + r) * D + 4 * d4) =
-          *reinterpret_cast<const f32x4*>(sm_acc + r * LD::kAccStride + 4 * d4);
-    }
-    for (int r = tid; r < wg_rows; r += kThreads) {
-      p.ws_ml[(base + r) * 2 + 0] = sm_ms[r];
-      p.ws_ml[(base + r) * 2 + 1] = sm_ls[r];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int r = rt * 16 + c;
+      if (r >= wg_rows) continue;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) store_coherent(p.ws_acc + (base + r) * D + 16 * dt + 4 * g, acc[rt][dt]);
+      if (g == 0) store_coherent2(p.ws_ml + (base + r) * 2, ms_r[rt], ls_r[rt]);
     }
   }
-  const int ngmax = (p.nseg + kMergeGroup - 1) / kMergeGroup;
   int* counters = p.ws_cnt + ((int64_t(s) * p.num_kv_heads + kvh) * p.row_groups + rg) * (1 + ngmax);
-  int* sm_flag = reinterpret_cast<int*>(lds + LD::kBytes - 16);
+  int* sm_flag = reinterpret_cast<int*>(lds + SH::kBytes - 16);
   const int grp = seg / kMergeGroup;
   const int gsize = min(kMergeGroup, n_live - grp * kMergeGroup);
   if (!arrive(counters + 1 + grp, gsize, sm_flag)) return;
@@ -534,7 +587,8 @@ __global__ void zero_kernel(uint32_t* p, size_t n) {
 
 template <typename T, int D, int RT>
 int launch_t(const Plan& pl, const Params& pr, hipStream_t st) {
-  hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT>), dim3(pl.grid_x, pl.grid_y), dim3(kThreads), 0, st, pr);
+  hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT>), dim3(pl.grid_x, pl.grid_y), dim3(Shape<D, RT>::kThreads), 0,
+                     st, pr);
   return int(hipGetLastError());
 }
 

@@ -46,11 +46,11 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   Plan p{};
   p.path = PAD_PATH_MFMA;
   p.rows = rows;
-  p.waves = kWaves;
   const int tiles_total = int(ceil_div(rows, 16));
   int rt = std::min(tiles_total, max_row_tiles(sh.head_size));
   p.row_groups = int(ceil_div(tiles_total, rt));
   p.row_tiles = int(ceil_div(tiles_total, p.row_groups));
+  p.waves = waves_for(sh.head_size, p.row_tiles);
 
   // Keys one unit may have to read: the whole table bound, or the window
   // span (window + M - 1 keys) plus one tile of alignment slack.
@@ -66,8 +66,8 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   span_tiles = std::max<int64_t>(1, span_tiles);
 
   const int64_t units = int64_t(sh.num_seqs) * sh.num_kv_heads * p.row_groups;
-  const int resident = (sh.head_size * p.row_tiles <= 128) ? 2 : 1;  // workgroups per CU
-  const int64_t slots = int64_t(num_cus) * resident;
+  // One workgroup fills a CU (8 waves at two per SIMD, or 4 large waves).
+  const int64_t slots = num_cus;
   int64_t nseg;
   if (sh.num_segments > 0) {
     nseg = sh.num_segments;

@@ -20,13 +20,16 @@
 namespace pad {
 
 constexpr int kTileKeys = 16;    // keys per MFMA tile (page sizes are multiples of 16)
-constexpr int kWaves = 4;        // waves per workgroup
 constexpr int kMaxSegments = 256;
-constexpr int kMergeGroupSize = 8;  // segments merged per group of the two-level merge tree
+constexpr int kMergeGroupSize = 32;  // segments merged per group of the two-level merge tree
 // Arrival counters live in a fixed-size prefix of the workspace, so calls of
 // different shapes can share one workspace: partials never land where any
 // shape keeps counters, and every call leaves its counters zero.
 constexpr size_t kCounterBytes = size_t(1) << 20;
+
+// Waves per workgroup: eight when a wave's state (accumulator of
+// head_size x 16 x row_tiles) allows two waves per SIMD, else four.
+constexpr int waves_for(int head_size, int row_tiles) { return head_size * row_tiles <= 128 ? 8 : 4; }
 
 struct Plan {
   int path;          // PAD_PATH_MFMA / PAD_PATH_DOT

@@ -85,9 +85,9 @@ def test_plan_invariants(kw):
         assert p["workspace_bytes"] == 0
     else:
         # a fixed 1 MiB counter prefix, then segment slots plus one slot per
-        # merge group of 8 segments
+        # merge group of 32 segments
         S, H, n = sh.num_seqs, sh.num_kv_heads, p["num_segments"]
-        ng = -(-n // 8)
+        ng = -(-n // 32)
         want = (1 << 20) + _align(S * H * (n + ng) * rows * 2 * 4) + _align(S * H * (n + ng) * rows * sh.head_size * 4)
         assert p["workspace_bytes"] == want
 
