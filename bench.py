@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 POOL_BYTES = 512 << 20
+COPY_BYTES = 256 << 20  # --copy-calibration: bytes read (and written) per copy
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_config2.json")
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_decode_block_amd", "csrc", "decode_mfma.hip")
 
@@ -159,6 +160,8 @@ def main() -> int:
     ap.add_argument("--queries", type=int, default=None)
     ap.add_argument("--no-sweep", action="store_true", help="skip the per-(context, M) sweep of the config")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run device copies of COPY_BYTES (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the decode-attention path has no multi-GPU mode "
@@ -189,6 +192,13 @@ def main() -> int:
     wall = time.perf_counter() - t0
     print(f"[bench] timed {args.steps} steps: {ms * 1e3:.2f} us/step", file=sys.stderr, flush=True)
     gbs = nbytes / (ms * 1e-3) / 1e9
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").normal_()
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     sweep = []
     if not args.no_sweep:

@@ -110,17 +110,19 @@ struct Shape {
   static constexpr int kVStride = D + 8;    // elements per staged V row (16-byte padded)
   static constexpr int kAccStride = D + 4;  // floats per accumulator row in LDS
   static constexpr int kRows = RT * 16;
+  // Tiles in flight beyond the one being computed (register budget).
+  static constexpr int PF = D * RT <= 128 ? 2 : (D * RT <= 256 ? 1 : 0);
   // LDS: V staging during the tile loop; afterwards the wave-combine area,
   // then the merge staging.  The last 16 bytes hold the arrival flag.
   static constexpr int kVBytes = NW * 16 * kVStride * 2;
-  static constexpr int kCombineBytes = (2 * NW * kRows) * 4 + (NW / 2) * kRows * kAccStride * 4;
+  static constexpr int kCombineBytes = (2 * NW * kRows + 2 * kRows) * 4 + NW * kRows * kAccStride * 4;
   static constexpr int kMergeBytes = (2 * kMergeSlots * kMaxWgRows + 2 * kMaxWgRows) * 4;
   static constexpr int kMax0 = kVBytes > kCombineBytes ? kVBytes : kCombineBytes;
   static constexpr int kBytes = (kMax0 > kMergeBytes ? kMax0 : kMergeBytes) + 16;
   // Merge load batch: IB output items x JC partial slots per thread.
   static constexpr int kItemsPerThread = (kRows * (D / 4) + kThreads - 1) / kThreads;
   static constexpr int IB = kItemsPerThread < 1 ? 1 : (kItemsPerThread > 4 ? 4 : kItemsPerThread);
-  static constexpr int JC = (NW == 8 ? 16 : 32) / IB;
+  static constexpr int JC = 32 / IB;
 };
 
 template <typename T>
@@ -137,7 +139,7 @@ __device__ __forceinline__ T* out_row(const Params& p, T* out_s, int kvh, int ru
 // otherwise (acc*, m*, l*) becomes partial slot `dst_slot` (coherent
 // stores).  The caller has acquired the partials.
 template <typename T, int D, int RT>
-__device__ void merge_slots(const Params& p, unsigned char* lds, int64_t unit_slot0, int first_slot, int count,
+__device__ __forceinline__ void merge_slots(const Params& p, unsigned char* lds, int64_t unit_slot0, int first_slot, int count,
                             int row0, int wg_rows, bool out_final, int dst_slot, T* out_s, int kvh) {
   using SH = Shape<D, RT>;
   using MF = Mfma<T>;
@@ -164,15 +166,19 @@ __device__ void merge_slots(const Params& p, unsigned char* lds, int64_t unit_sl
     }
   }
   f32x4 v[IB][JC];
+  // Slot bases are uniform (scalar), the item offset is a 32-bit per-lane
+  // value: no per-load 64-bit address registers.
   auto load_batch = [&](int it0, int j0) {
 #pragma unroll
     for (int b = 0; b < IB; ++b) {
       const int it = it0 + b * NT;
       const int r = it / (D / 4), d4 = it % (D / 4);
-      const float* src = src0 + int64_t(r) * D + 4 * d4;
+      const uint32_t off = uint32_t(r * D + 4 * d4) * 4u;
 #pragma unroll
       for (int u = 0; u < JC; ++u)
-        if (it < items && j0 + u < count) v[b][u] = *reinterpret_cast<const f32x4*>(src + (j0 + u) * jstride);
+        if (it < items && j0 + u < count)
+          v[b][u] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const unsigned char*>(src0 + (j0 + u) * jstride) +
+                                                    off);
     }
   };
   load_batch(tid, 0);
@@ -182,19 +188,25 @@ __device__ void merge_slots(const Params& p, unsigned char* lds, int64_t unit_sl
     if (idx < n) sm_ml[idx] = mlv[u];
   }
   __syncthreads();
-  for (int r = tid; r < wg_rows; r += NT) {
-    float ms = kNegInf;
-    for (int j = 0; j < count; ++j) ms = fmaxf(ms, sm_ml[j * wg_rows + r].x);
+  // Per row, one lane per slot (32-lane halves of a wave): max and sum by
+  // butterfly reductions in a fixed pattern (deterministic).
+  static_assert(kMergeSlots <= 32, "one lane per merged slot");
+  for (int r = tid >> 5; r < wg_rows; r += NT / 32) {
+    const int j = tid & 31;
+    const float2 ml = j < count ? sm_ml[j * wg_rows + r] : float2{kNegInf, 0.f};
+    float ms = ml.x;
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) ms = fmaxf(ms, __shfl_xor(ms, off, 32));
     const float mu = ms == kNegInf ? 0.f : ms;
-    float ls = 0.f;
-    for (int j = 0; j < count; ++j) {
-      const float2 ml = sm_ml[j * wg_rows + r];
-      const float w = fast_exp2(ml.x - mu);
-      sm_ml[j * wg_rows + r].x = w;  // weight of slot j for this row
-      ls += w * ml.y;
+    const float w = j < count ? fast_exp2(ml.x - mu) : 0.f;
+    float ls = w * ml.y;
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) ls += __shfl_xor(ls, off, 32);
+    if (j < count) sm_ml[j * wg_rows + r].x = w;  // weight of slot j for this row
+    if (j == 0) {
+      sm_ms[r] = ms;
+      sm_ls[r] = ls;
     }
-    sm_ms[r] = ms;
-    sm_ls[r] = ls;
   }
   __syncthreads();
 
@@ -254,7 +266,7 @@ __device__ __forceinline__ bool arrive(int* counter, int expected, int* sm_flag)
 }
 
 template <typename T, int D>
-__device__ void zero_rows(const Params& p, int s, int kvh, int row0, int nrows, int nthreads) {
+__device__ __forceinline__ void zero_rows(const Params& p, int s, int kvh, int row0, int nrows, int nthreads) {
   T* out_s = static_cast<T*>(p.out) + int64_t(s) * p.query_len * p.num_q_heads * D;
   const int items = nrows * (D / 8);
   for (int it = threadIdx.x; it < items; it += nthreads) {
@@ -268,7 +280,6 @@ __global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(P
   using MF = Mfma<T>;
   using SH = Shape<D, RT>;
   constexpr int NW = SH::NW, KC = SH::KC, DT = SH::DT;
-  constexpr bool kPrefetch = D <= 256;
   __shared__ __attribute__((aligned(16))) unsigned char lds[SH::kBytes];
 
   const int tid = threadIdx.x;
@@ -432,41 +443,34 @@ __global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(P
   };
 
   // Interleaved tiles per wave: tile i of this wave is ts + wave + i * NW.
-  // A tile's loads are issued before the previous tile is computed and its
-  // block id is read one tile earlier still.  The prefetch index is clamped
-  // to the wave's last tile instead of being skipped, so every iteration
-  // has the same loads in flight and the compiler's wait counts stay exact
-  // (the clamped re-read of the last tile hits in cache).
+  // PF tiles are in flight beyond the one being computed (a ring of PF + 1
+  // register buffers), and each tile's block id is read one tile before
+  // its loads are issued.  The prefetch index is clamped to the wave's last
+  // tile instead of being skipped, so every iteration has the same loads in
+  // flight and the compiler's wait counts stay exact (the clamped re-reads
+  // of the last tile hit in cache).
   const int first_t = ts + wave;
   const int n_w = first_t < te ? (te - first_t + NW - 1) / NW : 0;
   auto tile_at = [&](int i) { return first_t + min(i, n_w - 1) * NW; };
   if (n_w > 0) {
-    if constexpr (kPrefetch) {
-      Tile ta, tb;
-      issue_tile(ta, tile_at(0), block_of(tile_at(0)));
-      int blk_next = block_of(tile_at(1));
-      for (int i = 0;;) {
-        issue_tile(tb, tile_at(i + 1), blk_next);
-        blk_next = block_of(tile_at(i + 2));
-        compute_tile(ta, first_t + i * NW);
-        if (++i >= n_w) break;
-        issue_tile(ta, tile_at(i + 1), blk_next);
-        blk_next = block_of(tile_at(i + 2));
-        compute_tile(tb, first_t + i * NW);
-        if (++i >= n_w) break;
-      }
-    } else {
-      Tile ta;
-      int blk = block_of(tile_at(0));
-      for (int i = 0; i < n_w; ++i) {
-        issue_tile(ta, first_t + i * NW, blk);
-        blk = block_of(tile_at(i + 1));
-        compute_tile(ta, first_t + i * NW);
+    Tile ring[SH::PF + 1];
+#pragma unroll
+    for (int u = 0; u < SH::PF; ++u) issue_tile(ring[u], tile_at(u), block_of(tile_at(u)));
+    int blk_next = block_of(tile_at(SH::PF));
+    for (int i = 0;; i += SH::PF + 1) {
+#pragma unroll
+      for (int u = 0; u <= SH::PF; ++u) {
+        issue_tile(ring[(u + SH::PF) % (SH::PF + 1)], tile_at(i + u + SH::PF), blk_next);
+        blk_next = block_of(tile_at(i + u + SH::PF + 1));
+        compute_tile(ring[u], first_t + (i + u) * NW);
+        if (i + u + 1 >= n_w) goto tiles_done;
       }
     }
   }
+tiles_done:
 
-  // ---- combine the waves: pairwise halving, fixed order (deterministic) ----
+  // ---- combine the waves (one LDS slot per wave, summed in wave order:
+  //      deterministic) ----
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     l_run[rt] += __shfl_xor(l_run[rt], 16);
@@ -475,7 +479,9 @@ __global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(P
   __syncthreads();  // V staging area is reused below
   float* sm_m = reinterpret_cast<float*>(lds);  // [NW][kRows]
   float* sm_l = sm_m + NW * SH::kRows;           // [NW][kRows]
-  float* sm_acc = sm_l + NW * SH::kRows;         // [NW/2][kRows][kAccStride]
+  float* sm_ms = sm_l + NW * SH::kRows;          // [kRows] merged max
+  float* sm_ls = sm_ms + SH::kRows;              // [kRows] merged sum
+  float* sm_acc = sm_ls + SH::kRows;             // [NW][kRows][kAccStride]
   if (g == 0) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -484,7 +490,6 @@ __global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(P
     }
   }
   __syncthreads();
-  float ms_r[RT], ls_r[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int r = rt * 16 + c;
@@ -492,55 +497,39 @@ __global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(P
 #pragma unroll
     for (int w = 0; w < NW; ++w) ms = fmaxf(ms, sm_m[w * SH::kRows + r]);
     const float mu = ms == kNegInf ? 0.f : ms;
-    float ls = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) ls += sm_l[w * SH::kRows + r] * fast_exp2(sm_m[w * SH::kRows + r] - mu);
     const float f = fast_exp2(m_run[rt] - mu);
+    float* slot = sm_acc + (wave * SH::kRows + r) * SH::kAccStride + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= f;
-    ms_r[rt] = ms;
-    ls_r[rt] = ls;
-  }
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(slot + 16 * dt) = acc[rt][dt] * f;
+    if (wave == 0 && g == 0) {
+      float ls = 0.f;
 #pragma unroll
-  for (int half = NW / 2; half >= 1; half /= 2) {
-    if (wave >= half && wave < 2 * half) {
-      float* slot = sm_acc + (wave - half) * SH::kRows * SH::kAccStride;
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<f32x4*>(slot + (rt * 16 + c) * SH::kAccStride + 16 * dt + 4 * g) = acc[rt][dt];
+      for (int w = 0; w < NW; ++w) ls += sm_l[w * SH::kRows + r] * fast_exp2(sm_m[w * SH::kRows + r] - mu);
+      sm_ms[r] = ms;
+      sm_ls[r] = ls;
     }
-    __syncthreads();
-    if (wave < half) {
-      const float* slot = sm_acc + wave * SH::kRows * SH::kAccStride;
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          acc[rt][dt] += *reinterpret_cast<const f32x4*>(slot + (rt * 16 + c) * SH::kAccStride + 16 * dt + 4 * g);
-    }
-    __syncthreads();
   }
-  // Wave 0 now holds the workgroup's (acc, m, l) for its rows.
+  __syncthreads();
+  // Thread-distributed result: item (row r, 4 head-dim columns d4).
+  auto combined = [&](int r, int d4) {
+    const float* col = sm_acc + r * SH::kAccStride + 4 * d4;
+    f32x4 a = *reinterpret_cast<const f32x4*>(col);
+#pragma unroll
+    for (int w = 1; w < NW; ++w) a += *reinterpret_cast<const f32x4*>(col + w * SH::kRows * SH::kAccStride);
+    return a;
+  };
 
   T* out_s = static_cast<T*>(p.out) + int64_t(s) * M * p.num_q_heads * D;
   if (n_live == 1) {
-    if (wave == 0) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int r = rt * 16 + c;
-        if (r >= wg_rows) continue;
-        const float inv = ls_r[rt] > 0.f ? 1.f / ls_r[rt] : 0.f;
-        T* dst = out_row(p, out_s, kvh, row0 + r, D) + 4 * g;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          uint2 o;
-          o.x = uint32_t(MF::bits(acc[rt][dt][0] * inv)) | (uint32_t(MF::bits(acc[rt][dt][1] * inv)) << 16);
-          o.y = uint32_t(MF::bits(acc[rt][dt][2] * inv)) | (uint32_t(MF::bits(acc[rt][dt][3] * inv)) << 16);
-          *reinterpret_cast<uint2*>(dst + 16 * dt) = o;
-        }
-      }
+    for (int it = tid; it < wg_rows * (D / 4); it += SH::kThreads) {
+      const int r = it / (D / 4), d4 = it % (D / 4);
+      const f32x4 a = combined(r, d4);
+      const float ls = sm_ls[r];
+      const float inv = ls > 0.f ? 1.f / ls : 0.f;
+      uint2 o;
+      o.x = uint32_t(MF::bits(a[0] * inv)) | (uint32_t(MF::bits(a[1] * inv)) << 16);
+      o.y = uint32_t(MF::bits(a[2] * inv)) | (uint32_t(MF::bits(a[3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(out_row(p, out_s, kvh, row0 + r, D) + 4 * d4) = o;
     }
     return;
   }
@@ -552,16 +541,13 @@ __global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(P
   const int ngroups = (n_live + kMergeGroup - 1) / kMergeGroup;
   const int ngmax = (p.nseg + kMergeGroup - 1) / kMergeGroup;
   const int64_t unit_slot0 = (int64_t(s) * p.num_kv_heads + kvh) * (p.nseg + ngmax);
-  if (wave == 0) {
+  {
     const int64_t base = (unit_slot0 + seg) * p.rows + row0;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int r = rt * 16 + c;
-      if (r >= wg_rows) continue;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) store_coherent(p.ws_acc + (base + r) * D + 16 * dt + 4 * g, acc[rt][dt]);
-      if (g == 0) store_coherent2(p.ws_ml + (base + r) * 2, ms_r[rt], ls_r[rt]);
+    for (int it = tid; it < wg_rows * (D / 4); it += SH::kThreads) {
+      const int r = it / (D / 4), d4 = it % (D / 4);
+      store_coherent(p.ws_acc + (base + r) * D + 4 * d4, combined(r, d4));
     }
+    for (int r = tid; r < wg_rows; r += SH::kThreads) store_coherent2(p.ws_ml + (base + r) * 2, sm_ms[r], sm_ls[r]);
   }
   int* counters = p.ws_cnt + ((int64_t(s) * p.num_kv_heads + kvh) * p.row_groups + rg) * (1 + ngmax);
   int* sm_flag = reinterpret_cast<int*>(lds + SH::kBytes - 16);

@@ -75,8 +75,12 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
     // One full round of workgroups for a single sequence; two rounds when a
     // batch's lengths may differ, so short sequences leave no idle CUs.
     const int64_t target = sh.num_seqs > 1 ? 2 * slots : slots;
-    nseg = std::max<int64_t>(1, target / std::max<int64_t>(1, units));
-    nseg = std::min<int64_t>(nseg, std::max<int64_t>(1, span_tiles / 4));  // >= 64 keys each
+    const int64_t fill = std::max<int64_t>(1, target / std::max<int64_t>(1, units));
+    // About 16 tiles (256 keys) per segment: with fewer the merge costs more
+    // than the extra parallelism saves -- but keep at least 4 segments while
+    // the device has room, so short contexts still spread their latency.
+    const int64_t work = std::max<int64_t>(1, span_tiles / 16);
+    nseg = std::min<int64_t>(fill, std::max<int64_t>(work, std::min<int64_t>(4, fill)));
   }
   nseg = std::min<int64_t>(nseg, span_tiles);
   nseg = std::min<int64_t>(nseg, kMaxSegments);
