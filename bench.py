@@ -160,6 +160,8 @@ def main() -> int:
     ap.add_argument("--queries", type=int, default=None)
     ap.add_argument("--no-sweep", action="store_true", help="skip the per-(context, M) sweep of the config")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--path", choices=["auto", "mfma", "dot"], default="auto",
+                    help="kernel family (auto = the planner's choice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run device copies of COPY_BYTES (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -172,6 +174,9 @@ def main() -> int:
 
     import workloads as wl
 
+    import paged_kv_decode_block_amd as pad
+
+    path = {"auto": pad.PAD_PATH_AUTO, "mfma": pad.PAD_PATH_MFMA, "dot": pad.PAD_PATH_DOT}[args.path]
     cfg = args.config
     pts = wl.CONFIG_POINTS[cfg]
     context = args.context or max(pts["contexts"])
@@ -188,7 +193,7 @@ def main() -> int:
     nbytes = effective_bytes(case)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms, plan = time_calls(case, args.warmup, args.steps)
+    ms, plan = time_calls(case, args.warmup, args.steps, path=path)
     wall = time.perf_counter() - t0
     print(f"[bench] timed {args.steps} steps: {ms * 1e3:.2f} us/step", file=sys.stderr, flush=True)
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -204,8 +209,10 @@ def main() -> int:
     if not args.no_sweep:
         for ctx in pts["contexts"]:
             for m in pts["queries"]:
+                if path == pad.PAD_PATH_DOT and m * spec.num_q_heads // spec.num_kv_heads > 4:
+                    continue  # the dot family serves at most 4 query rows per kv head
                 c = build_case(ctx, m)
-                t, p = time_calls(c, 20, 100, graph=True)
+                t, p = time_calls(c, 20, 100, graph=True, path=path)
                 b = effective_bytes(c)
                 sweep.append({"context": ctx, "M": m, "us": round(t * 1e3, 3), "GB/s": round(b / (t * 1e-3) / 1e9, 1),
                               "frac": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "segments": p["num_segments"]})
@@ -243,7 +250,8 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "traffic": traffic_entry(),
+            # measured on config 2, context 32768, M = 4 with the MFMA family
+            "traffic": traffic_entry() if (cfg, context, M) == (2, 32768, 4) and path != pad.PAD_PATH_DOT else None,
         },
         "cpu_baseline": cpu,
         "sweep": sweep,

@@ -100,6 +100,20 @@ __device__ __forceinline__ void store_coherent2(float* dst, float a, float b) {
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// LDS layout of the wave combine: per wave its running max and sum per row
+// and its rescaled accumulator rows, plus the workgroup's merged max/sum.
+template <int D, int RT, int NW>
+struct Combine {
+  static constexpr int kRows = RT * 16;
+  static constexpr int kAccStride = D + 4;
+  static constexpr int kBytes = (2 * NW * kRows + 2 * kRows) * 4 + NW * kRows * kAccStride * 4;
+  static __device__ float* m(unsigned char* lds) { return reinterpret_cast<float*>(lds); }
+  static __device__ float* l(unsigned char* lds) { return m(lds) + NW * kRows; }
+  static __device__ float* ms(unsigned char* lds) { return l(lds) + NW * kRows; }
+  static __device__ float* ls(unsigned char* lds) { return ms(lds) + kRows; }
+  static __device__ float* acc(unsigned char* lds) { return ls(lds) + kRows; }
+};
+
 // Workgroup shape (waves per workgroup from waves_for) and LDS layout.
 template <int D, int RT>
 struct Shape {
@@ -111,18 +125,14 @@ struct Shape {
   static constexpr int kAccStride = D + 4;  // floats per accumulator row in LDS
   static constexpr int kRows = RT * 16;
   // Tiles in flight beyond the one being computed (register budget).
-  static constexpr int PF = D * RT <= 128 ? 2 : (D * RT <= 256 ? 1 : 0);
+  static constexpr int PF = D * RT <= 128 ? 2 : (D * RT <= 512 && D < 512 ? 1 : 0);
   // LDS: V staging during the tile loop; afterwards the wave-combine area,
   // then the merge staging.  The last 16 bytes hold the arrival flag.
   static constexpr int kVBytes = NW * 16 * kVStride * 2;
-  static constexpr int kCombineBytes = (2 * NW * kRows + 2 * kRows) * 4 + NW * kRows * kAccStride * 4;
+  static constexpr int kCombineBytes = Combine<D, RT, NW>::kBytes;
   static constexpr int kMergeBytes = (2 * kMergeSlots * kMaxWgRows + 2 * kMaxWgRows) * 4;
   static constexpr int kMax0 = kVBytes > kCombineBytes ? kVBytes : kCombineBytes;
   static constexpr int kBytes = (kMax0 > kMergeBytes ? kMax0 : kMergeBytes) + 16;
-  // Merge load batch: IB output items x JC partial slots per thread.
-  static constexpr int kItemsPerThread = (kRows * (D / 4) + kThreads - 1) / kThreads;
-  static constexpr int IB = kItemsPerThread < 1 ? 1 : (kItemsPerThread > 4 ? 4 : kItemsPerThread);
-  static constexpr int JC = 32 / IB;
 };
 
 template <typename T>
@@ -138,12 +148,15 @@ __device__ __forceinline__ T* out_row(const Params& p, T* out_s, int kvh, int ru
 // With `out_final` the normalised result acc*/l* goes to the output rows;
 // otherwise (acc*, m*, l*) becomes partial slot `dst_slot` (coherent
 // stores).  The caller has acquired the partials.
-template <typename T, int D, int RT>
-__device__ __forceinline__ void merge_slots(const Params& p, unsigned char* lds, int64_t unit_slot0, int first_slot, int count,
-                            int row0, int wg_rows, bool out_final, int dst_slot, T* out_s, int kvh) {
-  using SH = Shape<D, RT>;
+template <typename T, int D, int RT, int NW>
+__device__ __forceinline__ void merge_slots(const Params& p, unsigned char* lds, int64_t unit_slot0, int first_slot,
+                                            int count, int row0, int wg_rows, bool out_final, int dst_slot, T* out_s,
+                                            int kvh) {
   using MF = Mfma<T>;
-  constexpr int IB = SH::IB, JC = SH::JC, NT = SH::kThreads;
+  constexpr int NT = NW * 64;
+  constexpr int kItemsPerThread = (RT * 16 * (D / 4) + NT - 1) / NT;
+  constexpr int IB = kItemsPerThread < 1 ? 1 : (kItemsPerThread > 4 ? 4 : kItemsPerThread);
+  constexpr int JC = 32 / IB;
   constexpr int kMlPerThread = (kMergeSlots * kMaxWgRows + NT - 1) / NT;
   const int tid = threadIdx.x;
   float2* sm_ml = reinterpret_cast<float2*>(lds);                               // [count][wg_rows]
@@ -263,6 +276,78 @@ __device__ __forceinline__ bool arrive(int* counter, int expected, int* sm_flag)
   }
   __syncthreads();
   return *sm_flag;
+}
+
+// After the waves of a workgroup have left their results in LDS -- per
+// wave w: sm_m/sm_l[w][row] (running max and sum) and the accumulator
+// rows, already rescaled to the workgroup maximum, in slot w of sm_acc; and
+// the workgroup's merged max/sum in sm_ms/sm_ls -- sum the slots in wave
+// order (deterministic) and either write the output (single segment) or
+// publish this segment's partial and take part in the arrival tree:
+// segments form groups of kMergeGroup; the last arriver of a group merges
+// the group's partials (into the output when there is one group, else
+// into a group partial); the last group to finish merges the groups.
+
+template <typename T, int D, int RT, int NW>
+__device__ __forceinline__ void finish(const Params& p, unsigned char* lds, int s, int kvh, int rg, int seg, int row0,
+                                       int wg_rows, int n_live, int lds_bytes) {
+  using MF = Mfma<T>;
+  using CB = Combine<D, RT, NW>;
+  constexpr int NT = NW * 64;
+  const int tid = threadIdx.x;
+  const float* sm_acc = CB::acc(lds);
+  const float* sm_ms = CB::ms(lds);
+  const float* sm_ls = CB::ls(lds);
+  // Thread-distributed result: item (row r, 4 head-dim columns d4).
+  auto combined = [&](int r, int d4) {
+    const float* col = sm_acc + r * CB::kAccStride + 4 * d4;
+    f32x4 a = *reinterpret_cast<const f32x4*>(col);
+#pragma unroll
+    for (int w = 1; w < NW; ++w) a += *reinterpret_cast<const f32x4*>(col + w * CB::kRows * CB::kAccStride);
+    return a;
+  };
+
+  T* out_s = static_cast<T*>(p.out) + int64_t(s) * p.query_len * p.num_q_heads * D;
+  if (n_live == 1) {
+    for (int it = tid; it < wg_rows * (D / 4); it += NT) {
+      const int r = it / (D / 4), d4 = it % (D / 4);
+      const f32x4 a = combined(r, d4);
+      const float ls = sm_ls[r];
+      const float inv = ls > 0.f ? 1.f / ls : 0.f;
+      uint2 o;
+      o.x = uint32_t(MF::bits(a[0] * inv)) | (uint32_t(MF::bits(a[1] * inv)) << 16);
+      o.y = uint32_t(MF::bits(a[2] * inv)) | (uint32_t(MF::bits(a[3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(out_row(p, out_s, kvh, row0 + r, D) + 4 * d4) = o;
+    }
+    return;
+  }
+
+  const int ngroups = (n_live + kMergeGroup - 1) / kMergeGroup;
+  const int ngmax = (p.nseg + kMergeGroup - 1) / kMergeGroup;
+  const int64_t unit_slot0 = (int64_t(s) * p.num_kv_heads + kvh) * (p.nseg + ngmax);
+  {
+    const int64_t base = (unit_slot0 + seg) * p.rows + row0;
+    for (int it = tid; it < wg_rows * (D / 4); it += NT) {
+      const int r = it / (D / 4), d4 = it % (D / 4);
+      store_coherent(p.ws_acc + (base + r) * D + 4 * d4, combined(r, d4));
+    }
+    for (int r = tid; r < wg_rows; r += NT) store_coherent2(p.ws_ml + (base + r) * 2, sm_ms[r], sm_ls[r]);
+  }
+  int* counters = p.ws_cnt + ((int64_t(s) * p.num_kv_heads + kvh) * p.row_groups + rg) * (1 + ngmax);
+  int* sm_flag = reinterpret_cast<int*>(lds + lds_bytes - 16);
+  const int grp = seg / kMergeGroup;
+  const int gsize = min(kMergeGroup, n_live - grp * kMergeGroup);
+  if (!arrive(counters + 1 + grp, gsize, sm_flag)) return;
+  if (tid == 0) counters[1 + grp] = 0;  // last user of this counter in the launch
+  if (ngroups == 1) {
+    merge_slots<T, D, RT, NW>(p, lds, unit_slot0, 0, n_live, row0, wg_rows, true, 0, out_s, kvh);
+    return;
+  }
+  merge_slots<T, D, RT, NW>(p, lds, unit_slot0, grp * kMergeGroup, gsize, row0, wg_rows, false, p.nseg + grp, out_s,
+                            kvh);
+  if (!arrive(counters, ngroups, sm_flag)) return;
+  if (tid == 0) counters[0] = 0;
+  merge_slots<T, D, RT, NW>(p, lds, unit_slot0, p.nseg, ngroups, row0, wg_rows, true, 0, out_s, kvh);
 }
 
 template <typename T, int D>
@@ -477,11 +562,12 @@ tiles_done:
     l_run[rt] += __shfl_xor(l_run[rt], 32);
   }
   __syncthreads();  // V staging area is reused below
-  float* sm_m = reinterpret_cast<float*>(lds);  // [NW][kRows]
-  float* sm_l = sm_m + NW * SH::kRows;           // [NW][kRows]
-  float* sm_ms = sm_l + NW * SH::kRows;          // [kRows] merged max
-  float* sm_ls = sm_ms + SH::kRows;              // [kRows] merged sum
-  float* sm_acc = sm_ls + SH::kRows;             // [NW][kRows][kAccStride]
+  using CB = Combine<D, RT, NW>;
+  float* sm_m = CB::m(lds);      // [NW][kRows]
+  float* sm_l = CB::l(lds);      // [NW][kRows]
+  float* sm_ms = CB::ms(lds);    // [kRows] merged max
+  float* sm_ls = CB::ls(lds);    // [kRows] merged sum
+  float* sm_acc = CB::acc(lds);  // [NW][kRows][kAccStride]
   if (g == 0) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -498,7 +584,7 @@ tiles_done:
     for (int w = 0; w < NW; ++w) ms = fmaxf(ms, sm_m[w * SH::kRows + r]);
     const float mu = ms == kNegInf ? 0.f : ms;
     const float f = fast_exp2(m_run[rt] - mu);
-    float* slot = sm_acc + (wave * SH::kRows + r) * SH::kAccStride + 4 * g;
+    float* slot = sm_acc + (wave * SH::kRows + r) * CB::kAccStride + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(slot + 16 * dt) = acc[rt][dt] * f;
     if (wave == 0 && g == 0) {
@@ -510,60 +596,264 @@ tiles_done:
     }
   }
   __syncthreads();
-  // Thread-distributed result: item (row r, 4 head-dim columns d4).
-  auto combined = [&](int r, int d4) {
-    const float* col = sm_acc + r * SH::kAccStride + 4 * d4;
-    f32x4 a = *reinterpret_cast<const f32x4*>(col);
+  finish<T, D, RT, NW>(p, lds, s, kvh, rg, seg, row0, wg_rows, n_live, SH::kBytes);
+}
+
+// ---------------------------------------------------------------------------
+// Per-head dot-product family for small GQA (G*M <= 4 query rows per kv
+// head, head size <= 128): no MFMA and no row padding.  The K/V loads, the
+// tile loop, the combine and the split-KV epilogue are those of the MFMA
+// kernel; per 16-key tile a wave
+//   * forms each row's q.k with v_dot2_f32_{bf16,f16} over the eight
+//     head-dim elements a lane holds, then sums the four lane groups that
+//     split the head dimension (two cross-lane steps);
+//   * takes the online softmax over the tile's 16 keys (one key per lane);
+//   * accumulates p * v in fp32 per lane, i.e. per key slot; the key slots
+//     are summed once, after the last tile.
+template <typename T>
+struct Dot;
+
+template <>
+struct Dot<__bf16> {
+  typedef __bf16 x2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ float dot2(int a, int b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(x2, a), __builtin_bit_cast(x2, b), c, false);
+  }
+  static __device__ __forceinline__ float lo(int w) { return __builtin_bit_cast(float, uint32_t(w) << 16); }
+  static __device__ __forceinline__ float hi(int w) { return __builtin_bit_cast(float, uint32_t(w) & 0xffff0000u); }
+};
+
+template <>
+struct Dot<_Float16> {
+  typedef _Float16 x2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ float dot2(int a, int b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(x2, a), __builtin_bit_cast(x2, b), c, false);
+  }
+  static __device__ __forceinline__ float lo(int w) { return float(__builtin_bit_cast(x2, w)[0]); }
+  static __device__ __forceinline__ float hi(int w) { return float(__builtin_bit_cast(x2, w)[1]); }
+};
+
+constexpr int kDotWaves = kDotWaveCount;
+constexpr int kDotRows = kDotMaxRows;
+
+template <int D>
+struct DotShape {
+  static constexpr int NW = kDotWaves;
+  static constexpr int kThreads = NW * 64;
+  static constexpr int KC = D / 32;
+  static constexpr int PF = 1;
+  static constexpr int kMergeBytes = (2 * kMergeSlots * kMaxWgRows + 2 * kMaxWgRows) * 4;
+  static constexpr int kCombine = Combine<D, 1, NW>::kBytes;
+  static constexpr int kBytes = (kCombine > kMergeBytes ? kCombine : kMergeBytes) + 16;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kDotWaves * 64) void decode_dot_kernel(Params p) {
+  using DT2 = Dot<T>;
+  using SH = DotShape<D>;
+  using CB = Combine<D, 1, SH::NW>;
+  constexpr int NW = SH::NW, KC = SH::KC, R = kDotRows;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[SH::kBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int s = blockIdx.y;
+  const int kvh = blockIdx.x % p.num_kv_heads;
+  const int seg = blockIdx.x / p.num_kv_heads;
+  const int rows = p.rows;  // <= kDotRows
+  const int M = p.query_len;
+
+  const int L = p.seq_lens[s];
+  if (L <= 0) {
+    if (seg == 0) zero_rows<T, D>(p, s, kvh, 0, rows, SH::kThreads);
+    return;
+  }
+  const int k_lo = p.window > 0 ? max(0, L - M - p.window + 1) : 0;
+  const int t_lo = k_lo >> 4, t_hi = (L + 15) >> 4;
+  const int n_tiles = t_hi - t_lo;
+  const int seg_tiles = max(p.seg_tiles, (n_tiles + p.nseg - 1) / p.nseg);
+  const int n_live = (n_tiles + seg_tiles - 1) / seg_tiles;
+  if (seg >= n_live) return;
+  const int ts = t_lo + seg * seg_tiles, te = min(ts + seg_tiles, t_hi);
+  const int lo_last = p.window > 0 ? max(0, L - p.window) : 0;
+  const int qpos_first = L - M;
+
+  // Query rows (row = m * G + head in group), each lane holding the eight
+  // head-dim elements 32 kc + 8 g .. of every chunk kc.
+  int qpos_r[R], lo_r[R];
+  i32x4 q[R][KC];
+  const T* Q = static_cast<const T*>(p.q);
 #pragma unroll
-    for (int w = 1; w < NW; ++w) a += *reinterpret_cast<const f32x4*>(col + w * SH::kRows * SH::kAccStride);
-    return a;
+  for (int r = 0; r < R; ++r) {
+    if (r < rows) {
+      const int m = r / p.group, gq = r % p.group;
+      qpos_r[r] = L - M + m;
+      lo_r[r] = p.window > 0 ? max(0, qpos_r[r] - p.window + 1) : 0;
+      const T* qrow = Q + ((int64_t(s) * M + m) * p.num_q_heads + kvh * p.group + gq) * D;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) q[r][kc] = *reinterpret_cast<const i32x4*>(qrow + 32 * kc + 8 * g);
+    } else {
+      qpos_r[r] = -1;
+      lo_r[r] = 0;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) q[r][kc] = i32x4{0, 0, 0, 0};
+    }
+  }
+
+  float m_run[R], l_run[R];       // l_run: this lane's key slot only
+  float acc[R][KC][8];            // this lane's key slot, head-dim 32 kc + 8 g + e
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    m_run[r] = kNegInf;
+    l_run[r] = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[r][kc][e] = 0.f;
+  }
+
+  const unsigned char* KVh =
+      static_cast<const unsigned char*>(p.kv) + int64_t(kvh) * p.head_stride * int64_t(sizeof(T));
+  const int32_t* table = p.block_table + int64_t(s) * p.max_blocks;
+  const uint32_t lane_off = uint32_t(c * p.token_stride + 8 * g) * uint32_t(sizeof(T));
+
+  struct Tile {
+    i32x4 k[KC];
+    i32x4 v[KC];
+  };
+  auto block_of = [&](int t) { return table[(t * 16) / p.page_size]; };
+  auto issue_tile = [&](Tile& tl, int t, int blk) {
+    const int key0 = t * 16;
+    const unsigned char* row =
+        KVh + (int64_t(blk) * p.block_stride + int64_t(key0 % p.page_size) * p.token_stride) * int64_t(sizeof(T)) +
+        lane_off;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) tl.k[kc] = *reinterpret_cast<const i32x4*>(row + 64 * kc);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) tl.v[kc] = *reinterpret_cast<const i32x4*>(row + 2 * D + 64 * kc);
   };
 
-  T* out_s = static_cast<T*>(p.out) + int64_t(s) * M * p.num_q_heads * D;
-  if (n_live == 1) {
-    for (int it = tid; it < wg_rows * (D / 4); it += SH::kThreads) {
-      const int r = it / (D / 4), d4 = it % (D / 4);
-      const f32x4 a = combined(r, d4);
-      const float ls = sm_ls[r];
-      const float inv = ls > 0.f ? 1.f / ls : 0.f;
-      uint2 o;
-      o.x = uint32_t(MF::bits(a[0] * inv)) | (uint32_t(MF::bits(a[1] * inv)) << 16);
-      o.y = uint32_t(MF::bits(a[2] * inv)) | (uint32_t(MF::bits(a[3] * inv)) << 16);
-      *reinterpret_cast<uint2*>(out_row(p, out_s, kvh, row0 + r, D) + 4 * d4) = o;
+  auto compute_tile = [&](Tile& tl, int t) {
+    const int key0 = t * 16;
+    const int key = key0 + c;  // this lane's key
+    const bool edge = !(key0 >= lo_last && key0 + 15 <= qpos_first);
+    if (edge && (key < k_lo || key >= L)) {
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) tl.v[kc] = i32x4{0, 0, 0, 0};
     }
-    return;
+    float vf[KC][8];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        vf[kc][2 * w] = DT2::lo(tl.v[kc][w]);
+        vf[kc][2 * w + 1] = DT2::hi(tl.v[kc][w]);
+      }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r >= rows) continue;
+      float dotp = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) dotp = DT2::dot2(tl.k[kc][w], q[r][kc][w], dotp);
+      dotp += __shfl_xor(dotp, 16);
+      dotp += __shfl_xor(dotp, 32);
+      float x = dotp * p.scale_log2;
+      if (edge && (key < lo_r[r] || key > qpos_r[r])) x = kNegInf;
+      float tmax = x;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, off));
+      const float m_new = fmaxf(m_run[r], tmax);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[r] - m_use);
+      const float pr = fast_exp2(x - m_use);
+      l_run[r] = l_run[r] * alpha + pr;
+      m_run[r] = m_new;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r][kc][e] = acc[r][kc][e] * alpha + pr * vf[kc][e];
+    }
+  };
+
+  // Same tile schedule as the MFMA kernel (interleaved tiles, one tile of
+  // prefetch, clamped prefetch index).
+  const int first_t = ts + wave;
+  const int n_w = first_t < te ? (te - first_t + NW - 1) / NW : 0;
+  auto tile_at = [&](int i) { return first_t + min(i, n_w - 1) * NW; };
+  if (n_w > 0) {
+    Tile ring[SH::PF + 1];
+#pragma unroll
+    for (int u = 0; u < SH::PF; ++u) issue_tile(ring[u], tile_at(u), block_of(tile_at(u)));
+    int blk_next = block_of(tile_at(SH::PF));
+    for (int i = 0;; i += SH::PF + 1) {
+#pragma unroll
+      for (int u = 0; u <= SH::PF; ++u) {
+        issue_tile(ring[(u + SH::PF) % (SH::PF + 1)], tile_at(i + u + SH::PF), blk_next);
+        blk_next = block_of(tile_at(i + u + SH::PF + 1));
+        compute_tile(ring[u], first_t + (i + u) * NW);
+        if (i + u + 1 >= n_w) goto tiles_done;
+      }
+    }
+  }
+tiles_done:
+
+  // Sum the 16 key slots of each lane group (fixed butterfly order).
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) l_run[r] += __shfl_xor(l_run[r], off);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) acc[r][kc][e] += __shfl_xor(acc[r][kc][e], off);
   }
 
-  // ---- split-KV partial, then the arrival tree ----
-  // Segments form groups of kMergeGroup; the last arriver of a group merges
-  // the group's partials (into the output when there is one group, else
-  // into a group partial); the last group to finish merges the groups.
-  const int ngroups = (n_live + kMergeGroup - 1) / kMergeGroup;
-  const int ngmax = (p.nseg + kMergeGroup - 1) / kMergeGroup;
-  const int64_t unit_slot0 = (int64_t(s) * p.num_kv_heads + kvh) * (p.nseg + ngmax);
-  {
-    const int64_t base = (unit_slot0 + seg) * p.rows + row0;
-    for (int it = tid; it < wg_rows * (D / 4); it += SH::kThreads) {
-      const int r = it / (D / 4), d4 = it % (D / 4);
-      store_coherent(p.ws_acc + (base + r) * D + 4 * d4, combined(r, d4));
+  // Combine the waves through LDS, as in the MFMA kernel.
+  float* sm_m = CB::m(lds);
+  float* sm_l = CB::l(lds);
+  float* sm_ms = CB::ms(lds);
+  float* sm_ls = CB::ls(lds);
+  float* sm_acc = CB::acc(lds);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (lane == 0) {
+      sm_m[wave * CB::kRows + r] = m_run[r];
+      sm_l[wave * CB::kRows + r] = l_run[r];
     }
-    for (int r = tid; r < wg_rows; r += SH::kThreads) store_coherent2(p.ws_ml + (base + r) * 2, sm_ms[r], sm_ls[r]);
   }
-  int* counters = p.ws_cnt + ((int64_t(s) * p.num_kv_heads + kvh) * p.row_groups + rg) * (1 + ngmax);
-  int* sm_flag = reinterpret_cast<int*>(lds + SH::kBytes - 16);
-  const int grp = seg / kMergeGroup;
-  const int gsize = min(kMergeGroup, n_live - grp * kMergeGroup);
-  if (!arrive(counters + 1 + grp, gsize, sm_flag)) return;
-  if (tid == 0) counters[1 + grp] = 0;  // last user of this counter in the launch
-  if (ngroups == 1) {
-    merge_slots<T, D, RT>(p, lds, unit_slot0, 0, n_live, row0, wg_rows, true, 0, out_s, kvh);
-    return;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r >= rows) continue;
+    float ms = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) ms = fmaxf(ms, sm_m[w * CB::kRows + r]);
+    const float mu = ms == kNegInf ? 0.f : ms;
+    const float f = fast_exp2(m_run[r] - mu);
+    if (c == 0) {
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        float* dst = sm_acc + (wave * CB::kRows + r) * CB::kAccStride + 32 * kc + 8 * g;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{acc[r][kc][0], acc[r][kc][1], acc[r][kc][2], acc[r][kc][3]} * f;
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[r][kc][4], acc[r][kc][5], acc[r][kc][6], acc[r][kc][7]} * f;
+      }
+    }
+    if (wave == 0 && lane == 0) {
+      float ls = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) ls += sm_l[w * CB::kRows + r] * fast_exp2(sm_m[w * CB::kRows + r] - mu);
+      sm_ms[r] = ms;
+      sm_ls[r] = ls;
+    }
   }
-  merge_slots<T, D, RT>(p, lds, unit_slot0, grp * kMergeGroup, gsize, row0, wg_rows, false, p.nseg + grp, out_s,
-                        kvh);
-  if (!arrive(counters, ngroups, sm_flag)) return;
-  if (tid == 0) counters[0] = 0;
-  merge_slots<T, D, RT>(p, lds, unit_slot0, p.nseg, ngroups, row0, wg_rows, true, 0, out_s, kvh);
+  __syncthreads();
+  finish<T, D, 1, NW>(p, lds, s, kvh, 0, seg, 0, rows, n_live, SH::kBytes);
 }
 
 __global__ void zero_kernel(uint32_t* p, size_t n) {
@@ -589,8 +879,21 @@ int launch_d(const Plan& pl, const Params& pr, hipStream_t st) {
   return int(hipErrorInvalidValue);
 }
 
+template <typename T, int D>
+int launch_dot(const Plan& pl, const Params& pr, hipStream_t st) {
+  hipLaunchKernelGGL((decode_dot_kernel<T, D>), dim3(pl.grid_x, pl.grid_y), dim3(DotShape<D>::kThreads), 0, st, pr);
+  return int(hipGetLastError());
+}
+
 template <typename T>
 int launch_dtype(const Plan& pl, const Params& pr, int head_size, hipStream_t st) {
+  if (pl.path == PAD_PATH_DOT) {
+    switch (head_size) {
+      case 64: return launch_dot<T, 64>(pl, pr, st);
+      case 128: return launch_dot<T, 128>(pl, pr, st);
+    }
+    return int(hipErrorInvalidValue);
+  }
   switch (head_size) {
     case 64: return launch_d<T, 64>(pl, pr, st);
     case 128: return launch_d<T, 128>(pl, pr, st);

@@ -41,16 +41,25 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   const int G = sh.num_q_heads / sh.num_kv_heads;
   const int rows = G * sh.query_len;
   if (rows > 1024) return PAD_EUNSUPPORTED;
-  if (sh.path == PAD_PATH_DOT) return PAD_EUNSUPPORTED;  // dot-product family not built yet
+  const bool dot_ok = rows <= kDotMaxRows && sh.head_size <= kDotMaxHeadSize;
+  if (sh.path == PAD_PATH_DOT && !dot_ok) return PAD_EUNSUPPORTED;
 
   Plan p{};
-  p.path = PAD_PATH_MFMA;
+  // The MFMA family serves every shape; the per-head dot-product family is
+  // used when asked for (its rocprof A/B against MFMA decides the default).
+  p.path = sh.path == PAD_PATH_DOT ? PAD_PATH_DOT : PAD_PATH_MFMA;
   p.rows = rows;
-  const int tiles_total = int(ceil_div(rows, 16));
-  int rt = std::min(tiles_total, max_row_tiles(sh.head_size));
-  p.row_groups = int(ceil_div(tiles_total, rt));
-  p.row_tiles = int(ceil_div(tiles_total, p.row_groups));
-  p.waves = waves_for(sh.head_size, p.row_tiles);
+  if (p.path == PAD_PATH_DOT) {
+    p.row_tiles = 1;
+    p.row_groups = 1;
+    p.waves = kDotWaveCount;
+  } else {
+    const int tiles_total = int(ceil_div(rows, 16));
+    int rt = std::min(tiles_total, max_row_tiles(sh.head_size));
+    p.row_groups = int(ceil_div(tiles_total, rt));
+    p.row_tiles = int(ceil_div(tiles_total, p.row_groups));
+    p.waves = waves_for(sh.head_size, p.row_tiles);
+  }
 
   // Keys one unit may have to read: the whole table bound, or the window
   // span (window + M - 1 keys) plus one tile of alignment slack.

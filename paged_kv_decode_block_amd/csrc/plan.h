@@ -21,7 +21,12 @@ namespace pad {
 
 constexpr int kTileKeys = 16;    // keys per MFMA tile (page sizes are multiples of 16)
 constexpr int kMaxSegments = 256;
-constexpr int kMergeGroupSize = 32;  // segments merged per group of the two-level merge tree
+constexpr int kMergeGroupSize = 32;
+// The dot-product family serves up to this many query rows per kv head at
+// head sizes up to kDotMaxHeadSize, with kDotWaves waves per workgroup.
+constexpr int kDotMaxRows = 4;
+constexpr int kDotMaxHeadSize = 128;
+constexpr int kDotWaveCount = 4;  // segments merged per group of the two-level merge tree
 // Arrival counters live in a fixed-size prefix of the workspace, so calls of
 // different shapes can share one workspace: partials never land where any
 // shape keeps counters, and every call leaves its counters zero.

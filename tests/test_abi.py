@@ -108,6 +108,14 @@ def test_forced_segments():
             assert p["num_segments"] == -(-tiles // -(-tiles // n))
 
 
+def test_dot_path_plan():
+    p = plan(shape(query_len=1, path=pad.PAD_PATH_DOT))  # 4 rows, D=128
+    assert p["path"] == pad.PAD_PATH_DOT and p["waves"] == 4 and p["row_groups"] == 1
+    assert plan(shape(query_len=1))["path"] == pad.PAD_PATH_MFMA  # automatic choice
+    p = plan(shape(num_q_heads=8, num_kv_heads=8, head_size=64, query_len=1, path=pad.PAD_PATH_DOT))
+    assert p["rows"] == 1 and p["path"] == pad.PAD_PATH_DOT
+
+
 def test_window_plan_is_smaller():
     full = plan(shape(max_blocks_per_seq=1024))
     win = plan(shape(max_blocks_per_seq=1024), window=512)
@@ -131,6 +139,8 @@ def test_window_plan_is_smaller():
         (dict(max_seq_len=2048 * 16 + 1), pad.PAD_EINVAL),
         (dict(num_segments=-1), pad.PAD_EINVAL),
         (dict(path=3), pad.PAD_EINVAL),
+        (dict(path=pad.PAD_PATH_DOT), pad.PAD_EUNSUPPORTED),  # 16 rows: too many for the dot family
+        (dict(path=pad.PAD_PATH_DOT, query_len=1, head_size=256), pad.PAD_EUNSUPPORTED),
         (dict(num_seqs=-1), pad.PAD_EINVAL),
         (dict(max_blocks_per_seq=0), pad.PAD_EINVAL),
     ],

@@ -286,3 +286,37 @@ def test_config5_full_sampled():
     pick = [int(order[0]), int(order[len(order) // 2]), int(order[-1]), 3, 64]
     ref = oracle_out(c, 0, seqs=pick)
     check(out[pick], ref, c.q.dtype, f"config5 seqs {pick}")
+
+
+# ------------------------------------------- dot-product family (G*M <= 4)
+
+
+DOT_SHAPES = [
+    # D, Hq, Hkv, P, dtype, layout, lens, M, window
+    (64, 4, 1, 16, "fp16", wl.HND, [256], 1, 0),          # config 1
+    (128, 32, 8, 16, "bf16", wl.HND, [4096], 1, 0),       # config 2, M = 1
+    (128, 8, 4, 32, "fp16", wl.NHD, [777, 0, 5], 2, 0),   # padded and short sequences
+    (64, 2, 2, 16, "bf16", wl.HND, [300, 41], 3, 17),     # 3 rows, window
+    (128, 4, 4, 48, "bf16", wl.HND, [2, 1000], 4, 0),     # L < M rows
+    (64, 8, 2, 528, "fp16", wl.HND, [1100], 1, 0),
+]
+
+
+@pytest.mark.parametrize("shape", DOT_SHAPES, ids=[f"d{i}" for i in range(len(DOT_SHAPES))])
+@pytest.mark.parametrize("nseg", [0, 1, 5])
+def test_dot_path(shape, nseg):
+    D, Hq, Hkv, P, dt, layout, lens, M, W = shape
+    spec = wl.Spec(dt, D, Hq, Hkv, P, layout, window=W)
+    c = _case(spec, lens, M, 777 + D + Hq + M)
+    ref = oracle_out(c)
+    out_dot = run_gpu(c, path=pad.PAD_PATH_DOT, num_segments=nseg)
+    check(out_dot, ref, c.q.dtype, f"dot path {shape} nseg={nseg}")
+    out_mfma = run_gpu(c, path=pad.PAD_PATH_MFMA, num_segments=nseg)
+    check(out_mfma, ref, c.q.dtype, f"mfma path {shape} nseg={nseg}")
+    assert float((out_dot.float() - out_mfma.float()).abs().max()) <= 2 * ABS_TOL[c.q.dtype]
+
+
+def test_dot_path_full_config2():
+    say("config 2 full, M=1, dot family")
+    c = wl.config_case(2, 32768, 1, device=DEV, instances=2, pool_bytes=POOL)
+    check(run_gpu(c, 1, path=pad.PAD_PATH_DOT), oracle_out(c, 1), c.q.dtype, "dot config2 L=32768 M=1")
