@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define PAD_ABI_VERSION 1
+#define PAD_ABI_VERSION 2
 
 typedef enum pad_status {
   PAD_OK = 0,
@@ -121,7 +121,7 @@ typedef struct pad_plan {
   int32_t num_segments;      /* split-KV segments per (sequence, kv head, group)  */
   int32_t segment_tiles;     /* 16-key tiles per segment (planned)                */
   int32_t grid_x, grid_y;    /* launch grid                                       */
-  int32_t reserved;
+  int32_t merge_slices;      /* workgroups that share the merge of a split unit   */
   uint64_t workspace_bytes;  /* bytes pad_decode_attn needs for this call         */
 } pad_plan;
 
@@ -138,14 +138,16 @@ pad_status pad_decode_attn_plan(const pad_shape* shape, int32_t window, int32_t 
 
 /* Workspace bytes that serve every call of this shape (any window) on the
  * current device.  0 means no workspace is needed (a single segment). The
- * split partials are fp32 (acc[rows][D], m, l per row and segment) plus
- * one int32 arrival counter per (sequence, kv head, row group), as in
- * KernelVariant.scratch_shapes. */
+ * split partials are fp32 (acc[rows][D], m, l per row and segment), as in
+ * KernelVariant.scratch_shapes, after a fixed 1 MiB prefix of int32 merge
+ * control words (per sequence, kv head and row group: an arrival counter
+ * and one hand-over word per merge slice after the first, each in its own
+ * 128-byte line). */
 pad_status pad_decode_attn_workspace_size(const pad_shape* shape, size_t* bytes);
 
 /* Zero a workspace of `bytes` bytes (device pointer, 256-byte aligned) on
  * `stream`.  Needed once after allocation: every pad_decode_attn call
- * leaves the arrival counters zero again. */
+ * leaves the merge control words zero again. */
 pad_status pad_decode_attn_workspace_init(void* workspace, size_t bytes, void* stream);
 
 /* Paged-KV decode attention (see the top of this file).  `scale` multiplies
@@ -158,6 +160,15 @@ pad_status pad_decode_attn(const pad_shape* shape, const void* q, const void* kv
                            const int32_t* block_table, const int32_t* seq_lens, float scale,
                            int32_t window, void* out, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* Bound, in microseconds, on how long a workgroup that shares the split-KV
+ * merge waits for the last segment of its unit (process-wide; default 200;
+ * 0 .. 1000000 accepted, else PAD_EINVAL).  A workgroup that stops waiting
+ * leaves its merge slice to the last segment, so every value gives the
+ * same output bits; 0 makes every such workgroup give up at once, which
+ * lets tests exercise that hand-over.  Applies to calls enqueued after it
+ * returns. */
+pad_status pad_set_merge_wait(int32_t microseconds);
 
 #ifdef __cplusplus
 }

@@ -4,7 +4,7 @@ Thin ctypes marshalling over the C ABI declared in ``include/pad_attn.h``;
 the functions keep the C names.  PyTorch supplies device memory and the
 current stream; every step of the computation runs in the library's HIP
 kernels.  Importing this package fails if the library has not been built
-(``python -m paged_kv_decode_block_amd.build``): there is no fallback.
+(``python paged_kv_decode_block_amd/build.py``): there is no fallback.
 """
 
 from __future__ import annotations
@@ -21,6 +21,7 @@ __all__ = [
     "PadError", "pad_shape", "pad_plan", "lib", "LIB_PATH", "load_library",
     "pad_abi_version", "pad_status_string", "pad_decode_attn_plan",
     "pad_decode_attn_workspace_size", "pad_decode_attn_workspace_init", "pad_decode_attn",
+    "pad_set_merge_wait",
     "make_shape", "Workspace",
 ]
 
@@ -60,7 +61,7 @@ class pad_plan(ctypes.Structure):
         ("segment_tiles", ctypes.c_int32),
         ("grid_x", ctypes.c_int32),
         ("grid_y", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("merge_slices", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_uint64),
     ]
 
@@ -69,7 +70,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     """Open a build of the library and declare its C signatures."""
     if not os.path.exists(path):
         raise ImportError(
-            f"{path} is missing: build it with `python -m paged_kv_decode_block_amd.build` "
+            f"{path} is missing: build it with `python paged_kv_decode_block_amd/build.py` "
             "(the decode-attention path has no non-HIP fallback)"
         )
     L = ctypes.CDLL(path)
@@ -84,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.pad_decode_attn_workspace_size.argtypes = [P(pad_shape), P(ctypes.c_size_t)]
     L.pad_decode_attn_workspace_init.restype = ctypes.c_int
     L.pad_decode_attn_workspace_init.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.pad_set_merge_wait.restype = ctypes.c_int
+    L.pad_set_merge_wait.argtypes = [ctypes.c_int32]
     L.pad_decode_attn.restype = ctypes.c_int
     L.pad_decode_attn.argtypes = [
         P(pad_shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -157,7 +160,7 @@ def pad_decode_attn_plan(shape: pad_shape, window: int = 0, num_cus: int | None 
     plan = pad_plan()
     _check(lib.pad_decode_attn_plan(ctypes.byref(shape), int(window), int(num_cus), ctypes.byref(plan)),
            "pad_decode_attn_plan")
-    return {name: getattr(plan, name) for name, _ in pad_plan._fields_ if name != "reserved"}
+    return {name: getattr(plan, name) for name, _ in pad_plan._fields_}
 
 
 def pad_decode_attn_workspace_size(shape: pad_shape) -> int:
@@ -198,6 +201,11 @@ class Workspace:
             self.buf = torch.empty(need, dtype=torch.uint8, device=self.device)
             pad_decode_attn_workspace_init(self.buf)
         return self.buf
+
+
+def pad_set_merge_wait(microseconds: int) -> None:
+    """Bound on a merge helper's wait for the last segment (process-wide)."""
+    _check(lib.pad_set_merge_wait(int(microseconds)), "pad_set_merge_wait")
 
 
 _default_ws: dict[int, Workspace] = {}

@@ -1,7 +1,8 @@
 """Build libpad_attn.so (HIP kernels for gfx950 plus the C ABI) in-tree.
 
-Run as ``python -m paged_kv_decode_block_amd.build`` or through
-``__graft_entry__.build()``.  hipcc cross-compiles for gfx950 without a GPU.
+Run as ``python paged_kv_decode_block_amd/build.py`` or through
+``__graft_entry__.build()``; it imports nothing of the package, so it works
+when the library is missing or out of date.  hipcc cross-compiles for gfx950 without a GPU.
 """
 
 from __future__ import annotations

@@ -1,6 +1,7 @@
 // extern "C" entry points of libpad_attn.so (declared in include/pad_attn.h).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -32,9 +33,19 @@ int device_cus() {
   return cache[dev];
 }
 
+// Helpers' bound on waiting for the last segment, in ticks of the 100 MHz
+// device real-time counter (see pad_set_merge_wait).
+std::atomic<uint32_t> g_merge_wait_ticks{200 * 100};
+
 }  // namespace
 
 extern "C" {
+
+pad_status pad_set_merge_wait(int32_t microseconds) {
+  if (microseconds < 0 || microseconds > 1000000) return PAD_EINVAL;
+  g_merge_wait_ticks.store(uint32_t(microseconds) * 100u);
+  return PAD_OK;
+}
 
 int32_t pad_abi_version(void) { return PAD_ABI_VERSION; }
 
@@ -63,7 +74,7 @@ pad_status pad_decode_attn_plan(const pad_shape* shape, int32_t window, int32_t 
   plan->segment_tiles = p.seg_tiles;
   plan->grid_x = p.grid_x;
   plan->grid_y = p.grid_y;
-  plan->reserved = 0;
+  plan->merge_slices = p.merge_slices;
   plan->workspace_bytes = p.ws_bytes;
   return PAD_OK;
 }
@@ -134,6 +145,8 @@ pad_status pad_decode_attn(const pad_shape* shape, const void* q, const void* kv
   pr.nseg = p.nseg;
   pr.seg_tiles = p.seg_tiles;
   pr.row_groups = p.row_groups;
+  pr.merge_slices = p.merge_slices;
+  pr.merge_wait_ticks = g_merge_wait_ticks.load();
   pr.scale_log2 = float(double(scale) * 1.4426950408889634);  // log2(e)
   return pad::launch_decode(p, pr, shape->dtype, shape->head_size, stream) == 0 ? PAD_OK : PAD_EHIP;
 }

@@ -27,9 +27,11 @@
 //
 // Split partials are written with device-coherent (write-through) stores,
 // so publishing them costs no L2 write-back: each wave waits for its own
-// stores, then one atomic per workgroup counts the arrival.  Only the last
-// arriver invalidates its caches and merges, with every partial load in
-// flight before the merge weights are needed.
+// stores, then one atomic per workgroup counts the arrival.  The merge is
+// shared: the output is cut into slices, merged by the last arriver and by
+// the workgroups that arrived just before it, which wait (bounded) for the
+// last arriver's go; a slice whose helper stopped waiting falls back to the
+// last arriver.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -73,11 +75,6 @@ struct Mfma<_Float16> {
 };
 
 constexpr float kNegInf = -__builtin_huge_valf();
-// Split-KV merge tree: segments merge in groups of kMergeGroup, then the
-// groups merge; at most kMergeSlots partials are merged at once.
-constexpr int kMergeGroup = kMergeGroupSize;
-constexpr int kMergeSlots = kMergeGroup > kMaxSegments / kMergeGroup ? kMergeGroup : kMaxSegments / kMergeGroup;
-constexpr int kMaxWgRows = 64;  // rows of one workgroup (row tiles x 16)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -126,13 +123,11 @@ struct Shape {
   static constexpr int kRows = RT * 16;
   // Tiles in flight beyond the one being computed (register budget).
   static constexpr int PF = D * RT <= 128 ? 2 : (D * RT <= 512 && D < 512 ? 1 : 0);
-  // LDS: V staging during the tile loop; afterwards the wave-combine area,
-  // then the merge staging.  The last 16 bytes hold the arrival flag.
+  // LDS: V staging during the tile loop, afterwards the wave-combine area.
+  // The last 16 bytes hold the merge role and hand-over flags.
   static constexpr int kVBytes = NW * 16 * kVStride * 2;
   static constexpr int kCombineBytes = Combine<D, RT, NW>::kBytes;
-  static constexpr int kMergeBytes = (2 * kMergeSlots * kMaxWgRows + 2 * kMaxWgRows) * 4;
-  static constexpr int kMax0 = kVBytes > kCombineBytes ? kVBytes : kCombineBytes;
-  static constexpr int kBytes = (kMax0 > kMergeBytes ? kMax0 : kMergeBytes) + 16;
+  static constexpr int kBytes = (kVBytes > kCombineBytes ? kVBytes : kCombineBytes) + 16;
 };
 
 template <typename T>
@@ -141,141 +136,196 @@ __device__ __forceinline__ T* out_row(const Params& p, T* out_s, int kvh, int ru
   return out_s + (int64_t(m) * p.num_q_heads + kvh * p.group + gq) * D;
 }
 
-// Merge `count` split partials (slots first_slot .. first_slot + count - 1
-// of the unit) over this workgroup's rows [row0, row0 + wg_rows): the
-// log-sum-exp merge m* = max m_j, l* = sum l_j 2^(m_j - m*),
-// acc* = sum acc_j 2^(m_j - m*), in slot order (bitwise deterministic).
-// With `out_final` the normalised result acc*/l* goes to the output rows;
-// otherwise (acc*, m*, l*) becomes partial slot `dst_slot` (coherent
-// stores).  The caller has acquired the partials.
-template <typename T, int D, int RT, int NW>
-__device__ __forceinline__ void merge_slots(const Params& p, unsigned char* lds, int64_t unit_slot0, int first_slot,
-                                            int count, int row0, int wg_rows, bool out_final, int dst_slot, T* out_s,
-                                            int kvh) {
-  using MF = Mfma<T>;
-  constexpr int NT = NW * 64;
-  constexpr int kItemsPerThread = (RT * 16 * (D / 4) + NT - 1) / NT;
-  constexpr int IB = kItemsPerThread < 1 ? 1 : (kItemsPerThread > 4 ? 4 : kItemsPerThread);
-  constexpr int JC = 32 / IB;
-  constexpr int kMlPerThread = (kMergeSlots * kMaxWgRows + NT - 1) / NT;
-  const int tid = threadIdx.x;
-  float2* sm_ml = reinterpret_cast<float2*>(lds);                               // [count][wg_rows]
-  float* sm_ms = reinterpret_cast<float*>(lds) + 2 * kMergeSlots * kMaxWgRows;  // [wg_rows]
-  float* sm_ls = sm_ms + kMaxWgRows;                                            // [wg_rows]
-  const int64_t jstride = int64_t(p.rows) * D;
-  const float* src0 = p.ws_acc + ((unit_slot0 + first_slot) * p.rows + row0) * D;
-  const int items = wg_rows * (D / 4);
+// ---- split-KV merge ----
+// The merged output of a unit is rows x D floats, cut into items (row r,
+// four head-dim columns d4): item = r * (D / 4) + d4.  Merge slice `slice`
+// of `nslices` covers items [slice * I / nslices, (slice + 1) * I / nslices).
+// LN lanes serve one item; lane `sub` takes slots sub, sub + LN, ... in
+// chunks of LN * U slots (U per lane), keeping a running (m, l, acc) in the
+// exp2 domain:  m* = max m_j,  l* = sum l_j 2^(m_j - m*),
+// acc* = sum acc_j 2^(m_j - m*)  (the log-sum-exp merge of split
+// partials); the LN lanes then combine in a fixed butterfly.  Each item's
+// sums follow one fixed order for a given (slot count, LN, U), whichever
+// workgroup merges it.  Every load is unconditional (item and slot indices
+// clamped, extra slots weighted zero) so the wait counts stay exact, and
+// the (pass, chunk) work of a thread is one stream with the next unit's
+// loads in flight while the current one is consumed.
+template <int U>
+struct MergeChunk {
+  f32x4 acc[U];
+  float2 ml[U];
+};
 
-  // All (m, l) loads, then the first batch of partial-acc loads, go out
-  // before anything waits.
-  const int n = count * wg_rows;
-  float2 mlv[kMlPerThread];
+template <int D, int NT, int LN, int U>
+__device__ __forceinline__ void merge_load(const Params& p, MergeChunk<U>& b, int64_t slot0, int row0, int i0, int i1,
+                                           int n, int nch, int w) {
+  constexpr int IPP = NT / LN, CH = LN * U;
+  const int pass = w / nch, ch = w - pass * nch;
+  const int it = min(i0 + pass * IPP + int(threadIdx.x) / LN, i1 - 1);
+  const int r = it / (D / 4), d4 = it % (D / 4);
+  const float* acc0 = p.ws_acc + (slot0 * p.rows + row0 + r) * D + 4 * d4;
+  const float* ml0 = p.ws_ml + (slot0 * p.rows + row0 + r) * 2;
+  const int first = ch * CH + int(threadIdx.x) % LN;
 #pragma unroll
-  for (int u = 0; u < kMlPerThread; ++u) {
-    const int idx = u * NT + tid;
-    if (idx < n) {
-      const int j = idx / wg_rows, r = idx % wg_rows;
-      mlv[u] = *reinterpret_cast<const float2*>(p.ws_ml + ((unit_slot0 + first_slot + j) * p.rows + row0 + r) * 2);
-    }
-  }
-  f32x4 v[IB][JC];
-  // Slot bases are uniform (scalar), the item offset is a 32-bit per-lane
-  // value: no per-load 64-bit address registers.
-  auto load_batch = [&](int it0, int j0) {
-#pragma unroll
-    for (int b = 0; b < IB; ++b) {
-      const int it = it0 + b * NT;
-      const int r = it / (D / 4), d4 = it % (D / 4);
-      const uint32_t off = uint32_t(r * D + 4 * d4) * 4u;
-#pragma unroll
-      for (int u = 0; u < JC; ++u)
-        if (it < items && j0 + u < count)
-          v[b][u] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const unsigned char*>(src0 + (j0 + u) * jstride) +
-                                                    off);
-    }
-  };
-  load_batch(tid, 0);
-#pragma unroll
-  for (int u = 0; u < kMlPerThread; ++u) {
-    const int idx = u * NT + tid;
-    if (idx < n) sm_ml[idx] = mlv[u];
-  }
-  __syncthreads();
-  // Per row, one lane per slot (32-lane halves of a wave): max and sum by
-  // butterfly reductions in a fixed pattern (deterministic).
-  static_assert(kMergeSlots <= 32, "one lane per merged slot");
-  for (int r = tid >> 5; r < wg_rows; r += NT / 32) {
-    const int j = tid & 31;
-    const float2 ml = j < count ? sm_ml[j * wg_rows + r] : float2{kNegInf, 0.f};
-    float ms = ml.x;
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) ms = fmaxf(ms, __shfl_xor(ms, off, 32));
-    const float mu = ms == kNegInf ? 0.f : ms;
-    const float w = j < count ? fast_exp2(ml.x - mu) : 0.f;
-    float ls = w * ml.y;
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) ls += __shfl_xor(ls, off, 32);
-    if (j < count) sm_ml[j * wg_rows + r].x = w;  // weight of slot j for this row
-    if (j == 0) {
-      sm_ms[r] = ms;
-      sm_ls[r] = ls;
-    }
-  }
-  __syncthreads();
-
-  for (int it0 = tid; it0 < items; it0 += IB * NT) {
-    f32x4 a[IB];
-#pragma unroll
-    for (int b = 0; b < IB; ++b) a[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < count; j0 += JC) {
-      if (j0 > 0 || it0 != tid) load_batch(it0, j0);
-#pragma unroll
-      for (int b = 0; b < IB; ++b) {
-        const int it = it0 + b * NT;
-        const int r = it / (D / 4);
-#pragma unroll
-        for (int u = 0; u < JC; ++u)
-          if (it < items && j0 + u < count) a[b] += sm_ml[(j0 + u) * wg_rows + r].x * v[b][u];
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < IB; ++b) {
-      const int it = it0 + b * NT;
-      if (it >= items) continue;
-      const int r = it / (D / 4), d4 = it % (D / 4);
-      if (out_final) {
-        const float ls = sm_ls[r];
-        const float inv = ls > 0.f ? 1.f / ls : 0.f;
-        uint2 o;
-        o.x = uint32_t(MF::bits(a[b][0] * inv)) | (uint32_t(MF::bits(a[b][1] * inv)) << 16);
-        o.y = uint32_t(MF::bits(a[b][2] * inv)) | (uint32_t(MF::bits(a[b][3] * inv)) << 16);
-        *reinterpret_cast<uint2*>(out_row(p, out_s, kvh, row0 + r, D) + 4 * d4) = o;
-      } else {
-        store_coherent(p.ws_acc + ((unit_slot0 + dst_slot) * p.rows + row0 + r) * D + 4 * d4, a[b]);
-      }
-    }
-  }
-  if (!out_final) {
-    for (int r = tid; r < wg_rows; r += NT)
-      store_coherent2(p.ws_ml + ((unit_slot0 + dst_slot) * p.rows + row0 + r) * 2, sm_ms[r], sm_ls[r]);
+  for (int u = 0; u < U; ++u) {
+    const int j = min(first + LN * u, n - 1);
+    b.acc[u] = *reinterpret_cast<const f32x4*>(acc0 + int64_t(j) * p.rows * D);
+    b.ml[u] = *reinterpret_cast<const float2*>(ml0 + int64_t(j) * p.rows * 2);
   }
 }
 
-// Count this workgroup's arrival on `counter` once every wave's partial
-// stores (device-coherent) have completed; returns whether it arrived last
-// of `expected`.  The last arriver invalidates stale cache lines (acquire)
-// before it reads the other workgroups' partials.
-__device__ __forceinline__ bool arrive(int* counter, int expected, int* sm_flag) {
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = prev == expected - 1;
-    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    *sm_flag = last;
+template <typename T, int D, int NT, int LN, int U>
+__device__ __forceinline__ void merge_consume(const Params& p, const MergeChunk<U>& b, int i0, int i1, int n, int nch,
+                                              int w, int row0, T* out_s, int kvh, float& m_run, float& l_run,
+                                              f32x4& a_run) {
+  using MF = Mfma<T>;
+  constexpr int IPP = NT / LN, CH = LN * U;
+  const int pass = w / nch, ch = w - pass * nch;
+  const int sub = int(threadIdx.x) % LN;
+  if (ch == 0) {
+    m_run = kNegInf;
+    l_run = 0.f;
+    a_run = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  __syncthreads();
-  return *sm_flag;
+  const int first = ch * CH + sub;
+  float mj[U];
+  float mloc = kNegInf;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    mj[u] = first + LN * u < n ? b.ml[u].x : kNegInf;
+    mloc = fmaxf(mloc, mj[u]);
+  }
+  const float m_new = fmaxf(m_run, mloc);
+  const float m_use = m_new == kNegInf ? 0.f : m_new;
+  const float sc = fast_exp2(m_run - m_use);
+  l_run *= sc;
+  a_run *= sc;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float wgt = fast_exp2(mj[u] - m_use);
+    l_run += wgt * b.ml[u].y;
+    a_run += wgt * b.acc[u];
+  }
+  m_run = m_new;
+  if (ch != nch - 1) return;
+  // Last chunk of the pass: combine the item's lanes and write it.
+  float m_all = m_run;
+#pragma unroll
+  for (int o = 1; o < LN; o <<= 1) m_all = fmaxf(m_all, __shfl_xor(m_all, o));
+  const float f = fast_exp2(m_run - (m_all == kNegInf ? 0.f : m_all));
+  float l = l_run * f;
+  f32x4 a = a_run * f;
+#pragma unroll
+  for (int o = 1; o < LN; o <<= 1) {
+    l += __shfl_xor(l, o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] += __shfl_xor(a[e], o);
+  }
+  const int it = i0 + pass * IPP + int(threadIdx.x) / LN;
+  if (sub == 0 && it < i1) {
+    const int r = it / (D / 4), d4 = it % (D / 4);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint2 o;
+    o.x = uint32_t(MF::bits(a[0] * inv)) | (uint32_t(MF::bits(a[1] * inv)) << 16);
+    o.y = uint32_t(MF::bits(a[2] * inv)) | (uint32_t(MF::bits(a[3] * inv)) << 16);
+    *reinterpret_cast<uint2*>(out_row(p, out_s, kvh, row0 + r, D) + 4 * d4) = o;
+  }
+}
+
+template <typename T, int D, int NT, int LN, int U>
+__device__ __forceinline__ void merge_items(const Params& p, int64_t slot0, int n, int row0, int i0, int i1, T* out_s,
+                                         int kvh) {
+  constexpr int IPP = NT / LN, CH = LN * U;
+  const int nch = (n + CH - 1) / CH;
+  const int W = (i1 - i0 + IPP - 1) / IPP * nch;
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4 a_run = {0.f, 0.f, 0.f, 0.f};
+  MergeChunk<U> b0, b1;
+  merge_load<D, NT, LN, U>(p, b0, slot0, row0, i0, i1, n, nch, 0);
+  if (W == 1) {
+    merge_consume<T, D, NT, LN, U>(p, b0, i0, i1, n, nch, 0, row0, out_s, kvh, m_run, l_run, a_run);
+    return;
+  }
+  for (int w = 0; w < W; w += 2) {
+    merge_load<D, NT, LN, U>(p, b1, slot0, row0, i0, i1, n, nch, min(w + 1, W - 1));
+    merge_consume<T, D, NT, LN, U>(p, b0, i0, i1, n, nch, w, row0, out_s, kvh, m_run, l_run, a_run);
+    merge_load<D, NT, LN, U>(p, b0, slot0, row0, i0, i1, n, nch, min(w + 2, W - 1));
+    if (w + 1 < W)
+      merge_consume<T, D, NT, LN, U>(p, b1, i0, i1, n, nch, w + 1, row0, out_s, kvh, m_run, l_run, a_run);
+  }
+}
+
+// Merge slice `slice` of `nslices` of the n partials of a unit (slots
+// slot0 .. slot0 + n - 1, rows row0 .. row0 + wg_rows - 1 of each) into
+// the output.  Lanes per item and slots per lane follow the slice size and
+// the slot count: as many lanes per item as keep the slice in one pass.
+// The caller has acquired the partials.
+template <typename T, int D, int NT>
+__device__ __forceinline__ void merge_slice(const Params& p, int64_t slot0, int n, int row0, int wg_rows, int slice,
+                                            int nslices, T* out_s, int kvh) {
+  const int items = wg_rows * (D / 4);
+  const int i0 = slice * items / nslices, i1 = (slice + 1) * items / nslices;
+  if (i1 <= i0) return;
+  const int span = i1 - i0;
+  const int ln = span * 4 <= NT ? 4 : (span * 2 <= NT ? 2 : 1);
+  const int per = (n + ln - 1) / ln;
+  const int u = per <= 2 ? 2 : (per <= 4 ? 4 : 8);
+  switch (ln * 16 + u) {
+    case 4 * 16 + 2: merge_items<T, D, NT, 4, 2>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 4 * 16 + 4: merge_items<T, D, NT, 4, 4>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 4 * 16 + 8: merge_items<T, D, NT, 4, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 2 * 16 + 2: merge_items<T, D, NT, 2, 2>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 2 * 16 + 4: merge_items<T, D, NT, 2, 4>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 2 * 16 + 8: merge_items<T, D, NT, 2, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 1 * 16 + 2: merge_items<T, D, NT, 1, 2>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 1 * 16 + 4: merge_items<T, D, NT, 1, 4>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    default: merge_items<T, D, NT, 1, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+  }
+}
+
+// Hand-over word of a merge slice (one per slice after the first).  The
+// helper merging slice s (the s-th workgroup to arrive before the last)
+// and the last arriver each act on it once or twice:
+//   helper:  idle -> waiting, then waits (bounded) until the unit's arrival
+//            count is complete or the word says go; then waiting -> done
+//            (if the word already says go, the helper resets it to idle);
+//            on timeout waiting -> gave_up, leaving the slice to the last
+//            arriver (if go got there first, it merges after all).
+//   last:    -> go; finding done or gave_up, it resets the word to idle (and
+//            for gave_up merges the slice itself).
+// Whoever acts second leaves the word idle, so every launch starts clean.
+constexpr int kSliceIdle = 0, kSliceWaiting = 1, kSliceGo = 2, kSliceGaveUp = 3, kSliceDone = 4;
+// Control words of a unit sit one cache line (128 bytes) apart: the
+// helpers poll their own words while the last arriver updates them.
+constexpr int kCtlStride = kCtlWordStride;
+
+// A helper's side of the exchange (one thread): whether it merges its
+// slice.  Every path ends: the wait is bounded by wait_ticks of the
+// 100 MHz real-time counter.
+__device__ __forceinline__ bool helper_wait(int* word, const int* counter, int n, uint32_t wait_ticks) {
+  int seen = kSliceIdle;
+  if (!__hip_atomic_compare_exchange_strong(word, &seen, kSliceWaiting, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT)) {
+    // The last arriver came first (go): this is the word's last use.
+    __hip_atomic_store(word, kSliceIdle, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+  }
+  const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + wait_ticks;
+  while (__builtin_amdgcn_s_memrealtime() < t_end) {
+    if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n ||
+        __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kSliceGo) {
+      if (__hip_atomic_exchange(word, kSliceDone, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kSliceGo)
+        __hip_atomic_store(word, kSliceIdle, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return true;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  seen = kSliceWaiting;
+  if (__hip_atomic_compare_exchange_strong(word, &seen, kSliceGaveUp, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT))
+    return false;
+  __hip_atomic_store(word, kSliceIdle, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // go came first
+  return true;
 }
 
 // After the waves of a workgroup have left their results in LDS -- per
@@ -283,11 +333,9 @@ __device__ __forceinline__ bool arrive(int* counter, int expected, int* sm_flag)
 // rows, already rescaled to the workgroup maximum, in slot w of sm_acc; and
 // the workgroup's merged max/sum in sm_ms/sm_ls -- sum the slots in wave
 // order (deterministic) and either write the output (single segment) or
-// publish this segment's partial and take part in the arrival tree:
-// segments form groups of kMergeGroup; the last arriver of a group merges
-// the group's partials (into the output when there is one group, else
-// into a group partial); the last group to finish merges the groups.
-
+// publish this segment's partial and count its arrival.  Of the n arrivals
+// of a unit, the last one and the k - 1 before it (k = merge slices) merge
+// one slice of the output each; the rest are done.
 template <typename T, int D, int RT, int NW>
 __device__ __forceinline__ void finish(const Params& p, unsigned char* lds, int s, int kvh, int rg, int seg, int row0,
                                        int wg_rows, int n_live, int lds_bytes) {
@@ -322,32 +370,64 @@ __device__ __forceinline__ void finish(const Params& p, unsigned char* lds, int 
     return;
   }
 
-  const int ngroups = (n_live + kMergeGroup - 1) / kMergeGroup;
-  const int ngmax = (p.nseg + kMergeGroup - 1) / kMergeGroup;
-  const int64_t unit_slot0 = (int64_t(s) * p.num_kv_heads + kvh) * (p.nseg + ngmax);
+  // Publish the partial with device-coherent stores.
+  const int64_t slot0 = (int64_t(s) * p.num_kv_heads + kvh) * p.nseg;
   {
-    const int64_t base = (unit_slot0 + seg) * p.rows + row0;
+    const int64_t base = (slot0 + seg) * p.rows + row0;
     for (int it = tid; it < wg_rows * (D / 4); it += NT) {
       const int r = it / (D / 4), d4 = it % (D / 4);
       store_coherent(p.ws_acc + (base + r) * D + 4 * d4, combined(r, d4));
     }
     for (int r = tid; r < wg_rows; r += NT) store_coherent2(p.ws_ml + (base + r) * 2, sm_ms[r], sm_ls[r]);
   }
-  int* counters = p.ws_cnt + ((int64_t(s) * p.num_kv_heads + kvh) * p.row_groups + rg) * (1 + ngmax);
+  int* ctl = p.ws_cnt + ((int64_t(s) * p.num_kv_heads + kvh) * p.row_groups + rg) * p.merge_slices * kCtlStride;
   int* sm_flag = reinterpret_cast<int*>(lds + lds_bytes - 16);
-  const int grp = seg / kMergeGroup;
-  const int gsize = min(kMergeGroup, n_live - grp * kMergeGroup);
-  if (!arrive(counters + 1 + grp, gsize, sm_flag)) return;
-  if (tid == 0) counters[1 + grp] = 0;  // last user of this counter in the launch
-  if (ngroups == 1) {
-    merge_slots<T, D, RT, NW>(p, lds, unit_slot0, 0, n_live, row0, wg_rows, true, 0, out_s, kvh);
+  const int k = min(p.merge_slices, n_live);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    // Role: 0 = last arriver, 1 .. k-1 = helper merging that slice, -1 = done.
+    const int rank = __hip_atomic_fetch_add(ctl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int role = -1;
+    if (rank == n_live - 1) {
+      role = 0;
+    } else if (rank >= n_live - k) {
+      const int sl = n_live - 1 - rank;
+      if (helper_wait(ctl + sl * kCtlStride, ctl, n_live, p.merge_wait_ticks)) role = sl;
+    }
+    // Acquire: the other workgroups' partials are visible from here on.
+    if (role >= 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    sm_flag[0] = role;
+  }
+  __syncthreads();
+  const int role = sm_flag[0];
+  if (role < 0) return;
+  if (role > 0) {
+    merge_slice<T, D, NT>(p, slot0, n_live, row0, wg_rows, role, k, out_s, kvh);
     return;
   }
-  merge_slots<T, D, RT, NW>(p, lds, unit_slot0, grp * kMergeGroup, gsize, row0, wg_rows, false, p.nseg + grp, out_s,
-                            kvh);
-  if (!arrive(counters, ngroups, sm_flag)) return;
-  if (tid == 0) counters[0] = 0;
-  merge_slots<T, D, RT, NW>(p, lds, unit_slot0, p.nseg, ngroups, row0, wg_rows, true, 0, out_s, kvh);
+  // Last arriver: say go to the helpers (lanes 1 .. k-1 of wave 0), merge
+  // slice 0 while those exchanges are in flight, then settle each word and
+  // take over the slices whose helpers gave up.
+  int old = kSliceIdle;
+  if (tid >= 1 && tid < k)
+    old = __hip_atomic_exchange(ctl + tid * kCtlStride, kSliceGo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  merge_slice<T, D, NT>(p, slot0, n_live, row0, wg_rows, 0, k, out_s, kvh);
+  if (tid < 64) {
+    const bool mine = old == kSliceGaveUp;
+    if (mine || old == kSliceDone)
+      __hip_atomic_store(ctl + tid * kCtlStride, kSliceIdle, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t own = __ballot(mine);
+    if (tid == 0) {
+      sm_flag[1] = int(uint32_t(own));
+      // The arrival counter's last use in this launch: helpers that still
+      // poll it have the go word.
+      __hip_atomic_store(ctl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+  for (uint32_t own = uint32_t(sm_flag[1]); own != 0; own &= own - 1)
+    merge_slice<T, D, NT>(p, slot0, n_live, row0, wg_rows, __builtin_ctz(own), k, out_s, kvh);
 }
 
 template <typename T, int D>
@@ -642,9 +722,7 @@ struct DotShape {
   static constexpr int kThreads = NW * 64;
   static constexpr int KC = D / 32;
   static constexpr int PF = 1;
-  static constexpr int kMergeBytes = (2 * kMergeSlots * kMaxWgRows + 2 * kMaxWgRows) * 4;
-  static constexpr int kCombine = Combine<D, 1, NW>::kBytes;
-  static constexpr int kBytes = (kCombine > kMergeBytes ? kCombine : kMergeBytes) + 16;
+  static constexpr int kBytes = Combine<D, 1, NW>::kBytes + 16;
 };
 
 template <typename T, int D>

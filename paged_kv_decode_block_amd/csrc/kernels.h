@@ -14,7 +14,7 @@ struct Params {
   const int32_t* block_table; // [S, max_blocks]
   const int32_t* seq_lens;    // [S]
   void* out;                  // [S, M, Hq, D]
-  int32_t* ws_cnt;            // arrival counters [S, Hkv, row_groups]
+  int32_t* ws_cnt;            // merge control [S, Hkv, row_groups, merge_slices]
   float* ws_ml;               // partial (m, l) [S, Hkv, nseg, rows, 2]
   float* ws_acc;              // partial acc     [S, Hkv, nseg, rows, D]
   int64_t block_stride;       // elements between physical blocks
@@ -26,6 +26,8 @@ struct Params {
   int32_t nseg;               // segments per (sequence, kv head, row group)
   int32_t seg_tiles;          // planned 16-key tiles per segment
   int32_t row_groups;         // workgroups splitting the rows
+  int32_t merge_slices;       // slices of the merged output (merging workgroups)
+  uint32_t merge_wait_ticks;  // helpers' wait bound (100 MHz real-time ticks)
   float scale_log2;           // scale * log2(e): logits are kept in the exp2 domain
 };
 

@@ -102,14 +102,25 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
 
   if (p.nseg > 1) {
     const size_t S = size_t(sh.num_seqs), H = size_t(sh.num_kv_heads);
-    const size_t ngroups = size_t(ceil_div(p.nseg, kMergeGroupSize));
-    const size_t slot_rows = S * H * (size_t(p.nseg) + ngroups) * size_t(rows);
-    if (S * H * size_t(p.row_groups) * (1 + ngroups) * sizeof(int32_t) > kCounterBytes) return PAD_EUNSUPPORTED;
+    const size_t slot_rows = S * H * size_t(p.nseg) * size_t(rows);
+    // Slices: about kSliceBytes of partial accumulators each, limited by
+    // the segments (each merging workgroup must have arrived) and by the
+    // control words the counter prefix holds.
+    const size_t wg_rows = size_t(std::min(rows, p.row_tiles * 16));
+    const size_t vol = size_t(p.nseg) * wg_rows * size_t(sh.head_size) * sizeof(float);
+    int64_t k = int64_t((vol + kSliceBytes - 1) / kSliceBytes);
+    k = std::min<int64_t>(k, std::min(p.nseg, kMaxSlices));
+    const size_t ctl_units = S * H * size_t(p.row_groups);
+    k = std::min<int64_t>(
+        k, int64_t(kCounterBytes / (sizeof(int32_t) * kCtlWordStride * std::max<size_t>(1, ctl_units))));
+    if (k < 1) return PAD_EUNSUPPORTED;  // more units than the counter prefix holds
+    p.merge_slices = int(k);
     p.ws_counters = 0;
     p.ws_ml = kCounterBytes;
     p.ws_acc = p.ws_ml + align_up(slot_rows * 2 * sizeof(float));
     p.ws_bytes = p.ws_acc + align_up(slot_rows * size_t(sh.head_size) * sizeof(float));
   } else {
+    p.merge_slices = 1;
     p.ws_counters = p.ws_ml = p.ws_acc = p.ws_bytes = 0;
   }
   *pl = p;

@@ -4,8 +4,10 @@
 // head share one read of its K/V pages (ROCm/vllm pull request 1330,
 // "Summary": one workgroup per kv head, row group and KV segment).  The
 // key range of a unit is split into segments; each segment is one
-// workgroup whose partial (acc, m, l) is merged in-kernel by the last
-// segment to arrive.  The planner picks the row tiling (16-row MFMA tiles,
+// workgroup whose partial (acc, m, l) is merged in-kernel once every
+// segment has arrived: the merged output is cut into slices, and the last
+// arriver and the workgroups that arrived just before it merge one slice
+// each.  The planner picks the row tiling (16-row MFMA tiles,
 // the rows_padded rule of KernelVariant on the rocm_rdna_hip page), the
 // number of segments (enough workgroups to fill the device, cf. the
 // split cap of 256 "to fill its CUs with one query" of _mid_o_shape on the
@@ -21,12 +23,17 @@ namespace pad {
 
 constexpr int kTileKeys = 16;    // keys per MFMA tile (page sizes are multiples of 16)
 constexpr int kMaxSegments = 256;
-constexpr int kMergeGroupSize = 32;
+// Merge slices per unit: about kSliceBytes of partial accumulators each,
+// at most kMaxSlices (one control word per slice in the counter prefix).
+constexpr int kMaxSlices = 32;
+constexpr size_t kSliceBytes = size_t(32) << 10;
+// Merge control words are spaced one 128-byte line apart (in int32s).
+constexpr int kCtlWordStride = 32;
 // The dot-product family serves up to this many query rows per kv head at
 // head sizes up to kDotMaxHeadSize, with kDotWaves waves per workgroup.
 constexpr int kDotMaxRows = 4;
 constexpr int kDotMaxHeadSize = 128;
-constexpr int kDotWaveCount = 4;  // segments merged per group of the two-level merge tree
+constexpr int kDotWaveCount = 4;
 // Arrival counters live in a fixed-size prefix of the workspace, so calls of
 // different shapes can share one workspace: partials never land where any
 // shape keeps counters, and every call leaves its counters zero.
@@ -44,11 +51,13 @@ struct Plan {
   int waves;         // waves per workgroup
   int nseg;          // segments per (unit, row group)
   int seg_tiles;     // planned tiles per segment
+  int merge_slices;  // slices the merged output is cut into (1..kMaxSlices)
   int grid_x, grid_y;
   // Workspace layout (byte offsets; all 256-byte aligned): the counter
-  // prefix (kCounterBytes; per (unit, row group) one top counter plus one
-  // per merge group), then per unit nseg segment slots plus
-  // ceil(nseg / kMergeGroupSize) group slots of (m, l) and of acc.
+  // prefix (kCounterBytes; per (unit, row group) merge_slices words, one
+  // 128-byte line apart: the arrival counter, then one hand-over word per
+  // slice after the first),
+  // then per unit nseg segment slots of (m, l) and of acc.
   size_t ws_counters, ws_ml, ws_acc, ws_bytes;
 };
 

@@ -83,13 +83,22 @@ def test_plan_invariants(kw):
     assert p["grid_y"] == sh.num_seqs
     if p["num_segments"] == 1:
         assert p["workspace_bytes"] == 0
+        assert p["merge_slices"] == 1
     else:
-        # a fixed 1 MiB counter prefix, then segment slots plus one slot per
-        # merge group of 32 segments
+        # a fixed 1 MiB prefix of merge control words, then one (m, l) and one
+        # acc slot per segment
         S, H, n = sh.num_seqs, sh.num_kv_heads, p["num_segments"]
-        ng = -(-n // 32)
-        want = (1 << 20) + _align(S * H * (n + ng) * rows * 2 * 4) + _align(S * H * (n + ng) * rows * sh.head_size * 4)
+        want = (1 << 20) + _align(S * H * n * rows * 2 * 4) + _align(S * H * n * rows * sh.head_size * 4)
         assert p["workspace_bytes"] == want
+        # about 32 KiB of partial accumulators per merge slice, at most 32
+        # slices and no more than segments; control words fit the prefix
+        k = p["merge_slices"]
+        wg_rows = min(rows, p["row_tiles"] * 16)
+        vol = n * wg_rows * sh.head_size * 4
+        assert 1 <= k <= min(32, n)
+        # control words one 128-byte line apart
+        assert k == min(-(-vol // (32 << 10)), 32, n, (1 << 20) // (128 * S * H * p["row_groups"]))
+        assert S * H * p["row_groups"] * k * 128 <= (1 << 20)
 
 
 def test_plan_fills_device():
@@ -198,3 +207,10 @@ def test_workspace_size_and_init_validation():
     assert pad.lib.pad_decode_attn_workspace_init(P(0), ctypes.c_size_t(0), None) == pad.PAD_OK
     assert pad.lib.pad_decode_attn_workspace_init(P(0), ctypes.c_size_t(256), None) == pad.PAD_EINVAL
     assert pad.lib.pad_decode_attn_workspace_init(P(0x1010), ctypes.c_size_t(256), None) == pad.PAD_EINVAL
+
+
+def test_merge_wait_bounds():
+    assert pad.lib.pad_set_merge_wait(-1) == pad.PAD_EINVAL
+    assert pad.lib.pad_set_merge_wait(1000001) == pad.PAD_EINVAL
+    assert pad.lib.pad_set_merge_wait(0) == pad.PAD_OK
+    assert pad.lib.pad_set_merge_wait(200) == pad.PAD_OK

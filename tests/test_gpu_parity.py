@@ -160,6 +160,41 @@ def test_deterministic():
     assert torch.equal(a, b)
 
 
+# (config, lengths, M, forced segments): merges of 4 to 32 slices, with
+# row groups, wide heads and a ragged batch.
+MERGE_CASES = [
+    (2, [4096], 4, 0),
+    (2, [4096], 4, 256),
+    (4, [3000], 8, 0),
+    (4, [2048], 1, 128),
+    (5, [9000, 700, 0, 13000], 4, 0),
+]
+
+
+@pytest.mark.parametrize("cfg,lens,M,nseg", MERGE_CASES, ids=[f"m{i}" for i in range(len(MERGE_CASES))])
+def test_merge_handover(cfg, lens, M, nseg):
+    """Merge helpers that stop waiting at once leave their slices to the
+    last segment: the output keeps the same bits and every merge control
+    word is left zero."""
+    c = _case(wl.CONFIGS[cfg], lens, M, 300 + cfg)
+    shape = pad.make_shape(c.q, c.kv_cache, c.block_tables[0], c.layout, num_segments=nseg)
+    plan = pad.pad_decode_attn_plan(shape, c.window)
+    assert plan["num_segments"] > 1 and plan["merge_slices"] > 1, plan
+    ws = torch.empty(pad.pad_decode_attn_workspace_size(shape), dtype=torch.uint8, device=DEV)
+    pad.pad_decode_attn_workspace_init(ws)
+    ref = oracle_out(c)
+    a = run_gpu(c, workspace=ws, num_segments=nseg)
+    try:
+        pad.pad_set_merge_wait(0)
+        b = run_gpu(c, workspace=ws, num_segments=nseg)
+        torch.cuda.synchronize()
+    finally:
+        pad.pad_set_merge_wait(200)
+    check(a, ref, c.q.dtype, f"merge slices {plan['merge_slices']}")
+    assert torch.equal(a, b), "the fallback merge must give the same bits"
+    assert int(ws[: 1 << 20].view(torch.int32).abs().sum()) == 0
+
+
 def test_graph_replay():
     c = _case(wl.CONFIGS[4], [2500], 4, 6, instances=2)
     ref = [oracle_out(c, i) for i in range(2)]
