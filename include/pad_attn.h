@@ -56,10 +56,11 @@
  * visible on the host are validated (shape fields, pointer presence and
  * alignment, workspace size).  Device contents are the caller's contract:
  * block ids in the block table must address existing blocks for every page
- * a sequence's visible keys touch, and seq_lens[s] <= max_blocks_per_seq *
- * page_size; violating it is undefined behaviour.  Table entries of pages
- * no visible key touches (before a window, past a sequence's end, the rows
- * of length-0 sequences) are never read.
+ * a sequence's visible keys touch; violating it is undefined behaviour.  A
+ * seq_lens[s] above max_blocks_per_seq * page_size is treated as that
+ * capacity, and one <= 0 gives a zero output for the sequence.  Table
+ * entries of pages no visible key touches (before a window, past a
+ * sequence's end, the rows of length-0 sequences) are never read.
  */
 #ifndef PAD_ATTN_H
 #define PAD_ATTN_H

@@ -121,13 +121,18 @@ struct Shape {
   static constexpr int kVStride = D + 8;    // elements per staged V row (16-byte padded)
   static constexpr int kAccStride = D + 4;  // floats per accumulator row in LDS
   static constexpr int kRows = RT * 16;
-  // Tiles in flight beyond the one being computed (register budget).
-  static constexpr int PF = D * RT <= 128 ? 2 : (D * RT <= 512 && D < 512 ? 1 : 0);
-  // LDS: V staging during the tile loop, afterwards the wave-combine area.
-  // The last 16 bytes hold the merge role and hand-over flags.
+  // Tiles in flight beyond the one being computed: one while the register
+  // budget allows it (a second one measured slower).
+  static constexpr int PF = D * RT <= 512 && D < 512 ? 1 : 0;
+  // LDS: V staging and the segment's block ids during the tile loop,
+  // afterwards the wave-combine area.  The last 16 bytes hold the merge
+  // role and hand-over flags.
   static constexpr int kVBytes = NW * 16 * kVStride * 2;
+  // The segment's block ids, one per tile, follow the V staging area.
+  static constexpr int kIdsBytes = kMaxSegTiles * 4;
+  static constexpr int kLoopBytes = kVBytes + kIdsBytes;
   static constexpr int kCombineBytes = Combine<D, RT, NW>::kBytes;
-  static constexpr int kBytes = (kVBytes > kCombineBytes ? kVBytes : kCombineBytes) + 16;
+  static constexpr int kBytes = (kLoopBytes > kCombineBytes ? kLoopBytes : kCombineBytes) + 16;
 };
 
 template <typename T>
@@ -461,7 +466,8 @@ __global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(P
   const int wg_rows = min(RT * 16, p.rows - row0);
   const int M = p.query_len;
 
-  const int L = p.seq_lens[s];
+  // Lengths past the block table's capacity are clamped to it.
+  const int L = min(p.seq_lens[s], p.max_blocks * p.page_size);
   if (L <= 0) {
     if (seg == 0) zero_rows<T, D>(p, s, kvh, row0, wg_rows, SH::kThreads);
     return;
@@ -528,8 +534,14 @@ __global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(P
     i32x4 v[KC];
   };
 
-  // Physical block of tile t (a scalar load: t is wave-uniform).
-  auto block_of = [&](int t) { return table[(t * 16) / p.page_size]; };
+  // The segment's block ids (one per tile) go to LDS once, so a tile's
+  // page address costs an LDS read instead of a scalar load that may miss.
+  // The planner keeps segments within kMaxSegTiles tiles.
+  int* sm_ids = reinterpret_cast<int*>(lds + SH::kVBytes);
+  for (int t = tid; t < te - ts; t += SH::kThreads) sm_ids[t] = table[((ts + t) * 16) / p.page_size];
+  __syncthreads();
+  // Physical block of tile t (wave-uniform).
+  auto block_of = [&](int t) { return __builtin_amdgcn_readfirstlane(sm_ids[t - ts]); };
 
   auto issue_tile = [&](Tile& tl, int t, int blk) {
     const int key0 = t * 16;
@@ -743,7 +755,8 @@ __global__ __launch_bounds__(kDotWaves * 64) void decode_dot_kernel(Params p) {
   const int rows = p.rows;  // <= kDotRows
   const int M = p.query_len;
 
-  const int L = p.seq_lens[s];
+  // Lengths past the block table's capacity are clamped to it.
+  const int L = min(p.seq_lens[s], p.max_blocks * p.page_size);
   if (L <= 0) {
     if (seg == 0) zero_rows<T, D>(p, s, kvh, 0, rows, SH::kThreads);
     return;

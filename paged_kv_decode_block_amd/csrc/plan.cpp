@@ -33,6 +33,8 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   if (sh.path < PAD_PATH_AUTO || sh.path > PAD_PATH_DOT) return PAD_EINVAL;
   const int64_t table_keys = int64_t(sh.max_blocks_per_seq) * sh.page_size;
   if (sh.max_seq_len > table_keys) return PAD_EINVAL;
+  // Key and tile indices are 32-bit on the device.
+  if (table_keys > (int64_t(1) << 30)) return PAD_EUNSUPPORTED;
   // Decode and speculative verify only (M <= 8); other head sizes and page
   // sizes that are not multiples of the 16-key tile are not built.
   if (sh.query_len > 8 || !known_head_size(sh.head_size) || sh.page_size % kTileKeys != 0)
@@ -75,7 +77,7 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   span_tiles = std::max<int64_t>(1, span_tiles);
 
   const int64_t units = int64_t(sh.num_seqs) * sh.num_kv_heads * p.row_groups;
-  // One workgroup fills a CU (8 waves at two per SIMD, or 4 large waves).
+  // One workgroup per CU: its 4 waves keep enough loads in flight.
   const int64_t slots = num_cus;
   int64_t nseg;
   if (sh.num_segments > 0) {
@@ -96,6 +98,18 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   nseg = std::max<int64_t>(1, nseg);
   p.seg_tiles = int(ceil_div(span_tiles, nseg));
   p.nseg = int(ceil_div(span_tiles, p.seg_tiles));
+  // A workgroup stages its segment's block ids in LDS, so no segment may
+  // exceed kMaxSegTiles tiles -- also for device lengths beyond
+  // max_seq_len, up to the table's capacity (the kernel clamps to it and
+  // splits the tiles it finds over the planned segments).
+  int64_t max_tiles = ceil_div(table_keys, kTileKeys);
+  if (window > 0) max_tiles = std::min(max_tiles + 1, ceil_div(int64_t(window) + sh.query_len - 1, kTileKeys) + 1);
+  if (ceil_div(max_tiles, p.nseg) > kMaxSegTiles || p.seg_tiles > kMaxSegTiles) {
+    const int64_t need = ceil_div(max_tiles, kMaxSegTiles);
+    if (need > kMaxSegments) return PAD_EUNSUPPORTED;
+    p.nseg = int(std::max<int64_t>(p.nseg, need));
+    p.seg_tiles = int(ceil_div(span_tiles, p.nseg));
+  }
 
   p.grid_x = p.nseg * sh.num_kv_heads * p.row_groups;
   p.grid_y = std::max(1, sh.num_seqs);

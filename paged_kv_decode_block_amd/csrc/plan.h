@@ -23,6 +23,9 @@ namespace pad {
 
 constexpr int kTileKeys = 16;    // keys per MFMA tile (page sizes are multiples of 16)
 constexpr int kMaxSegments = 256;
+// Longest segment in tiles: a workgroup stages its segment's block ids
+// (one int32 per tile) in LDS.
+constexpr int kMaxSegTiles = 4096;
 // Merge slices per unit: about kSliceBytes of partial accumulators each,
 // at most kMaxSlices (one control word per slice in the counter prefix).
 constexpr int kMaxSlices = 32;
@@ -39,9 +42,12 @@ constexpr int kDotWaveCount = 4;
 // shape keeps counters, and every call leaves its counters zero.
 constexpr size_t kCounterBytes = size_t(1) << 20;
 
-// Waves per workgroup: eight when a wave's state (accumulator of
-// head_size x 16 x row_tiles) allows two waves per SIMD, else four.
-constexpr int waves_for(int head_size, int row_tiles) { return head_size * row_tiles <= 128 ? 8 : 4; }
+// Waves per workgroup.  Four for every shape: on one bf16 sequence with
+// 32 query / 8 kv heads of size 128 and 16-key pages, 4 waves with one
+// tile in flight beyond the one computed beat 8 waves with two (32k keys:
+// 31.9 vs 36.1 us; 4k keys: 12.4 vs 16.6 us) -- more loads in flight per
+// CU only queue longer.
+constexpr int waves_for(int head_size, int row_tiles) { return (void)head_size, (void)row_tiles, 4; }
 
 struct Plan {
   int path;          // PAD_PATH_MFMA / PAD_PATH_DOT

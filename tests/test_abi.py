@@ -79,6 +79,9 @@ def test_plan_invariants(kw):
     assert p["num_segments"] * p["segment_tiles"] >= tiles
     assert (p["num_segments"] - 1) * p["segment_tiles"] < tiles
     assert 1 <= p["num_segments"] <= 256
+    # segments stay within 4096 tiles (the LDS block-id stage) for any
+    # device length up to the table's capacity
+    assert p["segment_tiles"] <= 4096 and -(-tiles // p["num_segments"]) <= 4096
     assert p["grid_x"] == p["num_segments"] * sh.num_kv_heads * p["row_groups"]
     assert p["grid_y"] == sh.num_seqs
     if p["num_segments"] == 1:
@@ -99,6 +102,22 @@ def test_plan_invariants(kw):
         # control words one 128-byte line apart
         assert k == min(-(-vol // (32 << 10)), 32, n, (1 << 20) // (128 * S * H * p["row_groups"]))
         assert S * H * p["row_groups"] * k * 128 <= (1 << 20)
+
+
+def test_plan_bounds_segment_length():
+    # a large table with a small planning bound: segments still cover the
+    # whole table within 4096 tiles each
+    p = plan(shape(max_blocks_per_seq=200000, max_seq_len=1000))
+    tiles = 200000 * 16 // 16
+    assert -(-tiles // p["num_segments"]) <= 4096 and p["segment_tiles"] <= 4096
+    p = plan(shape(max_blocks_per_seq=200000, num_segments=1))
+    assert p["num_segments"] >= 49
+    with pytest.raises(pad.PadError) as e:
+        plan(shape(max_blocks_per_seq=(1 << 30) // 16 + 1))
+    assert e.value.status == pad.PAD_EUNSUPPORTED
+    with pytest.raises(pad.PadError) as e:
+        plan(shape(max_blocks_per_seq=(256 * 4096) + 1))
+    assert e.value.status == pad.PAD_EUNSUPPORTED
 
 
 def test_plan_fills_device():

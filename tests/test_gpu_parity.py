@@ -64,6 +64,20 @@ def test_config5_small_batch():
     check(out, oracle_out(c), c.q.dtype, "config5 small")
 
 
+def test_length_past_table_capacity():
+    """A device length above the block table's capacity is treated as that
+    capacity: no key past the table is read."""
+    c = _case(wl.CONFIGS[2], [1024, 700], 4, 91, max_blocks=64)
+    ref = oracle_out(c)
+    lens = c.seq_lens.clone()
+    lens[0] = 1 << 30
+    for nseg in (0, 1, 7):
+        out = torch.full_like(c.q, float("nan"))
+        pad.pad_decode_attn(c.q, c.kv_cache, c.block_tables[0], lens, c.scale, 0, out, layout=c.layout,
+                            num_segments=nseg)
+        check(out, ref, c.q.dtype, f"length clamped to the table, nseg={nseg}")
+
+
 # ------------------------------------------------------- random shapes
 
 
