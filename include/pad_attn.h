@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define PAD_ABI_VERSION 2
+#define PAD_ABI_VERSION 3
 
 typedef enum pad_status {
   PAD_OK = 0,
@@ -93,6 +93,15 @@ typedef enum pad_layout { PAD_NHD = 0, PAD_HND = 1 } pad_layout;
  * others force a family (tuning and tests). */
 typedef enum pad_path { PAD_PATH_AUTO = 0, PAD_PATH_MFMA = 1, PAD_PATH_DOT = 2 } pad_path;
 
+/* Work schedule.  AUTO picks the persistent grid for batches whose
+ * segments would oversubscribe the device, else one workgroup per item.
+ * Both give the same output bits for the same plan. */
+typedef enum pad_schedule {
+  PAD_SCHED_AUTO = 0,
+  PAD_SCHED_GRID = 1,        /* one workgroup per (sequence, kv head, segment)  */
+  PAD_SCHED_PERSISTENT = 2,  /* one workgroup per CU taking items from a queue  */
+} pad_schedule;
+
 /* Shape of one call.  Every field is host data. */
 typedef struct pad_shape {
   int32_t num_seqs;           /* S >= 0 (0: the call does nothing)                 */
@@ -110,6 +119,7 @@ typedef struct pad_shape {
   int32_t num_segments;       /* 0 = planner's choice; > 0 forces the split-KV
                                  segment count per (sequence, kv head)           */
   int32_t path;               /* pad_path                                        */
+  int32_t schedule;           /* pad_schedule                                    */
 } pad_shape;
 
 /* The launch the planner chose (introspection, tests and tuning). */
@@ -123,6 +133,10 @@ typedef struct pad_plan {
   int32_t segment_tiles;     /* 16-key tiles per segment (planned)                */
   int32_t grid_x, grid_y;    /* launch grid                                       */
   int32_t merge_slices;      /* workgroups that share the merge of a split unit   */
+  int32_t persistent;        /* 1: grid_x workgroups take the (sequence, kv head,
+                                segment) items from a queue in the workspace;
+                                0: one workgroup per item                        */
+  int32_t reserved;
   uint64_t workspace_bytes;  /* bytes pad_decode_attn needs for this call         */
 } pad_plan;
 
@@ -138,12 +152,14 @@ pad_status pad_decode_attn_plan(const pad_shape* shape, int32_t window, int32_t 
                                 pad_plan* plan);
 
 /* Workspace bytes that serve every call of this shape (any window) on the
- * current device.  0 means no workspace is needed (a single segment). The
+ * current device.  0 means no workspace is needed (a single segment on a
+ * grid of one workgroup per item). The
  * split partials are fp32 (acc[rows][D], m, l per row and segment), as in
  * KernelVariant.scratch_shapes, after a fixed 1 MiB prefix of int32 merge
  * control words (per sequence, kv head and row group: an arrival counter
  * and one hand-over word per merge slice after the first, each in its own
- * 128-byte line). */
+ * 128-byte line; the prefix's last line holds the persistent grid's work
+ * queue). */
 pad_status pad_decode_attn_workspace_size(const pad_shape* shape, size_t* bytes);
 
 /* Zero a workspace of `bytes` bytes (device pointer, 256-byte aligned) on

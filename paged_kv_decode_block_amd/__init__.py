@@ -18,6 +18,7 @@ __all__ = [
     "PAD_OK", "PAD_EINVAL", "PAD_EUNSUPPORTED", "PAD_EWORKSPACE", "PAD_EHIP",
     "PAD_F16", "PAD_BF16", "PAD_NHD", "PAD_HND",
     "PAD_PATH_AUTO", "PAD_PATH_MFMA", "PAD_PATH_DOT",
+    "PAD_SCHED_AUTO", "PAD_SCHED_GRID", "PAD_SCHED_PERSISTENT",
     "PadError", "pad_shape", "pad_plan", "lib", "LIB_PATH", "load_library",
     "pad_abi_version", "pad_status_string", "pad_decode_attn_plan",
     "pad_decode_attn_workspace_size", "pad_decode_attn_workspace_init", "pad_decode_attn",
@@ -29,6 +30,7 @@ PAD_OK, PAD_EINVAL, PAD_EUNSUPPORTED, PAD_EWORKSPACE, PAD_EHIP = 0, 1, 2, 3, 4
 PAD_F16, PAD_BF16 = 0, 1
 PAD_NHD, PAD_HND = 0, 1
 PAD_PATH_AUTO, PAD_PATH_MFMA, PAD_PATH_DOT = 0, 1, 2
+PAD_SCHED_AUTO, PAD_SCHED_GRID, PAD_SCHED_PERSISTENT = 0, 1, 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpad_attn.so")
 
@@ -47,6 +49,7 @@ class pad_shape(ctypes.Structure):
         ("layout", ctypes.c_int32),
         ("num_segments", ctypes.c_int32),
         ("path", ctypes.c_int32),
+        ("schedule", ctypes.c_int32),
     ]
 
 
@@ -62,6 +65,8 @@ class pad_plan(ctypes.Structure):
         ("grid_x", ctypes.c_int32),
         ("grid_y", ctypes.c_int32),
         ("merge_slices", ctypes.c_int32),
+        ("persistent", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_uint64),
     ]
 
@@ -129,6 +134,7 @@ def make_shape(
     max_seq_len: int = 0,
     num_segments: int = 0,
     path: int = PAD_PATH_AUTO,
+    schedule: int = PAD_SCHED_AUTO,
 ) -> pad_shape:
     """The ``pad_shape`` of a call, read off the tensors' sizes."""
     if q.dim() != 4 or kv_cache.dim() != 5 or block_table.dim() != 2:
@@ -149,7 +155,7 @@ def make_shape(
     return pad_shape(
         num_seqs=S, query_len=M, num_q_heads=Hq, num_kv_heads=Hkv, head_size=D, page_size=P,
         max_blocks_per_seq=block_table.shape[1], max_seq_len=max_seq_len, dtype=_DTYPE_CODE[q.dtype],
-        layout=layout, num_segments=num_segments, path=path,
+        layout=layout, num_segments=num_segments, path=path, schedule=schedule,
     )
 
 
@@ -160,7 +166,7 @@ def pad_decode_attn_plan(shape: pad_shape, window: int = 0, num_cus: int | None 
     plan = pad_plan()
     _check(lib.pad_decode_attn_plan(ctypes.byref(shape), int(window), int(num_cus), ctypes.byref(plan)),
            "pad_decode_attn_plan")
-    return {name: getattr(plan, name) for name, _ in pad_plan._fields_}
+    return {name: getattr(plan, name) for name, _ in pad_plan._fields_ if name != "reserved"}
 
 
 def pad_decode_attn_workspace_size(shape: pad_shape) -> int:
@@ -225,6 +231,7 @@ def pad_decode_attn(
     max_seq_len: int = 0,
     num_segments: int = 0,
     path: int = PAD_PATH_AUTO,
+    schedule: int = PAD_SCHED_AUTO,
     stream=None,
 ) -> torch.Tensor:
     """Paged-KV decode attention into ``out`` (see include/pad_attn.h).
@@ -247,7 +254,7 @@ def pad_decode_attn(
     if seq_lens.shape != (q.shape[0],):
         raise ValueError("seq_lens must have one entry per sequence")
     shape = make_shape(q, kv_cache, block_table, layout, max_seq_len=max_seq_len,
-                       num_segments=num_segments, path=path)
+                       num_segments=num_segments, path=path, schedule=schedule)
     if workspace is None:
         dev = q.device.index
         ws = _default_ws.setdefault(dev, Workspace(q.device)).get(shape)

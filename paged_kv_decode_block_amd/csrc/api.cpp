@@ -75,6 +75,8 @@ pad_status pad_decode_attn_plan(const pad_shape* shape, int32_t window, int32_t 
   plan->grid_x = p.grid_x;
   plan->grid_y = p.grid_y;
   plan->merge_slices = p.merge_slices;
+  plan->persistent = p.persistent;
+  plan->reserved = 0;
   plan->workspace_bytes = p.ws_bytes;
   return PAD_OK;
 }
@@ -146,6 +148,7 @@ pad_status pad_decode_attn(const pad_shape* shape, const void* q, const void* kv
   pr.seg_tiles = p.seg_tiles;
   pr.row_groups = p.row_groups;
   pr.merge_slices = p.merge_slices;
+  pr.persistent = p.persistent;
   pr.merge_wait_ticks = g_merge_wait_ticks.load();
   pr.scale_log2 = float(double(scale) * 1.4426950408889634);  // log2(e)
   return pad::launch_decode(p, pr, shape->dtype, shape->head_size, stream) == 0 ? PAD_OK : PAD_EHIP;

@@ -75,6 +75,7 @@ struct Mfma<_Float16> {
 };
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -125,14 +126,17 @@ struct Shape {
   // budget allows it (a second one measured slower).
   static constexpr int PF = D * RT <= 512 && D < 512 ? 1 : 0;
   // LDS: V staging and the segment's block ids during the tile loop,
-  // afterwards the wave-combine area.  The last 16 bytes hold the merge
-  // role and hand-over flags.
+  // afterwards the wave-combine area; then the persistent grid's tables.
+  // The last 16 bytes hold the merge role, hand-over and queue words.
   static constexpr int kVBytes = NW * 16 * kVStride * 2;
   // The segment's block ids, one per tile, follow the V staging area.
   static constexpr int kIdsBytes = kMaxSegTiles * 4;
   static constexpr int kLoopBytes = kVBytes + kIdsBytes;
   static constexpr int kCombineBytes = Combine<D, RT, NW>::kBytes;
-  static constexpr int kBytes = (kLoopBytes > kCombineBytes ? kLoopBytes : kCombineBytes) + 16;
+  // Then the persistent grid's rank order and item prefix.
+  static constexpr int kPersistOff = kLoopBytes > kCombineBytes ? kLoopBytes : kCombineBytes;
+  static constexpr int kBytes = kPersistOff + (2 * kPersistMaxSeqs + 1) * 4 + 16;
+  static_assert(kLoopBytes >= 2 * kPersistMaxSeqs * 4, "persistent prologue scratch fits the tile-loop area");
 };
 
 template <typename T>
@@ -262,17 +266,17 @@ __device__ __forceinline__ void merge_items(const Params& p, int64_t slot0, int 
 
 // Merge slice `slice` of `nslices` of the n partials of a unit (slots
 // slot0 .. slot0 + n - 1, rows row0 .. row0 + wg_rows - 1 of each) into
-// the output.  Lanes per item and slots per lane follow the slice size and
-// the slot count: as many lanes per item as keep the slice in one pass.
-// The caller has acquired the partials.
+// the output.  Lanes per item and slots per lane follow the slot count
+// only, so an item's sums take the same order whatever the slicing and
+// whichever workgroup merges it: the output bits depend on the sequence
+// and the segment split alone.  The caller has acquired the partials.
 template <typename T, int D, int NT>
 __device__ __forceinline__ void merge_slice(const Params& p, int64_t slot0, int n, int row0, int wg_rows, int slice,
                                             int nslices, T* out_s, int kvh) {
   const int items = wg_rows * (D / 4);
   const int i0 = slice * items / nslices, i1 = (slice + 1) * items / nslices;
   if (i1 <= i0) return;
-  const int span = i1 - i0;
-  const int ln = span * 4 <= NT ? 4 : (span * 2 <= NT ? 2 : 1);
+  const int ln = n >= 24 ? 4 : (n >= 8 ? 2 : 1);
   const int per = (n + ln - 1) / ln;
   const int u = per <= 2 ? 2 : (per <= 4 ? 4 : 8);
   switch (ln * 16 + u) {
@@ -445,40 +449,148 @@ __device__ __forceinline__ void zero_rows(const Params& p, int s, int kvh, int r
   }
 }
 
+// Segments of a sequence of (clamped) length L: its visible key range in
+// 16-key tiles [t_lo, t_hi), split into n_live segments of seg_tiles tiles
+// (at least the planned count, stretched when a device length exceeds the
+// planning bound).
+struct SegSplit {
+  int t_lo, t_hi, seg_tiles, n_live;
+};
+
+__device__ __forceinline__ int clamped_len(const Params& p, int s) {
+  // Lengths past the block table's capacity are clamped to it.
+  return min(p.seq_lens[s], p.max_blocks * p.page_size);
+}
+
+__device__ __forceinline__ SegSplit split_of(const Params& p, int L) {
+  SegSplit r;
+  const int k_lo = p.window > 0 ? max(0, L - p.query_len - p.window + 1) : 0;
+  r.t_lo = k_lo >> 4;
+  r.t_hi = (L + 15) >> 4;
+  const int n_tiles = r.t_hi - r.t_lo;
+  r.seg_tiles = max(p.seg_tiles, (n_tiles + p.nseg - 1) / p.nseg);
+  r.n_live = (n_tiles + r.seg_tiles - 1) / r.seg_tiles;
+  return r;
+}
+
+// Persistent grid (batched decode): one workgroup per CU takes work items
+// from a queue in the workspace until none are left.  Items are the live
+// segments of every (sequence, kv head, row group), longest sequences
+// first (ties by index; up to kPersistSortSeqs sequences, else in index
+// order) and, within a sequence, unit-major so the segments of a unit run
+// together and its merge helpers wait little.  An item's work does not
+// depend on which workgroup takes it, so results stay bitwise the same.
+// Sequences of length <= 0 get one item per unit (its zero output).
+// Every workgroup ends with one failed take; the last of those resets the
+// queue for the next launch.
+template <typename Body>
+__device__ __forceinline__ void persistent_loop(const Params& p, unsigned char* lds, int persist_off, int lds_bytes,
+                                               int nt, Body body) {
+  const int tid = threadIdx.x;
+  const int S = p.num_seqs;
+  const int units = p.num_kv_heads * p.row_groups;
+  int* sm_order = reinterpret_cast<int*>(lds + persist_off);  // [S]: sequence of rank r
+  int* sm_pref = sm_order + kPersistMaxSeqs;                   // [S + 1]: first item of rank r
+  // Scratch before the first item (the tile-loop area): lengths and item
+  // counts per rank.
+  int* sm_len = reinterpret_cast<int*>(lds);                   // [S]
+  int* sm_cnt = sm_len + kPersistMaxSeqs;                      // [S]
+  int* sm_take = reinterpret_cast<int*>(lds + lds_bytes - 16) + 2;
+  for (int i = tid; i < S; i += nt) sm_len[i] = clamped_len(p, i);
+  __syncthreads();
+  const bool sort = S <= kPersistSortSeqs;
+  for (int i = tid; i < S; i += nt) {
+    const int li = sm_len[i];
+    int rank = i;
+    if (sort) {
+      rank = 0;
+      for (int j = 0; j < S; ++j) {
+        const int lj = sm_len[j];
+        rank += (lj > li) || (lj == li && j < i);
+      }
+    }
+    sm_order[rank] = i;
+  }
+  __syncthreads();
+  // Items per rank, then an exclusive prefix (wave 0: lanes own
+  // contiguous chunks of ranks).
+  for (int r = tid; r < S; r += nt) {
+    const int L = sm_len[sm_order[r]];
+    sm_cnt[r] = L <= 0 ? units : units * split_of(p, L).n_live;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int chunk = (S + 63) / 64;
+    const int r0 = min(S, tid * chunk), r1 = min(S, r0 + chunk);
+    int sum = 0;
+    for (int r = r0; r < r1; ++r) sum += sm_cnt[r];
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (tid >= o) incl += v;
+    }
+    int run = incl - sum;
+    for (int r = r0; r < r1; ++r) {
+      sm_pref[r] = run;
+      run += sm_cnt[r];
+    }
+    if (tid == 63) sm_pref[S] = incl;
+  }
+  __syncthreads();
+  const int total = sm_pref[S];
+  int* queue = p.ws_cnt + kQueueWord;
+  for (;;) {
+    if (tid == 0) sm_take[0] = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int item = sm_take[0];
+    __syncthreads();
+    if (item >= total) {
+      if (tid == 0 && item == total + int(gridDim.x) - 1)
+        __hip_atomic_store(queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    // Rank holding the item: the last r with sm_pref[r] <= item.
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sm_pref[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const int s = sm_order[lo];
+    const int local = item - sm_pref[lo];
+    const int L = clamped_len(p, s);
+    const int per_unit = L <= 0 ? 1 : split_of(p, L).n_live;
+    const int unit = local / per_unit, seg = local % per_unit;
+    body(s, unit % p.num_kv_heads, unit / p.num_kv_heads, seg);
+    __syncthreads();  // LDS is reused by the next item
+  }
+}
+
+// One work item: segment `seg` of (sequence s, kv head kvh, row group rg).
 template <typename T, int D, int RT>
-__global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(Params p) {
+__device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds, int s, int kvh, int rg, int seg) {
   using MF = Mfma<T>;
   using SH = Shape<D, RT>;
   constexpr int NW = SH::NW, KC = SH::KC, DT = SH::DT;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[SH::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 4, c = lane & 15;
-  const int s = blockIdx.y;
-  const int units = p.num_kv_heads * p.row_groups;
-  const int unit = blockIdx.x % units;
-  const int seg = blockIdx.x / units;
-  const int kvh = unit % p.num_kv_heads;
-  const int rg = unit / p.num_kv_heads;
   const int row0 = rg * RT * 16;
   const int wg_rows = min(RT * 16, p.rows - row0);
   const int M = p.query_len;
 
-  // Lengths past the block table's capacity are clamped to it.
-  const int L = min(p.seq_lens[s], p.max_blocks * p.page_size);
+  const int L = clamped_len(p, s);
   if (L <= 0) {
     if (seg == 0) zero_rows<T, D>(p, s, kvh, row0, wg_rows, SH::kThreads);
     return;
   }
   const int k_lo = p.window > 0 ? max(0, L - M - p.window + 1) : 0;
-  const int t_lo = k_lo >> 4, t_hi = (L + 15) >> 4;
-  const int n_tiles = t_hi - t_lo;
-  const int seg_tiles = max(p.seg_tiles, (n_tiles + p.nseg - 1) / p.nseg);
-  const int n_live = (n_tiles + seg_tiles - 1) / seg_tiles;
+  const SegSplit sp = split_of(p, L);
+  const int t_hi = sp.t_hi, seg_tiles = sp.seg_tiles, n_live = sp.n_live;
   if (seg >= n_live) return;
-  const int ts = t_lo + seg * seg_tiles, te = min(ts + seg_tiles, t_hi);
+  const int ts = sp.t_lo + seg * seg_tiles, te = min(ts + seg_tiles, t_hi);
   // Tiles needing no mask: every key visible to every row.
   const int lo_last = p.window > 0 ? max(0, L - p.window) : 0;
   const int qpos_first = L - M;
@@ -689,6 +801,39 @@ tiles_done:
   }
   __syncthreads();
   finish<T, D, RT, NW>(p, lds, s, kvh, rg, seg, row0, wg_rows, n_live, SH::kBytes);
+}
+
+// PERSIST selects the grid: one workgroup per item, or the persistent
+// grid (separate instantiations, so each inlines the item body once).
+template <typename T, int D, int RT, bool PERSIST>
+__global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(Params p) {
+  using SH = Shape<D, RT>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[SH::kBytes];
+  if constexpr (!PERSIST) {
+    // One workgroup per item.  Workgroups are dealt to the 8 XCDs
+    // round-robin by index; when a kv head's rows take several row groups,
+    // the row groups of one (kv head, segment) are given consecutive
+    // indices on one XCD, so they run together and all but the first find
+    // the K/V tiles in that XCD's L2.
+    int kvh, rg, seg;
+    if (p.row_groups > 1 && gridDim.x % (kXcds * p.row_groups) == 0) {
+      const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
+      rg = local % p.row_groups;
+      const int pair = (local / p.row_groups) * kXcds + xcd;
+      kvh = pair % p.num_kv_heads;
+      seg = pair / p.num_kv_heads;
+    } else {
+      const int units = p.num_kv_heads * p.row_groups;
+      const int unit = blockIdx.x % units;
+      seg = blockIdx.x / units;
+      kvh = unit % p.num_kv_heads;
+      rg = unit / p.num_kv_heads;
+    }
+    decode_unit<T, D, RT>(p, lds, blockIdx.y, kvh, rg, seg);
+  } else {
+    persistent_loop(p, lds, SH::kPersistOff, SH::kBytes, SH::kThreads,
+                    [&](int s, int kvh, int rg, int seg) { decode_unit<T, D, RT>(p, lds, s, kvh, rg, seg); });
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -954,8 +1099,12 @@ __global__ void zero_kernel(uint32_t* p, size_t n) {
 
 template <typename T, int D, int RT>
 int launch_t(const Plan& pl, const Params& pr, hipStream_t st) {
-  hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT>), dim3(pl.grid_x, pl.grid_y), dim3(Shape<D, RT>::kThreads), 0,
-                     st, pr);
+  if (pl.persistent)
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT, true>), dim3(pl.grid_x, pl.grid_y), dim3(Shape<D, RT>::kThreads),
+                       0, st, pr);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT, false>), dim3(pl.grid_x, pl.grid_y), dim3(Shape<D, RT>::kThreads),
+                       0, st, pr);
   return int(hipGetLastError());
 }
 

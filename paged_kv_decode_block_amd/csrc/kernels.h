@@ -28,6 +28,7 @@ struct Params {
   int32_t row_groups;         // workgroups splitting the rows
   int32_t merge_slices;       // slices of the merged output (merging workgroups)
   uint32_t merge_wait_ticks;  // helpers' wait bound (100 MHz real-time ticks)
+  int32_t persistent;         // 1: workgroups take items from the queue word
   float scale_log2;           // scale * log2(e): logits are kept in the exp2 domain
 };
 

@@ -31,6 +31,7 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   if (sh.dtype != PAD_F16 && sh.dtype != PAD_BF16) return PAD_EINVAL;
   if (sh.layout != PAD_NHD && sh.layout != PAD_HND) return PAD_EINVAL;
   if (sh.path < PAD_PATH_AUTO || sh.path > PAD_PATH_DOT) return PAD_EINVAL;
+  if (sh.schedule < PAD_SCHED_AUTO || sh.schedule > PAD_SCHED_PERSISTENT) return PAD_EINVAL;
   const int64_t table_keys = int64_t(sh.max_blocks_per_seq) * sh.page_size;
   if (sh.max_seq_len > table_keys) return PAD_EINVAL;
   // Key and tile indices are 32-bit on the device.
@@ -79,18 +80,37 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   const int64_t units = int64_t(sh.num_seqs) * sh.num_kv_heads * p.row_groups;
   // One workgroup per CU: its 4 waves keep enough loads in flight.
   const int64_t slots = num_cus;
+  const int64_t tile_bytes = int64_t(kTileKeys) * 2 * sh.head_size * 2;
+  // A batch whose lengths may differ runs on a persistent grid when one
+  // workgroup per planned segment would oversubscribe the device: the
+  // lengths are only known on the device, and a static grid there leaves
+  // CUs idle behind dead or short workgroups.  Its segments hold about
+  // 1 MiB of K/V each: every item pays a fixed combine, publish and
+  // pipeline-fill cost, which smaller items repeat more often (measured on
+  // 64 bf16 sequences of 512..16384 keys, 16/2 heads of 256: 8 to 16
+  // segments per 16k sequence 276-282 us, 33 segments 332 us).
+  const int64_t seg_persist = std::max<int64_t>(4, (int64_t(1) << 20) / tile_bytes);
+  if (sh.schedule == PAD_SCHED_PERSISTENT && sh.num_seqs > kPersistMaxSeqs) return PAD_EUNSUPPORTED;
+  p.persistent = sh.schedule == PAD_SCHED_PERSISTENT ||
+                 (sh.schedule == PAD_SCHED_AUTO && sh.num_seqs > 1 && sh.num_seqs <= kPersistMaxSeqs &&
+                  units * std::max<int64_t>(1, sh.num_segments > 0 ? sh.num_segments : ceil_div(span_tiles, seg_persist)) >
+                      slots);
   int64_t nseg;
   if (sh.num_segments > 0) {
     nseg = sh.num_segments;
+  } else if (p.persistent) {
+    nseg = ceil_div(span_tiles, seg_persist);
   } else {
     // One full round of workgroups for a single sequence; two rounds when a
     // batch's lengths may differ, so short sequences leave no idle CUs.
     const int64_t target = sh.num_seqs > 1 ? 2 * slots : slots;
     const int64_t fill = std::max<int64_t>(1, target / std::max<int64_t>(1, units));
-    // About 16 tiles (256 keys) per segment: with fewer the merge costs more
-    // than the extra parallelism saves -- but keep at least 4 segments while
-    // the device has room, so short contexts still spread their latency.
-    const int64_t work = std::max<int64_t>(1, span_tiles / 16);
+    // About 128 KiB of K/V per segment (16 tiles at head size 128, 4 at
+    // 512): with less the merge costs more than the extra parallelism
+    // saves -- but keep at least 4 segments while the device has room, so
+    // short contexts still spread their latency.
+    const int64_t seg_target = std::max<int64_t>(4, (int64_t(128) << 10) / tile_bytes);
+    const int64_t work = std::max<int64_t>(1, span_tiles / seg_target);
     nseg = std::min<int64_t>(fill, std::max<int64_t>(work, std::min<int64_t>(4, fill)));
   }
   nseg = std::min<int64_t>(nseg, span_tiles);
@@ -111,10 +131,15 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
     p.seg_tiles = int(ceil_div(span_tiles, p.nseg));
   }
 
-  p.grid_x = p.nseg * sh.num_kv_heads * p.row_groups;
-  p.grid_y = std::max(1, sh.num_seqs);
+  if (p.persistent) {
+    p.grid_x = num_cus;
+    p.grid_y = 1;
+  } else {
+    p.grid_x = p.nseg * sh.num_kv_heads * p.row_groups;
+    p.grid_y = std::max(1, sh.num_seqs);
+  }
 
-  if (p.nseg > 1) {
+  if (p.nseg > 1 || p.persistent) {
     const size_t S = size_t(sh.num_seqs), H = size_t(sh.num_kv_heads);
     const size_t slot_rows = S * H * size_t(p.nseg) * size_t(rows);
     // Slices: about kSliceBytes of partial accumulators each, limited by
@@ -122,17 +147,25 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
     // control words the counter prefix holds.
     const size_t wg_rows = size_t(std::min(rows, p.row_tiles * 16));
     const size_t vol = size_t(p.nseg) * wg_rows * size_t(sh.head_size) * sizeof(float);
-    int64_t k = int64_t((vol + kSliceBytes - 1) / kSliceBytes);
-    k = std::min<int64_t>(k, std::min(p.nseg, kMaxSlices));
+    // On the persistent grid the segments of a unit start as workgroups
+    // free up, so helpers would wait up to a segment's time: the last
+    // arriver merges alone there.
+    int64_t k = p.persistent ? 1 : int64_t((vol + kSliceBytes - 1) / kSliceBytes);
+    k = std::max<int64_t>(1, std::min<int64_t>(k, std::min(p.nseg, kMaxSlices)));
     const size_t ctl_units = S * H * size_t(p.row_groups);
-    k = std::min<int64_t>(
-        k, int64_t(kCounterBytes / (sizeof(int32_t) * kCtlWordStride * std::max<size_t>(1, ctl_units))));
-    if (k < 1) return PAD_EUNSUPPORTED;  // more units than the counter prefix holds
-    p.merge_slices = int(k);
+    k = std::min<int64_t>(k, int64_t((kCounterBytes - 128) /
+                                     (sizeof(int32_t) * kCtlWordStride * std::max<size_t>(1, ctl_units))));
+    if (p.nseg > 1 && k < 1) return PAD_EUNSUPPORTED;  // more units than the control prefix holds
+    p.merge_slices = int(std::max<int64_t>(1, k));
     p.ws_counters = 0;
     p.ws_ml = kCounterBytes;
-    p.ws_acc = p.ws_ml + align_up(slot_rows * 2 * sizeof(float));
-    p.ws_bytes = p.ws_acc + align_up(slot_rows * size_t(sh.head_size) * sizeof(float));
+    if (p.nseg > 1) {
+      p.ws_acc = p.ws_ml + align_up(slot_rows * 2 * sizeof(float));
+      p.ws_bytes = p.ws_acc + align_up(slot_rows * size_t(sh.head_size) * sizeof(float));
+    } else {  // the work queue only: a single segment publishes no partial
+      p.ws_acc = p.ws_ml;
+      p.ws_bytes = kCounterBytes;
+    }
   } else {
     p.merge_slices = 1;
     p.ws_counters = p.ws_ml = p.ws_acc = p.ws_bytes = 0;

@@ -37,10 +37,16 @@ constexpr int kCtlWordStride = 32;
 constexpr int kDotMaxRows = 4;
 constexpr int kDotMaxHeadSize = 128;
 constexpr int kDotWaveCount = 4;
-// Arrival counters live in a fixed-size prefix of the workspace, so calls of
-// different shapes can share one workspace: partials never land where any
-// shape keeps counters, and every call leaves its counters zero.
+// Merge control words live in a fixed-size prefix of the workspace, so
+// calls of different shapes can share one workspace: partials never land
+// where any shape keeps control words, and every call leaves them zero.
+// The prefix's last 128-byte line holds the persistent grid's work queue.
 constexpr size_t kCounterBytes = size_t(1) << 20;
+constexpr int kQueueWord = int((kCounterBytes - 128) / 4);
+// Persistent grid (batched decode): at most this many sequences (its LDS
+// tables), sorted longest first up to kPersistSortSeqs of them.
+constexpr int kPersistMaxSeqs = 1024;
+constexpr int kPersistSortSeqs = 512;
 
 // Waves per workgroup.  Four for every shape: on one bf16 sequence with
 // 32 query / 8 kv heads of size 128 and 16-key pages, 4 waves with one
@@ -58,6 +64,7 @@ struct Plan {
   int nseg;          // segments per (unit, row group)
   int seg_tiles;     // planned tiles per segment
   int merge_slices;  // slices the merged output is cut into (1..kMaxSlices)
+  int persistent;    // 1: one workgroup per CU takes items from a queue
   int grid_x, grid_y;
   // Workspace layout (byte offsets; all 256-byte aligned): the counter
   // prefix (kCounterBytes; per (unit, row group) merge_slices words, one

@@ -25,7 +25,7 @@ def say(msg: str) -> None:
 
 
 def run_gpu(case: wl.Case, instance: int = 0, *, num_segments=0, path=0, max_seq_len=0, workspace=None,
-            out=None, window=None, scale=None):
+            out=None, window=None, scale=None, schedule=0):
     """One pad_decode_attn call on the case's device tensors."""
     if out is None:
         out = torch.full_like(case.q, float("nan"))
@@ -33,6 +33,7 @@ def run_gpu(case: wl.Case, instance: int = 0, *, num_segments=0, path=0, max_seq
         case.q, case.kv_cache, case.block_tables[instance], case.seq_lens,
         case.scale if scale is None else scale, case.window if window is None else window, out,
         layout=case.layout, workspace=workspace, num_segments=num_segments, path=path, max_seq_len=max_seq_len,
+        schedule=schedule,
     )
     return out
 

@@ -41,7 +41,7 @@ def test_status_strings():
 def shape(**kw):
     base = dict(num_seqs=1, query_len=4, num_q_heads=32, num_kv_heads=8, head_size=128, page_size=16,
                 max_blocks_per_seq=2048, max_seq_len=0, dtype=pad.PAD_BF16, layout=pad.PAD_HND,
-                num_segments=0, path=0)
+                num_segments=0, path=0, schedule=0)
     base.update(kw)
     return pad.pad_shape(**base)
 
@@ -82,12 +82,17 @@ def test_plan_invariants(kw):
     # segments stay within 4096 tiles (the LDS block-id stage) for any
     # device length up to the table's capacity
     assert p["segment_tiles"] <= 4096 and -(-tiles // p["num_segments"]) <= 4096
-    assert p["grid_x"] == p["num_segments"] * sh.num_kv_heads * p["row_groups"]
-    assert p["grid_y"] == sh.num_seqs
-    if p["num_segments"] == 1:
+    if p["persistent"]:
+        # one workgroup per CU; items come from the queue
+        assert (p["grid_x"], p["grid_y"]) == (256, 1)
+        assert p["workspace_bytes"] >= 1 << 20
+    else:
+        assert p["grid_x"] == p["num_segments"] * sh.num_kv_heads * p["row_groups"]
+        assert p["grid_y"] == sh.num_seqs
+    if p["num_segments"] == 1 and not p["persistent"]:
         assert p["workspace_bytes"] == 0
         assert p["merge_slices"] == 1
-    else:
+    elif p["num_segments"] > 1:
         # a fixed 1 MiB prefix of merge control words, then one (m, l) and one
         # acc slot per segment
         S, H, n = sh.num_seqs, sh.num_kv_heads, p["num_segments"]
@@ -99,9 +104,10 @@ def test_plan_invariants(kw):
         wg_rows = min(rows, p["row_tiles"] * 16)
         vol = n * wg_rows * sh.head_size * 4
         assert 1 <= k <= min(32, n)
-        # control words one 128-byte line apart
-        assert k == min(-(-vol // (32 << 10)), 32, n, (1 << 20) // (128 * S * H * p["row_groups"]))
-        assert S * H * p["row_groups"] * k * 128 <= (1 << 20)
+        # control words one 128-byte line apart, clear of the queue line
+        want_k = 1 if p["persistent"] else min(-(-vol // (32 << 10)), 32, n, ((1 << 20) - 128) // (128 * S * H * p["row_groups"]))
+        assert k == want_k
+        assert S * H * p["row_groups"] * k * 128 <= (1 << 20) - 128
 
 
 def test_plan_bounds_segment_length():
@@ -118,6 +124,24 @@ def test_plan_bounds_segment_length():
     with pytest.raises(pad.PadError) as e:
         plan(shape(max_blocks_per_seq=(256 * 4096) + 1))
     assert e.value.status == pad.PAD_EUNSUPPORTED
+
+
+def test_schedule_plan():
+    batch = dict(num_seqs=65, num_q_heads=16, num_kv_heads=2, head_size=256, page_size=1056, max_blocks_per_seq=16)
+    p = plan(shape(**batch))
+    assert p["persistent"] == 1 and p["grid_x"] == 256
+    g = plan(shape(schedule=pad.PAD_SCHED_GRID, **batch))
+    assert g["persistent"] == 0 and g["grid_y"] == 65
+    # with the segment count fixed, both schedules split the same way
+    a = plan(shape(num_segments=8, schedule=pad.PAD_SCHED_GRID, **batch))
+    b = plan(shape(num_segments=8, schedule=pad.PAD_SCHED_PERSISTENT, **batch))
+    assert (a["num_segments"], a["segment_tiles"]) == (b["num_segments"], b["segment_tiles"])
+    # the persistent grid's last arriver merges alone
+    assert b["merge_slices"] == 1
+    # batch 1 stays on one workgroup per item unless asked
+    assert plan(shape())["persistent"] == 0
+    one = plan(shape(schedule=pad.PAD_SCHED_PERSISTENT, num_segments=1, max_blocks_per_seq=4))
+    assert one["persistent"] == 1 and one["num_segments"] == 1 and one["workspace_bytes"] == 1 << 20
 
 
 def test_plan_fills_device():
@@ -167,6 +191,9 @@ def test_window_plan_is_smaller():
         (dict(max_seq_len=2048 * 16 + 1), pad.PAD_EINVAL),
         (dict(num_segments=-1), pad.PAD_EINVAL),
         (dict(path=3), pad.PAD_EINVAL),
+        (dict(schedule=3), pad.PAD_EINVAL),
+        (dict(schedule=-1), pad.PAD_EINVAL),
+        (dict(schedule=pad.PAD_SCHED_PERSISTENT, num_seqs=1025), pad.PAD_EUNSUPPORTED),
         (dict(path=pad.PAD_PATH_DOT), pad.PAD_EUNSUPPORTED),  # 16 rows: too many for the dot family
         (dict(path=pad.PAD_PATH_DOT, query_len=1, head_size=256), pad.PAD_EUNSUPPORTED),
         (dict(num_seqs=-1), pad.PAD_EINVAL),

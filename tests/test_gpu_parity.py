@@ -209,6 +209,41 @@ def test_merge_handover(cfg, lens, M, nseg):
     assert int(ws[: 1 << 20].view(torch.int32).abs().sum()) == 0
 
 
+# (config, lengths, M, window, segments): batches with ragged, empty and
+# windowed sequences.
+SCHEDULE_CASES = [
+    (5, None, 4, 0, 8),
+    (2, [3000, 17, 0, 900, 1], 4, 0, 16),
+    (3, [2000, 700, 40], 4, 512, 4),
+]
+
+
+@pytest.mark.parametrize("cfg,lens,M,window,nseg", SCHEDULE_CASES, ids=[f"sch{i}" for i in range(len(SCHEDULE_CASES))])
+def test_schedules_give_same_bits(cfg, lens, M, window, nseg):
+    """One workgroup per item and the persistent grid compute every item
+    alike: the same output bits, and the workspace's control prefix (merge
+    words and the work queue) is left zero."""
+    if lens is None:
+        c = wl.config_case(cfg, 3000, M, device=DEV)
+    else:
+        c = _case(wl.CONFIGS[cfg], lens, M, 500 + cfg, window=window)
+    ref = oracle_out(c)
+    outs = []
+    for sched in (pad.PAD_SCHED_GRID, pad.PAD_SCHED_PERSISTENT):
+        shape = pad.make_shape(c.q, c.kv_cache, c.block_tables[0], c.layout, num_segments=nseg, schedule=sched)
+        plan = pad.pad_decode_attn_plan(shape, c.window)
+        assert plan["persistent"] == (sched == pad.PAD_SCHED_PERSISTENT)
+        ws = torch.empty(pad.pad_decode_attn_workspace_size(shape), dtype=torch.uint8, device=DEV)
+        pad.pad_decode_attn_workspace_init(ws)
+        for _ in range(2):  # the queue must be reusable
+            out = run_gpu(c, workspace=ws, num_segments=nseg, schedule=sched)
+        torch.cuda.synchronize()
+        check(out, ref, c.q.dtype, f"schedule {sched}")
+        assert int(ws[: 1 << 20].view(torch.int32).abs().sum()) == 0
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1])
+
+
 def test_graph_replay():
     c = _case(wl.CONFIGS[4], [2500], 4, 6, instances=2)
     ref = [oracle_out(c, i) for i in range(2)]
