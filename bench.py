@@ -30,8 +30,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 POOL_BYTES = 512 << 20
 COPY_BYTES = 256 << 20  # --copy-calibration: bytes read (and written) per copy
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_config2.json")
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_decode_block_amd", "csrc", "decode_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_mfma_bf16_D128_Hq32_Hkv8_L32768_M4.json")
+CSRC = os.path.join(ROOT, "paged_kv_decode_block_amd", "csrc")
 
 
 def effective_bytes(case) -> int:
@@ -56,8 +56,13 @@ def effective_bytes(case) -> int:
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of every kernel and planner source: a change to any of them
+    makes the committed traffic counters stale."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def time_calls(case, n_warm: int, n_timed: int, graph: bool = False, **kw):
