@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpad_attn.so")
-SOURCES = ["decode_mfma.hip", "plan.cpp", "api.cpp"]
+SOURCES = ["decode_mfma.hip", "decode_rows.hip", "plan.cpp", "api.cpp"]
 
 # Packed fp32 VALU ops are turned off for every HIP source (the host pass
 # reports the feature as unknown; that warning is harmless).
@@ -36,24 +36,39 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libpad_attn.so)")
 
 
-def build(verbose: bool = False) -> str:
-    cc = hipcc()
-    tmp = LIB + ".tmp"
-    cmd = [cc, *HIP_FLAGS, "-shared", "-o", tmp]
-    for src in SOURCES:
-        path = os.path.join(CSRC, src)
-        # .cpp files hold host code only; compile them as HIP too so one
-        # hipcc line links everything against the HIP runtime.
-        cmd += (["-x", "hip"] if src.endswith(".cpp") else []) + [path]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     errs = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
+        raise RuntimeError(f"hipcc failed ({res.returncode}) on {cmd[-1]}:\n{errs}")
     if errs.strip() and verbose:
         print(errs, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link the
+    shared library; the result replaces LIB atomically."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    cc = hipcc()
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs, jobs = [], []
+    for src in SOURCES:
+        path = os.path.join(CSRC, src)
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        # .cpp files hold host code only; compile them as HIP too so the
+        # link step sees one toolchain.
+        jobs.append([cc, *HIP_FLAGS, "-c", "-o", obj] + (["-x", "hip"] if src.endswith(".cpp") else []) + [path])
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(lambda c: _run(c, verbose), jobs))
+    tmp = LIB + ".tmp"
+    _run([cc, *HIP_FLAGS, "-shared", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 

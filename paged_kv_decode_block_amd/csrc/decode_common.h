@@ -1,0 +1,472 @@
+// Device code shared by the decode-attention kernels (gfx950): MFMA
+// traits, stores, the split-KV merge and its hand-over protocol, segment
+// splits and the persistent grid's work loop.  Included by the kernel
+// sources only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+
+namespace pad {
+namespace dev {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<__bf16> {
+  typedef __bf16 x8 __attribute__((ext_vector_type(8)));
+  typedef short x4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f32x4 qk(i32x4 a, i32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(x8, a), __builtin_bit_cast(x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(uint64_t a, uint64_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(x4, a), __builtin_bit_cast(x4, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint16_t bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x)); }
+};
+
+template <>
+struct Mfma<_Float16> {
+  typedef _Float16 x8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 x4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f32x4 qk(i32x4 a, i32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(x8, a), __builtin_bit_cast(x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(uint64_t a, uint64_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(x4, a), __builtin_bit_cast(x4, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint16_t bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); }
+};
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint64_t pack4(uint16_t a, uint16_t b, uint16_t c, uint16_t d) {
+  return uint64_t(a) | (uint64_t(b) << 16) | (uint64_t(c) << 32) | (uint64_t(d) << 48);
+}
+
+// Device-coherent store of 16 bytes (two 8-byte write-through stores).
+__device__ __forceinline__ void store_coherent(float* dst, f32x4 v) {
+  uint64_t* d = reinterpret_cast<uint64_t*>(dst);
+  __hip_atomic_store(d, __builtin_bit_cast(uint64_t, __builtin_shufflevector(v, v, 0, 1)), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(d + 1, __builtin_bit_cast(uint64_t, __builtin_shufflevector(v, v, 2, 3)), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_coherent2(float* dst, float a, float b) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(dst),
+                     uint64_t(__builtin_bit_cast(uint32_t, a)) | (uint64_t(__builtin_bit_cast(uint32_t, b)) << 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T>
+__device__ __forceinline__ T* out_row(const Params& p, T* out_s, int kvh, int ru, int D) {
+  const int m = ru / p.group, gq = ru % p.group;
+  return out_s + (int64_t(m) * p.num_q_heads + kvh * p.group + gq) * D;
+}
+
+// ---- split-KV merge ----
+// The merged output of a unit is rows x D floats, cut into items (row r,
+// four head-dim columns d4): item = r * (D / 4) + d4.  Merge slice `slice`
+// of `nslices` covers items [slice * I / nslices, (slice + 1) * I / nslices).
+// LN lanes serve one item; lane `sub` takes slots sub, sub + LN, ... in
+// chunks of LN * U slots (U per lane), keeping a running (m, l, acc) in the
+// exp2 domain:  m* = max m_j,  l* = sum l_j 2^(m_j - m*),
+// acc* = sum acc_j 2^(m_j - m*)  (the log-sum-exp merge of split
+// partials); the LN lanes then combine in a fixed butterfly.  Each item's
+// sums follow one fixed order for a given (slot count, LN, U), whichever
+// workgroup merges it.  Every load is unconditional (item and slot indices
+// clamped, extra slots weighted zero) so the wait counts stay exact, and
+// the (pass, chunk) work of a thread is one stream with the next unit's
+// loads in flight while the current one is consumed.
+template <int U>
+struct MergeChunk {
+  f32x4 acc[U];
+  float2 ml[U];
+};
+
+// The unit's partial slots start at a wave-uniform 64-bit base; a slot
+// and an item are 32-bit byte offsets from it (a unit's partials span at
+// most 256 segments x 1024 rows x 512 columns x 4 bytes = 512 MiB).
+template <int D, int NT, int LN, int U>
+__device__ __forceinline__ void merge_load(const Params& p, MergeChunk<U>& b, const unsigned char* acc_base,
+                                           const unsigned char* ml_base, int row0, int i0, int i1, int n, int nch,
+                                           int w) {
+  constexpr int IPP = NT / LN, CH = LN * U;
+  const int pass = w / nch, ch = w - pass * nch;
+  const int it = min(i0 + pass * IPP + int(threadIdx.x) / LN, i1 - 1);
+  const int r = it / (D / 4), d4 = it % (D / 4);
+  const uint32_t acc_item = uint32_t((row0 + r) * D + 4 * d4) * 4u;
+  const uint32_t ml_item = uint32_t(row0 + r) * 8u;
+  const uint32_t acc_slot = uint32_t(p.rows) * uint32_t(D) * 4u, ml_slot = uint32_t(p.rows) * 8u;
+  const int first = ch * CH + int(threadIdx.x) % LN;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t j = uint32_t(min(first + LN * u, n - 1));
+    b.acc[u] = *reinterpret_cast<const f32x4*>(acc_base + (j * acc_slot + acc_item));
+    b.ml[u] = *reinterpret_cast<const float2*>(ml_base + (j * ml_slot + ml_item));
+  }
+}
+
+template <typename T, int D, int NT, int LN, int U>
+__device__ __forceinline__ void merge_consume(const Params& p, const MergeChunk<U>& b, int i0, int i1, int n, int nch,
+                                              int w, int row0, T* out_s, int kvh, float& m_run, float& l_run,
+                                              f32x4& a_run) {
+  using MF = Mfma<T>;
+  constexpr int IPP = NT / LN, CH = LN * U;
+  const int pass = w / nch, ch = w - pass * nch;
+  const int sub = int(threadIdx.x) % LN;
+  if (ch == 0) {
+    m_run = kNegInf;
+    l_run = 0.f;
+    a_run = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int first = ch * CH + sub;
+  float mj[U];
+  float mloc = kNegInf;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    mj[u] = first + LN * u < n ? b.ml[u].x : kNegInf;
+    mloc = fmaxf(mloc, mj[u]);
+  }
+  const float m_new = fmaxf(m_run, mloc);
+  const float m_use = m_new == kNegInf ? 0.f : m_new;
+  const float sc = fast_exp2(m_run - m_use);
+  l_run *= sc;
+  a_run *= sc;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float wgt = fast_exp2(mj[u] - m_use);
+    l_run += wgt * b.ml[u].y;
+    a_run += wgt * b.acc[u];
+  }
+  m_run = m_new;
+  if (ch != nch - 1) return;
+  // Last chunk of the pass: combine the item's lanes and write it.
+  float m_all = m_run;
+#pragma unroll
+  for (int o = 1; o < LN; o <<= 1) m_all = fmaxf(m_all, __shfl_xor(m_all, o));
+  const float f = fast_exp2(m_run - (m_all == kNegInf ? 0.f : m_all));
+  float l = l_run * f;
+  f32x4 a = a_run * f;
+#pragma unroll
+  for (int o = 1; o < LN; o <<= 1) {
+    l += __shfl_xor(l, o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] += __shfl_xor(a[e], o);
+  }
+  const int it = i0 + pass * IPP + int(threadIdx.x) / LN;
+  if (sub == 0 && it < i1) {
+    const int r = it / (D / 4), d4 = it % (D / 4);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint2 o;
+    o.x = uint32_t(MF::bits(a[0] * inv)) | (uint32_t(MF::bits(a[1] * inv)) << 16);
+    o.y = uint32_t(MF::bits(a[2] * inv)) | (uint32_t(MF::bits(a[3] * inv)) << 16);
+    *reinterpret_cast<uint2*>(out_row(p, out_s, kvh, row0 + r, D) + 4 * d4) = o;
+  }
+}
+
+template <typename T, int D, int NT, int LN, int U>
+__device__ __forceinline__ void merge_items(const Params& p, int64_t slot0, int n, int row0, int i0, int i1, T* out_s,
+                                         int kvh) {
+  constexpr int IPP = NT / LN, CH = LN * U;
+  const int nch = (n + CH - 1) / CH;
+  const int W = (i1 - i0 + IPP - 1) / IPP * nch;
+  const unsigned char* acc_base = reinterpret_cast<const unsigned char*>(p.ws_acc + slot0 * p.rows * D);
+  const unsigned char* ml_base = reinterpret_cast<const unsigned char*>(p.ws_ml + slot0 * p.rows * 2);
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4 a_run = {0.f, 0.f, 0.f, 0.f};
+  MergeChunk<U> b0, b1;
+  merge_load<D, NT, LN, U>(p, b0, acc_base, ml_base, row0, i0, i1, n, nch, 0);
+  if (W == 1) {
+    merge_consume<T, D, NT, LN, U>(p, b0, i0, i1, n, nch, 0, row0, out_s, kvh, m_run, l_run, a_run);
+    return;
+  }
+  for (int w = 0; w < W; w += 2) {
+    merge_load<D, NT, LN, U>(p, b1, acc_base, ml_base, row0, i0, i1, n, nch, min(w + 1, W - 1));
+    merge_consume<T, D, NT, LN, U>(p, b0, i0, i1, n, nch, w, row0, out_s, kvh, m_run, l_run, a_run);
+    merge_load<D, NT, LN, U>(p, b0, acc_base, ml_base, row0, i0, i1, n, nch, min(w + 2, W - 1));
+    if (w + 1 < W)
+      merge_consume<T, D, NT, LN, U>(p, b1, i0, i1, n, nch, w + 1, row0, out_s, kvh, m_run, l_run, a_run);
+  }
+}
+
+// Merge slice `slice` of `nslices` of the n partials of a unit (slots
+// slot0 .. slot0 + n - 1, rows row0 .. row0 + wg_rows - 1 of each) into
+// the output.  Lanes per item and slots per lane follow the slot count
+// only, so an item's sums take the same order whatever the slicing and
+// whichever workgroup merges it: the output bits depend on the sequence
+// and the segment split alone.  The caller has acquired the partials.
+template <typename T, int D, int NT>
+__device__ __forceinline__ void merge_slice(const Params& p, int64_t slot0, int n, int row0, int wg_rows, int slice,
+                                            int nslices, T* out_s, int kvh) {
+  const int items = wg_rows * (D / 4);
+  const int i0 = slice * items / nslices, i1 = (slice + 1) * items / nslices;
+  if (i1 <= i0) return;
+  const int ln = n >= 24 ? 4 : (n >= 8 ? 2 : 1);
+  const int per = (n + ln - 1) / ln;
+  const int u = per <= 2 ? 2 : (per <= 4 ? 4 : 8);
+  switch (ln * 16 + u) {
+    case 4 * 16 + 2: merge_items<T, D, NT, 4, 2>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 4 * 16 + 4: merge_items<T, D, NT, 4, 4>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 4 * 16 + 8: merge_items<T, D, NT, 4, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 2 * 16 + 2: merge_items<T, D, NT, 2, 2>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 2 * 16 + 4: merge_items<T, D, NT, 2, 4>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 2 * 16 + 8: merge_items<T, D, NT, 2, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 1 * 16 + 2: merge_items<T, D, NT, 1, 2>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 1 * 16 + 4: merge_items<T, D, NT, 1, 4>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    default: merge_items<T, D, NT, 1, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+  }
+}
+
+// Hand-over word of a merge slice (one per slice after the first).  The
+// helper merging slice s (the s-th workgroup to arrive before the last)
+// and the last arriver each act on it once or twice:
+//   helper:  idle -> waiting, then waits (bounded) until the unit's arrival
+//            count is complete or the word says go; then waiting -> done
+//            (if the word already says go, the helper resets it to idle);
+//            on timeout waiting -> gave_up, leaving the slice to the last
+//            arriver (if go got there first, it merges after all).
+//   last:    -> go; finding done or gave_up, it resets the word to idle (and
+//            for gave_up merges the slice itself).
+// Whoever acts second leaves the word idle, so every launch starts clean.
+constexpr int kSliceIdle = 0, kSliceWaiting = 1, kSliceGo = 2, kSliceGaveUp = 3, kSliceDone = 4;
+// Control words of a unit sit one cache line (128 bytes) apart: the
+// helpers poll their own words while the last arriver updates them.
+constexpr int kCtlStride = kCtlWordStride;
+
+// A helper's side of the exchange (one thread): whether it merges its
+// slice.  Every path ends: the wait is bounded by wait_ticks of the
+// 100 MHz real-time counter.
+__device__ __forceinline__ bool helper_wait(int* word, const int* counter, int n, uint32_t wait_ticks) {
+  int seen = kSliceIdle;
+  if (!__hip_atomic_compare_exchange_strong(word, &seen, kSliceWaiting, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT)) {
+    // The last arriver came first (go): this is the word's last use.
+    __hip_atomic_store(word, kSliceIdle, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+  }
+  const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + wait_ticks;
+  while (__builtin_amdgcn_s_memrealtime() < t_end) {
+    if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n ||
+        __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kSliceGo) {
+      if (__hip_atomic_exchange(word, kSliceDone, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kSliceGo)
+        __hip_atomic_store(word, kSliceIdle, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return true;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  seen = kSliceWaiting;
+  if (__hip_atomic_compare_exchange_strong(word, &seen, kSliceGaveUp, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT))
+    return false;
+  __hip_atomic_store(word, kSliceIdle, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // go came first
+  return true;
+}
+
+// Count this workgroup's arrival for its unit (its partial rows are
+// published with device-coherent stores) and take part in the merge: of
+// the n arrivals of a unit, the last one and the k - 1 before it (k = merge
+// slices) merge one slice of the output each; the rest are done.  `flags`
+// are 16 bytes of LDS (words 0 and 1).
+template <typename T, int D, int NT>
+__device__ __forceinline__ void arrive_and_merge(const Params& p, int* flags, int s, int kvh, int rg, int row0,
+                                                 int wg_rows, int n_live) {
+  const int tid = threadIdx.x;
+  T* out_s = static_cast<T*>(p.out) + int64_t(s) * p.query_len * p.num_q_heads * D;
+  const int64_t slot0 = (int64_t(s) * p.num_kv_heads + kvh) * p.nseg;
+  int* ctl = p.ws_cnt + ((int64_t(s) * p.num_kv_heads + kvh) * p.row_groups + rg) * p.merge_slices * kCtlStride;
+  int* sm_flag = flags;
+  const int k = min(p.merge_slices, n_live);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    // Role: 0 = last arriver, 1 .. k-1 = helper merging that slice, -1 = done.
+    const int rank = __hip_atomic_fetch_add(ctl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int role = -1;
+    if (rank == n_live - 1) {
+      role = 0;
+    } else if (rank >= n_live - k) {
+      const int sl = n_live - 1 - rank;
+      if (helper_wait(ctl + sl * kCtlStride, ctl, n_live, p.merge_wait_ticks)) role = sl;
+    }
+    // Acquire: the other workgroups' partials are visible from here on.
+    if (role >= 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    sm_flag[0] = role;
+  }
+  __syncthreads();
+  const int role = sm_flag[0];
+  if (role < 0) return;
+  // Slices this workgroup merges: its own (slice 0 for the last arriver),
+  // and for the last arriver those whose helpers gave up -- known once its
+  // "go" exchanges (issued before its own slice) return.  One merge call
+  // site keeps the kernel's code and register use small.
+  int old = kSliceIdle;
+  if (role == 0 && tid >= 1 && tid < k)
+    old = __hip_atomic_exchange(ctl + tid * kCtlStride, kSliceGo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t todo = 1u << role;
+  bool settled = role > 0;
+  while (todo != 0) {
+    const int sl = __builtin_ctz(todo);
+    todo &= todo - 1;
+    merge_slice<T, D, NT>(p, slot0, n_live, row0, wg_rows, sl, k, out_s, kvh);
+    if (!settled) {
+      settled = true;
+      if (tid < 64) {
+        const bool mine = old == kSliceGaveUp;
+        if (mine || old == kSliceDone)
+          __hip_atomic_store(ctl + tid * kCtlStride, kSliceIdle, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t own = __ballot(mine);
+        if (tid == 0) {
+          sm_flag[1] = int(uint32_t(own));
+          // The arrival counter's last use in this launch: helpers that
+          // still poll it have the go word.
+          __hip_atomic_store(ctl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      __syncthreads();
+      todo |= uint32_t(sm_flag[1]);
+    }
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void zero_rows(const Params& p, int s, int kvh, int row0, int nrows, int nthreads) {
+  T* out_s = static_cast<T*>(p.out) + int64_t(s) * p.query_len * p.num_q_heads * D;
+  const int items = nrows * (D / 8);
+  for (int it = threadIdx.x; it < items; it += nthreads) {
+    const int r = it / (D / 8), d8 = it % (D / 8);
+    *reinterpret_cast<i32x4*>(out_row(p, out_s, kvh, row0 + r, D) + 8 * d8) = i32x4{0, 0, 0, 0};
+  }
+}
+
+// Segments of a sequence of (clamped) length L: its visible key range in
+// 16-key tiles [t_lo, t_hi), split into n_live segments of seg_tiles tiles
+// (at least the planned count, stretched when a device length exceeds the
+// planning bound).
+struct SegSplit {
+  int t_lo, t_hi, seg_tiles, n_live;
+};
+
+__device__ __forceinline__ int clamped_len(const Params& p, int s) {
+  // Lengths past the block table's capacity are clamped to it.
+  return min(p.seq_lens[s], p.max_blocks * p.page_size);
+}
+
+__device__ __forceinline__ SegSplit split_of(const Params& p, int L) {
+  SegSplit r;
+  const int k_lo = p.window > 0 ? max(0, L - p.query_len - p.window + 1) : 0;
+  r.t_lo = k_lo >> 4;
+  r.t_hi = (L + 15) >> 4;
+  const int n_tiles = r.t_hi - r.t_lo;
+  r.seg_tiles = max(p.seg_tiles, (n_tiles + p.nseg - 1) / p.nseg);
+  r.n_live = (n_tiles + r.seg_tiles - 1) / r.seg_tiles;
+  return r;
+}
+
+// Persistent grid (batched decode): one workgroup per CU takes work items
+// from a queue in the workspace until none are left.  Items are the live
+// segments of every (sequence, kv head, row group), longest sequences
+// first (ties by index; up to kPersistSortSeqs sequences, else in index
+// order) and, within a sequence, unit-major so the segments of a unit run
+// together and its merge helpers wait little.  An item's work does not
+// depend on which workgroup takes it, so results stay bitwise the same.
+// Sequences of length <= 0 get one item per unit (its zero output).
+// Every workgroup ends with one failed take; the last of those resets the
+// queue for the next launch.
+template <typename Body>
+__device__ __forceinline__ void persistent_loop(const Params& p, unsigned char* lds, int persist_off, int lds_bytes,
+                                               int nt, Body body) {
+  const int tid = threadIdx.x;
+  const int S = p.num_seqs;
+  const int units = p.num_kv_heads * p.row_groups;
+  int* sm_order = reinterpret_cast<int*>(lds + persist_off);  // [S]: sequence of rank r
+  int* sm_pref = sm_order + kPersistMaxSeqs;                   // [S + 1]: first item of rank r
+  // Scratch before the first item (the tile-loop area): lengths and item
+  // counts per rank.
+  int* sm_len = reinterpret_cast<int*>(lds);                   // [S]
+  int* sm_cnt = sm_len + kPersistMaxSeqs;                      // [S]
+  int* sm_take = reinterpret_cast<int*>(lds + lds_bytes - 16) + 2;
+  for (int i = tid; i < S; i += nt) sm_len[i] = clamped_len(p, i);
+  __syncthreads();
+  const bool sort = S <= kPersistSortSeqs;
+  for (int i = tid; i < S; i += nt) {
+    const int li = sm_len[i];
+    int rank = i;
+    if (sort) {
+      rank = 0;
+      for (int j = 0; j < S; ++j) {
+        const int lj = sm_len[j];
+        rank += (lj > li) || (lj == li && j < i);
+      }
+    }
+    sm_order[rank] = i;
+  }
+  __syncthreads();
+  // Items per rank, then an exclusive prefix (wave 0: lanes own
+  // contiguous chunks of ranks).
+  for (int r = tid; r < S; r += nt) {
+    const int L = sm_len[sm_order[r]];
+    sm_cnt[r] = L <= 0 ? units : units * split_of(p, L).n_live;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int chunk = (S + 63) / 64;
+    const int r0 = min(S, tid * chunk), r1 = min(S, r0 + chunk);
+    int sum = 0;
+    for (int r = r0; r < r1; ++r) sum += sm_cnt[r];
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (tid >= o) incl += v;
+    }
+    int run = incl - sum;
+    for (int r = r0; r < r1; ++r) {
+      sm_pref[r] = run;
+      run += sm_cnt[r];
+    }
+    if (tid == 63) sm_pref[S] = incl;
+  }
+  __syncthreads();
+  const int total = sm_pref[S];
+  int* queue = p.ws_cnt + kQueueWord;
+  for (;;) {
+    if (tid == 0) sm_take[0] = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int item = sm_take[0];
+    __syncthreads();
+    if (item >= total) {
+      if (tid == 0 && item == total + int(gridDim.x) - 1)
+        __hip_atomic_store(queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    // Rank holding the item: the last r with sm_pref[r] <= item.
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sm_pref[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const int s = sm_order[lo];
+    const int local = item - sm_pref[lo];
+    const int L = clamped_len(p, s);
+    const int per_unit = L <= 0 ? 1 : split_of(p, L).n_live;
+    const int unit = local / per_unit, seg = local % per_unit;
+    body(s, unit % p.num_kv_heads, unit / p.num_kv_heads, seg);
+    __syncthreads();  // LDS is reused by the next item
+  }
+}
+
+}  // namespace dev
+}  // namespace pad

@@ -46,6 +46,7 @@ constexpr int kQueueWord = int((kCounterBytes - 128) / 4);
 // Persistent grid (batched decode): at most this many sequences (its LDS
 // tables), sorted longest first up to kPersistSortSeqs of them.
 constexpr int kPersistMaxSeqs = 1024;
+constexpr int64_t kLdsPerCu = 160 << 10;  // LDS bytes of a gfx950 CU
 constexpr int kPersistSortSeqs = 512;
 
 // Waves per workgroup.  Four for every shape: on one bf16 sequence with

@@ -73,7 +73,12 @@ def test_plan_invariants(kw):
     assert p["rows"] == rows
     # 16-row tiles per workgroup times workgroups per kv head cover the rows
     assert p["row_tiles"] * p["row_groups"] * 16 >= rows
-    assert (p["row_tiles"] - 1) * p["row_groups"] * 16 < rows
+    if p["path"] == pad.PAD_PATH_ROWS:
+        # one wave per row tile; every row group but the last is full
+        assert p["waves"] == p["row_tiles"] and p["waves"] in (2, 4, 8)
+        assert (p["row_groups"] - 1) * p["row_tiles"] * 16 < rows
+    else:
+        assert (p["row_tiles"] - 1) * p["row_groups"] * 16 < rows
     keys = sh.max_blocks_per_seq * sh.page_size
     tiles = -(-keys // 16)
     assert p["num_segments"] * p["segment_tiles"] >= tiles
@@ -83,8 +88,9 @@ def test_plan_invariants(kw):
     # device length up to the table's capacity
     assert p["segment_tiles"] <= 4096 and -(-tiles // p["num_segments"]) <= 4096
     if p["persistent"]:
-        # one workgroup per CU; items come from the queue
-        assert (p["grid_x"], p["grid_y"]) == (256, 1)
+        # one (or, for small row-owning workgroups, a few) workgroup per CU;
+        # items come from the queue
+        assert p["grid_y"] == 1 and p["grid_x"] % 256 == 0 and 256 <= p["grid_x"] <= 4 * 256
         assert p["workspace_bytes"] >= 1 << 20
     else:
         assert p["grid_x"] == p["num_segments"] * sh.num_kv_heads * p["row_groups"]
@@ -130,6 +136,9 @@ def test_schedule_plan():
     batch = dict(num_seqs=65, num_q_heads=16, num_kv_heads=2, head_size=256, page_size=1056, max_blocks_per_seq=16)
     p = plan(shape(**batch))
     assert p["persistent"] == 1 and p["grid_x"] == 256
+    # the row-owning family fits two 2-wave workgroups per CU
+    r = plan(shape(path=pad.PAD_PATH_ROWS, **batch))
+    assert r["persistent"] == 1 and r["grid_x"] == 2 * 256
     g = plan(shape(schedule=pad.PAD_SCHED_GRID, **batch))
     assert g["persistent"] == 0 and g["grid_y"] == 65
     # with the segment count fixed, both schedules split the same way
@@ -142,6 +151,30 @@ def test_schedule_plan():
     assert plan(shape())["persistent"] == 0
     one = plan(shape(schedule=pad.PAD_SCHED_PERSISTENT, num_segments=1, max_blocks_per_seq=4))
     assert one["persistent"] == 1 and one["num_segments"] == 1 and one["workspace_bytes"] == 1 << 20
+
+
+def test_rows_family_plan():
+    R = pad.PAD_PATH_ROWS
+    wide = dict(num_q_heads=16, num_kv_heads=2, head_size=512, page_size=32, max_blocks_per_seq=1024)
+    assert plan(shape(query_len=8, **wide))["path"] == pad.PAD_PATH_MFMA  # automatic choice
+    p = plan(shape(query_len=8, path=R, **wide))
+    assert p["path"] == R and (p["waves"], p["row_groups"]) == (4, 1)
+    p = plan(shape(query_len=4, path=R, **wide))
+    assert p["path"] == R and p["waves"] == 4  # four waves share loads at 512
+    p = plan(shape(num_q_heads=16, num_kv_heads=2, head_size=256, page_size=1056, max_blocks_per_seq=16,
+                   query_len=4, path=R))
+    assert p["path"] == R and (p["waves"], p["row_groups"]) == (2, 1)
+    # one row tile, or head size 128: key-split family unless forced
+    assert plan(shape(num_q_heads=16, num_kv_heads=2, head_size=512, query_len=2))["path"] == pad.PAD_PATH_MFMA
+    assert plan(shape(num_q_heads=64, num_kv_heads=2, head_size=128, query_len=2))["path"] == pad.PAD_PATH_MFMA
+    f = plan(shape(num_q_heads=64, num_kv_heads=2, head_size=128, query_len=4, path=pad.PAD_PATH_ROWS))
+    assert f["path"] == pad.PAD_PATH_ROWS and (f["waves"], f["row_groups"]) == (8, 1)  # 128 rows
+    g = plan(shape(num_q_heads=64, num_kv_heads=1, head_size=256, query_len=4, path=pad.PAD_PATH_ROWS))
+    assert (g["waves"], g["row_groups"]) == (4, 4)  # 256 rows in groups of 4 row tiles
+    for bad in (dict(head_size=64, num_q_heads=64, num_kv_heads=2), dict(query_len=1)):
+        with pytest.raises(pad.PadError) as e:
+            plan(shape(path=pad.PAD_PATH_ROWS, **bad))
+        assert e.value.status == pad.PAD_EUNSUPPORTED
 
 
 def test_plan_fills_device():
@@ -190,7 +223,7 @@ def test_window_plan_is_smaller():
         (dict(layout=5), pad.PAD_EINVAL),
         (dict(max_seq_len=2048 * 16 + 1), pad.PAD_EINVAL),
         (dict(num_segments=-1), pad.PAD_EINVAL),
-        (dict(path=3), pad.PAD_EINVAL),
+        (dict(path=4), pad.PAD_EINVAL),
         (dict(schedule=3), pad.PAD_EINVAL),
         (dict(schedule=-1), pad.PAD_EINVAL),
         (dict(schedule=pad.PAD_SCHED_PERSISTENT, num_seqs=1025), pad.PAD_EUNSUPPORTED),
