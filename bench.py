@@ -11,7 +11,11 @@ rotating instances stay out of the 256 MiB last-level cache.
 
 The metric is effective HBM bandwidth: bytes of the distinct K/V rows the
 call must read, plus Q and O, per second; and its fraction of the 8 TB/s
-HBM peak.  One JSON line is printed.
+HBM peak.  Beside it, ``read_ceiling`` reports what plain reads reach on
+the same device: a kernel that gathers exactly the call's pages with the
+same table walk and 16-byte loads but no arithmetic (best of a small sweep
+of launch shapes), and a contiguous stream over the pool.  One JSON line is
+printed.
 """
 
 from __future__ import annotations
@@ -53,6 +57,84 @@ def effective_bytes(case) -> int:
         total += keys * spec.num_kv_heads * 2 * spec.head_size * eb
         total += 2 * M * spec.num_q_heads * spec.head_size * eb  # Q in, O out
     return total
+
+
+def tile_bytes(case) -> int:
+    """K/V bytes the gather-ceiling kernel reads: the same key ranges as the
+    call, rounded out to whole 16-key tiles."""
+    spec = case.spec
+    eb = case.q.element_size()
+    total = 0
+    for L in case.seq_lens.tolist():
+        if L <= 0:
+            continue
+        lo = max(0, L - case.query_len - case.window + 1) if case.window > 0 else 0
+        tiles = -(-L // 16) - lo // 16
+        total += tiles * 16 * spec.num_kv_heads * 2 * spec.head_size * eb
+    return total
+
+
+def _event_time(call, n_warm: int, n_timed: int) -> float:
+    """Average ms per call(i), timed with HIP events on the current stream."""
+    import torch
+
+    for i in range(n_warm):
+        call(i)
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(n_timed):
+        call(n_warm + i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / n_timed
+
+
+def read_ceiling(case, nseg_hint: int) -> dict:
+    """Practical read ceilings beside the result: the best rate of a kernel
+    that gathers exactly this call's pages (same table walk, 16-byte loads,
+    no arithmetic) over a small sweep of launch shapes, and a contiguous
+    16-byte stream over the whole pool."""
+    import torch
+
+    import paged_kv_decode_block_amd as pad
+
+    sink = torch.zeros(1, dtype=torch.int32, device=case.q.device)
+    n_inst = len(case.block_tables)
+    M, Hq, D = case.query_len, case.q.shape[2], case.q.shape[3]
+    nbytes = tile_bytes(case)
+    best = None
+    segs = sorted({max(1, min(256, s)) for s in (nseg_hint, 2 * nseg_hint, 4 * nseg_hint, 64, 128, 256)})
+    for waves in (4, 8):
+        for tif in (1, 2):
+            if tif == 2 and D == 512:
+                continue
+            for sg in segs:
+                def call(i, waves=waves, tif=tif, sg=sg):
+                    pad.pad_calib_gather_read(case.kv_cache, case.block_tables[i % n_inst], case.seq_lens, M, Hq,
+                                              case.window, sink, layout=case.layout, waves=waves,
+                                              tiles_in_flight=tif, segments=sg)
+
+                ms = _event_time(call, 10, 100)
+                gbs = nbytes / (ms * 1e-3) / 1e9
+                if best is None or gbs > best["GB/s"]:
+                    best = {"GB/s": round(gbs, 1), "us": round(ms * 1e3, 3), "waves": waves,
+                            "tiles_in_flight": tif, "segments": sg}
+    pool = case.kv_cache.view(-1)
+    pool_bytes = pool.numel() * pool.element_size()
+    stream_best = None
+    for blocks in (1024, 2048, 4096, 8192):
+        ms = _event_time(lambda i, b=blocks: pad.pad_calib_stream_read(pool, sink, blocks=b), 5, 20)
+        gbs = pool_bytes / (ms * 1e-3) / 1e9
+        if stream_best is None or gbs > stream_best["GB/s"]:
+            stream_best = {"GB/s": round(gbs, 1), "blocks": blocks}
+    return {
+        "gather_read": best,
+        "gather_bytes_per_launch": nbytes,
+        "stream_read": stream_best,
+        "stream_bytes": pool_bytes,
+    }
 
 
 def kernel_hash() -> str:
@@ -165,7 +247,10 @@ def main() -> int:
     ap.add_argument("--queries", type=int, default=None)
     ap.add_argument("--no-sweep", action="store_true", help="skip the per-(context, M) sweep of the config")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--path", choices=["auto", "mfma", "dot"], default="auto",
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling calibration kernels")
+    ap.add_argument("--segments", type=int, default=0,
+                    help="force the split-KV segment count of the timed call (0 = the planner's choice)")
+    ap.add_argument("--path", choices=["auto", "mfma", "dot", "rows"], default="auto",
                     help="kernel family (auto = the planner's choice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run device copies of COPY_BYTES (reference for HBM byte counters)")
@@ -181,7 +266,8 @@ def main() -> int:
 
     import paged_kv_decode_block_amd as pad
 
-    path = {"auto": pad.PAD_PATH_AUTO, "mfma": pad.PAD_PATH_MFMA, "dot": pad.PAD_PATH_DOT}[args.path]
+    path = {"auto": pad.PAD_PATH_AUTO, "mfma": pad.PAD_PATH_MFMA, "dot": pad.PAD_PATH_DOT,
+            "rows": pad.PAD_PATH_ROWS}[args.path]
     cfg = args.config
     pts = wl.CONFIG_POINTS[cfg]
     context = args.context or max(pts["contexts"])
@@ -198,7 +284,7 @@ def main() -> int:
     nbytes = effective_bytes(case)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms, plan = time_calls(case, args.warmup, args.steps, path=path)
+    ms, plan = time_calls(case, args.warmup, args.steps, path=path, num_segments=args.segments)
     wall = time.perf_counter() - t0
     print(f"[bench] timed {args.steps} steps: {ms * 1e3:.2f} us/step", file=sys.stderr, flush=True)
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -210,6 +296,13 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = read_ceiling(case, plan["num_segments"])
+        ceiling["frac_of_gather_read"] = round(gbs / ceiling["gather_read"]["GB/s"], 4)
+        print(f"[bench] read ceiling: gather {ceiling['gather_read']['GB/s']} GB/s, "
+              f"stream {ceiling['stream_read']['GB/s']} GB/s", file=sys.stderr, flush=True)
+
     sweep = []
     if not args.no_sweep:
         for ctx in pts["contexts"]:
@@ -217,7 +310,13 @@ def main() -> int:
                 if path == pad.PAD_PATH_DOT and m * spec.num_q_heads // spec.num_kv_heads > 4:
                     continue  # the dot family serves at most 4 query rows per kv head
                 c = build_case(ctx, m)
-                t, p = time_calls(c, 20, 100, graph=True, path=path)
+                try:
+                    t, p = time_calls(c, 20, 100, graph=True, path=path)
+                except pad.PadError as e:
+                    if e.status != pad.PAD_EUNSUPPORTED:
+                        raise
+                    del c
+                    continue  # a forced family that does not serve this shape
                 b = effective_bytes(c)
                 sweep.append({"context": ctx, "M": m, "us": round(t * 1e3, 3), "GB/s": round(b / (t * 1e-3) / 1e9, 1),
                               "frac": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "segments": p["num_segments"]})
@@ -258,6 +357,7 @@ def main() -> int:
             # measured on config 2, context 32768, M = 4 with the MFMA family
             "traffic": traffic_entry() if (cfg, context, M) == (2, 32768, 4) and path != pad.PAD_PATH_DOT else None,
         },
+        "read_ceiling": ceiling,
         "cpu_baseline": cpu,
         "sweep": sweep,
         "wall_s": round(wall, 3),

@@ -22,7 +22,7 @@ __all__ = [
     "PadError", "pad_shape", "pad_plan", "lib", "LIB_PATH", "load_library",
     "pad_abi_version", "pad_status_string", "pad_decode_attn_plan",
     "pad_decode_attn_workspace_size", "pad_decode_attn_workspace_init", "pad_decode_attn",
-    "pad_set_merge_wait",
+    "pad_set_merge_wait", "pad_calib_gather_read", "pad_calib_stream_read",
     "make_shape", "Workspace",
 ]
 
@@ -97,6 +97,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         P(pad_shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
     ]
+    L.pad_calib_gather_read.restype = ctypes.c_int
+    L.pad_calib_gather_read.argtypes = [
+        P(pad_shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    L.pad_calib_stream_read.restype = ctypes.c_int
+    L.pad_calib_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p]
     return L
 
 
@@ -269,3 +277,25 @@ def pad_decode_attn(
         ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(_stream_ptr(stream)),
     ), "pad_decode_attn")
     return out
+
+
+def pad_calib_gather_read(kv_cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                          query_len: int, num_q_heads: int, window: int, sink: torch.Tensor, *,
+                          layout: int = PAD_HND, waves: int = 4, tiles_in_flight: int = 1, segments: int = 32,
+                          stream=None) -> None:
+    """Read the pages a decode call would attend, computing nothing
+    (include/pad_calib.h); ``sink`` is a device int32 tensor."""
+    D = kv_cache.shape[-1]
+    q_like = torch.empty((block_table.shape[0], query_len, num_q_heads, D), dtype=kv_cache.dtype, device="meta")
+    shape = make_shape(q_like, kv_cache, block_table, layout)
+    _check(lib.pad_calib_gather_read(
+        ctypes.byref(shape), ctypes.c_void_p(kv_cache.data_ptr()), ctypes.c_void_p(block_table.data_ptr()),
+        ctypes.c_void_p(seq_lens.data_ptr()), int(window), int(waves), int(tiles_in_flight), int(segments),
+        ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(_stream_ptr(stream))), "pad_calib_gather_read")
+
+
+def pad_calib_stream_read(src: torch.Tensor, sink: torch.Tensor, *, blocks: int = 2048, stream=None) -> None:
+    """Read every byte of the contiguous device tensor ``src`` (include/pad_calib.h)."""
+    _check(lib.pad_calib_stream_read(
+        ctypes.c_void_p(src.data_ptr()), src.numel() * src.element_size(), int(blocks),
+        ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(_stream_ptr(stream))), "pad_calib_stream_read")

@@ -214,19 +214,21 @@ __device__ __forceinline__ void merge_slice(const Params& p, int64_t slot0, int 
   const int items = wg_rows * (D / 4);
   const int i0 = slice * items / nslices, i1 = (slice + 1) * items / nslices;
   if (i1 <= i0) return;
-  const int ln = n >= 24 ? 4 : (n >= 8 ? 2 : 1);
+  // Enough lanes per item that one chunk of at most 8 loads per lane
+  // covers every slot (n <= 256): an item costs one round of loads, not
+  // several dependent ones.
+  const int ln = n <= 8 ? 1 : (n <= 16 ? 2 : (n <= 32 ? 4 : (n <= 64 ? 8 : (n <= 128 ? 16 : 32))));
   const int per = (n + ln - 1) / ln;
   const int u = per <= 2 ? 2 : (per <= 4 ? 4 : 8);
   switch (ln * 16 + u) {
-    case 4 * 16 + 2: merge_items<T, D, NT, 4, 2>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
-    case 4 * 16 + 4: merge_items<T, D, NT, 4, 4>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
-    case 4 * 16 + 8: merge_items<T, D, NT, 4, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
-    case 2 * 16 + 2: merge_items<T, D, NT, 2, 2>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
-    case 2 * 16 + 4: merge_items<T, D, NT, 2, 4>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
-    case 2 * 16 + 8: merge_items<T, D, NT, 2, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
     case 1 * 16 + 2: merge_items<T, D, NT, 1, 2>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
     case 1 * 16 + 4: merge_items<T, D, NT, 1, 4>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
-    default: merge_items<T, D, NT, 1, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 1 * 16 + 8: merge_items<T, D, NT, 1, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 2 * 16 + 8: merge_items<T, D, NT, 2, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 4 * 16 + 8: merge_items<T, D, NT, 4, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 8 * 16 + 8: merge_items<T, D, NT, 8, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    case 16 * 16 + 8: merge_items<T, D, NT, 16, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+    default: merge_items<T, D, NT, 32, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
   }
 }
 

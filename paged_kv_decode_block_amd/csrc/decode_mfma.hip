@@ -239,7 +239,10 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
     for (int kc = 0; kc < KC; ++kc) tl.v[kc] = *reinterpret_cast<const i32x4*>(row + 2 * D + 64 * kc);
   };
 
-  auto compute_tile = [&](Tile& tl, int t) {
+  // Scores of tile t: stage its V rows in LDS, S^T = K Q^T, mask, online
+  // softmax; leaves P (input dtype, MFMA B layout) in pb.  After it the
+  // tile's registers are free.
+  auto score_tile = [&](Tile& tl, int t, uint64_t (&pb)[RT]) {
     const int key0 = t * 16;
     const bool edge = !(key0 >= lo_last && key0 + 15 <= qpos_first);
     if (edge) {
@@ -255,7 +258,6 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
     for (int kc = 0; kc < KC; ++kc)
       *reinterpret_cast<i32x4*>(vs + c * SH::kVStride + 32 * kc + 8 * g) = tl.v[kc];
 
-    uint64_t pb[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -285,7 +287,10 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
       for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
       pb[rt] = pack4(MF::bits(pj[0]), MF::bits(pj[1]), MF::bits(pj[2]), MF::bits(pj[3]));
     }
+  };
 
+  // O^T += V^T P^T from the V rows staged in LDS.
+  auto pv_tile = [&](const uint64_t (&pb)[RT]) {
     // The staged V rows were written by other lanes of this wave; LDS
     // operations of a wave complete in order, the fences keep the compiler
     // from moving the reads above the writes.
@@ -314,7 +319,26 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
   const int first_t = ts + wave;
   const int n_w = first_t < te ? (te - first_t + NW - 1) / NW : 0;
   auto tile_at = [&](int i) { return first_t + min(i, n_w - 1) * NW; };
-  if (n_w > 0) {
+  auto compute_tile = [&](Tile& tl, int t) {
+    uint64_t pb[RT];
+    score_tile(tl, t, pb);
+    pv_tile(pb);
+  };
+  if constexpr (SH::PF == 0) {
+    // No register room for a second tile: the next tile's loads go out as
+    // soon as the scores have consumed the current one, so they overlap
+    // the PV product (whose V operand is already in LDS).
+    if (n_w > 0) {
+      Tile tl;
+      issue_tile(tl, first_t, block_of(first_t));
+      for (int i = 0; i < n_w; ++i) {
+        uint64_t pb[RT];
+        score_tile(tl, first_t + i * NW, pb);
+        if (i + 1 < n_w) issue_tile(tl, first_t + (i + 1) * NW, block_of(first_t + (i + 1) * NW));
+        pv_tile(pb);
+      }
+    }
+  } else if (n_w > 0) {
     Tile ring[SH::PF + 1];
 #pragma unroll
     for (int u = 0; u < SH::PF; ++u) issue_tile(ring[u], tile_at(u), block_of(tile_at(u)));

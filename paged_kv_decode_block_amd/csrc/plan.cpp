@@ -170,10 +170,15 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
     // control words the counter prefix holds.
     const size_t wg_rows = size_t(std::min(rows, p.row_tiles * 16));
     const size_t vol = size_t(p.nseg) * wg_rows * size_t(sh.head_size) * sizeof(float);
-    // On the persistent grid the segments of a unit start as workgroups
-    // free up, so helpers would wait up to a segment's time: the last
-    // arriver merges alone there.
-    int64_t k = p.persistent ? 1 : int64_t((vol + kSliceBytes - 1) / kSliceBytes);
+    // Helpers wait for their unit's last segment, so they are used only
+    // when every workgroup of the grid can be resident at once.  On the
+    // persistent grid, or on a grid larger than one workgroup per CU, the
+    // last segment may only start once a waiting helper's CU frees up
+    // (measured: 48 segments of a 512-wide head with 4 row groups, 384
+    // workgroups, took 425 us with helpers against 73 us at 32 segments):
+    // the last arriver merges alone there.
+    const bool resident = !p.persistent && int64_t(p.grid_x) * p.grid_y <= slots;
+    int64_t k = resident ? int64_t((vol + kSliceBytes - 1) / kSliceBytes) : 1;
     k = std::max<int64_t>(1, std::min<int64_t>(k, std::min(p.nseg, kMaxSlices)));
     const size_t ctl_units = S * H * size_t(p.row_groups);
     k = std::min<int64_t>(k, int64_t((kCounterBytes - 128) /

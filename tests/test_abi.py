@@ -11,17 +11,22 @@ import paged_kv_decode_block_amd as pad
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pad_attn.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 def _declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(pad_[a-z_]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(pad_[a-z_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():
     names = _declared_functions()
     assert "pad_decode_attn" in names and "pad_decode_attn_workspace_size" in names
+    assert "pad_calib_gather_read" in names and "pad_calib_stream_read" in names
     lib = ctypes.CDLL(pad.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"libpad_attn.so does not export {n}"
@@ -111,7 +116,10 @@ def test_plan_invariants(kw):
         vol = n * wg_rows * sh.head_size * 4
         assert 1 <= k <= min(32, n)
         # control words one 128-byte line apart, clear of the queue line
-        want_k = 1 if p["persistent"] else min(-(-vol // (32 << 10)), 32, n, ((1 << 20) - 128) // (128 * S * H * p["row_groups"]))
+        # helpers only when the whole grid is resident (one workgroup per CU)
+        resident = not p["persistent"] and p["grid_x"] * p["grid_y"] <= 256
+        want_k = min(-(-vol // (32 << 10)), 32, n, ((1 << 20) - 128) // (128 * S * H * p["row_groups"])) \
+            if resident else 1
         assert k == want_k
         assert S * H * p["row_groups"] * k * 128 <= (1 << 20) - 128
 
@@ -147,6 +155,11 @@ def test_schedule_plan():
     assert (a["num_segments"], a["segment_tiles"]) == (b["num_segments"], b["segment_tiles"])
     # the persistent grid's last arriver merges alone
     assert b["merge_slices"] == 1
+    # so does one on a grid larger than one workgroup per CU
+    assert a["grid_x"] * a["grid_y"] > 256 and a["merge_slices"] == 1
+    wide = dict(num_q_heads=16, num_kv_heads=2, head_size=512, page_size=32, max_blocks_per_seq=1024, query_len=8)
+    assert plan(shape(num_segments=32, **wide))["merge_slices"] == 32  # 256 workgroups
+    assert plan(shape(num_segments=48, **wide))["merge_slices"] == 1  # 384 workgroups
     # batch 1 stays on one workgroup per item unless asked
     assert plan(shape())["persistent"] == 0
     one = plan(shape(schedule=pad.PAD_SCHED_PERSISTENT, num_segments=1, max_blocks_per_seq=4))
@@ -293,3 +306,28 @@ def test_merge_wait_bounds():
     assert pad.lib.pad_set_merge_wait(1000001) == pad.PAD_EINVAL
     assert pad.lib.pad_set_merge_wait(0) == pad.PAD_OK
     assert pad.lib.pad_set_merge_wait(200) == pad.PAD_OK
+
+
+def test_calibration_validation():
+    """The read-ceiling kernels reject bad arguments on the host (no launch)."""
+    P = ctypes.c_void_p
+    L = pad.lib
+
+    def g(sh, waves=4, tif=1, segs=32, window=0, ptr=0x1000):
+        return L.pad_calib_gather_read(ctypes.byref(sh), P(ptr), P(ptr), P(ptr), window, waves, tif, segs, P(ptr),
+                                       None)
+
+    assert g(shape(num_seqs=0)) == pad.PAD_OK  # nothing to read
+    assert g(shape(num_seqs=0), waves=5) == pad.PAD_EINVAL
+    assert g(shape(num_seqs=0), tif=3) == pad.PAD_EINVAL
+    assert g(shape(num_seqs=0), segs=0) == pad.PAD_EINVAL
+    assert g(shape(num_seqs=0), segs=257) == pad.PAD_EINVAL
+    assert g(shape(num_seqs=0, head_size=96)) == pad.PAD_EUNSUPPORTED
+    assert g(shape(num_seqs=0, head_size=512, num_q_heads=16, num_kv_heads=2), tif=2) == pad.PAD_EUNSUPPORTED
+    assert g(shape(), window=-1) == pad.PAD_EINVAL
+    assert g(shape(), ptr=0) == pad.PAD_EINVAL  # missing buffers
+    assert g(shape(), ptr=0x1008) == pad.PAD_EINVAL  # kv_cache not 16-byte aligned
+    assert L.pad_calib_stream_read(P(0), ctypes.c_size_t(0), 256, P(0), None) == pad.PAD_OK
+    assert L.pad_calib_stream_read(P(0x1000), ctypes.c_size_t(24), 256, P(0x1000), None) == pad.PAD_EINVAL
+    assert L.pad_calib_stream_read(P(0x1000), ctypes.c_size_t(32), 0, P(0x1000), None) == pad.PAD_EINVAL
+    assert L.pad_calib_stream_read(P(0x1008), ctypes.c_size_t(32), 256, P(0x1000), None) == pad.PAD_EINVAL
