@@ -30,7 +30,7 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   if (sh.num_q_heads % sh.num_kv_heads != 0) return PAD_EINVAL;
   if (sh.dtype != PAD_F16 && sh.dtype != PAD_BF16) return PAD_EINVAL;
   if (sh.layout != PAD_NHD && sh.layout != PAD_HND) return PAD_EINVAL;
-  if (sh.path < PAD_PATH_AUTO || sh.path > PAD_PATH_ROWS) return PAD_EINVAL;
+  if (sh.path < PAD_PATH_AUTO || sh.path > PAD_PATH_DSPLIT) return PAD_EINVAL;
   if (sh.schedule < PAD_SCHED_AUTO || sh.schedule > PAD_SCHED_PERSISTENT) return PAD_EINVAL;
   const int64_t table_keys = int64_t(sh.max_blocks_per_seq) * sh.page_size;
   if (sh.max_seq_len > table_keys) return PAD_EINVAL;
@@ -47,31 +47,26 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   const bool dot_ok = rows <= kDotMaxRows && sh.head_size <= kDotMaxHeadSize;
   if (sh.path == PAD_PATH_DOT && !dot_ok) return PAD_EUNSUPPORTED;
   const int tiles_total = int(ceil_div(rows, 16));
-  const bool rows_ok = sh.head_size >= 128 && tiles_total >= 2;
-  if (sh.path == PAD_PATH_ROWS && !rows_ok) return PAD_EUNSUPPORTED;
+  const bool split_ok = sh.head_size >= 128 && tiles_total >= 2;
+  if (sh.path == PAD_PATH_DSPLIT && !split_ok) return PAD_EUNSUPPORTED;
 
   Plan p{};
   // The key-split MFMA family serves every shape and is the automatic
-  // choice.  The row-owning family (each K/V tile read once per workgroup
-  // for all rows, no cross-wave combine) and the per-head dot-product
-  // family are used when asked for: both measured slower than the key-split
-  // family on their target shapes so far.
+  // choice.  The head-dimension-split family (each K/V tile read once per
+  // workgroup for up to four row tiles, no cross-wave combine) and the
+  // per-head dot-product family are used when asked for.
   p.path = sh.path == PAD_PATH_AUTO ? PAD_PATH_MFMA : sh.path;
   p.rows = rows;
   if (p.path == PAD_PATH_DOT) {
     p.row_tiles = 1;
     p.row_groups = 1;
     p.waves = kDotWaveCount;
-  } else if (p.path == PAD_PATH_ROWS) {
-    // One wave per row tile: 2, 4 or (head size 128) 8 waves, more rows in
-    // row groups.  At head size 512 four waves share a tile's loads even
-    // for two row tiles (fewer staging registers per thread).
-    const int nw_max = sh.head_size == 128 ? 8 : 4;
-    const int nw_min = sh.head_size == 512 ? 4 : 2;
-    const int nw = std::max(nw_min, tiles_total <= 2 ? 2 : (tiles_total <= 4 ? 4 : nw_max));
-    p.waves = nw;
-    p.row_tiles = nw;
-    p.row_groups = int(ceil_div(tiles_total, nw));
+  } else if (p.path == PAD_PATH_DSPLIT) {
+    // Four waves serve two or four row tiles (three use four, one idle);
+    // more rows take row groups of four tiles.
+    p.waves = 4;
+    p.row_tiles = tiles_total <= 2 ? 2 : 4;
+    p.row_groups = int(ceil_div(tiles_total, p.row_tiles));
   } else {
     int rt = std::min(tiles_total, max_row_tiles(sh.head_size));
     p.row_groups = int(ceil_div(tiles_total, rt));
@@ -149,12 +144,7 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   if (p.persistent) {
     // Workgroups one CU holds at once (LDS and waves); the key-split and
     // dot families fill a CU with one.
-    int per_cu = 1;
-    if (p.path == PAD_PATH_ROWS) {
-      const int64_t lds = 2 * int64_t(kTileKeys) * 4 * sh.head_size + 4 * kMaxSegTiles +
-                          (2 * kPersistMaxSeqs + 1) * 4 + 16;
-      per_cu = int(std::max<int64_t>(1, std::min<int64_t>(kLdsPerCu / lds, 8 / p.waves)));
-    }
+    const int per_cu = 1;
     p.grid_x = num_cus * per_cu;
     p.grid_y = 1;
   } else {

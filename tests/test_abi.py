@@ -78,9 +78,9 @@ def test_plan_invariants(kw):
     assert p["rows"] == rows
     # 16-row tiles per workgroup times workgroups per kv head cover the rows
     assert p["row_tiles"] * p["row_groups"] * 16 >= rows
-    if p["path"] == pad.PAD_PATH_ROWS:
-        # one wave per row tile; every row group but the last is full
-        assert p["waves"] == p["row_tiles"] and p["waves"] in (2, 4, 8)
+    if p["path"] == pad.PAD_PATH_DSPLIT:
+        # four waves over two or four row tiles; every row group but the last is full
+        assert p["waves"] == 4 and p["row_tiles"] in (2, 4)
         assert (p["row_groups"] - 1) * p["row_tiles"] * 16 < rows
     else:
         assert (p["row_tiles"] - 1) * p["row_groups"] * 16 < rows
@@ -93,7 +93,7 @@ def test_plan_invariants(kw):
     # device length up to the table's capacity
     assert p["segment_tiles"] <= 4096 and -(-tiles // p["num_segments"]) <= 4096
     if p["persistent"]:
-        # one (or, for small row-owning workgroups, a few) workgroup per CU;
+        # one workgroup per CU;
         # items come from the queue
         assert p["grid_y"] == 1 and p["grid_x"] % 256 == 0 and 256 <= p["grid_x"] <= 4 * 256
         assert p["workspace_bytes"] >= 1 << 20
@@ -144,9 +144,9 @@ def test_schedule_plan():
     batch = dict(num_seqs=65, num_q_heads=16, num_kv_heads=2, head_size=256, page_size=1056, max_blocks_per_seq=16)
     p = plan(shape(**batch))
     assert p["persistent"] == 1 and p["grid_x"] == 256
-    # the row-owning family fits two 2-wave workgroups per CU
-    r = plan(shape(path=pad.PAD_PATH_ROWS, **batch))
-    assert r["persistent"] == 1 and r["grid_x"] == 2 * 256
+    # the head-dim-split family also runs one workgroup per CU
+    r = plan(shape(path=pad.PAD_PATH_DSPLIT, **batch))
+    assert r["persistent"] == 1 and r["grid_x"] == 256
     g = plan(shape(schedule=pad.PAD_SCHED_GRID, **batch))
     assert g["persistent"] == 0 and g["grid_y"] == 65
     # with the segment count fixed, both schedules split the same way
@@ -166,27 +166,21 @@ def test_schedule_plan():
     assert one["persistent"] == 1 and one["num_segments"] == 1 and one["workspace_bytes"] == 1 << 20
 
 
-def test_rows_family_plan():
-    R = pad.PAD_PATH_ROWS
+def test_split_family_plan():
+    S = pad.PAD_PATH_DSPLIT
     wide = dict(num_q_heads=16, num_kv_heads=2, head_size=512, page_size=32, max_blocks_per_seq=1024)
-    assert plan(shape(query_len=8, **wide))["path"] == pad.PAD_PATH_MFMA  # automatic choice
-    p = plan(shape(query_len=8, path=R, **wide))
-    assert p["path"] == R and (p["waves"], p["row_groups"]) == (4, 1)
-    p = plan(shape(query_len=4, path=R, **wide))
-    assert p["path"] == R and p["waves"] == 4  # four waves share loads at 512
-    p = plan(shape(num_q_heads=16, num_kv_heads=2, head_size=256, page_size=1056, max_blocks_per_seq=16,
-                   query_len=4, path=R))
-    assert p["path"] == R and (p["waves"], p["row_groups"]) == (2, 1)
-    # one row tile, or head size 128: key-split family unless forced
-    assert plan(shape(num_q_heads=16, num_kv_heads=2, head_size=512, query_len=2))["path"] == pad.PAD_PATH_MFMA
-    assert plan(shape(num_q_heads=64, num_kv_heads=2, head_size=128, query_len=2))["path"] == pad.PAD_PATH_MFMA
-    f = plan(shape(num_q_heads=64, num_kv_heads=2, head_size=128, query_len=4, path=pad.PAD_PATH_ROWS))
-    assert f["path"] == pad.PAD_PATH_ROWS and (f["waves"], f["row_groups"]) == (8, 1)  # 128 rows
-    g = plan(shape(num_q_heads=64, num_kv_heads=1, head_size=256, query_len=4, path=pad.PAD_PATH_ROWS))
-    assert (g["waves"], g["row_groups"]) == (4, 4)  # 256 rows in groups of 4 row tiles
+    p = plan(shape(query_len=8, path=S, **wide))  # 64 rows: four row tiles, one workgroup
+    assert p["path"] == S and (p["waves"], p["row_tiles"], p["row_groups"]) == (4, 4, 1)
+    p = plan(shape(query_len=3, path=S, **wide))  # 24 rows: two row tiles
+    assert p["path"] == S and (p["row_tiles"], p["row_groups"]) == (2, 1)
+    p = plan(shape(query_len=5, path=S, **wide))  # 40 rows: three tiles take a four-tile workgroup
+    assert (p["row_tiles"], p["row_groups"]) == (4, 1)
+    g = plan(shape(num_q_heads=64, num_kv_heads=1, head_size=256, query_len=4, path=S))
+    assert (g["row_tiles"], g["row_groups"]) == (4, 4)  # 256 rows in groups of four row tiles
+    # one row tile, or head size 64: not served
     for bad in (dict(head_size=64, num_q_heads=64, num_kv_heads=2), dict(query_len=1)):
         with pytest.raises(pad.PadError) as e:
-            plan(shape(path=pad.PAD_PATH_ROWS, **bad))
+            plan(shape(path=S, **bad))
         assert e.value.status == pad.PAD_EUNSUPPORTED
 
 
