@@ -250,7 +250,7 @@ def main() -> int:
     ap.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling calibration kernels")
     ap.add_argument("--segments", type=int, default=0,
                     help="force the split-KV segment count of the timed call (0 = the planner's choice)")
-    ap.add_argument("--path", choices=["auto", "mfma", "dot", "dsplit"], default="auto",
+    ap.add_argument("--path", choices=["auto", "mfma", "dot"], default="auto",
                     help="kernel family (auto = the planner's choice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run device copies of COPY_BYTES (reference for HBM byte counters)")
@@ -266,8 +266,7 @@ def main() -> int:
 
     import paged_kv_decode_block_amd as pad
 
-    path = {"auto": pad.PAD_PATH_AUTO, "mfma": pad.PAD_PATH_MFMA, "dot": pad.PAD_PATH_DOT,
-            "dsplit": pad.PAD_PATH_DSPLIT}[args.path]
+    path = {"auto": pad.PAD_PATH_AUTO, "mfma": pad.PAD_PATH_MFMA, "dot": pad.PAD_PATH_DOT}[args.path]
     cfg = args.config
     pts = wl.CONFIG_POINTS[cfg]
     context = args.context or max(pts["contexts"])

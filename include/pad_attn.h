@@ -92,15 +92,11 @@ typedef enum pad_layout { PAD_NHD = 0, PAD_HND = 1 } pad_layout;
 /* Which kernel family serves a call.  AUTO lets the planner choose; the
  * others force a family (tuning and tests).  MFMA: the waves of a workgroup
  * split a segment's keys and are combined at the end.  DOT: per-head dot
- * products (G*M <= 4, head size <= 128).  DSPLIT: MFMA where each wave
- * computes the scores of one 16-row tile from K tiles shared through LDS,
- * then every wave accumulates P V for all row tiles over its quarter of
- * the head dimension (head size >= 128, two or more row tiles). */
+ * products (G*M <= 4, head size <= 128). */
 typedef enum pad_path {
   PAD_PATH_AUTO = 0,
   PAD_PATH_MFMA = 1,
   PAD_PATH_DOT = 2,
-  PAD_PATH_DSPLIT = 3,
 } pad_path;
 
 /* Work schedule.  AUTO picks the persistent grid for batches whose

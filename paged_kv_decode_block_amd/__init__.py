@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "PAD_OK", "PAD_EINVAL", "PAD_EUNSUPPORTED", "PAD_EWORKSPACE", "PAD_EHIP",
     "PAD_F16", "PAD_BF16", "PAD_NHD", "PAD_HND",
-    "PAD_PATH_AUTO", "PAD_PATH_MFMA", "PAD_PATH_DOT", "PAD_PATH_DSPLIT",
+    "PAD_PATH_AUTO", "PAD_PATH_MFMA", "PAD_PATH_DOT",
     "PAD_SCHED_AUTO", "PAD_SCHED_GRID", "PAD_SCHED_PERSISTENT",
     "PadError", "pad_shape", "pad_plan", "lib", "LIB_PATH", "load_library",
     "pad_abi_version", "pad_status_string", "pad_decode_attn_plan",
@@ -29,7 +29,7 @@ __all__ = [
 PAD_OK, PAD_EINVAL, PAD_EUNSUPPORTED, PAD_EWORKSPACE, PAD_EHIP = 0, 1, 2, 3, 4
 PAD_F16, PAD_BF16 = 0, 1
 PAD_NHD, PAD_HND = 0, 1
-PAD_PATH_AUTO, PAD_PATH_MFMA, PAD_PATH_DOT, PAD_PATH_DSPLIT = 0, 1, 2, 3
+PAD_PATH_AUTO, PAD_PATH_MFMA, PAD_PATH_DOT = 0, 1, 2
 PAD_SCHED_AUTO, PAD_SCHED_GRID, PAD_SCHED_PERSISTENT = 0, 1, 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpad_attn.so")

@@ -743,7 +743,6 @@ int launch_dtype(const Plan& pl, const Params& pr, int head_size, hipStream_t st
 }  // namespace
 
 int launch_decode(const Plan& plan, const Params& params, int dtype, int head_size, void* stream) {
-  if (plan.path == PAD_PATH_DSPLIT) return launch_split(plan, params, dtype, head_size, stream);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == PAD_BF16) return launch_dtype<__bf16>(plan, params, head_size, st);
   return launch_dtype<_Float16>(plan, params, head_size, st);

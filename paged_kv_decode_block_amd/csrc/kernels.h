@@ -36,10 +36,6 @@ struct Params {
 // (0 = success).
 int launch_decode(const Plan& plan, const Params& params, int dtype, int head_size, void* stream);
 
-// The head-dimension-split family (plan.path == PAD_PATH_DSPLIT); called by
-// launch_decode.
-int launch_split(const Plan& plan, const Params& params, int dtype, int head_size, void* stream);
-
 // Enqueue a fill of `words` 32-bit zeros at `ptr`.
 int launch_zero(void* ptr, size_t words, void* stream);
 

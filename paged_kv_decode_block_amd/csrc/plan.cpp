@@ -30,7 +30,7 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   if (sh.num_q_heads % sh.num_kv_heads != 0) return PAD_EINVAL;
   if (sh.dtype != PAD_F16 && sh.dtype != PAD_BF16) return PAD_EINVAL;
   if (sh.layout != PAD_NHD && sh.layout != PAD_HND) return PAD_EINVAL;
-  if (sh.path < PAD_PATH_AUTO || sh.path > PAD_PATH_DSPLIT) return PAD_EINVAL;
+  if (sh.path < PAD_PATH_AUTO || sh.path > PAD_PATH_DOT) return PAD_EINVAL;
   if (sh.schedule < PAD_SCHED_AUTO || sh.schedule > PAD_SCHED_PERSISTENT) return PAD_EINVAL;
   const int64_t table_keys = int64_t(sh.max_blocks_per_seq) * sh.page_size;
   if (sh.max_seq_len > table_keys) return PAD_EINVAL;
@@ -47,26 +47,16 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   const bool dot_ok = rows <= kDotMaxRows && sh.head_size <= kDotMaxHeadSize;
   if (sh.path == PAD_PATH_DOT && !dot_ok) return PAD_EUNSUPPORTED;
   const int tiles_total = int(ceil_div(rows, 16));
-  const bool split_ok = sh.head_size >= 128 && tiles_total >= 2;
-  if (sh.path == PAD_PATH_DSPLIT && !split_ok) return PAD_EUNSUPPORTED;
 
   Plan p{};
   // The key-split MFMA family serves every shape and is the automatic
-  // choice.  The head-dimension-split family (each K/V tile read once per
-  // workgroup for up to four row tiles, no cross-wave combine) and the
-  // per-head dot-product family are used when asked for.
+  // choice; the per-head dot-product family is used when asked for.
   p.path = sh.path == PAD_PATH_AUTO ? PAD_PATH_MFMA : sh.path;
   p.rows = rows;
   if (p.path == PAD_PATH_DOT) {
     p.row_tiles = 1;
     p.row_groups = 1;
     p.waves = kDotWaveCount;
-  } else if (p.path == PAD_PATH_DSPLIT) {
-    // Four waves serve two or four row tiles (three use four, one idle);
-    // more rows take row groups of four tiles.
-    p.waves = 4;
-    p.row_tiles = tiles_total <= 2 ? 2 : 4;
-    p.row_groups = int(ceil_div(tiles_total, p.row_tiles));
   } else {
     int rt = std::min(tiles_total, max_row_tiles(sh.head_size));
     p.row_groups = int(ceil_div(tiles_total, rt));
@@ -142,10 +132,9 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   }
 
   if (p.persistent) {
-    // Workgroups one CU holds at once (LDS and waves); the key-split and
-    // dot families fill a CU with one.
-    const int per_cu = 1;
-    p.grid_x = num_cus * per_cu;
+    // One workgroup per CU: the key-split and dot families fill a CU's
+    // registers (and, for the key-split combine, most of its LDS).
+    p.grid_x = num_cus;
     p.grid_y = 1;
   } else {
     p.grid_x = p.nseg * sh.num_kv_heads * p.row_groups;

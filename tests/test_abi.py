@@ -78,12 +78,7 @@ def test_plan_invariants(kw):
     assert p["rows"] == rows
     # 16-row tiles per workgroup times workgroups per kv head cover the rows
     assert p["row_tiles"] * p["row_groups"] * 16 >= rows
-    if p["path"] == pad.PAD_PATH_DSPLIT:
-        # four waves over two or four row tiles; every row group but the last is full
-        assert p["waves"] == 4 and p["row_tiles"] in (2, 4)
-        assert (p["row_groups"] - 1) * p["row_tiles"] * 16 < rows
-    else:
-        assert (p["row_tiles"] - 1) * p["row_groups"] * 16 < rows
+    assert (p["row_tiles"] - 1) * p["row_groups"] * 16 < rows
     keys = sh.max_blocks_per_seq * sh.page_size
     tiles = -(-keys // 16)
     assert p["num_segments"] * p["segment_tiles"] >= tiles
@@ -144,9 +139,6 @@ def test_schedule_plan():
     batch = dict(num_seqs=65, num_q_heads=16, num_kv_heads=2, head_size=256, page_size=1056, max_blocks_per_seq=16)
     p = plan(shape(**batch))
     assert p["persistent"] == 1 and p["grid_x"] == 256
-    # the head-dim-split family also runs one workgroup per CU
-    r = plan(shape(path=pad.PAD_PATH_DSPLIT, **batch))
-    assert r["persistent"] == 1 and r["grid_x"] == 256
     g = plan(shape(schedule=pad.PAD_SCHED_GRID, **batch))
     assert g["persistent"] == 0 and g["grid_y"] == 65
     # with the segment count fixed, both schedules split the same way
@@ -164,24 +156,6 @@ def test_schedule_plan():
     assert plan(shape())["persistent"] == 0
     one = plan(shape(schedule=pad.PAD_SCHED_PERSISTENT, num_segments=1, max_blocks_per_seq=4))
     assert one["persistent"] == 1 and one["num_segments"] == 1 and one["workspace_bytes"] == 1 << 20
-
-
-def test_split_family_plan():
-    S = pad.PAD_PATH_DSPLIT
-    wide = dict(num_q_heads=16, num_kv_heads=2, head_size=512, page_size=32, max_blocks_per_seq=1024)
-    p = plan(shape(query_len=8, path=S, **wide))  # 64 rows: four row tiles, one workgroup
-    assert p["path"] == S and (p["waves"], p["row_tiles"], p["row_groups"]) == (4, 4, 1)
-    p = plan(shape(query_len=3, path=S, **wide))  # 24 rows: two row tiles
-    assert p["path"] == S and (p["row_tiles"], p["row_groups"]) == (2, 1)
-    p = plan(shape(query_len=5, path=S, **wide))  # 40 rows: three tiles take a four-tile workgroup
-    assert (p["row_tiles"], p["row_groups"]) == (4, 1)
-    g = plan(shape(num_q_heads=64, num_kv_heads=1, head_size=256, query_len=4, path=S))
-    assert (g["row_tiles"], g["row_groups"]) == (4, 4)  # 256 rows in groups of four row tiles
-    # one row tile, or head size 64: not served
-    for bad in (dict(head_size=64, num_q_heads=64, num_kv_heads=2), dict(query_len=1)):
-        with pytest.raises(pad.PadError) as e:
-            plan(shape(path=S, **bad))
-        assert e.value.status == pad.PAD_EUNSUPPORTED
 
 
 def test_plan_fills_device():
@@ -230,6 +204,7 @@ def test_window_plan_is_smaller():
         (dict(layout=5), pad.PAD_EINVAL),
         (dict(max_seq_len=2048 * 16 + 1), pad.PAD_EINVAL),
         (dict(num_segments=-1), pad.PAD_EINVAL),
+        (dict(path=3), pad.PAD_EINVAL),
         (dict(path=4), pad.PAD_EINVAL),
         (dict(schedule=3), pad.PAD_EINVAL),
         (dict(schedule=-1), pad.PAD_EINVAL),

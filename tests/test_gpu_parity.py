@@ -246,42 +246,6 @@ def test_schedules_give_same_bits(cfg, lens, M, window, nseg):
     assert torch.equal(outs[0], outs[1])
 
 
-# Head-dim-split family: (D, Hq, Hkv, P, dtype, layout, lens, M, window, nseg)
-SPLIT_SHAPES = [
-    (512, 16, 2, 32, "bf16", wl.HND, [1000], 4, 0, 0),
-    (512, 16, 2, 32, "bf16", wl.HND, [777], 8, 0, 5),
-    (512, 16, 2, 32, "fp16", wl.NHD, [333, 20], 3, 0, 1),
-    (512, 16, 2, 32, "bf16", wl.HND, [1500], 5, 0, 0),        # 40 rows: a four-tile workgroup, one tile empty
-    (256, 16, 2, 1056, "bf16", wl.HND, [2500, 1, 0, 700], 4, 0, 0),
-    (256, 32, 2, 32, "fp16", wl.HND, [401], 4, 100, 3),
-    (256, 16, 1, 48, "bf16", wl.NHD, [900], 8, 0, 17),        # 128 rows: row groups of 4 tiles
-    (128, 64, 2, 16, "bf16", wl.HND, [1234], 4, 0, 0),        # 128 rows
-    (128, 12, 3, 16, "fp16", wl.HND, [99, 300], 8, 64, 2),    # 32 rows, window
-    (512, 8, 1, 16, "bf16", wl.HND, [5, 3], 4, 0, 0),         # L < M: rows with no key
-]
-
-
-@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=[f"s{i}" for i in range(len(SPLIT_SHAPES))])
-def test_split_family(shape):
-    D, Hq, Hkv, P, dt, layout, lens, M, window, nseg = shape
-    c = _case(wl.Spec(dt, D, Hq, Hkv, P, layout), lens, M, 700 + D + M, window=window)
-    ref = oracle_out(c)
-    out = run_gpu(c, num_segments=nseg, path=pad.PAD_PATH_DSPLIT)
-    check(out, ref, c.q.dtype, "head-dim-split family")
-    again = run_gpu(c, num_segments=nseg, path=pad.PAD_PATH_DSPLIT)
-    assert torch.equal(out, again), "bitwise deterministic"
-    keys = run_gpu(c, num_segments=nseg, path=pad.PAD_PATH_MFMA)
-    check(keys, ref, c.q.dtype, "key-split family")
-    if len(lens) > 1:
-        # the same segment split on the persistent grid gives the same bits
-        shape_ = pad.make_shape(c.q, c.kv_cache, c.block_tables[0], c.layout, num_segments=nseg,
-                                path=pad.PAD_PATH_DSPLIT, schedule=pad.PAD_SCHED_GRID)
-        n = pad.pad_decode_attn_plan(shape_, c.window)["num_segments"]
-        grid = run_gpu(c, num_segments=n, path=pad.PAD_PATH_DSPLIT, schedule=pad.PAD_SCHED_GRID)
-        per = run_gpu(c, num_segments=n, path=pad.PAD_PATH_DSPLIT, schedule=pad.PAD_SCHED_PERSISTENT)
-        assert torch.equal(grid, per), "schedules give the same bits"
-
-
 def test_graph_replay():
     c = _case(wl.CONFIGS[4], [2500], 4, 6, instances=2)
     ref = [oracle_out(c, i) for i in range(2)]
