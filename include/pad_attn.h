@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define PAD_ABI_VERSION 4
+#define PAD_ABI_VERSION 5
 
 typedef enum pad_status {
   PAD_OK = 0,
@@ -183,6 +183,29 @@ pad_status pad_decode_attn(const pad_shape* shape, const void* q, const void* kv
                            const int32_t* block_table, const int32_t* seq_lens, float scale,
                            int32_t window, void* out, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* Paged-KV decode attention with a query count per sequence (mixed decode
+ * and speculative-verify batches in one call).  The query rows are packed:
+ * q and out are [T, num_q_heads, head_size] and sequence s owns tokens
+ * q_start[s] .. q_start[s + 1] - 1, i.e. M_s = q_start[s + 1] - q_start[s]
+ * query tokens whose positions are L_s - M_s + m, m < M_s, with the same
+ * causal and window rule as above (query i of a request with q_len queries
+ * and seq_len tokens sees K length seq_len - q_len + i + 1:
+ * RocmOctaveMetadataBuilder._fill_query_maps on the octave page).
+ * q_start is a device int32 array of num_seqs + 1 entries, read only on
+ * the device (no host synchronisation; the call can be captured in a HIP
+ * graph).  shape->query_len is the host bound on every M_s (1..8; it sizes
+ * the plan and the workspace like a uniform call of that M).  Contract on
+ * the device values: q_start non-decreasing, q_start[0] >= 0, M_s <=
+ * query_len, and q/out hold at least q_start[num_seqs] rows; a count
+ * outside [0, query_len] is clamped into it (M_s = 0: the sequence is
+ * skipped and its rows, if any, are left untouched).  Other arguments,
+ * errors and ownership as pad_decode_attn; q_start must be 4-byte aligned
+ * (PAD_EINVAL if missing or misaligned). */
+pad_status pad_decode_attn_varlen(const pad_shape* shape, const void* q, const int32_t* q_start,
+                                  const void* kv_cache, const int32_t* block_table, const int32_t* seq_lens,
+                                  float scale, int32_t window, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /* Bound, in microseconds, on how long a workgroup that shares the split-KV
  * merge waits for the last segment of its unit (process-wide; default 200;

@@ -15,9 +15,11 @@ from .attention import (  # noqa: F401
     HND,
     NHD,
     decode_attention,
+    decode_attention_varlen,
     gather_kv,
     key_bounds,
     merge_states,
+    query_maps,
     segment_state,
     split_decode_attention,
 )

@@ -142,6 +142,69 @@ def decode_attention(
     return out
 
 
+def query_maps(q_start: Sequence[int], seq_lens: Sequence[int]) -> tuple[np.ndarray, np.ndarray]:
+    """Per packed query token: its request and its K length.
+
+    ``RocmOctaveMetadataBuilder._fill_query_maps`` (octave page): the
+    tokens of request ``s`` are ``q_start[s] .. q_start[s + 1] - 1``; query
+    ``i`` of a request with ``q_len`` queries and ``seq_len`` tokens attends
+    to K length ``seq_len - q_len + i + 1``, and padding (``seq_len`` 0)
+    gets K length 0.  Tokens before ``q_start[0]`` belong to no request
+    (request -1, K length 0).
+    """
+    S = len(q_start) - 1
+    T = int(q_start[S])
+    q_to_req = np.full(T, -1, dtype=np.int64)
+    q_to_klen = np.zeros(T, dtype=np.int64)
+    for s in range(S):
+        a, b = int(q_start[s]), int(q_start[s + 1])
+        q_len, L = b - a, int(seq_lens[s])
+        for i in range(q_len):
+            q_to_req[a + i] = s
+            q_to_klen[a + i] = max(0, L - q_len + i + 1) if L > 0 else 0
+    return q_to_req, q_to_klen
+
+
+def decode_attention_varlen(
+    q: np.ndarray,
+    q_start: Sequence[int],
+    kv: np.ndarray,
+    block_table: np.ndarray,
+    seq_lens: Sequence[int],
+    scale: float,
+    window: int,
+    layout: int,
+) -> np.ndarray:
+    """Reference output ``[T, Hq, D]`` in fp64 for packed queries with a
+    query count per request (mixed decode and speculative verify).
+
+    Token ``t`` of request ``r = q_to_req[t]`` with K length ``k =
+    q_to_klen[t]`` (``query_maps``) sees keys ``lo .. k - 1`` of its
+    request, ``lo = 0`` or, with a window ``W > 0``, ``max(0, k - W)``
+    (the window ends at the token itself: ``plan_prefill``, rdna_hip page).
+    Tokens with K length 0 output zeros.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    T, Hq, D = q.shape
+    Hkv = kv.shape[1] if layout == HND else kv.shape[2]
+    if Hq % Hkv:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    G = Hq // Hkv
+    q_to_req, q_to_klen = query_maps(q_start, seq_lens)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for t in range(T):
+        r, k = int(q_to_req[t]), int(q_to_klen[t])
+        if r < 0 or k <= 0:
+            continue
+        lo = max(0, k - window) if window > 0 else 0
+        for kvh in range(Hkv):
+            K, V = gather_kv(kv, layout, block_table[r], kvh, range(lo, k))
+            for g in range(G):
+                h = kvh * G + g
+                out[t, h] = _softmax_attend(q[t, h], K, V, scale)
+    return out
+
+
 def segment_state(
     qrow: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float
 ) -> tuple[np.ndarray, float, float]:

@@ -22,6 +22,7 @@ __all__ = [
     "PadError", "pad_shape", "pad_plan", "lib", "LIB_PATH", "load_library",
     "pad_abi_version", "pad_status_string", "pad_decode_attn_plan",
     "pad_decode_attn_workspace_size", "pad_decode_attn_workspace_init", "pad_decode_attn",
+    "pad_decode_attn_varlen",
     "pad_set_merge_wait", "pad_calib_gather_read", "pad_calib_stream_read",
     "make_shape", "Workspace",
 ]
@@ -105,6 +106,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.pad_calib_stream_read.restype = ctypes.c_int
     L.pad_calib_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_void_p]
+    L.pad_decode_attn_varlen.restype = ctypes.c_int
+    L.pad_decode_attn_varlen.argtypes = [
+        P(pad_shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+    ]
     return L
 
 
@@ -276,6 +282,66 @@ def pad_decode_attn(
         ctypes.c_float(scale), ctypes.c_int32(window), ctypes.c_void_p(out.data_ptr()),
         ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(_stream_ptr(stream)),
     ), "pad_decode_attn")
+    return out
+
+
+def pad_decode_attn_varlen(
+    q: torch.Tensor,
+    q_start: torch.Tensor,
+    kv_cache: torch.Tensor,
+    block_table: torch.Tensor,
+    seq_lens: torch.Tensor,
+    scale: float,
+    window: int,
+    out: torch.Tensor,
+    *,
+    max_query_len: int = 8,
+    layout: int = PAD_HND,
+    workspace: torch.Tensor | None = None,
+    max_seq_len: int = 0,
+    num_segments: int = 0,
+    path: int = PAD_PATH_AUTO,
+    schedule: int = PAD_SCHED_AUTO,
+    stream=None,
+) -> torch.Tensor:
+    """Decode attention with a query count per sequence (include/pad_attn.h).
+
+    ``q`` and ``out`` are packed ``[T, Hq, D]``; sequence ``s`` owns rows
+    ``q_start[s] .. q_start[s + 1] - 1`` (``q_start``: device int32,
+    ``S + 1`` entries, never read on the host).  ``max_query_len`` bounds
+    every per-sequence count (it sizes the plan and the workspace).
+    """
+    for name, t in (("q", q), ("q_start", q_start), ("kv_cache", kv_cache), ("block_table", block_table),
+                    ("seq_lens", seq_lens), ("out", out)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must be packed [T, Hq, D] tensors of one dtype")
+    S = block_table.shape[0]
+    if q_start.dtype != torch.int32 or q_start.shape != (S + 1,):
+        raise ValueError("q_start must be int32 with one entry per sequence plus one")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or seq_lens.shape != (S,):
+        raise ValueError("block_table and seq_lens must be int32, one row / entry per sequence")
+    T, Hq, D = q.shape
+    q_like = torch.empty((S, max_query_len, Hq, D), dtype=q.dtype, device="meta")
+    shape = make_shape(q_like, kv_cache, block_table, layout, max_seq_len=max_seq_len,
+                       num_segments=num_segments, path=path, schedule=schedule)
+    if workspace is None:
+        dev = q.device.index
+        ws = _default_ws.setdefault(dev, Workspace(q.device)).get(shape)
+    else:
+        ws = workspace
+    ws_ptr = ws.data_ptr() if ws is not None else 0
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib.pad_decode_attn_varlen(
+        ctypes.byref(shape), ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(q_start.data_ptr()),
+        ctypes.c_void_p(kv_cache.data_ptr()), ctypes.c_void_p(block_table.data_ptr()),
+        ctypes.c_void_p(seq_lens.data_ptr()), ctypes.c_float(scale), ctypes.c_int32(window),
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes),
+        ctypes.c_void_p(_stream_ptr(stream)),
+    ), "pad_decode_attn_varlen")
     return out
 
 

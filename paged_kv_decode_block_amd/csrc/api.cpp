@@ -98,10 +98,14 @@ pad_status pad_decode_attn_workspace_init(void* workspace, size_t bytes, void* s
   return pad::launch_zero(workspace, bytes / 4, stream) == 0 ? PAD_OK : PAD_EHIP;
 }
 
-pad_status pad_decode_attn(const pad_shape* shape, const void* q, const void* kv_cache,
-                           const int32_t* block_table, const int32_t* seq_lens, float scale,
-                           int32_t window, void* out, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// One decode launch; q_start is null for the uniform [S, M, Hq, D] layout.
+pad_status decode(const pad_shape* shape, const void* q, const int32_t* q_start, const void* kv_cache,
+                  const int32_t* block_table, const int32_t* seq_lens, float scale, int32_t window, void* out,
+                  void* workspace, size_t workspace_bytes, void* stream) {
   if (!shape) return PAD_EINVAL;
   if (!std::isfinite(scale)) return PAD_EINVAL;
   pad::Plan p;
@@ -118,6 +122,7 @@ pad_status pad_decode_attn(const pad_shape* shape, const void* q, const void* kv
   const int64_t D = shape->head_size, P = shape->page_size, H = shape->num_kv_heads;
   pad::Params pr{};
   pr.q = q;
+  pr.q_start = q_start;
   pr.kv = kv_cache;
   pr.block_table = block_table;
   pr.seq_lens = seq_lens;
@@ -152,6 +157,27 @@ pad_status pad_decode_attn(const pad_shape* shape, const void* q, const void* kv
   pr.merge_wait_ticks = g_merge_wait_ticks.load();
   pr.scale_log2 = float(double(scale) * 1.4426950408889634);  // log2(e)
   return pad::launch_decode(p, pr, shape->dtype, shape->head_size, stream) == 0 ? PAD_OK : PAD_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+pad_status pad_decode_attn(const pad_shape* shape, const void* q, const void* kv_cache,
+                           const int32_t* block_table, const int32_t* seq_lens, float scale,
+                           int32_t window, void* out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return decode(shape, q, nullptr, kv_cache, block_table, seq_lens, scale, window, out, workspace,
+                workspace_bytes, stream);
+}
+
+pad_status pad_decode_attn_varlen(const pad_shape* shape, const void* q, const int32_t* q_start,
+                                  const void* kv_cache, const int32_t* block_table, const int32_t* seq_lens,
+                                  float scale, int32_t window, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (shape && shape->num_seqs > 0 && (!q_start || !aligned(q_start, 4))) return PAD_EINVAL;
+  return decode(shape, q, q_start, kv_cache, block_table, seq_lens, scale, window, out, workspace,
+                workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -76,6 +76,26 @@ __device__ __forceinline__ T* out_row(const Params& p, T* out_s, int kvh, int ru
   return out_s + (int64_t(m) * p.num_q_heads + kvh * p.group + gq) * D;
 }
 
+// Query tokens of sequence s (at most query_len) and the index of its first
+// token in q and out: the uniform layout, or the packed one whose tokens
+// of sequence s start at q_start[s] (per-request query counts, as the
+// query maps of the octave page's metadata builder give them).  Counts
+// outside [0, query_len] are clamped into it.
+struct SeqQ {
+  int m, first;
+};
+__device__ __forceinline__ SeqQ seq_queries(const Params& p, int s) {
+  if (p.q_start == nullptr) return SeqQ{p.query_len, s * p.query_len};
+  const int a = p.q_start[s];
+  return SeqQ{min(max(p.q_start[s + 1] - a, 0), p.query_len), a};
+}
+
+// Output rows of sequence s.
+template <typename T>
+__device__ __forceinline__ T* seq_out(const Params& p, int s, int D) {
+  return static_cast<T*>(p.out) + int64_t(seq_queries(p, s).first) * p.num_q_heads * D;
+}
+
 // ---- split-KV merge ----
 // The merged output of a unit is rows x D floats, cut into items (row r,
 // four head-dim columns d4): item = r * (D / 4) + d4.  Merge slice `slice`
@@ -286,7 +306,7 @@ template <typename T, int D, int NT>
 __device__ __forceinline__ void arrive_and_merge(const Params& p, int* flags, int s, int kvh, int rg, int row0,
                                                  int wg_rows, int n_live) {
   const int tid = threadIdx.x;
-  T* out_s = static_cast<T*>(p.out) + int64_t(s) * p.query_len * p.num_q_heads * D;
+  T* out_s = seq_out<T>(p, s, D);
   const int64_t slot0 = (int64_t(s) * p.num_kv_heads + kvh) * p.nseg;
   int* ctl = p.ws_cnt + ((int64_t(s) * p.num_kv_heads + kvh) * p.row_groups + rg) * p.merge_slices * kCtlStride;
   int* sm_flag = flags;
@@ -345,7 +365,7 @@ __device__ __forceinline__ void arrive_and_merge(const Params& p, int* flags, in
 
 template <typename T, int D>
 __device__ __forceinline__ void zero_rows(const Params& p, int s, int kvh, int row0, int nrows, int nthreads) {
-  T* out_s = static_cast<T*>(p.out) + int64_t(s) * p.query_len * p.num_q_heads * D;
+  T* out_s = seq_out<T>(p, s, D);
   const int items = nrows * (D / 8);
   for (int it = threadIdx.x; it < items; it += nthreads) {
     const int r = it / (D / 8), d8 = it % (D / 8);
@@ -366,9 +386,9 @@ __device__ __forceinline__ int clamped_len(const Params& p, int s) {
   return min(p.seq_lens[s], p.max_blocks * p.page_size);
 }
 
-__device__ __forceinline__ SegSplit split_of(const Params& p, int L) {
+__device__ __forceinline__ SegSplit split_of(const Params& p, int L, int M) {
   SegSplit r;
-  const int k_lo = p.window > 0 ? max(0, L - p.query_len - p.window + 1) : 0;
+  const int k_lo = p.window > 0 ? max(0, L - M - p.window + 1) : 0;
   r.t_lo = k_lo >> 4;
   r.t_hi = (L + 15) >> 4;
   const int n_tiles = r.t_hi - r.t_lo;
@@ -384,7 +404,8 @@ __device__ __forceinline__ SegSplit split_of(const Params& p, int L) {
 // order) and, within a sequence, unit-major so the segments of a unit run
 // together and its merge helpers wait little.  An item's work does not
 // depend on which workgroup takes it, so results stay bitwise the same.
-// Sequences of length <= 0 get one item per unit (its zero output).
+// Sequences of length <= 0 get one item per unit (its zero output), those
+// without query tokens none.
 // Every workgroup ends with one failed take; the last of those resets the
 // queue for the next launch.
 template <typename Body>
@@ -418,9 +439,11 @@ __device__ __forceinline__ void persistent_loop(const Params& p, unsigned char* 
   __syncthreads();
   // Items per rank, then an exclusive prefix (wave 0: lanes own
   // contiguous chunks of ranks).
+  // A sequence with no query token has no item.
   for (int r = tid; r < S; r += nt) {
-    const int L = sm_len[sm_order[r]];
-    sm_cnt[r] = L <= 0 ? units : units * split_of(p, L).n_live;
+    const int s = sm_order[r];
+    const int L = sm_len[s], M = seq_queries(p, s).m;
+    sm_cnt[r] = M == 0 ? 0 : (L <= 0 ? units : units * split_of(p, L, M).n_live);
   }
   __syncthreads();
   if (tid < 64) {
@@ -463,7 +486,7 @@ __device__ __forceinline__ void persistent_loop(const Params& p, unsigned char* 
     const int s = sm_order[lo];
     const int local = item - sm_pref[lo];
     const int L = clamped_len(p, s);
-    const int per_unit = L <= 0 ? 1 : split_of(p, L).n_live;
+    const int per_unit = L <= 0 ? 1 : split_of(p, L, seq_queries(p, s).m).n_live;
     const int unit = local / per_unit, seg = local % per_unit;
     body(s, unit % p.num_kv_heads, unit / p.num_kv_heads, seg);
     __syncthreads();  // LDS is reused by the next item

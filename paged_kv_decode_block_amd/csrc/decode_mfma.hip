@@ -111,7 +111,7 @@ __device__ __forceinline__ void finish(const Params& p, unsigned char* lds, int 
     return a;
   };
 
-  T* out_s = static_cast<T*>(p.out) + int64_t(s) * p.query_len * p.num_q_heads * D;
+  T* out_s = seq_out<T>(p, s, D);
   if (n_live == 1) {
     for (int it = tid; it < wg_rows * (D / 4); it += NT) {
       const int r = it / (D / 4), d4 = it % (D / 4);
@@ -150,9 +150,12 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 4, c = lane & 15;
+  const SeqQ sq = seq_queries(p, s);
+  const int M = sq.m;
+  const int rows = p.group * M;  // this sequence's query rows
   const int row0 = rg * RT * 16;
-  const int wg_rows = min(RT * 16, p.rows - row0);
-  const int M = p.query_len;
+  const int wg_rows = min(RT * 16, rows - row0);
+  if (wg_rows <= 0) return;  // no query token, or a row group past this sequence's rows
 
   const int L = clamped_len(p, s);
   if (L <= 0) {
@@ -160,7 +163,7 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
     return;
   }
   const int k_lo = p.window > 0 ? max(0, L - M - p.window + 1) : 0;
-  const SegSplit sp = split_of(p, L);
+  const SegSplit sp = split_of(p, L, M);
   const int t_hi = sp.t_hi, seg_tiles = sp.seg_tiles, n_live = sp.n_live;
   if (seg >= n_live) return;
   const int ts = sp.t_lo + seg * seg_tiles, te = min(ts + seg_tiles, t_hi);
@@ -176,11 +179,11 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int ru = row0 + rt * 16 + c;
-    if (ru < p.rows) {
+    if (ru < rows) {
       const int m = ru / p.group, gq = ru % p.group;
       qpos_r[rt] = L - M + m;
       lo_r[rt] = p.window > 0 ? max(0, qpos_r[rt] - p.window + 1) : 0;
-      const T* qrow = Q + ((int64_t(s) * M + m) * p.num_q_heads + kvh * p.group + gq) * D;
+      const T* qrow = Q + ((int64_t(sq.first) + m) * p.num_q_heads + kvh * p.group + gq) * D;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) qop[rt][kc] = *reinterpret_cast<const i32x4*>(qrow + 32 * kc + 8 * g);
     } else {
@@ -494,8 +497,10 @@ __global__ __launch_bounds__(kDotWaves * 64) void decode_dot_kernel(Params p) {
   const int s = blockIdx.y;
   const int kvh = blockIdx.x % p.num_kv_heads;
   const int seg = blockIdx.x / p.num_kv_heads;
-  const int rows = p.rows;  // <= kDotRows
-  const int M = p.query_len;
+  const SeqQ sq = seq_queries(p, s);
+  const int M = sq.m;
+  const int rows = p.group * M;  // <= kDotRows
+  if (rows == 0) return;
 
   // Lengths past the block table's capacity are clamped to it.
   const int L = min(p.seq_lens[s], p.max_blocks * p.page_size);
@@ -524,7 +529,7 @@ __global__ __launch_bounds__(kDotWaves * 64) void decode_dot_kernel(Params p) {
       const int m = r / p.group, gq = r % p.group;
       qpos_r[r] = L - M + m;
       lo_r[r] = p.window > 0 ? max(0, qpos_r[r] - p.window + 1) : 0;
-      const T* qrow = Q + ((int64_t(s) * M + m) * p.num_q_heads + kvh * p.group + gq) * D;
+      const T* qrow = Q + ((int64_t(sq.first) + m) * p.num_q_heads + kvh * p.group + gq) * D;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) q[r][kc] = *reinterpret_cast<const i32x4*>(qrow + 32 * kc + 8 * g);
     } else {

@@ -9,11 +9,13 @@ namespace pad {
 
 // Everything a decode-attention workgroup needs; passed by value.
 struct Params {
-  const void* q;              // [S, M, Hq, D]
+  const void* q;              // [S, M, Hq, D], or packed [T, Hq, D] with q_start
+  const int32_t* q_start;     // packed layout: first query token of each sequence
+                              // [S + 1] (device); null: uniform M = query_len
   const void* kv;             // packed K+V cache (HND or NHD)
   const int32_t* block_table; // [S, max_blocks]
   const int32_t* seq_lens;    // [S]
-  void* out;                  // [S, M, Hq, D]
+  void* out;                  // same layout as q
   int32_t* ws_cnt;            // merge control [S, Hkv, row_groups, merge_slices]
   float* ws_ml;               // partial (m, l) [S, Hkv, nseg, rows, 2]
   float* ws_acc;              // partial acc     [S, Hkv, nseg, rows, D]

@@ -284,3 +284,75 @@ def pin_padding(attn, rng):
     assert np.all(out[1] == 0)
     sub = attn(q[[0, 2]], kv, table[[0, 2]], lens[[0, 2]], 0.5, 0, HND)
     assert np.array_equal(out[[0, 2]], sub)
+
+
+# ---- per-request query counts (packed queries) ----
+
+def pin_varlen_maps(maps):
+    """Query maps of a hand-worked batch: q_start [0, 1, 4, 4, 6] over
+    lengths [10, 3, 5, 0].  Request 0 has one query at position 9 (K length
+    10); request 1 has three queries at positions 0, 1, 2 (K lengths 1, 2,
+    3); request 2 has none; request 3 is padding (K length 0)."""
+    req, klen = maps([0, 1, 4, 4, 6], [10, 3, 5, 0])
+    assert list(req) == [0, 1, 1, 1, 3, 3], req
+    assert list(klen) == [10, 1, 2, 3, 0, 0], klen
+
+
+def varlen_brute_force(q, q_start, kv, table, lens, scale, window, layout):
+    """Pure-Python loop over packed tokens: token i of request s (with
+    M_s = q_start[s + 1] - q_start[s] tokens) sits at position
+    p = L_s - M_s + i and sees key t iff t <= p and (window == 0 or
+    p - t < window)."""
+    T, Hq, D = q.shape
+    P = kv.shape[2] if layout == HND else kv.shape[1]
+    Hkv = kv.shape[1] if layout == HND else kv.shape[2]
+    G = Hq // Hkv
+    out = np.zeros_like(q)
+    for s in range(len(q_start) - 1):
+        a, b = int(q_start[s]), int(q_start[s + 1])
+        L, Ms = int(lens[s]), b - a
+        for i in range(Ms):
+            p = L - Ms + i
+            for h in range(Hq):
+                kvh = h // G
+                zs, vs = [], []
+                for t in range(L):
+                    if not (t <= p and (window == 0 or p - t < window)):
+                        continue
+                    blk, o = int(table[s, t // P]), t % P
+                    sl = kv[blk, kvh, o] if layout == HND else kv[blk, o, kvh]
+                    zs.append(scale * sum(float(q[a + i, h, d]) * float(sl[0, d]) for d in range(D)))
+                    vs.append(sl[1])
+                if not zs:
+                    continue
+                mx = max(zs)
+                ws = [math.exp(z - mx) for z in zs]
+                out[a + i, h] = sum(w * v for w, v in zip(ws, vs)) / sum(ws)
+    return out
+
+
+def pin_varlen_brute_force(varlen, rng):
+    """Mixed counts (including a request with no query, one with more
+    queries than keys, and padding) against the brute-force loop, with and
+    without a window, in both layouts."""
+    lens = (37, 3, 20, 0, 16)
+    counts = (3, 5, 0, 2, 1)
+    q_start = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    _, kv, table, lens = tiny_case(rng, S=5, M=1, lens=lens)
+    q = rng.standard_normal((int(q_start[-1]), 4, 8))
+    for layout, kvl in ((HND, kv), (NHD, to_nhd(kv))):
+        for window in (0, 4):
+            got = varlen(q, q_start, kvl, table, lens, 0.3, window, layout)
+            want = varlen_brute_force(q, q_start, kvl, table, lens, 0.3, window, layout)
+            assert np.max(np.abs(got - want)) < 1e-12
+
+
+def pin_varlen_uniform(varlen, attn, rng):
+    """Equal counts reproduce the uniform [S, M, Hq, D] call row for row."""
+    q, kv, table, lens = tiny_case(rng, S=2, M=3, lens=(37, 2))
+    S, M, Hq, D = q.shape
+    q_start = np.arange(S + 1) * M
+    for window in (0, 5):
+        got = varlen(q.reshape(S * M, Hq, D), q_start, kv, table, lens, 0.7, window, HND)
+        want = attn(q, kv, table, lens, 0.7, window, HND).reshape(S * M, Hq, D)
+        assert np.max(np.abs(got - want)) < 1e-12

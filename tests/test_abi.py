@@ -300,3 +300,19 @@ def test_calibration_validation():
     assert L.pad_calib_stream_read(P(0x1000), ctypes.c_size_t(24), 256, P(0x1000), None) == pad.PAD_EINVAL
     assert L.pad_calib_stream_read(P(0x1000), ctypes.c_size_t(32), 0, P(0x1000), None) == pad.PAD_EINVAL
     assert L.pad_calib_stream_read(P(0x1008), ctypes.c_size_t(32), 256, P(0x1000), None) == pad.PAD_EINVAL
+
+
+def test_varlen_validation():
+    """The packed-query entry point needs its q_start array (checked on the
+    host before any launch); an empty batch needs nothing."""
+    P = ctypes.c_void_p
+    L = pad.lib
+
+    def v(sh, qs):
+        return L.pad_decode_attn_varlen(ctypes.byref(sh), P(0x1000), P(qs), P(0x1000), P(0x1000), P(0x1000),
+                                        ctypes.c_float(0.1), 0, P(0x1000), P(0), ctypes.c_size_t(0), None)
+
+    assert v(shape(num_seqs=0), 0) == pad.PAD_OK
+    assert v(shape(), 0) == pad.PAD_EINVAL  # missing q_start
+    assert v(shape(), 0x1002) == pad.PAD_EINVAL  # misaligned q_start
+    assert v(shape(query_len=9), 0x1000) == pad.PAD_EUNSUPPORTED  # bound on the per-sequence counts

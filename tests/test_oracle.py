@@ -131,3 +131,15 @@ def test_golden_merge():
     g = _load("merge_example.json")
     parts = [(np.asarray(a, dtype=np.float64), -math.inf if m == "-inf" else m, l) for a, m, l in g["partials"]]
     np.testing.assert_allclose(oracle.merge_states(parts), g["expected"], rtol=0, atol=1e-15)
+
+
+def test_varlen_maps():
+    pins.pin_varlen_maps(oracle.query_maps)
+
+
+def test_varlen_brute_force(rng):
+    pins.pin_varlen_brute_force(oracle.decode_attention_varlen, rng)
+
+
+def test_varlen_uniform(rng):
+    pins.pin_varlen_uniform(oracle.decode_attention_varlen, oracle.decode_attention, rng)

@@ -24,6 +24,10 @@ MUTATIONS = [
     ("nhd_axes_swapped", "return kv[block, offset, kv_head]", "return kv[block, kv_head, offset]"),
     ("page_offset_wrong", "offsets = keys % P", "offsets = (keys // P) % P"),
     ("first_key_dropped", "K, V = K_all[lo : hi + 1], V_all[lo : hi + 1]", "K, V = K_all[lo + 1 : hi + 1], V_all[lo + 1 : hi + 1]"),
+    ("varlen_klen_off_by_one", "max(0, L - q_len + i + 1) if L > 0", "max(0, L - q_len + i) if L > 0"),
+    ("varlen_window_one_too_few", "lo = max(0, k - window) if window > 0 else 0", "lo = max(0, k - window + 1) if window > 0 else 0"),
+    ("varlen_request_shifted", "K, V = gather_kv(kv, layout, block_table[r], kvh, range(lo, k))",
+     "K, V = gather_kv(kv, layout, block_table[max(r - 1, 0)], kvh, range(lo, k))"),
 ]
 
 
@@ -49,6 +53,9 @@ def _all_pins(mod):
     yield lambda: pins.pin_sdpa(mod.decode_attention, rng)
     yield lambda: pins.pin_padding(mod.decode_attention, rng)
     yield lambda: pins.pin_brute_force(mod.decode_attention, rng)
+    yield lambda: pins.pin_varlen_maps(mod.query_maps)
+    yield lambda: pins.pin_varlen_uniform(mod.decode_attention_varlen, mod.decode_attention, rng)
+    yield lambda: pins.pin_varlen_brute_force(mod.decode_attention_varlen, rng)
 
 
 @pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
