@@ -142,7 +142,9 @@ typedef struct pad_plan {
   int32_t persistent;        /* 1: grid_x workgroups take the (sequence, kv head,
                                 segment) items from a queue in the workspace;
                                 0: one workgroup per item                        */
-  int32_t reserved;
+  int32_t workspace_segments; /* segment slots per unit the workspace is sized for:
+                                 a bound on num_segments over every window, so
+                                 workspace_bytes is the same for every window  */
   uint64_t workspace_bytes;  /* bytes pad_decode_attn needs for this call         */
 } pad_plan;
 

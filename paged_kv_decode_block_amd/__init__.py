@@ -67,7 +67,7 @@ class pad_plan(ctypes.Structure):
         ("grid_y", ctypes.c_int32),
         ("merge_slices", ctypes.c_int32),
         ("persistent", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("workspace_segments", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_uint64),
     ]
 
@@ -180,7 +180,7 @@ def pad_decode_attn_plan(shape: pad_shape, window: int = 0, num_cus: int | None 
     plan = pad_plan()
     _check(lib.pad_decode_attn_plan(ctypes.byref(shape), int(window), int(num_cus), ctypes.byref(plan)),
            "pad_decode_attn_plan")
-    return {name: getattr(plan, name) for name, _ in pad_plan._fields_ if name != "reserved"}
+    return {name: getattr(plan, name) for name, _ in pad_plan._fields_}
 
 
 def pad_decode_attn_workspace_size(shape: pad_shape) -> int:

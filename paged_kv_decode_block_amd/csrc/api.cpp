@@ -76,7 +76,7 @@ pad_status pad_decode_attn_plan(const pad_shape* shape, int32_t window, int32_t 
   plan->grid_y = p.grid_y;
   plan->merge_slices = p.merge_slices;
   plan->persistent = p.persistent;
-  plan->reserved = 0;
+  plan->workspace_segments = p.ws_nseg;
   plan->workspace_bytes = p.ws_bytes;
   return PAD_OK;
 }
@@ -84,8 +84,8 @@ pad_status pad_decode_attn_plan(const pad_shape* shape, int32_t window, int32_t 
 pad_status pad_decode_attn_workspace_size(const pad_shape* shape, size_t* bytes) {
   if (!shape || !bytes) return PAD_EINVAL;
   pad::Plan p;
-  // Without a window the key span is largest, so this plan needs the most
-  // segments and therefore the most workspace of any window.
+  // The planner sizes the workspace for a segment bound that does not
+  // depend on the window, so any window's plan gives the same bytes.
   const pad_status st = pad::make_plan(*shape, 0, device_cus(), &p);
   if (st != PAD_OK) return st;
   *bytes = p.ws_bytes;

@@ -64,18 +64,14 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
     p.waves = waves_for(sh.head_size, p.row_tiles);
   }
 
-  // Keys one unit may have to read: the whole table bound, or the window
-  // span (window + M - 1 keys) plus one tile of alignment slack.
+  // Tiles one unit may have to read: the whole length bound, or the window
+  // span (window + M - 1 keys) plus one tile of alignment slack -- never
+  // more than the whole bound, so no window plans more than window 0.
   const int64_t max_len = sh.max_seq_len ? sh.max_seq_len : table_keys;
-  int64_t span = max_len;
-  int64_t span_tiles;
-  if (window > 0) {
-    span = std::min<int64_t>(max_len, int64_t(window) + sh.query_len - 1);
-    span_tiles = ceil_div(span, kTileKeys) + 1;
-  } else {
-    span_tiles = ceil_div(span, kTileKeys);
-  }
-  span_tiles = std::max<int64_t>(1, span_tiles);
+  const int64_t all_tiles = std::max<int64_t>(1, ceil_div(max_len, kTileKeys));
+  int64_t span_tiles = all_tiles;
+  if (window > 0)
+    span_tiles = std::min(all_tiles, ceil_div(int64_t(window) + sh.query_len - 1, kTileKeys) + 1);
 
   const int64_t units = int64_t(sh.num_seqs) * sh.num_kv_heads * p.row_groups;
   // One workgroup per CU: its 4 waves keep enough loads in flight.
@@ -141,9 +137,37 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
     p.grid_y = std::max(1, sh.num_seqs);
   }
 
-  if (p.nseg > 1 || p.persistent) {
+  // The workspace holds partial slots for a segment count that bounds what
+  // any window plans for this shape (forced, the static grid's fill, the
+  // persistent grid's 1 MiB segments and the LDS block-id bound, all at
+  // the window-free span), so one pad_decode_attn_workspace_size serves
+  // every call of the shape; the slot stride of a call is its own count.
+  int64_t ws_nseg;
+  {
+    const bool may_persist = sh.schedule == PAD_SCHED_PERSISTENT ||
+                             (sh.schedule == PAD_SCHED_AUTO && sh.num_seqs > 1 && sh.num_seqs <= kPersistMaxSeqs);
+    const bool may_grid = sh.schedule != PAD_SCHED_PERSISTENT;
+    if (sh.num_segments > 0) {
+      ws_nseg = sh.num_segments;
+    } else {
+      const int64_t target = sh.num_seqs > 1 ? 2 * slots : slots;
+      ws_nseg = may_grid ? std::max<int64_t>(1, target / std::max<int64_t>(1, units)) : 1;
+      if (may_persist) ws_nseg = std::max(ws_nseg, ceil_div(all_tiles, seg_persist));
+    }
+    ws_nseg = std::min(ws_nseg, std::min<int64_t>(all_tiles, kMaxSegments));
+    ws_nseg = std::max<int64_t>(ws_nseg, ceil_div(ceil_div(table_keys, kTileKeys), kMaxSegTiles));
+    ws_nseg = std::max<int64_t>(ws_nseg, p.nseg);
+  }
+  p.ws_nseg = int(ws_nseg);
+  // Whether the window-free span plans the persistent grid: a window only
+  // shortens the span, so no window plans it otherwise.
+  const bool persist_any =
+      sh.schedule == PAD_SCHED_PERSISTENT ||
+      (sh.schedule == PAD_SCHED_AUTO && sh.num_seqs > 1 && sh.num_seqs <= kPersistMaxSeqs &&
+       units * std::max<int64_t>(1, sh.num_segments > 0 ? sh.num_segments : ceil_div(all_tiles, seg_persist)) > slots);
+  if (ws_nseg > 1 || persist_any) {
     const size_t S = size_t(sh.num_seqs), H = size_t(sh.num_kv_heads);
-    const size_t slot_rows = S * H * size_t(p.nseg) * size_t(rows);
+    const size_t slot_rows = S * H * size_t(ws_nseg) * size_t(rows);
     // Slices: about kSliceBytes of partial accumulators each, limited by
     // the segments (each merging workgroup must have arrived) and by the
     // control words the counter prefix holds.
@@ -166,7 +190,7 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
     p.merge_slices = int(std::max<int64_t>(1, k));
     p.ws_counters = 0;
     p.ws_ml = kCounterBytes;
-    if (p.nseg > 1) {
+    if (ws_nseg > 1) {
       p.ws_acc = p.ws_ml + align_up(slot_rows * 2 * sizeof(float));
       p.ws_bytes = p.ws_acc + align_up(slot_rows * size_t(sh.head_size) * sizeof(float));
     } else {  // the work queue only: a single segment publishes no partial

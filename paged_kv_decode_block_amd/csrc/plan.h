@@ -65,6 +65,7 @@ struct Plan {
   int nseg;          // segments per (unit, row group)
   int seg_tiles;     // planned tiles per segment
   int merge_slices;  // slices the merged output is cut into (1..kMaxSlices)
+  int ws_nseg;       // segment slots the workspace holds (>= nseg, the same for every window)
   int persistent;    // 1: one workgroup per CU takes items from a queue
   int grid_x, grid_y;
   // Workspace layout (byte offsets; all 256-byte aligned): the counter

@@ -102,7 +102,9 @@ def test_plan_invariants(kw):
         # a fixed 1 MiB prefix of merge control words, then one (m, l) and one
         # acc slot per segment
         S, H, n = sh.num_seqs, sh.num_kv_heads, p["num_segments"]
-        want = (1 << 20) + _align(S * H * n * rows * 2 * 4) + _align(S * H * n * rows * sh.head_size * 4)
+        nw = p["workspace_segments"]
+        assert nw >= n
+        want = (1 << 20) + _align(S * H * nw * rows * 2 * 4) + _align(S * H * nw * rows * sh.head_size * 4)
         assert p["workspace_bytes"] == want
         # about 32 KiB of partial accumulators per merge slice, at most 32
         # slices and no more than segments; control words fit the prefix
@@ -316,3 +318,29 @@ def test_varlen_validation():
     assert v(shape(), 0) == pad.PAD_EINVAL  # missing q_start
     assert v(shape(), 0x1002) == pad.PAD_EINVAL  # misaligned q_start
     assert v(shape(query_len=9), 0x1000) == pad.PAD_EUNSUPPORTED  # bound on the per-sequence counts
+
+
+def test_workspace_serves_every_window():
+    """One workspace size per shape: every window's plan needs the same
+    bytes, with at least as many segment slots as it uses (seeded shapes,
+    forced and planned segment counts, all schedules)."""
+    import numpy as np
+
+    r = np.random.default_rng(11)
+    for _ in range(300):
+        D = int(r.choice([64, 128, 256, 512]))
+        Hkv = int(r.choice([1, 2, 4, 8]))
+        G = int(r.choice([1, 2, 4, 8, 16]))
+        M = int(r.integers(1, 9))
+        P = int(r.choice([16, 32, 48, 1056]))
+        sh = shape(num_seqs=int(r.choice([1, 2, 5, 65, 1100])), query_len=M, num_q_heads=G * Hkv, num_kv_heads=Hkv,
+                   head_size=D, page_size=P, max_blocks_per_seq=int(r.integers(1, 600)),
+                   num_segments=int(r.choice([0, 0, 1, 3, 16, 200])), schedule=int(r.choice([0, 1, 2])))
+        try:
+            base = pad.pad_decode_attn_workspace_size(sh)
+        except pad.PadError:
+            continue
+        for w in (0, 1, 5, 16, 17, 100, 511, 512, 4000, 10 ** 6):
+            p = plan(sh, w)
+            assert p["workspace_bytes"] == base, (sh.num_seqs, D, Hkv, G, M, P, w, p)
+            assert p["workspace_segments"] >= p["num_segments"]
