@@ -190,6 +190,16 @@ def time_calls(case, n_warm: int, n_timed: int, graph: bool = False, **kw):
     return start.elapsed_time(stop) / n_timed, pad.pad_decode_attn_plan(shape, case.window)
 
 
+def _blas_threads() -> int:
+    """Threads the oracle's BLAS calls may use (as the thread pools report)."""
+    try:
+        from threadpoolctl import threadpool_info
+
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def cpu_baseline(cfg: int, context: int, M: int, budget_s: float = 12.0) -> dict:
     """The fp64 oracle on the host, on a bounded sample of the workload."""
     import numpy as np
@@ -207,12 +217,7 @@ def cpu_baseline(cfg: int, context: int, M: int, budget_s: float = 12.0) -> dict
         el = time.perf_counter() - t0
         if el >= budget_s or calls >= 50:
             break
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = 1
+    cores = _blas_threads()
     gbs = effective_bytes(case) * calls / el / 1e9
     return {
         "value": round(gbs, 4),
@@ -237,6 +242,144 @@ def traffic_entry():
     return t.get("bytes_per_launch")
 
 
+def varlen_main(args) -> int:
+    """Mixed decode / speculative-verify batch through pad_decode_attn_varlen:
+    the batched workload's 64 sequences (plus one padded) with a seeded
+    query count of 1..4 each, queries packed, counts read on the device."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+
+    import paged_kv_decode_block_amd as pad
+
+    cfg, ctx, mmax = 5, 16384, 4
+    spec = wl.CONFIGS[cfg]
+    case = wl.config_case(cfg, ctx, mmax, device="cuda")
+    S = case.num_seqs
+    counts = torch.randint(1, mmax + 1, (S,), generator=torch.Generator().manual_seed(20261202)).tolist()
+    q = torch.cat([case.q[s, :n] for s, n in enumerate(counts)], dim=0).contiguous()
+    starts = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    q_start = torch.from_numpy(starts).to("cuda")
+    out = torch.empty_like(q)
+    eb = q.element_size()
+    lens = case.seq_lens.tolist()
+    nbytes = sum(L * spec.num_kv_heads * 2 * spec.head_size * eb + 2 * n * spec.num_q_heads * spec.head_size * eb
+                 for L, n in zip(lens, counts) if L > 0)
+    q_like = torch.empty((S, mmax, spec.num_q_heads, spec.head_size), dtype=q.dtype, device="meta")
+    shape = pad.make_shape(q_like, case.kv_cache, case.block_tables[0], case.layout)
+    ws = pad.Workspace(q.device).get(shape)
+
+    def call(i):
+        pad.pad_decode_attn_varlen(q, q_start, case.kv_cache, case.block_tables[0], case.seq_lens, case.scale,
+                                   case.window, out, max_query_len=mmax, layout=case.layout, workspace=ws)
+
+    ms = _event_time(call, args.warmup, args.steps)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+
+        kv64, table, lens64 = wl.compact(case)
+        q64 = wl.as_f64(q)
+        t0, done, moved = time.perf_counter(), 0, 0
+        while done < S and time.perf_counter() - t0 < 12.0:
+            a, b = int(starts[done]), int(starts[done + 1])
+            oracle.decode_attention_varlen(q64[a:b], [0, b - a], kv64, table[done:done + 1], lens64[done:done + 1],
+                                           case.scale, case.window, case.layout)
+            L = int(lens64[done])
+            if L > 0:
+                moved += L * spec.num_kv_heads * 2 * spec.head_size * eb + 2 * (b - a) * spec.num_q_heads * spec.head_size * eb
+            done += 1
+        el = time.perf_counter() - t0
+        cpu = {"value": round(moved / el / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
+               "sample": f"{done} of {S} sequences of the mixed batch, one varlen oracle call each, {el:.1f} s"}
+    line = {
+        "metric": "decode-attention effective HBM GB/s (K+V rows read + Q + O) and fraction of 8 TB/s",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": spec.dtype, "data": "synthetic",
+        "config": {"workload": f"mixed decode/verify batch: {S} sequences (one padded), bf16, D={spec.head_size}, "
+                               f"{spec.num_q_heads}/{spec.num_kv_heads} heads, page {spec.page_size}, lengths "
+                               f"512..{ctx}, per-sequence M in 1..{mmax} packed ({int(starts[-1])} query tokens)",
+                   "bytes_per_step": nbytes, "plan": pad.pad_decode_attn_plan(shape, case.window)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cache_write_main(args) -> int:
+    """The KV-cache write with a full-width rotation (the step before decode)
+    on one prefill-sized chunk of tokens of the default workload's shapes:
+    new keys and values land in shuffled slots of a 512 MiB pool and the
+    query rows are rotated in place."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+
+    import paged_kv_decode_block_amd as pad
+
+    spec = wl.CONFIGS[2]
+    T, Hq, Hkv, D = 16384, spec.num_q_heads, spec.num_kv_heads, spec.head_size
+    rd, max_pos = D, 32768
+    eb = 2
+    g = torch.Generator(device="cuda").manual_seed(20261202)
+    nb = POOL_BYTES // spec.block_bytes
+    kv = torch.empty((nb, Hkv, spec.page_size, 2, D), dtype=torch.bfloat16, device="cuda").normal_(generator=g)
+    key = torch.randn((T, Hkv, D), generator=g, device="cuda").to(torch.bfloat16)
+    val = torch.randn((T, Hkv, D), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((T, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+    slots = torch.randperm(nb * spec.page_size, generator=g, device="cuda")[:T].to(torch.int64)
+    pos = torch.randint(0, max_pos, (T,), generator=g, device="cuda", dtype=torch.int64)
+    inv = 10000.0 ** (-np.arange(rd // 2) * 2.0 / rd)
+    ang = np.arange(max_pos)[:, None] * inv[None, :]
+    tab = torch.from_numpy(np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)).to("cuda")
+    # bytes the step must move: key and value in, the K+V slots out, the
+    # rotated query rows in and out, and one cos/sin row per token
+    nbytes = 2 * T * Hkv * D * eb * 2 + 2 * T * Hq * rd * eb + T * rd * 4
+
+    def call(i):
+        pad.pad_rope_cache_write(key, val, kv, slots, q=q, positions=pos, cos_sin_cache=tab)
+
+    ms = _event_time(call, args.warmup, args.steps)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu:
+        from oracle import rope as orope
+
+        n = 256
+        f64 = lambda t: t[:n].to(torch.float64).cpu().numpy()  # noqa: E731
+        kv_small = np.zeros((n, Hkv, 1, 2, D))
+        t0, calls = time.perf_counter(), 0
+        while time.perf_counter() - t0 < 10.0 and calls < 20:
+            orope.cache_write(kv_small, wl.HND, f64(key), f64(val), np.arange(n), pos[:n].cpu().numpy(),
+                              tab.cpu().numpy(), rd, f64(q))
+            calls += 1
+        el = time.perf_counter() - t0
+        per_tok = nbytes / T
+        cpu = {"value": round(per_tok * n * calls / el / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
+               "kind": "oracle", "sample": f"{calls} oracle call(s) on the first {n} tokens, {el:.1f} s"}
+    line = {
+        "metric": "KV-cache write effective HBM GB/s (key, value, query rows, cos/sin in; cache slots, query rows out) "
+                  "and fraction of 8 TB/s",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"cache write: {T} tokens, bf16, D={D}, {Hq}/{Hkv} heads, page {spec.page_size}, HND, "
+                               f"rotation over all {rd} dims, shuffled slots in a {POOL_BYTES >> 20} MiB pool",
+                   "bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,11 +397,20 @@ def main() -> int:
                     help="kernel family (auto = the planner's choice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run device copies of COPY_BYTES (reference for HBM byte counters)")
+    ap.add_argument("--cache-write", action="store_true",
+                    help="time the KV-cache write with rotation (the step before decode) instead")
+    ap.add_argument("--varlen", action="store_true",
+                    help="time a mixed decode/verify batch through the per-sequence-count entry point instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the decode-attention path has no multi-GPU mode "
               f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
         return 2
+
+    if args.varlen:
+        return varlen_main(args)
+    if args.cache_write:
+        return cache_write_main(args)
 
     import torch
 

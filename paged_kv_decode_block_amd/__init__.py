@@ -22,7 +22,7 @@ __all__ = [
     "PadError", "pad_shape", "pad_plan", "lib", "LIB_PATH", "load_library",
     "pad_abi_version", "pad_status_string", "pad_decode_attn_plan",
     "pad_decode_attn_workspace_size", "pad_decode_attn_workspace_init", "pad_decode_attn",
-    "pad_decode_attn_varlen",
+    "pad_decode_attn_varlen", "pad_rope_cache_write", "pad_cache_shape",
     "pad_set_merge_wait", "pad_calib_gather_read", "pad_calib_stream_read",
     "make_shape", "Workspace",
 ]
@@ -72,6 +72,21 @@ class pad_plan(ctypes.Structure):
     ]
 
 
+class pad_cache_shape(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_size", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
+        ("rope_dim", ctypes.c_int32),
+        ("max_position", ctypes.c_int32),
+    ]
+
+
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     """Open a build of the library and declare its C signatures."""
     if not os.path.exists(path):
@@ -106,6 +121,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.pad_calib_stream_read.restype = ctypes.c_int
     L.pad_calib_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_void_p]
+    L.pad_rope_cache_write.restype = ctypes.c_int
+    L.pad_rope_cache_write.argtypes = [
+        P(pad_cache_shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+    ]
     L.pad_decode_attn_varlen.restype = ctypes.c_int
     L.pad_decode_attn_varlen.argtypes = [
         P(pad_shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -343,6 +363,60 @@ def pad_decode_attn_varlen(
         ctypes.c_void_p(_stream_ptr(stream)),
     ), "pad_decode_attn_varlen")
     return out
+
+
+def pad_rope_cache_write(
+    key: torch.Tensor,
+    value: torch.Tensor,
+    kv_cache: torch.Tensor,
+    slot_mapping: torch.Tensor,
+    *,
+    layout: int = PAD_HND,
+    q: torch.Tensor | None = None,
+    positions: torch.Tensor | None = None,
+    cos_sin_cache: torch.Tensor | None = None,
+    stream=None,
+) -> None:
+    """Store new tokens' K (rotated when a cos/sin table is given) and V in
+    their cache slots, and rotate ``q`` in place (include/pad_cache.h).
+
+    ``key``/``value`` ``[T, Hkv, D]``, ``q`` ``[T, Hq, D]``, ``slot_mapping``
+    and ``positions`` int64 ``[T]``, ``cos_sin_cache`` fp32
+    ``[max_position, rope_dim]`` (cos then sin).
+    """
+    tensors = [("key", key), ("value", value), ("kv_cache", kv_cache), ("slot_mapping", slot_mapping)]
+    tensors += [(n, t) for n, t in (("q", q), ("positions", positions), ("cos_sin_cache", cos_sin_cache)) if t is not None]
+    for name, t in tensors:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if key.dim() != 3 or value.shape != key.shape or key.dtype not in _DTYPE_CODE or kv_cache.dtype != key.dtype:
+        raise ValueError("key and value must be [T, Hkv, D] of the cache's dtype (float16 or bfloat16)")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (key.shape[0],):
+        raise ValueError("slot_mapping must be int64 [T]")
+    if layout == PAD_HND:
+        nb, Hkv, P, two, D = kv_cache.shape
+    else:
+        nb, P, Hkv, two, D = kv_cache.shape
+    if two != 2 or D != key.shape[2] or Hkv != key.shape[1]:
+        raise ValueError("kv_cache must hold packed (K, V) slots of key's heads and head size")
+    rope_dim, max_pos = 0, 0
+    if cos_sin_cache is not None:
+        if positions is None or positions.dtype != torch.int64 or positions.shape != (key.shape[0],):
+            raise ValueError("a cos/sin table needs int64 positions [T]")
+        if cos_sin_cache.dtype != torch.float32 or cos_sin_cache.dim() != 2:
+            raise ValueError("cos_sin_cache must be float32 [max_position, rope_dim]")
+        max_pos, rope_dim = cos_sin_cache.shape
+    if q is not None and (q.dim() != 3 or q.shape[0] != key.shape[0] or q.shape[2] != D or q.dtype != key.dtype):
+        raise ValueError("q must be [T, Hq, D] of key's dtype")
+    shape = pad_cache_shape(
+        num_tokens=key.shape[0], num_q_heads=q.shape[1] if q is not None else 0, num_kv_heads=Hkv, head_size=D,
+        page_size=P, num_blocks=nb, dtype=_DTYPE_CODE[key.dtype], layout=layout, rope_dim=rope_dim,
+        max_position=max_pos,
+    )
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)  # noqa: E731
+    _check(lib.pad_rope_cache_write(
+        ctypes.byref(shape), ptr(q), ptr(key), ptr(value), ptr(slot_mapping), ptr(positions), ptr(cos_sin_cache),
+        ptr(kv_cache), ctypes.c_void_p(_stream_ptr(stream))), "pad_rope_cache_write")
 
 
 def pad_calib_gather_read(kv_cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,

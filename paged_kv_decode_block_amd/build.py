@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpad_attn.so")
-SOURCES = ["decode_mfma.hip", "calib.hip", "plan.cpp", "api.cpp"]
+SOURCES = ["decode_mfma.hip", "cache_write.hip", "calib.hip", "plan.cpp", "api.cpp"]
 
 # Packed fp32 VALU ops are turned off for every HIP source (the host pass
 # reports the feature as unknown; that warning is harmless).

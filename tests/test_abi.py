@@ -344,3 +344,26 @@ def test_workspace_serves_every_window():
             p = plan(sh, w)
             assert p["workspace_bytes"] == base, (sh.num_seqs, D, Hkv, G, M, P, w, p)
             assert p["workspace_segments"] >= p["num_segments"]
+
+
+def test_cache_write_validation():
+    """Host checks of the cache write, before any launch."""
+    P = ctypes.c_void_p
+    L = pad.lib
+
+    def w(ptr=0x1000, pos=0x1000, tab=0x1000, **kw):
+        base = dict(num_tokens=4, num_q_heads=8, num_kv_heads=2, head_size=128, page_size=16, num_blocks=4,
+                    dtype=pad.PAD_BF16, layout=pad.PAD_HND, rope_dim=64, max_position=100)
+        base.update(kw)
+        sh = pad.pad_cache_shape(**base)
+        return L.pad_rope_cache_write(ctypes.byref(sh), P(ptr), P(ptr), P(ptr), P(ptr), P(pos), P(tab), P(ptr), None)
+
+    assert w(num_tokens=0) == pad.PAD_OK
+    assert w(head_size=96) == pad.PAD_EUNSUPPORTED
+    assert w(rope_dim=40) == pad.PAD_EUNSUPPORTED  # not a multiple of 16
+    assert w(rope_dim=256) == pad.PAD_EUNSUPPORTED  # wider than the head
+    assert w(num_q_heads=3) == pad.PAD_EINVAL
+    assert w(max_position=0) == pad.PAD_EINVAL
+    assert w(pos=0) == pad.PAD_EINVAL  # rotation without positions
+    assert w(ptr=0x1008) == pad.PAD_EINVAL  # misaligned tensors
+    assert w(dtype=5) == pad.PAD_EINVAL
