@@ -32,6 +32,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of one MI355X
 POOL_BYTES = 512 << 20
 COPY_BYTES = 256 << 20  # --copy-calibration: bytes read (and written) per copy
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_mfma_bf16_D128_Hq32_Hkv8_L32768_M4.json")
@@ -380,6 +381,55 @@ def cache_write_main(args) -> int:
     return 0
 
 
+def prefill_main(args) -> int:
+    """A prefill chunk through the same entry point: 256 new tokens over a
+    4096-key context, the default workload's shapes (1024 GQA-packed rows
+    per kv head in 16 row groups, each reading only the keys its tokens
+    reach).  Arithmetic intensity ~1000 flop/byte: bound by the matrix
+    cores, reported against the dense bf16 MFMA peak."""
+    import torch
+
+    import workloads as wl
+
+    import paged_kv_decode_block_amd as pad
+
+    cfg, context, M = 2, 4096, 256
+    spec = wl.CONFIGS[cfg]
+    L = context + M
+    case = wl.make_case(spec, [L], M, seed=20261202 + 7, device="cuda")
+    G, D = spec.num_q_heads // spec.num_kv_heads, spec.head_size
+    # QK^T and PV: 2 flops per multiply-add, two products per visible key and head dim
+    visible = sum(context + m + 1 for m in range(M))
+    flops = 4 * visible * spec.num_q_heads * D
+    ms, plan = time_calls(case, args.warmup, args.steps, num_segments=args.segments)
+    tflops = flops / (ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+
+        kv64, table, lens = wl.compact(case)
+        q64 = wl.as_f64(case.q)
+        t0 = time.perf_counter()
+        oracle.decode_attention(q64, kv64, table, lens, case.scale, case.window, case.layout)
+        el = time.perf_counter() - t0
+        cpu = {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+               "sample": f"one full call, {el:.1f} s"}
+    line = {
+        "metric": "prefill-chunk attention TFLOP/s (QK^T + PV over visible keys) and fraction of the bf16 MFMA peak",
+        "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": spec.dtype, "data": "synthetic",
+        "config": {"workload": f"prefill chunk: {M} tokens over a {context}-key context, bf16, D={D}, "
+                               f"{spec.num_q_heads}/{spec.num_kv_heads} heads, page {spec.page_size}, HND",
+                   "flops_per_step": flops, "plan": plan},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -397,6 +447,8 @@ def main() -> int:
                     help="kernel family (auto = the planner's choice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run device copies of COPY_BYTES (reference for HBM byte counters)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time a 256-token prefill chunk over a 4096-key context instead (matrix-core bound)")
     ap.add_argument("--cache-write", action="store_true",
                     help="time the KV-cache write with rotation (the step before decode) instead")
     ap.add_argument("--varlen", action="store_true",
@@ -411,6 +463,8 @@ def main() -> int:
         return varlen_main(args)
     if args.cache_write:
         return cache_write_main(args)
+    if args.prefill:
+        return prefill_main(args)
 
     import torch
 

@@ -3,7 +3,8 @@
  * library (libpad_attn.so, HIP kernels for gfx950 / CDNA4).
  *
  * What it computes.  For every sequence s of a batch, every one of its M
- * newest query tokens m (M <= 8) and every query head h, with L the
+ * newest query tokens m (M <= 8 for decode and speculative verify, up to
+ * 256 for a prefill chunk) and every query head h, with L the
  * sequence's length (which already counts the M new tokens) and
  * qpos = L - M + m:
  *
@@ -102,7 +103,7 @@ typedef enum pad_path {
 /* Work schedule.  AUTO picks the persistent grid for batches whose
  * segments would oversubscribe the device, else one workgroup per item.
  * Both give the same output bits for the same plan. */
-typedef enum pad_schedule {
+typedef enum pad_schedule {  /* the dot family runs on the grid schedule only */
   PAD_SCHED_AUTO = 0,
   PAD_SCHED_GRID = 1,        /* one workgroup per (sequence, kv head, segment)  */
   PAD_SCHED_PERSISTENT = 2,  /* one workgroup per CU taking items from a queue  */
@@ -111,7 +112,8 @@ typedef enum pad_schedule {
 /* Shape of one call.  Every field is host data. */
 typedef struct pad_shape {
   int32_t num_seqs;           /* S >= 0 (0: the call does nothing)                 */
-  int32_t query_len;          /* M, 1..8 query tokens per sequence               */
+  int32_t query_len;          /* M, 1..256 query tokens per sequence; at most
+                                 4096 rows G * M per kv head                     */
   int32_t num_q_heads;        /* Hq >= 1                                         */
   int32_t num_kv_heads;       /* Hkv >= 1, divides Hq                            */
   int32_t head_size;          /* D in {64, 128, 256, 512}                        */
@@ -196,7 +198,7 @@ pad_status pad_decode_attn(const pad_shape* shape, const void* q, const void* kv
  * RocmOctaveMetadataBuilder._fill_query_maps on the octave page).
  * q_start is a device int32 array of num_seqs + 1 entries, read only on
  * the device (no host synchronisation; the call can be captured in a HIP
- * graph).  shape->query_len is the host bound on every M_s (1..8; it sizes
+ * graph).  shape->query_len is the host bound on every M_s (1..256; it sizes
  * the plan and the workspace like a uniform call of that M).  Contract on
  * the device values: q_start non-decreasing, q_start[0] >= 0, M_s <=
  * query_len, and q/out hold at least q_start[num_seqs] rows; a count

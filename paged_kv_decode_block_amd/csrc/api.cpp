@@ -152,6 +152,7 @@ pad_status decode(const pad_shape* shape, const void* q, const int32_t* q_start,
   pr.nseg = p.nseg;
   pr.seg_tiles = p.seg_tiles;
   pr.row_groups = p.row_groups;
+  pr.group_rows = p.path == PAD_PATH_DOT ? p.rows : p.row_tiles * 16;
   pr.merge_slices = p.merge_slices;
   pr.persistent = p.persistent;
   pr.merge_wait_ticks = g_merge_wait_ticks.load();

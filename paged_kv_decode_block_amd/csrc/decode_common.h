@@ -373,10 +373,16 @@ __device__ __forceinline__ void zero_rows(const Params& p, int s, int kvh, int r
   }
 }
 
-// Segments of a sequence of (clamped) length L: its visible key range in
-// 16-key tiles [t_lo, t_hi), split into n_live segments of seg_tiles tiles
-// (at least the planned count, stretched when a device length exceeds the
-// planning bound).
+// Segments of row group rg of a sequence of (clamped) length L with M query
+// tokens: the key range its rows can see, in 16-key tiles [t_lo, t_hi),
+// split into n_live segments of seg_tiles tiles (at least the planned
+// count, stretched when a device length exceeds the planning bound).  The
+// group's rows (row = m * G + head) hold tokens first_m .. last_m, which
+// see keys below L - M + last_m + 1 and, with a window W, from
+// L - M + first_m - W + 1 on: a tile of a prefill chunk reads only the
+// keys its own tokens reach (the work list entries of plan_prefill on the
+// rdna_hip page).  A group with no row has no segment; one whose tokens
+// all sit before the first key keeps one tile (all masked: zero rows).
 struct SegSplit {
   int t_lo, t_hi, seg_tiles, n_live;
 };
@@ -386,15 +392,31 @@ __device__ __forceinline__ int clamped_len(const Params& p, int s) {
   return min(p.seq_lens[s], p.max_blocks * p.page_size);
 }
 
-__device__ __forceinline__ SegSplit split_of(const Params& p, int L, int M) {
+__device__ __forceinline__ SegSplit split_of(const Params& p, int L, int M, int rg) {
   SegSplit r;
-  const int k_lo = p.window > 0 ? max(0, L - M - p.window + 1) : 0;
+  const int rows = p.group * M;
+  const int r0 = rg * p.group_rows;
+  if (r0 >= rows) {
+    r.t_lo = r.t_hi = r.seg_tiles = r.n_live = 0;
+    return r;
+  }
+  const int first_m = r0 / p.group, last_m = (min(rows, r0 + p.group_rows) - 1) / p.group;
+  const int k_end = min(L, L - M + last_m + 1);
+  const int k_lo = p.window > 0 ? max(0, L - M + first_m - p.window + 1) : 0;
   r.t_lo = k_lo >> 4;
-  r.t_hi = (L + 15) >> 4;
+  r.t_hi = max((k_end + 15) >> 4, r.t_lo + 1);
   const int n_tiles = r.t_hi - r.t_lo;
   r.seg_tiles = max(p.seg_tiles, (n_tiles + p.nseg - 1) / p.nseg);
   r.n_live = (n_tiles + r.seg_tiles - 1) / r.seg_tiles;
   return r;
+}
+
+// Items of a live sequence on the persistent grid: every (row group, kv
+// head, segment).
+__device__ __forceinline__ int seq_items(const Params& p, int L, int M) {
+  int n = 0;
+  for (int rg = 0; rg < p.row_groups; ++rg) n += split_of(p, L, M, rg).n_live;
+  return n * p.num_kv_heads;
 }
 
 // Persistent grid (batched decode): one workgroup per CU takes work items
@@ -443,7 +465,7 @@ __device__ __forceinline__ void persistent_loop(const Params& p, unsigned char* 
   for (int r = tid; r < S; r += nt) {
     const int s = sm_order[r];
     const int L = sm_len[s], M = seq_queries(p, s).m;
-    sm_cnt[r] = M == 0 ? 0 : (L <= 0 ? units : units * split_of(p, L, M).n_live);
+    sm_cnt[r] = M == 0 ? 0 : (L <= 0 ? units : seq_items(p, L, M));
   }
   __syncthreads();
   if (tid < 64) {
@@ -486,9 +508,21 @@ __device__ __forceinline__ void persistent_loop(const Params& p, unsigned char* 
     const int s = sm_order[lo];
     const int local = item - sm_pref[lo];
     const int L = clamped_len(p, s);
-    const int per_unit = L <= 0 ? 1 : split_of(p, L, seq_queries(p, s).m).n_live;
-    const int unit = local / per_unit, seg = local % per_unit;
-    body(s, unit % p.num_kv_heads, unit / p.num_kv_heads, seg);
+    if (L <= 0) {
+      body(s, local % p.num_kv_heads, local / p.num_kv_heads, 0);
+    } else {
+      // Row groups last (heaviest) first, then kv heads, then segments.
+      const int M = seq_queries(p, s).m;
+      int rest = local;
+      for (int rg = p.row_groups - 1; rg >= 0; --rg) {
+        const int n = split_of(p, L, M, rg).n_live;
+        if (rest < n * p.num_kv_heads) {
+          body(s, rest / n, rg, rest % n);
+          break;
+        }
+        rest -= n * p.num_kv_heads;
+      }
+    }
     __syncthreads();  // LDS is reused by the next item
   }
 }

@@ -163,7 +163,7 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
     return;
   }
   const int k_lo = p.window > 0 ? max(0, L - M - p.window + 1) : 0;
-  const SegSplit sp = split_of(p, L, M);
+  const SegSplit sp = split_of(p, L, M, rg);
   const int t_hi = sp.t_hi, seg_tiles = sp.seg_tiles, n_live = sp.n_live;
   if (seg >= n_live) return;
   const int ts = sp.t_lo + seg * seg_tiles, te = min(ts + seg_tiles, t_hi);

@@ -28,6 +28,7 @@ struct Params {
   int32_t nseg;               // segments per (sequence, kv head, row group)
   int32_t seg_tiles;          // planned 16-key tiles per segment
   int32_t row_groups;         // workgroups splitting the rows
+  int32_t group_rows;         // query rows per row group (row tiles * 16)
   int32_t merge_slices;       // slices of the merged output (merging workgroups)
   uint32_t merge_wait_ticks;  // helpers' wait bound (100 MHz real-time ticks)
   int32_t persistent;         // 1: workgroups take items from the queue word

@@ -36,14 +36,15 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   if (sh.max_seq_len > table_keys) return PAD_EINVAL;
   // Key and tile indices are 32-bit on the device.
   if (table_keys > (int64_t(1) << 30)) return PAD_EUNSUPPORTED;
-  // Decode and speculative verify only (M <= 8); other head sizes and page
-  // sizes that are not multiples of the 16-key tile are not built.
-  if (sh.query_len > 8 || !known_head_size(sh.head_size) || sh.page_size % kTileKeys != 0)
+  // Decode and speculative verify (M <= 8) and prefill chunks up to
+  // kMaxQueryLen tokens (kMaxRows GQA-packed rows); other head sizes and
+  // page sizes that are not multiples of the 16-key tile are not built.
+  if (sh.query_len > kMaxQueryLen || !known_head_size(sh.head_size) || sh.page_size % kTileKeys != 0)
     return PAD_EUNSUPPORTED;
   if (sh.num_seqs > 65535) return PAD_EUNSUPPORTED;
   const int G = sh.num_q_heads / sh.num_kv_heads;
   const int rows = G * sh.query_len;
-  if (rows > 1024) return PAD_EUNSUPPORTED;
+  if (rows > kMaxRows) return PAD_EUNSUPPORTED;
   const bool dot_ok = rows <= kDotMaxRows && sh.head_size <= kDotMaxHeadSize;
   if (sh.path == PAD_PATH_DOT && !dot_ok) return PAD_EUNSUPPORTED;
   const int tiles_total = int(ceil_div(rows, 16));
@@ -87,8 +88,11 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   // segments per 16k sequence 276-282 us, 33 segments 332 us).
   const int64_t seg_persist = std::max<int64_t>(4, (int64_t(1) << 20) / tile_bytes);
   if (sh.schedule == PAD_SCHED_PERSISTENT && sh.num_seqs > kPersistMaxSeqs) return PAD_EUNSUPPORTED;
+  // The dot family is built for one workgroup per item only.
+  const bool can_persist = p.path != PAD_PATH_DOT;
+  if (sh.schedule == PAD_SCHED_PERSISTENT && !can_persist) return PAD_EUNSUPPORTED;
   p.persistent = sh.schedule == PAD_SCHED_PERSISTENT ||
-                 (sh.schedule == PAD_SCHED_AUTO && sh.num_seqs > 1 && sh.num_seqs <= kPersistMaxSeqs &&
+                 (sh.schedule == PAD_SCHED_AUTO && can_persist && sh.num_seqs > 1 && sh.num_seqs <= kPersistMaxSeqs &&
                   units * std::max<int64_t>(1, sh.num_segments > 0 ? sh.num_segments : ceil_div(span_tiles, seg_persist)) >
                       slots);
   int64_t nseg;
@@ -144,8 +148,9 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   // every call of the shape; the slot stride of a call is its own count.
   int64_t ws_nseg;
   {
-    const bool may_persist = sh.schedule == PAD_SCHED_PERSISTENT ||
-                             (sh.schedule == PAD_SCHED_AUTO && sh.num_seqs > 1 && sh.num_seqs <= kPersistMaxSeqs);
+    const bool may_persist = can_persist && (sh.schedule == PAD_SCHED_PERSISTENT ||
+                                             (sh.schedule == PAD_SCHED_AUTO && sh.num_seqs > 1 &&
+                                              sh.num_seqs <= kPersistMaxSeqs));
     const bool may_grid = sh.schedule != PAD_SCHED_PERSISTENT;
     if (sh.num_segments > 0) {
       ws_nseg = sh.num_segments;
@@ -163,7 +168,7 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   // shortens the span, so no window plans it otherwise.
   const bool persist_any =
       sh.schedule == PAD_SCHED_PERSISTENT ||
-      (sh.schedule == PAD_SCHED_AUTO && sh.num_seqs > 1 && sh.num_seqs <= kPersistMaxSeqs &&
+      (sh.schedule == PAD_SCHED_AUTO && can_persist && sh.num_seqs > 1 && sh.num_seqs <= kPersistMaxSeqs &&
        units * std::max<int64_t>(1, sh.num_segments > 0 ? sh.num_segments : ceil_div(all_tiles, seg_persist)) > slots);
   if (ws_nseg > 1 || persist_any) {
     const size_t S = size_t(sh.num_seqs), H = size_t(sh.num_kv_heads);

@@ -22,6 +22,12 @@
 namespace pad {
 
 constexpr int kTileKeys = 16;    // keys per MFMA tile (page sizes are multiples of 16)
+// Query tokens per sequence and GQA-packed query rows per kv head of one
+// call: decode and speculative verify use M <= 8; longer prefill chunks
+// take one row group per 16-row tiles of a workgroup, each reading only
+// the keys its own tokens reach.
+constexpr int kMaxQueryLen = 256;
+constexpr int kMaxRows = 4096;
 constexpr int kMaxSegments = 256;
 // Longest segment in tiles: a workgroup stages its segment's block ids
 // (one int32 per tile) in LDS.

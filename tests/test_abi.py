@@ -195,7 +195,8 @@ def test_window_plan_is_smaller():
     "kw,status",
     [
         (dict(query_len=0), pad.PAD_EINVAL),
-        (dict(query_len=9), pad.PAD_EUNSUPPORTED),
+        (dict(query_len=257), pad.PAD_EUNSUPPORTED),
+        (dict(query_len=256, num_q_heads=256, num_kv_heads=8), pad.PAD_EUNSUPPORTED),  # 8192 rows
         (dict(head_size=96), pad.PAD_EUNSUPPORTED),
         (dict(head_size=0), pad.PAD_EINVAL),
         (dict(page_size=8), pad.PAD_EUNSUPPORTED),
@@ -253,7 +254,7 @@ def test_decode_validates_before_launch():
     assert _call(one_seg, out=0x5002) == pad.PAD_EINVAL
     assert _call(one_seg, bt=0x3002) == pad.PAD_EINVAL  # 4-byte alignment
     assert _call(one_seg, window=-3) == pad.PAD_EINVAL
-    assert _call(shape(query_len=9)) == pad.PAD_EUNSUPPORTED
+    assert _call(shape(query_len=257)) == pad.PAD_EUNSUPPORTED
     split = shape(num_segments=4)
     need = plan(split)["workspace_bytes"]
     assert need > 0
@@ -317,7 +318,7 @@ def test_varlen_validation():
     assert v(shape(num_seqs=0), 0) == pad.PAD_OK
     assert v(shape(), 0) == pad.PAD_EINVAL  # missing q_start
     assert v(shape(), 0x1002) == pad.PAD_EINVAL  # misaligned q_start
-    assert v(shape(query_len=9), 0x1000) == pad.PAD_EUNSUPPORTED  # bound on the per-sequence counts
+    assert v(shape(query_len=257), 0x1000) == pad.PAD_EUNSUPPORTED  # bound on the per-sequence counts
 
 
 def test_workspace_serves_every_window():
@@ -367,3 +368,16 @@ def test_cache_write_validation():
     assert w(pos=0) == pad.PAD_EINVAL  # rotation without positions
     assert w(ptr=0x1008) == pad.PAD_EINVAL  # misaligned tensors
     assert w(dtype=5) == pad.PAD_EINVAL
+
+
+def test_dot_family_stays_on_the_grid():
+    """The dot family has no persistent-grid build: a batch that would
+    otherwise go persistent keeps one workgroup per item, and asking for the
+    persistent schedule is rejected."""
+    batch = dict(num_seqs=200, query_len=1, path=pad.PAD_PATH_DOT)
+    p = plan(shape(**batch))
+    assert p["path"] == pad.PAD_PATH_DOT and p["persistent"] == 0 and p["grid_y"] == 200
+    assert plan(shape(num_seqs=200, query_len=1))["persistent"] == 1  # the key-split family does go persistent
+    with pytest.raises(pad.PadError) as e:
+        plan(shape(schedule=pad.PAD_SCHED_PERSISTENT, **batch))
+    assert e.value.status == pad.PAD_EUNSUPPORTED

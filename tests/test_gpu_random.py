@@ -45,6 +45,8 @@ def test_random_shape(i):
     D, Hkv, G, M, P, layout, dtype, S, lens, window, nseg, schedule, path, counts = _draw(i)
     if counts is not None and path == pad.PAD_PATH_DOT:
         path = pad.PAD_PATH_AUTO
+    if path == pad.PAD_PATH_DOT and schedule == pad.PAD_SCHED_PERSISTENT:
+        schedule = pad.PAD_SCHED_GRID  # the dot family runs on the grid schedule only
     say(f"random {i}: D={D} Hkv={Hkv} G={G} M={M} P={P} layout={layout} {dtype} lens={lens} window={window} "
         f"nseg={nseg} schedule={schedule} path={path} counts={counts}")
     spec = wl.Spec(dtype, D, G * Hkv, Hkv, P, layout)
