@@ -47,6 +47,9 @@ struct Mfma<_Float16> {
 };
 
 constexpr float kNegInf = -__builtin_huge_valf();
+// Slack of a row's reference maximum in the exp2 domain: scores up to this
+// far above it keep it (softmax weights up to 2^8 before normalisation).
+constexpr float kMaxSlack = 8.f;
 constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -278,16 +278,24 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
       float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run[rt], tmax);
+      // The row's reference maximum moves only when a tile exceeds it by
+      // more than kMaxSlack (weights then stay below 2^kMaxSlack), so the
+      // accumulator is rescaled rarely -- and skipped by the whole wave
+      // when none of its rows moved.  m, l and acc stay consistent with
+      // the reference, which is all the combine and the merge need.
+      const bool move = tmax > m_run[rt] + kMaxSlack;
+      const float m_new = move ? tmax : m_run[rt];
       const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[rt] - m_use);
+      const float alpha = move ? fast_exp2(m_run[rt] - m_use) : 1.f;
       float pj[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) pj[j] = fast_exp2(x[j] - m_use);
       l_run[rt] = l_run[rt] * alpha + ((pj[0] + pj[1]) + (pj[2] + pj[3]));
       m_run[rt] = m_new;
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
+        for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
+      }
       pb[rt] = pack4(MF::bits(pj[0]), MF::bits(pj[1]), MF::bits(pj[2]), MF::bits(pj[3]));
     }
   };
