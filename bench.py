@@ -226,7 +226,7 @@ def cpu_baseline(cfg: int, context: int, M: int, budget_s: float = 12.0) -> dict
         "cores": int(cores),
         "kind": "oracle",
         "sample": f"{calls} full call(s) of the config {cfg} workload at context {context}, M={M} "
-                  f"(one sequence, all kv heads), {el:.1f} s of host time; BLAS threads as reported",
+                  f"({case.num_seqs} sequence(s), all kv heads), {el:.1f} s of host time; BLAS threads as reported",
     }
 
 
