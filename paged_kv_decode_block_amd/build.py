@@ -15,7 +15,11 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpad_attn.so")
-SOURCES = ["decode_mfma.hip", "cache_write.hip", "calib.hip", "plan.cpp", "api.cpp"]
+# (source, object name, extra flags): the decode kernels build once per
+# head size, in parallel.
+SOURCES = [("decode_mfma.hip", f"decode_mfma_d{d}", [f"-DPAD_HEAD_SIZE={d}"]) for d in (64, 128, 256, 512)] + [
+    (src, src.rsplit(".", 1)[0], []) for src in ("zero.hip", "cache_write.hip", "calib.hip", "plan.cpp", "api.cpp")
+]
 
 # Packed fp32 VALU ops are turned off for every HIP source (the host pass
 # reports the feature as unknown; that warning is harmless).
@@ -57,13 +61,14 @@ def build(verbose: bool = False) -> str:
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs, jobs = [], []
-    for src in SOURCES:
+    for src, name, extra in SOURCES:
         path = os.path.join(CSRC, src)
-        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(objdir, name + ".o")
         objs.append(obj)
         # .cpp files hold host code only; compile them as HIP too so the
         # link step sees one toolchain.
-        jobs.append([cc, *HIP_FLAGS, "-c", "-o", obj] + (["-x", "hip"] if src.endswith(".cpp") else []) + [path])
+        jobs.append([cc, *HIP_FLAGS, *extra, "-c", "-o", obj] + (["-x", "hip"] if src.endswith(".cpp") else []) +
+                    [path])
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with ThreadPoolExecutor(workers) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))

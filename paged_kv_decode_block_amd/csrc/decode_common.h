@@ -103,93 +103,79 @@ __device__ __forceinline__ T* seq_out(const Params& p, int s, int D) {
 // The merged output of a unit is rows x D floats, cut into items (row r,
 // four head-dim columns d4): item = r * (D / 4) + d4.  Merge slice `slice`
 // of `nslices` covers items [slice * I / nslices, (slice + 1) * I / nslices).
-// LN lanes serve one item; lane `sub` takes slots sub, sub + LN, ... in
-// chunks of LN * U slots (U per lane), keeping a running (m, l, acc) in the
-// exp2 domain:  m* = max m_j,  l* = sum l_j 2^(m_j - m*),
-// acc* = sum acc_j 2^(m_j - m*)  (the log-sum-exp merge of split
-// partials); the LN lanes then combine in a fixed butterfly.  Each item's
-// sums follow one fixed order for a given (slot count, LN, U), whichever
-// workgroup merges it.  Every load is unconditional (item and slot indices
-// clamped, extra slots weighted zero) so the wait counts stay exact, and
-// the (pass, chunk) work of a thread is one stream with the next unit's
-// loads in flight while the current one is consumed.
-template <int U>
+// LN = 2^lg lanes serve one item, enough that kMergeU slots per lane cover
+// all n slots (n <= 256): lane `sub` takes slots sub, sub + LN, ..., so an
+// item costs one round of loads.  Each lane forms the log-sum-exp merge of
+// its slots in the exp2 domain,  m* = max m_j,  l* = sum l_j 2^(m_j - m*),
+// acc* = sum acc_j 2^(m_j - m*),  and the LN lanes then combine in a fixed
+// butterfly.  Each item's sums follow one fixed order for a given slot
+// count, whichever workgroup merges it.  Every load is unconditional (item
+// and slot indices clamped, extra slots weighted zero) so the wait counts
+// stay exact, and the passes of a thread form one stream with the next
+// pass's loads in flight while the current one is consumed.  LN is a
+// run-time value: one compiled body serves every slot count, which keeps
+// this once-per-launch code small (as several unrolled variants it cost
+// the merge about a microsecond of instruction fetch).
+constexpr int kMergeU = 8;
 struct MergeChunk {
-  f32x4 acc[U];
-  float2 ml[U];
+  f32x4 acc[kMergeU];
+  float2 ml[kMergeU];
 };
 
 // The unit's partial slots start at a wave-uniform 64-bit base; a slot
 // and an item are 32-bit byte offsets from it (a unit's partials span at
 // most 256 segments x 1024 rows x 512 columns x 4 bytes = 512 MiB).
-template <int D, int NT, int LN, int U>
-__device__ __forceinline__ void merge_load(const Params& p, MergeChunk<U>& b, const unsigned char* acc_base,
-                                           const unsigned char* ml_base, int row0, int i0, int i1, int n, int nch,
-                                           int w) {
-  constexpr int IPP = NT / LN, CH = LN * U;
-  const int pass = w / nch, ch = w - pass * nch;
-  const int it = min(i0 + pass * IPP + int(threadIdx.x) / LN, i1 - 1);
+template <int D, int NT>
+__device__ __forceinline__ void merge_load(const Params& p, MergeChunk& b, const unsigned char* acc_base,
+                                           const unsigned char* ml_base, int row0, int i0, int i1, int n, int lg,
+                                           int pass) {
+  const int it = min(i0 + pass * (NT >> lg) + (int(threadIdx.x) >> lg), i1 - 1);
   const int r = it / (D / 4), d4 = it % (D / 4);
   const uint32_t acc_item = uint32_t((row0 + r) * D + 4 * d4) * 4u;
   const uint32_t ml_item = uint32_t(row0 + r) * 8u;
   const uint32_t acc_slot = uint32_t(p.rows) * uint32_t(D) * 4u, ml_slot = uint32_t(p.rows) * 8u;
-  const int first = ch * CH + int(threadIdx.x) % LN;
+  const int sub = int(threadIdx.x) & ((1 << lg) - 1);
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const uint32_t j = uint32_t(min(first + LN * u, n - 1));
+  for (int u = 0; u < kMergeU; ++u) {
+    const uint32_t j = uint32_t(min(sub + (u << lg), n - 1));
     b.acc[u] = *reinterpret_cast<const f32x4*>(acc_base + (j * acc_slot + acc_item));
     b.ml[u] = *reinterpret_cast<const float2*>(ml_base + (j * ml_slot + ml_item));
   }
 }
 
-template <typename T, int D, int NT, int LN, int U>
-__device__ __forceinline__ void merge_consume(const Params& p, const MergeChunk<U>& b, int i0, int i1, int n, int nch,
-                                              int w, int row0, T* out_s, int kvh, float& m_run, float& l_run,
-                                              f32x4& a_run) {
+template <typename T, int D, int NT>
+__device__ __forceinline__ void merge_consume(const Params& p, const MergeChunk& b, int i0, int i1, int n, int lg,
+                                              int pass, int row0, T* out_s, int kvh) {
   using MF = Mfma<T>;
-  constexpr int IPP = NT / LN, CH = LN * U;
-  const int pass = w / nch, ch = w - pass * nch;
-  const int sub = int(threadIdx.x) % LN;
-  if (ch == 0) {
-    m_run = kNegInf;
-    l_run = 0.f;
-    a_run = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const int first = ch * CH + sub;
-  float mj[U];
+  const int sub = int(threadIdx.x) & ((1 << lg) - 1);
+  float mj[kMergeU];
   float mloc = kNegInf;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    mj[u] = first + LN * u < n ? b.ml[u].x : kNegInf;
+  for (int u = 0; u < kMergeU; ++u) {
+    mj[u] = sub + (u << lg) < n ? b.ml[u].x : kNegInf;
     mloc = fmaxf(mloc, mj[u]);
   }
-  const float m_new = fmaxf(m_run, mloc);
-  const float m_use = m_new == kNegInf ? 0.f : m_new;
-  const float sc = fast_exp2(m_run - m_use);
-  l_run *= sc;
-  a_run *= sc;
+  const float m_use = mloc == kNegInf ? 0.f : mloc;
+  float l_loc = 0.f;
+  f32x4 a_loc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
+  for (int u = 0; u < kMergeU; ++u) {
     const float wgt = fast_exp2(mj[u] - m_use);
-    l_run += wgt * b.ml[u].y;
-    a_run += wgt * b.acc[u];
+    l_loc += wgt * b.ml[u].y;
+    a_loc += wgt * b.acc[u];
   }
-  m_run = m_new;
-  if (ch != nch - 1) return;
-  // Last chunk of the pass: combine the item's lanes and write it.
-  float m_all = m_run;
-#pragma unroll
-  for (int o = 1; o < LN; o <<= 1) m_all = fmaxf(m_all, __shfl_xor(m_all, o));
-  const float f = fast_exp2(m_run - (m_all == kNegInf ? 0.f : m_all));
-  float l = l_run * f;
-  f32x4 a = a_run * f;
-#pragma unroll
-  for (int o = 1; o < LN; o <<= 1) {
+  // Combine the item's lanes and write it.
+  float m_all = mloc;
+  for (int o = 1; o < (1 << lg); o <<= 1) m_all = fmaxf(m_all, __shfl_xor(m_all, o));
+  const float f = fast_exp2(mloc - (m_all == kNegInf ? 0.f : m_all));
+  float l = l_loc * f;
+  f32x4 a = a_loc * f;
+  for (int o = 1; o < (1 << lg); o <<= 1) {
     l += __shfl_xor(l, o);
 #pragma unroll
     for (int e = 0; e < 4; ++e) a[e] += __shfl_xor(a[e], o);
   }
-  const int it = i0 + pass * IPP + int(threadIdx.x) / LN;
+  const int it = i0 + pass * (NT >> lg) + (int(threadIdx.x) >> lg);
   if (sub == 0 && it < i1) {
     const int r = it / (D / 4), d4 = it % (D / 4);
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -200,58 +186,34 @@ __device__ __forceinline__ void merge_consume(const Params& p, const MergeChunk<
   }
 }
 
-template <typename T, int D, int NT, int LN, int U>
-__device__ __forceinline__ void merge_items(const Params& p, int64_t slot0, int n, int row0, int i0, int i1, T* out_s,
-                                         int kvh) {
-  constexpr int IPP = NT / LN, CH = LN * U;
-  const int nch = (n + CH - 1) / CH;
-  const int W = (i1 - i0 + IPP - 1) / IPP * nch;
-  const unsigned char* acc_base = reinterpret_cast<const unsigned char*>(p.ws_acc + slot0 * p.rows * D);
-  const unsigned char* ml_base = reinterpret_cast<const unsigned char*>(p.ws_ml + slot0 * p.rows * 2);
-  float m_run = kNegInf, l_run = 0.f;
-  f32x4 a_run = {0.f, 0.f, 0.f, 0.f};
-  MergeChunk<U> b0, b1;
-  merge_load<D, NT, LN, U>(p, b0, acc_base, ml_base, row0, i0, i1, n, nch, 0);
-  if (W == 1) {
-    merge_consume<T, D, NT, LN, U>(p, b0, i0, i1, n, nch, 0, row0, out_s, kvh, m_run, l_run, a_run);
-    return;
-  }
-  for (int w = 0; w < W; w += 2) {
-    merge_load<D, NT, LN, U>(p, b1, acc_base, ml_base, row0, i0, i1, n, nch, min(w + 1, W - 1));
-    merge_consume<T, D, NT, LN, U>(p, b0, i0, i1, n, nch, w, row0, out_s, kvh, m_run, l_run, a_run);
-    merge_load<D, NT, LN, U>(p, b0, acc_base, ml_base, row0, i0, i1, n, nch, min(w + 2, W - 1));
-    if (w + 1 < W)
-      merge_consume<T, D, NT, LN, U>(p, b1, i0, i1, n, nch, w + 1, row0, out_s, kvh, m_run, l_run, a_run);
-  }
-}
-
 // Merge slice `slice` of `nslices` of the n partials of a unit (slots
 // slot0 .. slot0 + n - 1, rows row0 .. row0 + wg_rows - 1 of each) into
-// the output.  Lanes per item and slots per lane follow the slot count
-// only, so an item's sums take the same order whatever the slicing and
-// whichever workgroup merges it: the output bits depend on the sequence
-// and the segment split alone.  The caller has acquired the partials.
+// the output.  Lanes per item follow the slot count only, so an item's
+// sums take the same order whatever the slicing and whichever workgroup
+// merges it: the output bits depend on the sequence and the segment split
+// alone.  The caller has acquired the partials.
 template <typename T, int D, int NT>
 __device__ __forceinline__ void merge_slice(const Params& p, int64_t slot0, int n, int row0, int wg_rows, int slice,
                                             int nslices, T* out_s, int kvh) {
   const int items = wg_rows * (D / 4);
   const int i0 = slice * items / nslices, i1 = (slice + 1) * items / nslices;
   if (i1 <= i0) return;
-  // Enough lanes per item that one chunk of at most 8 loads per lane
-  // covers every slot (n <= 256): an item costs one round of loads, not
-  // several dependent ones.
-  const int ln = n <= 8 ? 1 : (n <= 16 ? 2 : (n <= 32 ? 4 : (n <= 64 ? 8 : (n <= 128 ? 16 : 32))));
-  const int per = (n + ln - 1) / ln;
-  const int u = per <= 2 ? 2 : (per <= 4 ? 4 : 8);
-  switch (ln * 16 + u) {
-    case 1 * 16 + 2: merge_items<T, D, NT, 1, 2>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
-    case 1 * 16 + 4: merge_items<T, D, NT, 1, 4>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
-    case 1 * 16 + 8: merge_items<T, D, NT, 1, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
-    case 2 * 16 + 8: merge_items<T, D, NT, 2, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
-    case 4 * 16 + 8: merge_items<T, D, NT, 4, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
-    case 8 * 16 + 8: merge_items<T, D, NT, 8, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
-    case 16 * 16 + 8: merge_items<T, D, NT, 16, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
-    default: merge_items<T, D, NT, 32, 8>(p, slot0, n, row0, i0, i1, out_s, kvh); break;
+  const int lg = n <= 8 ? 0 : (n <= 16 ? 1 : (n <= 32 ? 2 : (n <= 64 ? 3 : (n <= 128 ? 4 : 5))));
+  const int ipp = NT >> lg;
+  const int W = (i1 - i0 + ipp - 1) / ipp;
+  const unsigned char* acc_base = reinterpret_cast<const unsigned char*>(p.ws_acc + slot0 * p.rows * D);
+  const unsigned char* ml_base = reinterpret_cast<const unsigned char*>(p.ws_ml + slot0 * p.rows * 2);
+  MergeChunk b0, b1;
+  merge_load<D, NT>(p, b0, acc_base, ml_base, row0, i0, i1, n, lg, 0);
+  if (W == 1) {
+    merge_consume<T, D, NT>(p, b0, i0, i1, n, lg, 0, row0, out_s, kvh);
+    return;
+  }
+  for (int w = 0; w < W; w += 2) {
+    merge_load<D, NT>(p, b1, acc_base, ml_base, row0, i0, i1, n, lg, min(w + 1, W - 1));
+    merge_consume<T, D, NT>(p, b0, i0, i1, n, lg, w, row0, out_s, kvh);
+    merge_load<D, NT>(p, b0, acc_base, ml_base, row0, i0, i1, n, lg, min(w + 2, W - 1));
+    if (w + 1 < W) merge_consume<T, D, NT>(p, b1, i0, i1, n, lg, w + 1, row0, out_s, kvh);
   }
 }
 
@@ -272,32 +234,35 @@ constexpr int kSliceIdle = 0, kSliceWaiting = 1, kSliceGo = 2, kSliceGaveUp = 3,
 constexpr int kCtlStride = kCtlWordStride;
 
 // A helper's side of the exchange (one thread): whether it merges its
-// slice.  Every path ends: the wait is bounded by wait_ticks of the
-// 100 MHz real-time counter.
-__device__ __forceinline__ bool helper_wait(int* word, const int* counter, int n, uint32_t wait_ticks) {
+// slice, and whether its word still needs the helper's second action.
+// Every path ends: the wait is bounded by wait_ticks of the 100 MHz
+// real-time counter.  Seeing the unit complete, the helper merges at once
+// and posts "done" alongside its merge loads (kHelperSettle): the exchange
+// only settles who resets the word, so it need not delay the merge.
+constexpr int kHelperGaveUp = 0, kHelperMerge = 1, kHelperSettle = 2;
+__device__ __forceinline__ int helper_wait(int* word, const int* counter, int n, uint32_t wait_ticks) {
   int seen = kSliceIdle;
   if (!__hip_atomic_compare_exchange_strong(word, &seen, kSliceWaiting, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT)) {
     // The last arriver came first (go): this is the word's last use.
     __hip_atomic_store(word, kSliceIdle, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return true;
+    return kHelperMerge;
   }
   const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + wait_ticks;
-  while (__builtin_amdgcn_s_memrealtime() < t_end) {
-    if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n ||
-        __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kSliceGo) {
-      if (__hip_atomic_exchange(word, kSliceDone, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kSliceGo)
-        __hip_atomic_store(word, kSliceIdle, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return true;
-    }
+  for (;;) {
+    // Both words are read in one round trip.
+    const int cnt = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int w = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (cnt == n || w == kSliceGo) return kHelperSettle;
+    if (__builtin_amdgcn_s_memrealtime() >= t_end) break;
     __builtin_amdgcn_s_sleep(1);
   }
   seen = kSliceWaiting;
   if (__hip_atomic_compare_exchange_strong(word, &seen, kSliceGaveUp, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT))
-    return false;
+    return kHelperGaveUp;
   __hip_atomic_store(word, kSliceIdle, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // go came first
-  return true;
+  return kHelperMerge;
 }
 
 // Count this workgroup's arrival for its unit (its partial rows are
@@ -316,6 +281,9 @@ __device__ __forceinline__ void arrive_and_merge(const Params& p, int* flags, in
   const int k = min(p.merge_slices, n_live);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
   __syncthreads();
+  // Thread 0 of a helper that saw the unit complete still posts "done" on
+  // its word (kHelperSettle).
+  bool settle = false;
   if (tid == 0) {
     // Role: 0 = last arriver, 1 .. k-1 = helper merging that slice, -1 = done.
     const int rank = __hip_atomic_fetch_add(ctl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -324,9 +292,13 @@ __device__ __forceinline__ void arrive_and_merge(const Params& p, int* flags, in
       role = 0;
     } else if (rank >= n_live - k) {
       const int sl = n_live - 1 - rank;
-      if (helper_wait(ctl + sl * kCtlStride, ctl, n_live, p.merge_wait_ticks)) role = sl;
+      const int h = helper_wait(ctl + sl * kCtlStride, ctl, n_live, p.merge_wait_ticks);
+      if (h != kHelperGaveUp) role = sl;
+      settle = h == kHelperSettle;
     }
     // Acquire: the other workgroups' partials are visible from here on.
+    // (Device-coherent loads of the partials instead of this fence, which
+    // invalidates the die's L2, measured slower.)
     if (role >= 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     sm_flag[0] = role;
   }
@@ -335,11 +307,15 @@ __device__ __forceinline__ void arrive_and_merge(const Params& p, int* flags, in
   if (role < 0) return;
   // Slices this workgroup merges: its own (slice 0 for the last arriver),
   // and for the last arriver those whose helpers gave up -- known once its
-  // "go" exchanges (issued before its own slice) return.  One merge call
-  // site keeps the kernel's code and register use small.
+  // "go" exchanges (issued before its own slice) return.  A settling
+  // helper's "done" exchange is likewise issued before its merge loads and
+  // read after them.  One merge call site keeps the kernel's code and
+  // register use small.
   int old = kSliceIdle;
   if (role == 0 && tid >= 1 && tid < k)
     old = __hip_atomic_exchange(ctl + tid * kCtlStride, kSliceGo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (settle)
+    old = __hip_atomic_exchange(ctl + role * kCtlStride, kSliceDone, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   uint32_t todo = 1u << role;
   bool settled = role > 0;
   while (todo != 0) {
@@ -364,6 +340,9 @@ __device__ __forceinline__ void arrive_and_merge(const Params& p, int* flags, in
       todo |= uint32_t(sm_flag[1]);
     }
   }
+  // A settling helper that finds go on its word acts second: it resets it.
+  if (settle && old == kSliceGo)
+    __hip_atomic_store(ctl + role * kCtlStride, kSliceIdle, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T, int D>

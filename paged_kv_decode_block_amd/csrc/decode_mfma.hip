@@ -39,6 +39,10 @@
 #include "decode_common.h"
 #include "kernels.h"
 
+#ifndef PAD_HEAD_SIZE
+#error "compile once per head size with -DPAD_HEAD_SIZE=64|128|256|512"
+#endif
+
 namespace pad {
 namespace {
 
@@ -157,7 +161,49 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
   const int wg_rows = min(RT * 16, rows - row0);
   if (wg_rows <= 0) return;  // no query token, or a row group past this sequence's rows
 
-  const int L = clamped_len(p, s);
+  // The length is read first and used last in this prologue: the loads
+  // that do not depend on it (the query rows and, without a window, the
+  // segment's block ids) are in flight at the same time.
+  const int L_dev = p.seq_lens[s];
+  const int32_t* table = p.block_table + int64_t(s) * p.max_blocks;
+  // The segment's block ids (one per tile) go to LDS once, so a tile's
+  // page address costs an LDS read instead of a scalar load that may miss.
+  // The planner keeps segments within kMaxSegTiles tiles.  Without a
+  // window a segment starts at tile seg * seg_tiles whatever the length
+  // (unless a length past the planning bound stretches the segments), so
+  // its planned tiles are staged before the length is known; entries past
+  // the sequence's end are staged but never used.  A thread stages the
+  // same slots in both passes, so a second pass needs no barrier first.
+  int* sm_ids = reinterpret_cast<int*>(lds + SH::kVBytes);
+  const bool spec_ids = p.window == 0;
+  if (spec_ids) {
+    const int ts0 = seg * p.seg_tiles;
+    for (int t = tid; t < p.seg_tiles; t += SH::kThreads) {
+      const int b = ((ts0 + t) * 16) / p.page_size;
+      if (b < p.max_blocks) sm_ids[t] = table[b];
+    }
+  }
+
+  // Per-lane query row (row = lane % 16 of each row tile); rows past G*M
+  // see nothing.
+  i32x4 qop[RT][KC];
+  const T* Q = static_cast<const T*>(p.q);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int ru = row0 + rt * 16 + c;
+    if (ru < rows) {
+      const int m = ru / p.group, gq = ru % p.group;
+      const T* qrow = Q + ((int64_t(sq.first) + m) * p.num_q_heads + kvh * p.group + gq) * D;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) qop[rt][kc] = *reinterpret_cast<const i32x4*>(qrow + 32 * kc + 8 * g);
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) qop[rt][kc] = i32x4{0, 0, 0, 0};
+    }
+  }
+
+  // Lengths past the block table's capacity are clamped to it.
+  const int L = min(L_dev, p.max_blocks * p.page_size);
   if (L <= 0) {
     if (seg == 0) zero_rows<T, D>(p, s, kvh, row0, wg_rows, SH::kThreads);
     return;
@@ -171,27 +217,14 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
   const int lo_last = p.window > 0 ? max(0, L - p.window) : 0;
   const int qpos_first = L - M;
 
-  // Per-lane query row (row = lane % 16 of each row tile): position and
-  // window start; rows past G*M see nothing.
+  // Per-lane query row: position and window start (rows past G*M see
+  // nothing).
   int qpos_r[RT], lo_r[RT];
-  i32x4 qop[RT][KC];
-  const T* Q = static_cast<const T*>(p.q);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int ru = row0 + rt * 16 + c;
-    if (ru < rows) {
-      const int m = ru / p.group, gq = ru % p.group;
-      qpos_r[rt] = L - M + m;
-      lo_r[rt] = p.window > 0 ? max(0, qpos_r[rt] - p.window + 1) : 0;
-      const T* qrow = Q + ((int64_t(sq.first) + m) * p.num_q_heads + kvh * p.group + gq) * D;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) qop[rt][kc] = *reinterpret_cast<const i32x4*>(qrow + 32 * kc + 8 * g);
-    } else {
-      qpos_r[rt] = -1;
-      lo_r[rt] = 0;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) qop[rt][kc] = i32x4{0, 0, 0, 0};
-    }
+    qpos_r[rt] = ru < rows ? L - M + ru / p.group : -1;
+    lo_r[rt] = ru < rows && p.window > 0 ? max(0, qpos_r[rt] - p.window + 1) : 0;
   }
 
   float m_run[RT], l_run[RT];
@@ -206,7 +239,6 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
 
   const unsigned char* KVh =
       static_cast<const unsigned char*>(p.kv) + int64_t(kvh) * p.head_stride * int64_t(sizeof(T));
-  const int32_t* table = p.block_table + int64_t(s) * p.max_blocks;
   // Byte offset of this lane's 16-byte chunk inside a tile: key row c,
   // head-dim elements 8g..8g+7 of chunk 0 (32-bit, per lane); the tile base
   // itself is wave-uniform, so the loads take a scalar base address.
@@ -222,11 +254,8 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
     i32x4 v[KC];
   };
 
-  // The segment's block ids (one per tile) go to LDS once, so a tile's
-  // page address costs an LDS read instead of a scalar load that may miss.
-  // The planner keeps segments within kMaxSegTiles tiles.
-  int* sm_ids = reinterpret_cast<int*>(lds + SH::kVBytes);
-  for (int t = tid; t < te - ts; t += SH::kThreads) sm_ids[t] = table[((ts + t) * 16) / p.page_size];
+  if (!(spec_ids && seg_tiles == p.seg_tiles && ts == seg * p.seg_tiles))
+    for (int t = tid; t < te - ts; t += SH::kThreads) sm_ids[t] = table[((ts + t) * 16) / p.page_size];
   __syncthreads();
   // Physical block of tile t (wave-uniform).
   auto block_of = [&](int t) { return __builtin_amdgcn_readfirstlane(sm_ids[t - ts]); };
@@ -330,11 +359,6 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
   const int first_t = ts + wave;
   const int n_w = first_t < te ? (te - first_t + NW - 1) / NW : 0;
   auto tile_at = [&](int i) { return first_t + min(i, n_w - 1) * NW; };
-  auto compute_tile = [&](Tile& tl, int t) {
-    uint64_t pb[RT];
-    score_tile(tl, t, pb);
-    pv_tile(pb);
-  };
   if constexpr (SH::PF == 0) {
     // No register room for a second tile: the next tile's loads go out as
     // soon as the scores have consumed the current one, so they overlap
@@ -350,6 +374,8 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
       }
     }
   } else if (n_w > 0) {
+    // (Reloading a tile's registers right after its scores, which keeps
+    // PF + 1 tiles in flight through the PV product, measured slower.)
     Tile ring[SH::PF + 1];
 #pragma unroll
     for (int u = 0; u < SH::PF; ++u) issue_tile(ring[u], tile_at(u), block_of(tile_at(u)));
@@ -357,9 +383,11 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
     for (int i = 0;; i += SH::PF + 1) {
 #pragma unroll
       for (int u = 0; u <= SH::PF; ++u) {
+        uint64_t pb[RT];
         issue_tile(ring[(u + SH::PF) % (SH::PF + 1)], tile_at(i + u + SH::PF), blk_next);
         blk_next = block_of(tile_at(i + u + SH::PF + 1));
-        compute_tile(ring[u], first_t + (i + u) * NW);
+        score_tile(ring[u], first_t + (i + u) * NW, pb);
+        pv_tile(pb);
         if (i + u + 1 >= n_w) goto tiles_done;
       }
     }
@@ -702,11 +730,6 @@ tiles_done:
   finish<T, D, 1, NW>(p, lds, s, kvh, 0, seg, 0, rows, n_live, SH::kBytes);
 }
 
-__global__ void zero_kernel(uint32_t* p, size_t n) {
-  const size_t stride = size_t(gridDim.x) * blockDim.x;
-  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
-}
-
 template <typename T, int D, int RT>
 int launch_t(const Plan& pl, const Params& pr, hipStream_t st) {
   if (pl.persistent)
@@ -730,44 +753,27 @@ int launch_d(const Plan& pl, const Params& pr, hipStream_t st) {
 }
 
 template <typename T, int D>
-int launch_dot(const Plan& pl, const Params& pr, hipStream_t st) {
-  hipLaunchKernelGGL((decode_dot_kernel<T, D>), dim3(pl.grid_x, pl.grid_y), dim3(DotShape<D>::kThreads), 0, st, pr);
-  return int(hipGetLastError());
-}
-
-template <typename T>
-int launch_dtype(const Plan& pl, const Params& pr, int head_size, hipStream_t st) {
+int launch_dtype(const Plan& pl, const Params& pr, hipStream_t st) {
   if (pl.path == PAD_PATH_DOT) {
-    switch (head_size) {
-      case 64: return launch_dot<T, 64>(pl, pr, st);
-      case 128: return launch_dot<T, 128>(pl, pr, st);
+    if constexpr (D <= kDotMaxHeadSize) {
+      hipLaunchKernelGGL((decode_dot_kernel<T, D>), dim3(pl.grid_x, pl.grid_y), dim3(DotShape<D>::kThreads), 0, st,
+                         pr);
+      return int(hipGetLastError());
     }
     return int(hipErrorInvalidValue);
   }
-  switch (head_size) {
-    case 64: return launch_d<T, 64>(pl, pr, st);
-    case 128: return launch_d<T, 128>(pl, pr, st);
-    case 256: return launch_d<T, 256>(pl, pr, st);
-    case 512: return launch_d<T, 512>(pl, pr, st);
-  }
-  return int(hipErrorInvalidValue);
+  return launch_d<T, D>(pl, pr, st);
 }
 
 }  // namespace
 
-int launch_decode(const Plan& plan, const Params& params, int dtype, int head_size, void* stream) {
+// This source is compiled once per head size (PAD_HEAD_SIZE), so the
+// instantiations of the four sizes build in parallel.
+template <>
+int launch_decode_hs<PAD_HEAD_SIZE>(const Plan& plan, const Params& params, int dtype, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dtype == PAD_BF16) return launch_dtype<__bf16>(plan, params, head_size, st);
-  return launch_dtype<_Float16>(plan, params, head_size, st);
-}
-
-int launch_zero(void* ptr, size_t words, void* stream) {
-  if (words == 0) return 0;
-  const size_t blocks = (words + 255) / 256;
-  const unsigned grid = unsigned(blocks < 1024 ? blocks : 1024);
-  hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<uint32_t*>(ptr), words);
-  return int(hipGetLastError());
+  if (dtype == PAD_BF16) return launch_dtype<__bf16, PAD_HEAD_SIZE>(plan, params, st);
+  return launch_dtype<_Float16, PAD_HEAD_SIZE>(plan, params, st);
 }
 
 }  // namespace pad

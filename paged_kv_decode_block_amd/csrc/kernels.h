@@ -39,6 +39,10 @@ struct Params {
 // (0 = success).
 int launch_decode(const Plan& plan, const Params& params, int dtype, int head_size, void* stream);
 
+// The same for one head size D (64, 128, 256 or 512).
+template <int D>
+int launch_decode_hs(const Plan& plan, const Params& params, int dtype, void* stream);
+
 // Enqueue a fill of `words` 32-bit zeros at `ptr`.
 int launch_zero(void* ptr, size_t words, void* stream);
 
