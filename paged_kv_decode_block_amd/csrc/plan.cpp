@@ -82,11 +82,12 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   // workgroup per planned segment would oversubscribe the device: the
   // lengths are only known on the device, and a static grid there leaves
   // CUs idle behind dead or short workgroups.  Its segments hold about
-  // 1 MiB of K/V each: every item pays a fixed combine, publish and
-  // pipeline-fill cost, which smaller items repeat more often (measured on
-  // 64 bf16 sequences of 512..16384 keys, 16/2 heads of 256: 8 to 16
-  // segments per 16k sequence 276-282 us, 33 segments 332 us).
-  const int64_t seg_persist = std::max<int64_t>(4, (int64_t(1) << 20) / tile_bytes);
+  // 3 MiB of K/V each: every item pays a fixed prologue, combine, publish
+  // and pipeline-fill cost, which smaller items repeat more often, while
+  // larger ones balance worse over the CUs (measured on 64 bf16 sequences
+  // of 512..16384 keys, 16/2 heads of 256: items of 0.5, 1, 2, 3 and 4 MiB
+  // took 303, 265, 256, 246 and 267 us).
+  const int64_t seg_persist = std::max<int64_t>(4, (int64_t(3) << 20) / tile_bytes);
   if (sh.schedule == PAD_SCHED_PERSISTENT && sh.num_seqs > kPersistMaxSeqs) return PAD_EUNSUPPORTED;
   // The dot family is built for one workgroup per item only.
   const bool can_persist = p.path != PAD_PATH_DOT;
@@ -143,7 +144,7 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
 
   // The workspace holds partial slots for a segment count that bounds what
   // any window plans for this shape (forced, the static grid's fill, the
-  // persistent grid's 1 MiB segments and the LDS block-id bound, all at
+  // persistent grid's 3 MiB segments and the LDS block-id bound, all at
   // the window-free span), so one pad_decode_attn_workspace_size serves
   // every call of the shape; the slot stride of a call is its own count.
   int64_t ws_nseg;
