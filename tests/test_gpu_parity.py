@@ -121,6 +121,19 @@ def test_forced_segments(nseg):
     assert float((out.float() - base.float()).abs().max()) < 1e-2
 
 
+@pytest.mark.parametrize("nseg", [8, 9, 16, 17, 32, 36, 63, 84, 125, 250])
+def test_merge_lane_counts(nseg):
+    """Every lanes-per-item count of the merge (one lane for up to 8 slots,
+    then 2, 4, 8, 16 and 32 lanes up to 256 slots), near both edges of each
+    range, matches the oracle (4000 keys are 250 tiles: these counts split
+    them evenly enough that the planner keeps them)."""
+    c = _case(wl.CONFIGS[2], [4000], 4, 91)
+    shape = pad.make_shape(c.q, c.kv_cache, c.block_tables[0], c.layout, num_segments=nseg)
+    assert pad.pad_decode_attn_plan(shape, c.window)["num_segments"] == nseg
+    out = run_gpu(c, num_segments=nseg)
+    check(out, oracle_out(c), c.q.dtype, f"merge of {nseg} slots")
+
+
 def test_counters_left_zero_and_nan_scratch():
     spec = wl.CONFIGS[4]
     c = _case(spec, [3000], 8, 11)
