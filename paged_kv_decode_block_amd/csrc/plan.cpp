@@ -110,7 +110,18 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
     // 512): with less the merge costs more than the extra parallelism
     // saves -- but keep at least 4 segments while the device has room, so
     // short contexts still spread their latency.
-    const int64_t seg_target = std::max<int64_t>(4, (int64_t(128) << 10) / tile_bytes);
+    int64_t seg_target = std::max<int64_t>(4, (int64_t(128) << 10) / tile_bytes);
+    // Where that still leaves 32 or more segments, a segment also keeps its
+    // partial (wg_rows rows of D + 2 floats, written and read back) below a
+    // sixth of its K/V bytes: wide heads with many live rows otherwise spend
+    // more on the merge than the extra workgroups save (head size 512, 16
+    // rows per workgroup: 32 segments against 64 at 4k keys, 19.8 against
+    // 21.3 us; 64 against 128 at 8k keys, 24.8 against 27.5 us).  Shorter
+    // contexts keep the smaller segments (there 16 segments of 1k keys beat
+    // 8, 15.5 against 18.0 us).
+    const int64_t wg_rows = std::min(rows, p.row_tiles * 16);
+    const int64_t part_min = ceil_div(6 * wg_rows * (sh.head_size + 2) * int64_t(sizeof(float)), tile_bytes);
+    if (part_min > seg_target && span_tiles / part_min >= 32) seg_target = part_min;
     const int64_t work = std::max<int64_t>(1, span_tiles / seg_target);
     nseg = std::min<int64_t>(fill, std::max<int64_t>(work, std::min<int64_t>(4, fill)));
   }
@@ -119,6 +130,22 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   nseg = std::max<int64_t>(1, nseg);
   p.seg_tiles = int(ceil_div(span_tiles, nseg));
   p.nseg = int(ceil_div(span_tiles, p.seg_tiles));
+  // The row groups of one (kv head, segment) read the same tiles; the
+  // kernel places them on one XCD (sharing its L2) when segments x kv
+  // heads is a multiple of the 8 XCDs.  An automatic count keeps that
+  // (measured at head size 512, M = 5, three row groups, 16k keys: 41
+  // segments 45.0 us, 32 segments 41.6 us).
+  if (sh.num_segments == 0 && !p.persistent && p.row_groups > 1 && (int64_t(p.nseg) * sh.num_kv_heads) % 8 != 0) {
+    for (int64_t n = p.nseg - 1; n >= 1; --n) {
+      const int64_t st = ceil_div(span_tiles, n);
+      const int64_t n2 = ceil_div(span_tiles, st);
+      if ((n2 * sh.num_kv_heads) % 8 == 0) {
+        p.seg_tiles = int(st);
+        p.nseg = int(n2);
+        break;
+      }
+    }
+  }
   // A workgroup stages its segment's block ids in LDS, so no segment may
   // exceed kMaxSegTiles tiles -- also for device lengths beyond
   // max_seq_len, up to the table's capacity (the kernel clamps to it and
