@@ -216,7 +216,7 @@ def cpu_baseline(cfg: int, context: int, M: int, budget_s: float = 12.0) -> dict
         oracle.decode_attention(q64, kv64, table, lens, case.scale, case.window, case.layout)
         calls += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or calls >= 50:
+        if el >= budget_s or calls >= 1000:
             break
     cores = _blas_threads()
     gbs = effective_bytes(case) * calls / el / 1e9

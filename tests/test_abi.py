@@ -166,6 +166,34 @@ def test_plan_fills_device():
     assert p["grid_x"] * p["grid_y"] >= 256
 
 
+@pytest.mark.parametrize("M", [3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("keys", [1024, 4096, 8192, 16384, 32768])
+def test_plan_keeps_row_groups_on_one_xcd(M, keys):
+    """With several row groups an automatic plan keeps segments x kv heads
+    a multiple of the 8 XCDs, the condition under which the kernel places a
+    (kv head, segment)'s row groups on one die."""
+    p = plan(shape(num_q_heads=16, num_kv_heads=2, head_size=512, page_size=32,
+                   max_blocks_per_seq=keys // 32, query_len=M))
+    assert p["row_groups"] > 1
+    assert (p["num_segments"] * 2) % 8 == 0, p
+    assert p["grid_x"] <= 256  # resident: merge helpers take part
+
+
+def test_plan_partial_bound_for_wide_heads():
+    """Head size 512 with 16 live rows per workgroup: segments keep their
+    partial below a sixth of their K/V bytes while 32 or more remain; short
+    contexts keep the shorter segments that fill the device."""
+    wide = dict(num_q_heads=16, num_kv_heads=2, head_size=512, page_size=32, query_len=2)
+    part, tile = 16 * (512 + 2) * 4, 16 * 2 * 512 * 2
+    for keys in (4096, 8192, 32768):
+        p = plan(shape(max_blocks_per_seq=keys // 32, **wide))
+        assert p["segment_tiles"] * tile >= 6 * part or p["num_segments"] < 32, (keys, p)
+    short = plan(shape(max_blocks_per_seq=1024 // 32, **wide))
+    assert short["num_segments"] == 16
+    # the default workload's plan does not move
+    assert plan(shape())["num_segments"] == 32
+
+
 def test_forced_segments():
     for n in (1, 2, 7, 256):
         p = plan(shape(num_segments=n, max_blocks_per_seq=64))
