@@ -64,7 +64,8 @@ struct Combine {
 };
 
 // Workgroup shape (waves per workgroup from waves_for) and LDS layout.
-template <int D, int RT>
+// LEAN selects the tile loop with a single copy of its body (below).
+template <int D, int RT, bool LEAN = false>
 struct Shape {
   static constexpr int NW = waves_for(D, RT);
   static constexpr int kThreads = NW * 64;
@@ -74,8 +75,15 @@ struct Shape {
   static constexpr int kAccStride = D + 4;  // floats per accumulator row in LDS
   static constexpr int kRows = RT * 16;
   // Tiles in flight beyond the one being computed: one while the register
-  // budget allows it (a second one measured slower).
-  static constexpr int PF = D * RT <= 512 && D < 512 ? 1 : 0;
+  // budget allows it (a second one measured slower).  The ring of PF + 1
+  // register tiles unrolls the loop body PF + 1 times, and the first pass
+  // through each copy is fetched cold; the lean loop (PF = 0: a tile's
+  // successor is issued once its scores have consumed it) keeps one copy.
+  // The planner picks it for grids that fill the device with one row tile
+  // per wave, and for the persistent grid (batch workload 246 -> 239 us,
+  // one sequence of 32k keys 33.2 -> 32.9 us); latency-bound grids and
+  // waves with several row tiles keep the ring.
+  static constexpr int PF = !LEAN && D * RT <= 512 && D < 512 ? 1 : 0;
   // LDS: V staging and the segment's block ids during the tile loop,
   // afterwards the wave-combine area; then the persistent grid's tables.
   // The last 16 bytes hold the merge role, hand-over and queue words.
@@ -144,10 +152,10 @@ __device__ __forceinline__ void finish(const Params& p, unsigned char* lds, int 
 }
 
 // One work item: segment `seg` of (sequence s, kv head kvh, row group rg).
-template <typename T, int D, int RT>
+template <typename T, int D, int RT, bool LEAN>
 __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds, int s, int kvh, int rg, int seg) {
   using MF = Mfma<T>;
-  using SH = Shape<D, RT>;
+  using SH = Shape<D, RT, LEAN>;
   constexpr int NW = SH::NW, KC = SH::KC, DT = SH::DT;
 
   const int tid = threadIdx.x;
@@ -441,9 +449,9 @@ tiles_done:
 
 // PERSIST selects the grid: one workgroup per item, or the persistent
 // grid (separate instantiations, so each inlines the item body once).
-template <typename T, int D, int RT, bool PERSIST>
+template <typename T, int D, int RT, bool PERSIST, bool LEAN>
 __global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(Params p) {
-  using SH = Shape<D, RT>;
+  using SH = Shape<D, RT, LEAN>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[SH::kBytes];
   if constexpr (!PERSIST) {
     // One workgroup per item.  Workgroups are dealt to the 8 XCDs
@@ -465,10 +473,10 @@ __global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(P
       kvh = unit % p.num_kv_heads;
       rg = unit / p.num_kv_heads;
     }
-    decode_unit<T, D, RT>(p, lds, blockIdx.y, kvh, rg, seg);
+    decode_unit<T, D, RT, LEAN>(p, lds, blockIdx.y, kvh, rg, seg);
   } else {
     persistent_loop(p, lds, SH::kPersistOff, SH::kBytes, SH::kThreads,
-                    [&](int s, int kvh, int rg, int seg) { decode_unit<T, D, RT>(p, lds, s, kvh, rg, seg); });
+                    [&](int s, int kvh, int rg, int seg) { decode_unit<T, D, RT, LEAN>(p, lds, s, kvh, rg, seg); });
   }
 }
 
@@ -730,14 +738,19 @@ tiles_done:
   finish<T, D, 1, NW>(p, lds, s, kvh, 0, seg, 0, rows, n_live, SH::kBytes);
 }
 
+// The persistent grid always fills the device and runs the lean loop; a
+// grid of one workgroup per item takes it when the plan says it fills the
+// device.  Where the ring has one tile anyway, one variant serves both.
 template <typename T, int D, int RT>
 int launch_t(const Plan& pl, const Params& pr, hipStream_t st) {
+  constexpr bool kTwo = Shape<D, RT, false>::PF != Shape<D, RT, true>::PF;
+  const dim3 grid(pl.grid_x, pl.grid_y), block(Shape<D, RT>::kThreads);
   if (pl.persistent)
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT, true>), dim3(pl.grid_x, pl.grid_y), dim3(Shape<D, RT>::kThreads),
-                       0, st, pr);
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT, true, kTwo>), grid, block, 0, st, pr);
+  else if (kTwo && pl.lean)
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT, false, kTwo>), grid, block, 0, st, pr);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT, false>), dim3(pl.grid_x, pl.grid_y), dim3(Shape<D, RT>::kThreads),
-                       0, st, pr);
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT, false, false>), grid, block, 0, st, pr);
   return int(hipGetLastError());
 }
 

@@ -73,6 +73,7 @@ struct Plan {
   int merge_slices;  // slices the merged output is cut into (1..kMaxSlices)
   int ws_nseg;       // segment slots the workspace holds (>= nseg, the same for every window)
   int persistent;    // 1: one workgroup per CU takes items from a queue
+  int lean;          // 1: the grid fills the device (single-copy tile loop)
   int grid_x, grid_y;
   // Workspace layout (byte offsets; all 256-byte aligned): the counter
   // prefix (kCounterBytes; per (unit, row group) merge_slices words, one
