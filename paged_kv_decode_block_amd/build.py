@@ -15,9 +15,17 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpad_attn.so")
+# The decode kernels keep MFMA accumulators in the VGPR form (results and
+# accumulator operands in ordinary vector registers): in the default form
+# the compiler parked the accumulators in the accumulation registers and
+# moved them back and forth around the softmax rescale on every pass of
+# the tile loop (thousands of v_accvgpr moves per kernel), and at head
+# size 512 it spilled.
+MFMA_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+
 # (source, object name, extra flags): the decode kernels build once per
 # head size, in parallel.
-SOURCES = [("decode_mfma.hip", f"decode_mfma_d{d}", [f"-DPAD_HEAD_SIZE={d}"]) for d in (64, 128, 256, 512)] + [
+SOURCES = [("decode_mfma.hip", f"decode_mfma_d{d}", [f"-DPAD_HEAD_SIZE={d}", *MFMA_FLAGS]) for d in (64, 128, 256, 512)] + [
     (src, src.rsplit(".", 1)[0], []) for src in ("zero.hip", "cache_write.hip", "calib.hip", "plan.cpp", "api.cpp")
 ]
 
