@@ -139,12 +139,15 @@ def read_ceiling(case, nseg_hint: int) -> dict:
 
 
 def kernel_hash() -> str:
-    """Hash of every kernel and planner source: a change to any of them
-    makes the committed traffic counters stale."""
+    """Hash of every kernel and planner source and of the build script
+    (its compiler flags): a change to any of them makes the committed
+    traffic counters stale."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+    paths = [os.path.join(CSRC, n) for n in sorted(os.listdir(CSRC))]
+    paths.append(os.path.join(ROOT, "paged_kv_decode_block_amd", "build.py"))
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
