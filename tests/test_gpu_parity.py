@@ -78,6 +78,18 @@ def test_length_past_table_capacity():
         check(out, ref, c.q.dtype, f"length clamped to the table, nseg={nseg}")
 
 
+@pytest.mark.parametrize("window", [0, 700])
+@pytest.mark.parametrize("schedule", [pad.PAD_SCHED_GRID, pad.PAD_SCHED_PERSISTENT])
+def test_lengths_past_planning_bound(window, schedule):
+    """Device lengths above the host's max_seq_len bound (up to the table's
+    capacity) stretch the planned segments: the block ids a segment stages
+    before its length is known are then replaced, and the result matches
+    the oracle; shorter sequences in the same batch keep the plan."""
+    c = _case(wl.CONFIGS[2], [3000, 200, 1000], 4, 93, max_blocks=192)
+    out = run_gpu(c, max_seq_len=1000, window=window, schedule=schedule)
+    check(out, oracle_out(c, window=window), c.q.dtype, f"lengths past the bound, window={window}")
+
+
 # ------------------------------------------------------- random shapes
 
 
