@@ -1,5 +1,7 @@
-// Workspace fill: the split-KV control words start at zero once per
-// workspace, and every decode launch leaves them zero.
+// Launch dispatch of the decode kernels by head size (each head size's
+// kernels live in their own build of decode_mfma.hip), and the workspace
+// fill: the split-KV control words start at zero once per workspace, and
+// every decode launch leaves them zero.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
