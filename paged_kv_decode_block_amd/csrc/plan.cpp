@@ -106,11 +106,16 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
     // batch's lengths may differ, so short sequences leave no idle CUs.
     const int64_t target = sh.num_seqs > 1 ? 2 * slots : slots;
     const int64_t fill = std::max<int64_t>(1, target / std::max<int64_t>(1, units));
-    // About 128 KiB of K/V per segment (16 tiles at head size 128, 4 at
-    // 512): with less the merge costs more than the extra parallelism
-    // saves -- but keep at least 4 segments while the device has room, so
-    // short contexts still spread their latency.
-    int64_t seg_target = std::max<int64_t>(4, (int64_t(128) << 10) / tile_bytes);
+    // About 64 KiB of K/V per segment, 4 to 8 tiles (two tiles per wave at
+    // head size 128, one at 512), and 4 tiles while that leaves fewer than
+    // 16 segments: short contexts are latency-bound, and more, shorter
+    // segments overlap more of their dependent round trips (one bf16
+    // sequence, 32/8 heads of 128, M=1: 1k keys in 16 segments 9.1 us
+    // against 11.2 us in 4; 2k keys in 16 segments 10.2 against 11.3 us in
+    // 8; 4k keys in 32 segments 12.0 against 12.6 us in 16).  At least 4
+    // segments while the device has room.
+    int64_t seg_target = std::max<int64_t>(4, std::min<int64_t>(8, (int64_t(64) << 10) / tile_bytes));
+    if (span_tiles / seg_target < 16) seg_target = 4;
     // Where that still leaves 32 or more segments, a segment also keeps its
     // partial (wg_rows rows of D + 2 floats, written and read back) below a
     // sixth of its K/V bytes: wide heads with many live rows otherwise spend
