@@ -194,6 +194,16 @@ def test_plan_partial_bound_for_wide_heads():
     assert plan(shape())["num_segments"] == 32
 
 
+def test_plan_short_contexts_use_short_segments():
+    """About 64 KiB of K/V per segment (8 tiles at head size 128), 4 tiles
+    while that leaves fewer than 16 segments, capped by one workgroup per
+    CU: 1k keys split 16 ways, 2k keys 16, 4k and longer 32 (8 kv heads)."""
+    for keys, want in ((512, 8), (1024, 16), (2048, 16), (4096, 32), (8192, 32), (32768, 32)):
+        p = plan(shape(max_blocks_per_seq=keys // 16))
+        assert p["num_segments"] == want, (keys, p)
+        assert p["segment_tiles"] >= 4
+
+
 def test_forced_segments():
     for n in (1, 2, 7, 256):
         p = plan(shape(num_segments=n, max_blocks_per_seq=64))
