@@ -107,15 +107,19 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
     const int64_t target = sh.num_seqs > 1 ? 2 * slots : slots;
     const int64_t fill = std::max<int64_t>(1, target / std::max<int64_t>(1, units));
     // About 64 KiB of K/V per segment, 4 to 8 tiles (two tiles per wave at
-    // head size 128, one at 512), and 4 tiles while that leaves fewer than
-    // 16 segments: short contexts are latency-bound, and more, shorter
-    // segments overlap more of their dependent round trips (one bf16
-    // sequence, 32/8 heads of 128, M=1: 1k keys in 16 segments 9.1 us
-    // against 11.2 us in 4; 2k keys in 16 segments 10.2 against 11.3 us in
-    // 8; 4k keys in 32 segments 12.0 against 12.6 us in 16).  At least 4
-    // segments while the device has room.
+    // head size 128, one at 512), 4 tiles while that leaves fewer than 16
+    // segments, and 2 where that makes at most 16 (a 512-key window of head
+    // size 256 at M=4 took 12.1 us in 17 two-tile segments against 11.4 in
+    // 7 longer ones): short contexts are latency-bound, and more,
+    // shorter segments overlap more of their dependent round trips (one
+    // bf16 sequence, 32/8 heads of 128, M=1: 256 keys in 8 segments 7.5 us
+    // against 8.3 in 4; 1k keys in 16 segments 9.1 us against 11.2 us in 4;
+    // 2k keys in 16 segments 10.2 against 11.3 us in 8; 4k keys in 32
+    // segments 12.0 against 12.6 us in 16).  At least 4 segments while the
+    // device has room.
     int64_t seg_target = std::max<int64_t>(4, std::min<int64_t>(8, (int64_t(64) << 10) / tile_bytes));
     if (span_tiles / seg_target < 16) seg_target = 4;
+    if (span_tiles / seg_target < 16 && ceil_div(span_tiles, 2) <= 16) seg_target = 2;
     // Where that still leaves 32 or more segments, a segment also keeps its
     // partial (wg_rows rows of D + 2 floats, written and read back) below a
     // sixth of its K/V bytes: wide heads with many live rows otherwise spend
@@ -129,6 +133,11 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
     if (part_min > seg_target && span_tiles / part_min >= 32) seg_target = part_min;
     const int64_t work = std::max<int64_t>(1, span_tiles / seg_target);
     nseg = std::min<int64_t>(fill, std::max<int64_t>(work, std::min<int64_t>(4, fill)));
+    // A unit of at most 64 KiB of K/V runs as one segment: its loop is a
+    // single round of loads, shorter than the split-KV epilogue (one bf16
+    // sequence, 32/8 heads of 128, 128 keys: 6.4 us against 7.2 us at the
+    // best split; fp16, 4/1 heads of 64, 256 keys: 5.5 against 6.5 us).
+    if (span_tiles * tile_bytes <= (int64_t(64) << 10)) nseg = 1;
   }
   nseg = std::min<int64_t>(nseg, span_tiles);
   nseg = std::min<int64_t>(nseg, kMaxSegments);
@@ -196,7 +205,10 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
       ws_nseg = sh.num_segments;
     } else {
       const int64_t target = sh.num_seqs > 1 ? 2 * slots : slots;
-      ws_nseg = may_grid ? std::max<int64_t>(1, target / std::max<int64_t>(1, units)) : 1;
+      // A window-free span of at most 64 KiB per unit plans one segment
+      // (and so does every window, which only shortens it).
+      const bool one_seg = all_tiles * tile_bytes <= (int64_t(64) << 10);
+      ws_nseg = may_grid && !one_seg ? std::max<int64_t>(1, target / std::max<int64_t>(1, units)) : 1;
       if (may_persist) ws_nseg = std::max(ws_nseg, ceil_div(all_tiles, seg_persist));
     }
     ws_nseg = std::min(ws_nseg, std::min<int64_t>(all_tiles, kMaxSegments));

@@ -195,13 +195,17 @@ def test_plan_partial_bound_for_wide_heads():
 
 
 def test_plan_short_contexts_use_short_segments():
-    """About 64 KiB of K/V per segment (8 tiles at head size 128), 4 tiles
-    while that leaves fewer than 16 segments, capped by one workgroup per
-    CU: 1k keys split 16 ways, 2k keys 16, 4k and longer 32 (8 kv heads)."""
-    for keys, want in ((512, 8), (1024, 16), (2048, 16), (4096, 32), (8192, 32), (32768, 32)):
+    """About 64 KiB of K/V per segment (8 tiles at head size 128), 4 and
+    then 2 tiles while that leaves fewer than 16 segments, capped by one
+    workgroup per CU; a unit of at most 64 KiB of K/V is one segment."""
+    for keys, want in ((128, 1), (256, 8), (512, 16), (1024, 16), (2048, 16), (4096, 32), (8192, 32),
+                       (32768, 32)):
         p = plan(shape(max_blocks_per_seq=keys // 16))
         assert p["num_segments"] == want, (keys, p)
-        assert p["segment_tiles"] >= 4
+        assert p["segment_tiles"] >= 2 or p["num_segments"] == 1
+    one = plan(shape(num_q_heads=4, num_kv_heads=1, head_size=64, max_blocks_per_seq=16, dtype=pad.PAD_F16,
+                     query_len=1))  # 256 keys of head size 64: 64 KiB per unit
+    assert one["num_segments"] == 1 and one["workspace_bytes"] == 0
 
 
 def test_forced_segments():
