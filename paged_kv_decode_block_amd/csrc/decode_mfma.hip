@@ -184,6 +184,16 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
   // same slots in both passes, so a second pass needs no barrier first.
   int* sm_ids = reinterpret_cast<int*>(lds + SH::kVBytes);
   const bool spec_ids = p.window == 0;
+  // The block id of each wave's first tile (without a window) by one
+  // wave-uniform load beside the length, issued before the staging loads:
+  // an in-range read of the table row, used only once the length shows the
+  // tile exists, so the first K/V loads wait neither for the staged ids
+  // nor for the barrier.
+  int blk_first = 0;
+  if (spec_ids) {
+    const int b = ((seg * p.seg_tiles + wave) * 16) / p.page_size;
+    blk_first = __builtin_amdgcn_readfirstlane(table[min(b, p.max_blocks - 1)]);
+  }
   if (spec_ids) {
     const int ts0 = seg * p.seg_tiles;
     for (int t = tid; t < p.seg_tiles; t += SH::kThreads) {
@@ -262,11 +272,11 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
     i32x4 v[KC];
   };
 
-  if (!(spec_ids && seg_tiles == p.seg_tiles && ts == seg * p.seg_tiles))
+  // Without a window (and unless a length past the planning bound
+  // stretched the segments) the ids staged above are the segment's.
+  const bool early = spec_ids && seg_tiles == p.seg_tiles && ts == seg * p.seg_tiles;
+  if (!early)
     for (int t = tid; t < te - ts; t += SH::kThreads) sm_ids[t] = table[((ts + t) * 16) / p.page_size];
-  __syncthreads();
-  // Physical block of tile t (wave-uniform).
-  auto block_of = [&](int t) { return __builtin_amdgcn_readfirstlane(sm_ids[t - ts]); };
 
   auto issue_tile = [&](Tile& tl, int t, int blk) {
     const int key0 = t * 16;
@@ -278,6 +288,18 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) tl.v[kc] = *reinterpret_cast<const i32x4*>(row + 2 * D + 64 * kc);
   };
+
+  // Interleaved tiles per wave: tile i of this wave is ts + wave + i * NW.
+  const int first_t = ts + wave;
+  const int n_w = first_t < te ? (te - first_t + NW - 1) / NW : 0;
+  // The first tile's loads go out before the barrier that publishes the
+  // staged ids when its block id is already known.
+  Tile ring[SH::PF + 1];
+  if (early && n_w > 0) issue_tile(ring[0], first_t, blk_first);
+  __syncthreads();
+  // Physical block of tile t (wave-uniform).
+  auto block_of = [&](int t) { return __builtin_amdgcn_readfirstlane(sm_ids[t - ts]); };
+  if (!early && n_w > 0) issue_tile(ring[0], first_t, block_of(first_t));
 
   // Scores of tile t: stage its V rows in LDS, S^T = K Q^T, mask, online
   // softmax; leaves P (input dtype, MFMA B layout) in pb.  After it the
@@ -357,23 +379,19 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // Interleaved tiles per wave: tile i of this wave is ts + wave + i * NW.
   // PF tiles are in flight beyond the one being computed (a ring of PF + 1
-  // register buffers), and each tile's block id is read one tile before
-  // its loads are issued.  The prefetch index is clamped to the wave's last
-  // tile instead of being skipped, so every iteration has the same loads in
-  // flight and the compiler's wait counts stay exact (the clamped re-reads
-  // of the last tile hit in cache).
-  const int first_t = ts + wave;
-  const int n_w = first_t < te ? (te - first_t + NW - 1) / NW : 0;
+  // register buffers, the first issued above), and each tile's block id is
+  // read one tile before its loads are issued.  The prefetch index is
+  // clamped to the wave's last tile instead of being skipped, so every
+  // iteration has the same loads in flight and the compiler's wait counts
+  // stay exact (the clamped re-reads of the last tile hit in cache).
   auto tile_at = [&](int i) { return first_t + min(i, n_w - 1) * NW; };
   if constexpr (SH::PF == 0) {
     // No register room for a second tile: the next tile's loads go out as
     // soon as the scores have consumed the current one, so they overlap
     // the PV product (whose V operand is already in LDS).
     if (n_w > 0) {
-      Tile tl;
-      issue_tile(tl, first_t, block_of(first_t));
+      Tile& tl = ring[0];
       for (int i = 0; i < n_w; ++i) {
         uint64_t pb[RT];
         score_tile(tl, first_t + i * NW, pb);
@@ -384,9 +402,8 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
   } else if (n_w > 0) {
     // (Reloading a tile's registers right after its scores, which keeps
     // PF + 1 tiles in flight through the PV product, measured slower.)
-    Tile ring[SH::PF + 1];
 #pragma unroll
-    for (int u = 0; u < SH::PF; ++u) issue_tile(ring[u], tile_at(u), block_of(tile_at(u)));
+    for (int u = 1; u < SH::PF; ++u) issue_tile(ring[u], tile_at(u), block_of(tile_at(u)));
     int blk_next = block_of(tile_at(SH::PF));
     for (int i = 0;; i += SH::PF + 1) {
 #pragma unroll
