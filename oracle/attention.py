@@ -30,7 +30,8 @@ the window counts the current key; a row with no visible key (sequence
 length 0, or a position before the first key) outputs zeros.
 
 Parity status: every function below is pinned (tests/test_oracle.py,
-tests/test_oracle_pins.py, tests/golden/).  No function is "parity unpinned".
+tests/oracle_pins.py, tests/test_oracle_mutants.py, tests/golden/).  No function
+is "parity unpinned".
 """
 
 from __future__ import annotations
