@@ -21,7 +21,10 @@ LIB = os.path.join(HERE, "libpad_attn.so")
 # moved them back and forth around the softmax rescale on every pass of
 # the tile loop (thousands of v_accvgpr moves per kernel), and at head
 # size 512 it spilled.
-MFMA_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+MFMA_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
+              # The decode kernel's leading scalar arguments (what its first
+              # loads depend on) are preloaded into scalar registers.
+              "-mllvm", "-amdgpu-kernarg-preload-count=14"]
 
 # (source, object name, extra flags): the decode kernels build once per
 # head size, in parallel.

@@ -162,16 +162,11 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 4, c = lane & 15;
-  const SeqQ sq = seq_queries(p, s);
-  const int M = sq.m;
-  const int rows = p.group * M;  // this sequence's query rows
-  const int row0 = rg * RT * 16;
-  const int wg_rows = min(RT * 16, rows - row0);
-  if (wg_rows <= 0) return;  // no query token, or a row group past this sequence's rows
-
   // The length is read first and used last in this prologue: the loads
   // that do not depend on it (the query rows and, without a window, the
-  // segment's block ids) are in flight at the same time.
+  // segment's block ids) are in flight at the same time.  It and the first
+  // block id are read before the query count is known (both reads are in
+  // range for any sequence), so they depend on preloaded arguments only.
   const int L_dev = p.seq_lens[s];
   const int32_t* table = p.block_table + int64_t(s) * p.max_blocks;
   // The segment's block ids (one per tile) go to LDS once, so a tile's
@@ -194,6 +189,13 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
     const int b = ((seg * p.seg_tiles + wave) * 16) / p.page_size;
     blk_first = __builtin_amdgcn_readfirstlane(table[min(b, p.max_blocks - 1)]);
   }
+  const SeqQ sq = seq_queries(p, s);
+  const int M = sq.m;
+  const int rows = p.group * M;  // this sequence's query rows
+  const int row0 = rg * RT * 16;
+  const int wg_rows = min(RT * 16, rows - row0);
+  if (wg_rows <= 0) return;  // no query token, or a row group past this sequence's rows
+
   if (spec_ids) {
     const int ts0 = seg * p.seg_tiles;
     for (int t = tid; t < p.seg_tiles; t += SH::kThreads) {
@@ -466,8 +468,33 @@ tiles_done:
 
 // PERSIST selects the grid: one workgroup per item, or the persistent
 // grid (separate instantiations, so each inlines the item body once).
+// The arguments the prologue's first loads depend on (the length, the first
+// block id and the first K/V tile's address) lead the argument list as
+// scalars, and the build preloads their first 14 dwords (all but the
+// token stride, which is needed only once the length has arrived) into
+// scalar registers before the waves start (the compiler option
+// -amdgpu-kernarg-preload-count): those loads then wait for no
+// kernel-argument fetch.  The other fields stay in the Params block; the
+// host keeps the three strides within 32 bits.  (One sequence of 32k keys: 31.35 ->
+// 31.03 us; 4k keys: 12.89 -> 12.65 us.)
 template <typename T, int D, int RT, bool PERSIST, bool LEAN>
-__global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(Params p) {
+__global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(
+    const int32_t* seq_lens, const int32_t* block_table, const void* kv, int32_t row_groups, int32_t num_kv_heads,
+    int32_t max_blocks, int32_t seg_tiles, int32_t page_size, int32_t window, int32_t block_stride,
+    int32_t head_stride, int32_t token_stride, Params params) {
+  Params p = params;
+  p.seq_lens = seq_lens;
+  p.block_table = block_table;
+  p.kv = kv;
+  p.row_groups = row_groups;
+  p.num_kv_heads = num_kv_heads;
+  p.max_blocks = max_blocks;
+  p.seg_tiles = seg_tiles;
+  p.page_size = page_size;
+  p.window = window;
+  p.block_stride = block_stride;
+  p.head_stride = head_stride;
+  p.token_stride = token_stride;
   using SH = Shape<D, RT, LEAN>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[SH::kBytes];
   if constexpr (!PERSIST) {
@@ -763,11 +790,11 @@ int launch_t(const Plan& pl, const Params& pr, hipStream_t st) {
   constexpr bool kTwo = Shape<D, RT, false>::PF != Shape<D, RT, true>::PF;
   const dim3 grid(pl.grid_x, pl.grid_y), block(Shape<D, RT>::kThreads);
   if (pl.persistent)
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT, true, kTwo>), grid, block, 0, st, pr);
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT, true, kTwo>), grid, block, 0, st, pr.seq_lens, pr.block_table, pr.kv, pr.row_groups, pr.num_kv_heads, pr.max_blocks, pr.seg_tiles, pr.page_size, pr.window, int32_t(pr.block_stride), int32_t(pr.head_stride), int32_t(pr.token_stride), pr);
   else if (kTwo && pl.lean)
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT, false, kTwo>), grid, block, 0, st, pr);
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT, false, kTwo>), grid, block, 0, st, pr.seq_lens, pr.block_table, pr.kv, pr.row_groups, pr.num_kv_heads, pr.max_blocks, pr.seg_tiles, pr.page_size, pr.window, int32_t(pr.block_stride), int32_t(pr.head_stride), int32_t(pr.token_stride), pr);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT, false, false>), grid, block, 0, st, pr);
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT, false, false>), grid, block, 0, st, pr.seq_lens, pr.block_table, pr.kv, pr.row_groups, pr.num_kv_heads, pr.max_blocks, pr.seg_tiles, pr.page_size, pr.window, int32_t(pr.block_stride), int32_t(pr.head_stride), int32_t(pr.token_stride), pr);
   return int(hipGetLastError());
 }
 

@@ -42,6 +42,9 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   if (sh.query_len > kMaxQueryLen || !known_head_size(sh.head_size) || sh.page_size % kTileKeys != 0)
     return PAD_EUNSUPPORTED;
   if (sh.num_seqs > 65535) return PAD_EUNSUPPORTED;
+  // The decode kernel takes the cache strides (at most one block's
+  // elements) as 32-bit values.
+  if (int64_t(sh.num_kv_heads) * sh.page_size * 2 * sh.head_size > INT32_MAX) return PAD_EUNSUPPORTED;
   const int G = sh.num_q_heads / sh.num_kv_heads;
   const int rows = G * sh.query_len;
   if (rows > kMaxRows) return PAD_EUNSUPPORTED;

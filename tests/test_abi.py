@@ -258,12 +258,21 @@ def test_window_plan_is_smaller():
         (dict(path=pad.PAD_PATH_DOT, query_len=1, head_size=256), pad.PAD_EUNSUPPORTED),
         (dict(num_seqs=-1), pad.PAD_EINVAL),
         (dict(max_blocks_per_seq=0), pad.PAD_EINVAL),
+        # one block of more than 2^31 - 1 elements (the kernel's strides are 32-bit)
+        (dict(head_size=512, num_q_heads=64, num_kv_heads=64, page_size=32768, query_len=1, max_blocks_per_seq=4),
+         pad.PAD_EUNSUPPORTED),
     ],
 )
 def test_plan_rejects(kw, status):
     with pytest.raises(pad.PadError) as e:
         plan(shape(**kw))
     assert e.value.status == status
+
+
+def test_plan_accepts_largest_32bit_block():
+    # 64 kv heads x 32752 tokens x 2 x 512 elements = 2,146,435,072 < 2^31.
+    p = plan(shape(head_size=512, num_q_heads=64, num_kv_heads=64, page_size=32752, query_len=1, max_blocks_per_seq=4))
+    assert p["num_segments"] >= 1
 
 
 def test_plan_rejects_bad_window_and_cus():
