@@ -475,8 +475,8 @@ tiles_done:
 // scalar registers before the waves start (the compiler option
 // -amdgpu-kernarg-preload-count): those loads then wait for no
 // kernel-argument fetch.  The other fields stay in the Params block; the
-// host keeps the three strides within 32 bits.  (One sequence of 32k keys: 31.35 ->
-// 31.03 us; 4k keys: 12.89 -> 12.65 us.)
+// host keeps the three strides within 32 bits.  (One sequence of 32k
+// keys: 31.35 -> 31.03 us; 4k keys: 12.89 -> 12.65 us.)
 template <typename T, int D, int RT, bool PERSIST, bool LEAN>
 __global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(
     const int32_t* seq_lens, const int32_t* block_table, const void* kv, int32_t row_groups, int32_t num_kv_heads,
@@ -789,12 +789,13 @@ template <typename T, int D, int RT>
 int launch_t(const Plan& pl, const Params& pr, hipStream_t st) {
   constexpr bool kTwo = Shape<D, RT, false>::PF != Shape<D, RT, true>::PF;
   const dim3 grid(pl.grid_x, pl.grid_y), block(Shape<D, RT>::kThreads);
-  if (pl.persistent)
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT, true, kTwo>), grid, block, 0, st, pr.seq_lens, pr.block_table, pr.kv, pr.row_groups, pr.num_kv_heads, pr.max_blocks, pr.seg_tiles, pr.page_size, pr.window, int32_t(pr.block_stride), int32_t(pr.head_stride), int32_t(pr.token_stride), pr);
-  else if (kTwo && pl.lean)
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT, false, kTwo>), grid, block, 0, st, pr.seq_lens, pr.block_table, pr.kv, pr.row_groups, pr.num_kv_heads, pr.max_blocks, pr.seg_tiles, pr.page_size, pr.window, int32_t(pr.block_stride), int32_t(pr.head_stride), int32_t(pr.token_stride), pr);
-  else
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, RT, false, false>), grid, block, 0, st, pr.seq_lens, pr.block_table, pr.kv, pr.row_groups, pr.num_kv_heads, pr.max_blocks, pr.seg_tiles, pr.page_size, pr.window, int32_t(pr.block_stride), int32_t(pr.head_stride), int32_t(pr.token_stride), pr);
+  const auto kernel = pl.persistent      ? decode_mfma_kernel<T, D, RT, true, kTwo>
+                      : kTwo && pl.lean ? decode_mfma_kernel<T, D, RT, false, kTwo>
+                                        : decode_mfma_kernel<T, D, RT, false, false>;
+  // The strides fit in 32 bits (checked by the planner).
+  hipLaunchKernelGGL(kernel, grid, block, 0, st, pr.seq_lens, pr.block_table, pr.kv, pr.row_groups, pr.num_kv_heads,
+                     pr.max_blocks, pr.seg_tiles, pr.page_size, pr.window, int32_t(pr.block_stride),
+                     int32_t(pr.head_stride), int32_t(pr.token_stride), pr);
   return int(hipGetLastError());
 }
 
