@@ -4,18 +4,20 @@
 A step is one pad_decode_attn call (the whole hot path: plan, page gather,
 QK^T, mask, online softmax, PV, split partials and in-kernel merge) over one
 batch of seeded synthetic inputs.  The default workload is benchmark
-configuration 2 -- batch 1, bf16, head size 128, 32 q heads / 8 kv heads,
-page size 16, HND, shuffled block table -- at its longest context (32768)
-and largest query count (M = 4), with the K/V pool at 512 MiB so the
-rotating instances stay out of the 256 MiB last-level cache.
+configuration 5, the largest: a batch of 64 bf16 sequences with lengths
+uniform in [512, 16384] plus one padded sequence, head size 256, 16 q heads
+/ 2 kv heads, page size 1056, HND, random block table, M = 4 -- about
+1.15 GB of K/V per call, so no call is served from the 256 MiB last-level
+cache.
 
 The metric is effective HBM bandwidth: bytes of the distinct K/V rows the
 call must read, plus Q and O, per second; and its fraction of the 8 TB/s
 HBM peak.  Beside it, ``read_ceiling`` reports what plain reads reach on
-the same device: a kernel that gathers exactly the call's pages with the
-same table walk and 16-byte loads but no arithmetic (best of a small sweep
-of launch shapes), and a contiguous stream over the pool.  One JSON line is
-printed.
+the same device (a gather of exactly the call's pages with the same table
+walk and no arithmetic, contiguous streams over a 512 MiB buffer with
+several workgroup sizes and loads in flight, and a device-to-device copy),
+and ``sweep`` times every (context, M) point of the other benchmark
+configurations, graph-timed.  One JSON line is printed.
 """
 
 from __future__ import annotations
@@ -35,7 +37,15 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of one MI355X
 POOL_BYTES = 512 << 20
 COPY_BYTES = 256 << 20  # --copy-calibration: bytes read (and written) per copy
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_mfma_bf16_D128_Hq32_Hkv8_L32768_M4.json")
+# Committed HBM-traffic counter runs, by (config, context, M) of the
+# workload they were taken on (MFMA family, automatic plan).
+TRAFFIC_FILES = {
+    (2, 32768, 4): "traffic_decode_mfma_bf16_D128_Hq32_Hkv8_L32768_M4.json",
+    (3, 16384, 4): "traffic_decode_mfma_fp16_D256_Hq8_Hkv2_NHD_W512_L16384_M4.json",
+    (4, 32768, 1): "traffic_decode_mfma_bf16_D512_Hq16_Hkv2_L32768_M1.json",
+    (4, 32768, 8): "traffic_decode_mfma_bf16_D512_Hq16_Hkv2_L32768_M8.json",
+    (5, 16384, 4): "traffic_decode_mfma_persistent_bf16_D256_Hq16_Hkv2_P1056_batch64_M4.json",
+}
 CSRC = os.path.join(ROOT, "paged_kv_decode_block_amd", "csrc")
 
 
@@ -122,19 +132,35 @@ def read_ceiling(case, nseg_hint: int) -> dict:
                 if best is None or gbs > best["GB/s"]:
                     best = {"GB/s": round(gbs, 1), "us": round(ms * 1e3, 3), "waves": waves,
                             "tiles_in_flight": tif, "segments": sg}
-    pool = case.kv_cache.view(-1)
-    pool_bytes = pool.numel() * pool.element_size()
-    stream_best = None
-    for blocks in (1024, 2048, 4096, 8192):
-        ms = _event_time(lambda i, b=blocks: pad.pad_calib_stream_read(pool, sink, blocks=b), 5, 20)
-        gbs = pool_bytes / (ms * 1e-3) / 1e9
-        if stream_best is None or gbs > stream_best["GB/s"]:
-            stream_best = {"GB/s": round(gbs, 1), "blocks": blocks}
+    buf = torch.empty(POOL_BYTES // 2, dtype=torch.bfloat16, device=case.q.device)
+    buf_bytes = buf.numel() * buf.element_size()
+    stream_best, stream_all = None, []
+    for threads in (256, 512, 1024):
+        for loads in (4, 8, 16):
+            for blocks in (1024, 2048, 4096, 8192):
+                ms = _event_time(lambda i, b=blocks, t=threads, u=loads: pad.pad_calib_stream_read(
+                    buf, sink, blocks=b, threads=t, loads_in_flight=u), 3, 10)
+                gbs = buf_bytes / (ms * 1e-3) / 1e9
+                stream_all.append(round(gbs, 1))
+                if stream_best is None or gbs > stream_best["GB/s"]:
+                    stream_best = {"GB/s": round(gbs, 1), "blocks": blocks, "threads": threads,
+                                   "loads_in_flight": loads}
+    # torch's device-to-device copy of half the buffer into the other half:
+    # bytes read plus bytes written per second
+    half = buf.numel() // 2
+    src, dst = buf[:half], buf[half:]
+    ms = _event_time(lambda i: dst.copy_(src), 3, 10)
+    copy = {"GB/s": round(2 * half * buf.element_size() / (ms * 1e-3) / 1e9, 1),
+            "bytes_read": half * buf.element_size()}
+    del buf, src, dst
     return {
         "gather_read": best,
         "gather_bytes_per_launch": nbytes,
         "stream_read": stream_best,
-        "stream_bytes": pool_bytes,
+        "stream_read_variants": len(stream_all),
+        "stream_read_median_GB/s": sorted(stream_all)[len(stream_all) // 2],
+        "stream_bytes": buf_bytes,
+        "device_copy": copy,
     }
 
 
@@ -227,17 +253,23 @@ def cpu_baseline(cfg: int, context: int, M: int, budget_s: float = 12.0) -> dict
         "value": round(gbs, 4),
         "unit": "GB/s",
         "cores": int(cores),
+        "host_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": f"{calls} full call(s) of the config {cfg} workload at context {context}, M={M} "
-                  f"({case.num_seqs} sequence(s), all kv heads), {el:.1f} s of host time; BLAS threads as reported",
+                  f"({case.num_seqs} sequence(s), all kv heads), {el:.1f} s of host time; cores = the BLAS "
+                  f"threads the oracle's products use, host_cpus = os.cpu_count()",
     }
 
 
-def traffic_entry():
-    """Measured HBM bytes per launch from the committed counter runs, if
-    they were taken on the current kernel source."""
+def traffic_entry(cfg: int, context: int, M: int):
+    """Measured HBM bytes per launch from the committed counter runs of
+    this workload, if there are any and they were taken on the current
+    kernel source."""
+    name = TRAFFIC_FILES.get((cfg, context, M))
+    if name is None:
+        return None
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(ROOT, "profiles", name)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -296,7 +328,7 @@ def varlen_main(args) -> int:
                 moved += L * spec.num_kv_heads * 2 * spec.head_size * eb + 2 * (b - a) * spec.num_q_heads * spec.head_size * eb
             done += 1
         el = time.perf_counter() - t0
-        cpu = {"value": round(moved / el / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
+        cpu = {"value": round(moved / el / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(), "host_cpus": os.cpu_count(), "kind": "oracle",
                "sample": f"{done} of {S} sequences of the mixed batch, one varlen oracle call each, {el:.1f} s"}
     line = {
         "metric": "decode-attention effective HBM GB/s (K+V rows read + Q + O) and fraction of 8 TB/s",
@@ -366,6 +398,7 @@ def cache_write_main(args) -> int:
         el = time.perf_counter() - t0
         per_tok = nbytes / T
         cpu = {"value": round(per_tok * n * calls / el / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
+               "host_cpus": os.cpu_count(),
                "kind": "oracle", "sample": f"{calls} oracle call(s) on the first {n} tokens, {el:.1f} s"}
     line = {
         "metric": "KV-cache write effective HBM GB/s (key, value, query rows, cos/sin in; cache slots, query rows out) "
@@ -415,7 +448,7 @@ def prefill_main(args) -> int:
         t0 = time.perf_counter()
         oracle.decode_attention(q64, kv64, table, lens, case.scale, case.window, case.layout)
         el = time.perf_counter() - t0
-        cpu = {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+        cpu = {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": _blas_threads(), "host_cpus": os.cpu_count(), "kind": "oracle",
                "sample": f"one full call, {el:.1f} s"}
     line = {
         "metric": "prefill-chunk attention TFLOP/s (QK^T + PV over visible keys) and fraction of the bf16 MFMA peak",
@@ -438,10 +471,13 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--context", type=int, default=None)
     ap.add_argument("--queries", type=int, default=None)
-    ap.add_argument("--no-sweep", action="store_true", help="skip the per-(context, M) sweep of the config")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the per-(context, M) sweep of every benchmark configuration")
+    ap.add_argument("--sweep-configs", default="1,2,3,4,5",
+                    help="configurations whose points the sweep times (comma-separated)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling calibration kernels")
     ap.add_argument("--segments", type=int, default=0,
@@ -482,13 +518,14 @@ def main() -> int:
     M = args.queries or max(pts["queries"])
     spec = wl.CONFIGS[cfg]
 
-    def build_case(ctx, m):
-        per_inst = spec.block_bytes * (-(-ctx // spec.page_size))
-        inst = max(1, POOL_BYTES // per_inst) if cfg != 5 else 1
-        return wl.config_case(cfg, ctx, m, device="cuda", instances=inst, pool_bytes=POOL_BYTES)
+    def build_case(c, ctx, m):
+        sp = wl.CONFIGS[c]
+        per_inst = sp.block_bytes * (-(-ctx // sp.page_size))
+        inst = max(1, POOL_BYTES // per_inst) if c != 5 else 1
+        return wl.config_case(c, ctx, m, device="cuda", instances=inst, pool_bytes=POOL_BYTES)
 
     print(f"[bench] config {cfg}: context {context}, M={M}: building inputs", file=sys.stderr, flush=True)
-    case = build_case(context, M)
+    case = build_case(cfg, context, M)
     nbytes = effective_bytes(case)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -509,27 +546,34 @@ def main() -> int:
         ceiling = read_ceiling(case, plan["num_segments"])
         ceiling["frac_of_gather_read"] = round(gbs / ceiling["gather_read"]["GB/s"], 4)
         print(f"[bench] read ceiling: gather {ceiling['gather_read']['GB/s']} GB/s, "
-              f"stream {ceiling['stream_read']['GB/s']} GB/s", file=sys.stderr, flush=True)
+              f"stream {ceiling['stream_read']['GB/s']} GB/s, copy {ceiling['device_copy']['GB/s']} GB/s",
+              file=sys.stderr, flush=True)
 
     sweep = []
     if not args.no_sweep:
-        for ctx in pts["contexts"]:
-            for m in pts["queries"]:
-                if path == pad.PAD_PATH_DOT and m * spec.num_q_heads // spec.num_kv_heads > 4:
-                    continue  # the dot family serves at most 4 query rows per kv head
-                c = build_case(ctx, m)
-                try:
-                    t, p = time_calls(c, 20, 100, graph=True, path=path)
-                except pad.PadError as e:
-                    if e.status != pad.PAD_EUNSUPPORTED:
-                        raise
-                    del c
-                    continue  # a forced family that does not serve this shape
-                b = effective_bytes(c)
-                sweep.append({"context": ctx, "M": m, "us": round(t * 1e3, 3), "GB/s": round(b / (t * 1e-3) / 1e9, 1),
-                              "frac": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "segments": p["num_segments"]})
-                del c
-        print(f"[bench] sweep done ({len(sweep)} points)", file=sys.stderr, flush=True)
+        for c in [int(x) for x in args.sweep_configs.split(",") if x]:
+            pts_c, spec_c = wl.CONFIG_POINTS[c], wl.CONFIGS[c]
+            for ctx in pts_c["contexts"]:
+                for m in pts_c["queries"]:
+                    if (c, ctx, m) == (cfg, context, M):
+                        continue  # the headline itself
+                    if path == pad.PAD_PATH_DOT and m * spec_c.num_q_heads // spec_c.num_kv_heads > 4:
+                        continue  # the dot family serves at most 4 query rows per kv head
+                    cs = build_case(c, ctx, m)
+                    try:
+                        t, p = time_calls(cs, 20, 100, graph=True, path=path)
+                    except pad.PadError as e:
+                        if e.status != pad.PAD_EUNSUPPORTED:
+                            raise
+                        del cs
+                        continue  # a forced family that does not serve this shape
+                    b = effective_bytes(cs)
+                    sweep.append({"config": c, "context": ctx, "M": m, "us": round(t * 1e3, 3),
+                                  "GB/s": round(b / (t * 1e-3) / 1e9, 1),
+                                  "frac": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "segments": p["num_segments"]})
+                    del cs
+            print(f"[bench] sweep of config {c} done ({len(sweep)} points so far)", file=sys.stderr, flush=True)
 
     cpu = None if args.no_cpu else cpu_baseline(cfg, context, M)
     line = {
@@ -546,12 +590,13 @@ def main() -> int:
         "dtype": spec.dtype,
         "data": "synthetic",
         "config": {
-            "workload": f"config {cfg}: batch {case.num_seqs}, {spec.dtype}, D={spec.head_size}, "
-                        f"{spec.num_q_heads}/{spec.num_kv_heads} heads, page {spec.page_size}, "
-                        f"{'HND' if spec.layout == wl.HND else 'NHD'}, window {case.window}",
+            "workload": f"config {cfg}: batch {case.num_seqs}"
+                        + (f" ({case.num_seqs - 1} sequences of 512..{context} keys + 1 padded)" if cfg == 5 else "")
+                        + f", {spec.dtype}, D={spec.head_size}, {spec.num_q_heads}/{spec.num_kv_heads} heads, "
+                        f"page {spec.page_size}, {'HND' if spec.layout == wl.HND else 'NHD'}, window {case.window}, M={M}",
             "context": context,
             "query_len": M,
-            "pool_bytes": POOL_BYTES,
+            "pool_bytes": max(POOL_BYTES, case.kv_cache.numel() * case.kv_cache.element_size()),
             "instances": len(case.block_tables),
             "bytes_per_step": nbytes,
             "plan": plan,
@@ -562,8 +607,9 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
-            # measured on config 2, context 32768, M = 4 with the MFMA family
-            "traffic": traffic_entry() if (cfg, context, M) == (2, 32768, 4) and path != pad.PAD_PATH_DOT else None,
+            # HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE
+            # runs of this workload, while the kernel source is unchanged
+            "traffic": traffic_entry(cfg, context, M) if path != pad.PAD_PATH_DOT and args.segments == 0 else None,
         },
         "read_ceiling": ceiling,
         "cpu_baseline": cpu,

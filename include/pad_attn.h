@@ -59,9 +59,12 @@
  * block ids in the block table must address existing blocks for every page
  * a sequence's visible keys touch; violating it is undefined behaviour.  A
  * seq_lens[s] above max_blocks_per_seq * page_size is treated as that
- * capacity, and one <= 0 gives a zero output for the sequence.  Table
- * entries of pages no visible key touches (before a window, past a
- * sequence's end, the rows of length-0 sequences) are never read.
+ * capacity, and one <= 0 gives a zero output for the sequence.  The block
+ * table must span [num_seqs, max_blocks_per_seq] int32 entries, all
+ * readable: the kernel may read entries of pages no visible key touches
+ * (before a window, past a sequence's end, the rows of length-0 sequences)
+ * ahead of knowing the length, but never uses them, so their values are
+ * don't-care (they need not name valid blocks).
  */
 #ifndef PAD_ATTN_H
 #define PAD_ATTN_H
@@ -73,7 +76,7 @@
 extern "C" {
 #endif
 
-#define PAD_ABI_VERSION 5
+#define PAD_ABI_VERSION 6
 
 typedef enum pad_status {
   PAD_OK = 0,

@@ -49,10 +49,12 @@ pad_status pad_calib_gather_read(const pad_shape* shape, const void* kv_cache, c
                                  int32_t tiles_in_flight, int32_t segments, int32_t* sink, void* stream);
 
 /* Read `bytes` contiguous bytes from `src` (16-byte aligned, bytes a
- * multiple of 16) with 16-byte loads over a grid of `blocks` workgroups of
- * 256 threads (1..65536); each workgroup reads one contiguous range, four
- * loads in flight per thread. */
-pad_status pad_calib_stream_read(const void* src, size_t bytes, int32_t blocks, int32_t* sink, void* stream);
+ * multiple of 16) with 16-byte loads over a grid of `blocks` workgroups
+ * (1..65536) of `threads` threads (256, 512 or 1024); each workgroup reads
+ * one contiguous range with `loads_in_flight` loads per thread issued
+ * before any is consumed (4, 8 or 16).  Other values: PAD_EINVAL. */
+pad_status pad_calib_stream_read(const void* src, size_t bytes, int32_t blocks, int32_t threads,
+                                 int32_t loads_in_flight, int32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -119,8 +119,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
     ]
     L.pad_calib_stream_read.restype = ctypes.c_int
-    L.pad_calib_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
-                                        ctypes.c_void_p]
+    L.pad_calib_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     L.pad_rope_cache_write.restype = ctypes.c_int
     L.pad_rope_cache_write.argtypes = [
         P(pad_cache_shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -210,6 +210,15 @@ def pad_decode_attn_workspace_size(shape: pad_shape) -> int:
     return int(n.value)
 
 
+def _require_device(**tensors: torch.Tensor) -> None:
+    """Every argument must be a contiguous device tensor."""
+    for name, t in tensors.items():
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
 def _stream_ptr(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -225,22 +234,37 @@ def pad_decode_attn_workspace_init(workspace: torch.Tensor, stream=None) -> None
 class Workspace:
     """A zero-initialised device workspace (allocate it outside graph capture).
 
-    ``get(shape)`` returns a buffer of at least the bytes ``shape`` needs,
-    growing (and re-zeroing) it when a larger shape comes along.
+    ``get(shape, stream)`` returns a buffer of at least the bytes ``shape``
+    needs, growing (and re-zeroing) it when a larger shape comes along.  The
+    fill is enqueued on ``stream`` -- the stream the decode will run on --
+    so the launch that follows sees the zeroed control words; a buffer
+    allocated while another stream is current is recorded on ``stream``, so
+    the caching allocator does not hand its memory out again while work on
+    that stream may still use it (also when a larger shape replaces it).
+    Calls on one workspace must be issued on one stream at a time.
     """
 
     def __init__(self, device=None):
         self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
         self.buf: torch.Tensor | None = None
 
-    def get(self, shape: pad_shape) -> torch.Tensor | None:
+    def get(self, shape: pad_shape, stream=None) -> torch.Tensor | None:
         need = pad_decode_attn_workspace_size(shape)
         if need == 0:
             return self.buf
         if self.buf is None or self.buf.numel() < need:
-            self.buf = torch.empty(need, dtype=torch.uint8, device=self.device)
-            pad_decode_attn_workspace_init(self.buf)
+            buf = torch.empty(need, dtype=torch.uint8, device=self.device)
+            _record_on(buf, stream)
+            pad_decode_attn_workspace_init(buf, stream)
+            self.buf = buf
         return self.buf
+
+
+def _record_on(t: torch.Tensor, stream) -> None:
+    """Tell the caching allocator that ``stream`` (None: the current one)
+    uses ``t``, when that is not the stream it was allocated on."""
+    if stream is not None and t.is_cuda and stream != torch.cuda.current_stream(t.device):
+        t.record_stream(stream)
 
 
 def pad_set_merge_wait(microseconds: int) -> None:
@@ -248,7 +272,17 @@ def pad_set_merge_wait(microseconds: int) -> None:
     _check(lib.pad_set_merge_wait(int(microseconds)), "pad_set_merge_wait")
 
 
-_default_ws: dict[int, Workspace] = {}
+# Default workspaces, one per (device, stream): a workspace serves one
+# in-flight call at a time, so calls on different streams get their own.
+_default_ws: dict[tuple[int, int], Workspace] = {}
+
+
+def _default_workspace(device: torch.device, shape: pad_shape, stream) -> torch.Tensor | None:
+    key = (device.index, _stream_ptr(stream))
+    ws = _default_ws.get(key)
+    if ws is None:
+        ws = _default_ws[key] = Workspace(device)
+    return ws.get(shape, stream)
 
 
 def pad_decode_attn(
@@ -275,12 +309,7 @@ def pad_decode_attn(
     buffer is kept by this module (allocated on first use, so make one call
     before capturing a graph).
     """
-    for name, t in (("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
-                    ("seq_lens", seq_lens), ("out", out)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+    _require_device(q=q, kv_cache=kv_cache, block_table=block_table, seq_lens=seq_lens, out=out)
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise ValueError("block_table and seq_lens must be int32")
     if out.shape != q.shape or out.dtype != q.dtype:
@@ -289,11 +318,7 @@ def pad_decode_attn(
         raise ValueError("seq_lens must have one entry per sequence")
     shape = make_shape(q, kv_cache, block_table, layout, max_seq_len=max_seq_len,
                        num_segments=num_segments, path=path, schedule=schedule)
-    if workspace is None:
-        dev = q.device.index
-        ws = _default_ws.setdefault(dev, Workspace(q.device)).get(shape)
-    else:
-        ws = workspace
+    ws = _default_workspace(q.device, shape, stream) if workspace is None else workspace
     ws_ptr = ws.data_ptr() if ws is not None else 0
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(lib.pad_decode_attn(
@@ -331,12 +356,7 @@ def pad_decode_attn_varlen(
     ``S + 1`` entries, never read on the host).  ``max_query_len`` bounds
     every per-sequence count (it sizes the plan and the workspace).
     """
-    for name, t in (("q", q), ("q_start", q_start), ("kv_cache", kv_cache), ("block_table", block_table),
-                    ("seq_lens", seq_lens), ("out", out)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+    _require_device(q=q, q_start=q_start, kv_cache=kv_cache, block_table=block_table, seq_lens=seq_lens, out=out)
     if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("q and out must be packed [T, Hq, D] tensors of one dtype")
     S = block_table.shape[0]
@@ -348,11 +368,7 @@ def pad_decode_attn_varlen(
     q_like = torch.empty((S, max_query_len, Hq, D), dtype=q.dtype, device="meta")
     shape = make_shape(q_like, kv_cache, block_table, layout, max_seq_len=max_seq_len,
                        num_segments=num_segments, path=path, schedule=schedule)
-    if workspace is None:
-        dev = q.device.index
-        ws = _default_ws.setdefault(dev, Workspace(q.device)).get(shape)
-    else:
-        ws = workspace
+    ws = _default_workspace(q.device, shape, stream) if workspace is None else workspace
     ws_ptr = ws.data_ptr() if ws is not None else 0
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(lib.pad_decode_attn_varlen(
@@ -434,8 +450,10 @@ def pad_calib_gather_read(kv_cache: torch.Tensor, block_table: torch.Tensor, seq
         ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(_stream_ptr(stream))), "pad_calib_gather_read")
 
 
-def pad_calib_stream_read(src: torch.Tensor, sink: torch.Tensor, *, blocks: int = 2048, stream=None) -> None:
+def pad_calib_stream_read(src: torch.Tensor, sink: torch.Tensor, *, blocks: int = 2048, threads: int = 256,
+                          loads_in_flight: int = 4, stream=None) -> None:
     """Read every byte of the contiguous device tensor ``src`` (include/pad_calib.h)."""
     _check(lib.pad_calib_stream_read(
-        ctypes.c_void_p(src.data_ptr()), src.numel() * src.element_size(), int(blocks),
-        ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(_stream_ptr(stream))), "pad_calib_stream_read")
+        ctypes.c_void_p(src.data_ptr()), src.numel() * src.element_size(), int(blocks), int(threads),
+        int(loads_in_flight), ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(_stream_ptr(stream))),
+        "pad_calib_stream_read")

@@ -22,14 +22,17 @@ LIB = os.path.join(HERE, "libpad_attn.so")
 # the tile loop (thousands of v_accvgpr moves per kernel), and at head
 # size 512 it spilled.
 MFMA_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
-              # The decode kernel's leading scalar arguments (what its first
-              # loads depend on) are preloaded into scalar registers.
-              "-mllvm", "-amdgpu-kernarg-preload-count=14"]
+              # The decode kernel's first 11 arguments -- three pointers and
+              # eight int32 scalars, 14 dwords: what its first loads depend
+              # on -- are preloaded into scalar registers (the count is in
+              # arguments, not dwords).
+              "-mllvm", "-amdgpu-kernarg-preload-count=11"]
 
 # (source, object name, extra flags): the decode kernels build once per
 # head size, in parallel.
 SOURCES = [("decode_mfma.hip", f"decode_mfma_d{d}", [f"-DPAD_HEAD_SIZE={d}", *MFMA_FLAGS]) for d in (64, 128, 256, 512)] + [
-    (src, src.rsplit(".", 1)[0], []) for src in ("launch.hip", "cache_write.hip", "calib.hip", "plan.cpp", "api.cpp")
+    (src, src.rsplit(".", 1)[0], [])
+    for src in ("launch.hip", "cache_write.hip", "calib.hip", "plan.cpp", "api.cpp")
 ]
 
 # Packed fp32 VALU ops are turned off for every HIP source (the host pass

@@ -8,12 +8,17 @@
 #include <vector>
 
 #include "../../include/pad_attn.h"
+#include "entry.h"
 #include "kernels.h"
 #include "plan.h"
 
 namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+namespace pad {
 
 // Compute units of the current device (cached per device); 256 when no
 // device can be queried.
@@ -32,6 +37,12 @@ int device_cus() {
   }
   return cache[dev];
 }
+
+}  // namespace pad
+
+namespace {
+
+using pad::device_cus;
 
 // Helpers' bound on waiting for the last segment, in ticks of the 100 MHz
 // device real-time counter (see pad_set_merge_wait).
@@ -100,22 +111,30 @@ pad_status pad_decode_attn_workspace_init(void* workspace, size_t bytes, void* s
 
 }  // extern "C"
 
-namespace {
+namespace pad {
+
+pad_status check_buffers(const pad_shape* shape, const void* q, const void* kv_cache, const int32_t* block_table,
+                         const int32_t* seq_lens, float scale, const void* out) {
+  if (!std::isfinite(scale)) return PAD_EINVAL;
+  if (shape->num_seqs == 0) return PAD_OK;
+  if (!q || !kv_cache || !block_table || !seq_lens || !out) return PAD_EINVAL;
+  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(block_table, 4) ||
+      !aligned(seq_lens, 4))
+    return PAD_EINVAL;
+  return PAD_OK;
+}
 
 // One decode launch; q_start is null for the uniform [S, M, Hq, D] layout.
 pad_status decode(const pad_shape* shape, const void* q, const int32_t* q_start, const void* kv_cache,
                   const int32_t* block_table, const int32_t* seq_lens, float scale, int32_t window, void* out,
                   void* workspace, size_t workspace_bytes, void* stream) {
   if (!shape) return PAD_EINVAL;
-  if (!std::isfinite(scale)) return PAD_EINVAL;
   pad::Plan p;
   const pad_status st = pad::make_plan(*shape, window, device_cus(), &p);
   if (st != PAD_OK) return st;
+  const pad_status vb = check_buffers(shape, q, kv_cache, block_table, seq_lens, scale, out);
+  if (vb != PAD_OK) return vb;
   if (shape->num_seqs == 0) return PAD_OK;
-  if (!q || !kv_cache || !block_table || !seq_lens || !out) return PAD_EINVAL;
-  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(block_table, 4) ||
-      !aligned(seq_lens, 4))
-    return PAD_EINVAL;
   if (p.ws_bytes > 0 && (!workspace || !aligned(workspace, 256) || workspace_bytes < p.ws_bytes))
     return PAD_EWORKSPACE;
 
@@ -160,7 +179,9 @@ pad_status decode(const pad_shape* shape, const void* q, const int32_t* q_start,
   return pad::launch_decode(p, pr, shape->dtype, shape->head_size, stream) == 0 ? PAD_OK : PAD_EHIP;
 }
 
-}  // namespace
+}  // namespace pad
+
+using pad::decode;
 
 extern "C" {
 

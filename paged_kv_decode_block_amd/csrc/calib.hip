@@ -86,25 +86,36 @@ __global__ __launch_bounds__(NW * 64) void gather_read_kernel(GatherArgs a) {
   if (x == kSinkValue) *a.sink = x;
 }
 
-// Each workgroup reads one contiguous range, 16 KiB per step (four 16-byte
-// loads per thread in flight).
-__global__ __launch_bounds__(256) void stream_read_kernel(const i32x4* src, size_t n, int* sink) {
+// Each workgroup of NT threads reads one contiguous range with U 16-byte
+// loads in flight per thread (NT * U * 16 bytes per step).
+template <int NT, int U>
+__global__ __launch_bounds__(NT) void stream_read_kernel(const i32x4* src, size_t n, int* sink) {
   const size_t per = (n + gridDim.x - 1) / gridDim.x;
   const size_t begin = size_t(blockIdx.x) * per;
   const size_t end = begin + per < n ? begin + per : n;
   i32x4 acc = {0, 0, 0, 0};
-  for (size_t i = begin + threadIdx.x; i < end; i += 4 * 256) {
-    i32x4 v[4];
+  for (size_t i = begin + threadIdx.x; i < end; i += size_t(U) * NT) {
+    i32x4 v[U];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const size_t j = i + k * 256;
+    for (int k = 0; k < U; ++k) {
+      const size_t j = i + size_t(k) * NT;
       v[k] = j < end ? src[j] : i32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc ^= v[k];
+    for (int k = 0; k < U; ++k) acc ^= v[k];
   }
   const int x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
   if (x == kSinkValue) *sink = x;
+}
+
+template <int NT>
+int launch_stream(int loads, const i32x4* src, size_t n, unsigned blocks, int* sink, hipStream_t st) {
+  switch (loads) {
+    case 4: hipLaunchKernelGGL((stream_read_kernel<NT, 4>), dim3(blocks), dim3(NT), 0, st, src, n, sink); return 0;
+    case 8: hipLaunchKernelGGL((stream_read_kernel<NT, 8>), dim3(blocks), dim3(NT), 0, st, src, n, sink); return 0;
+    case 16: hipLaunchKernelGGL((stream_read_kernel<NT, 16>), dim3(blocks), dim3(NT), 0, st, src, n, sink); return 0;
+  }
+  return -1;
 }
 
 template <int NW, int U, int CPL>
@@ -189,12 +200,20 @@ pad_status pad_calib_gather_read(const pad_shape* shape, const void* kv_cache, c
   return hipGetLastError() == hipSuccess ? PAD_OK : PAD_EHIP;
 }
 
-pad_status pad_calib_stream_read(const void* src, size_t bytes, int32_t blocks, int32_t* sink, void* stream) {
+pad_status pad_calib_stream_read(const void* src, size_t bytes, int32_t blocks, int32_t threads,
+                                 int32_t loads_in_flight, int32_t* sink, void* stream) {
+  if (threads != 256 && threads != 512 && threads != 1024) return PAD_EINVAL;
+  if (loads_in_flight != 4 && loads_in_flight != 8 && loads_in_flight != 16) return PAD_EINVAL;
+  if (blocks < 1 || blocks > 65536) return PAD_EINVAL;
   if (bytes == 0) return PAD_OK;
   if (!src || !sink || !aligned(src, 16) || !aligned(sink, 4) || bytes % 16 != 0) return PAD_EINVAL;
-  if (blocks < 1 || blocks > 65536) return PAD_EINVAL;
-  hipLaunchKernelGGL(stream_read_kernel, dim3(unsigned(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const i32x4*>(src), bytes / 16, sink);
+  const i32x4* s = static_cast<const i32x4*>(src);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const unsigned g = unsigned(blocks);
+  const int rc = threads == 256   ? launch_stream<256>(loads_in_flight, s, bytes / 16, g, sink, hs)
+                 : threads == 512 ? launch_stream<512>(loads_in_flight, s, bytes / 16, g, sink, hs)
+                                  : launch_stream<1024>(loads_in_flight, s, bytes / 16, g, sink, hs);
+  if (rc != 0) return PAD_EINVAL;
   return hipGetLastError() == hipSuccess ? PAD_OK : PAD_EHIP;
 }
 

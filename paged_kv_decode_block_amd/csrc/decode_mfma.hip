@@ -470,11 +470,12 @@ tiles_done:
 // grid (separate instantiations, so each inlines the item body once).
 // The arguments the prologue's first loads depend on (the length, the first
 // block id and the first K/V tile's address) lead the argument list as
-// scalars, and the build preloads their first 14 dwords (all but the
-// token stride, which is needed only once the length has arrived) into
-// scalar registers before the waves start (the compiler option
-// -amdgpu-kernarg-preload-count): those loads then wait for no
-// kernel-argument fetch.  The other fields stay in the Params block; the
+// scalars, and the build preloads the first 11 arguments -- the three
+// pointers and seq_lens .. head_stride, 14 dwords; the token stride, needed
+// only once the length has arrived, is not among them -- into scalar
+// registers before the waves start (the compiler option
+// -amdgpu-kernarg-preload-count counts arguments): those loads then wait
+// for no kernel-argument fetch.  The other fields stay in the Params block; the
 // host keeps the three strides within 32 bits.  (One sequence of 32k
 // keys: 31.35 -> 31.03 us; 4k keys: 12.89 -> 12.65 us.)
 template <typename T, int D, int RT, bool PERSIST, bool LEAN>

@@ -350,10 +350,13 @@ def test_calibration_validation():
     assert g(shape(), window=-1) == pad.PAD_EINVAL
     assert g(shape(), ptr=0) == pad.PAD_EINVAL  # missing buffers
     assert g(shape(), ptr=0x1008) == pad.PAD_EINVAL  # kv_cache not 16-byte aligned
-    assert L.pad_calib_stream_read(P(0), ctypes.c_size_t(0), 256, P(0), None) == pad.PAD_OK
-    assert L.pad_calib_stream_read(P(0x1000), ctypes.c_size_t(24), 256, P(0x1000), None) == pad.PAD_EINVAL
-    assert L.pad_calib_stream_read(P(0x1000), ctypes.c_size_t(32), 0, P(0x1000), None) == pad.PAD_EINVAL
-    assert L.pad_calib_stream_read(P(0x1008), ctypes.c_size_t(32), 256, P(0x1000), None) == pad.PAD_EINVAL
+    assert L.pad_calib_stream_read(P(0), ctypes.c_size_t(0), 256, 256, 4, P(0), None) == pad.PAD_OK
+    assert L.pad_calib_stream_read(P(0x1000), ctypes.c_size_t(24), 256, 256, 4, P(0x1000), None) == pad.PAD_EINVAL
+    assert L.pad_calib_stream_read(P(0x1000), ctypes.c_size_t(32), 0, 256, 4, P(0x1000), None) == pad.PAD_EINVAL
+    assert L.pad_calib_stream_read(P(0x1008), ctypes.c_size_t(32), 256, 256, 4, P(0x1000), None) == pad.PAD_EINVAL
+    for threads, loads in ((128, 4), (256, 2), (2048, 8), (512, 32)):
+        assert L.pad_calib_stream_read(P(0x1000), ctypes.c_size_t(32), 256, threads, loads, P(0x1000),
+                                       None) == pad.PAD_EINVAL
 
 
 def test_varlen_validation():
@@ -432,3 +435,4 @@ def test_dot_family_stays_on_the_grid():
     with pytest.raises(pad.PadError) as e:
         plan(shape(schedule=pad.PAD_SCHED_PERSISTENT, **batch))
     assert e.value.status == pad.PAD_EUNSUPPORTED
+

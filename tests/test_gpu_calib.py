@@ -32,6 +32,8 @@ def test_stream_read_runs():
     src = torch.randn((3 << 20) // 2 + 24, dtype=torch.bfloat16, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     for blocks in (1, 13, 4096):
-        pad.pad_calib_stream_read(src, sink, blocks=blocks)
+        for threads in (256, 512, 1024):
+            for loads in (4, 8, 16):
+                pad.pad_calib_stream_read(src, sink, blocks=blocks, threads=threads, loads_in_flight=loads)
     torch.cuda.synchronize()
     assert int(sink.item()) == 0

@@ -34,7 +34,7 @@ def test_config1_exact(M):
     check(run_gpu(c), oracle_out(c), c.q.dtype, "config1")
 
 
-@pytest.mark.parametrize("ctx", [128, 1000, 4096])
+@pytest.mark.parametrize("ctx", [128, 1000, 4096, 5003])
 @pytest.mark.parametrize("M", [1, 2, 4])
 def test_config2_small(ctx, M):
     spec = wl.CONFIGS[2]
@@ -49,7 +49,7 @@ def test_config3_window_nhd(M):
     check(run_gpu(c), oracle_out(c), c.q.dtype, f"config3 M={M}")
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_config4_small(M):
     spec = wl.CONFIGS[4]
     c = _case(spec, [1500], M, wl.seed_for(4, 1500, M))
