@@ -83,7 +83,9 @@ typedef enum pad_status {
   PAD_EINVAL = 1,        /* a shape field, pointer or alignment is invalid   */
   PAD_EUNSUPPORTED = 2,  /* valid but not built (e.g. head size 96)          */
   PAD_EWORKSPACE = 3,    /* workspace missing, misaligned or too small       */
-  PAD_EHIP = 4           /* the HIP runtime reported an error at launch      */
+  PAD_EHIP = 4,          /* the HIP runtime reported an error at launch      */
+  PAD_ESCRATCH = 5       /* pad_decode_attn_noalloc: the call needs more than
+                            the library's fixed PAD_NOALLOC_SCRATCH_BYTES     */
 } pad_status;
 
 /* Element type of q, kv_cache and out (same 0/1 flag as KernelVariant's
@@ -213,6 +215,29 @@ pad_status pad_decode_attn_varlen(const pad_shape* shape, const void* q, const i
                                   const void* kv_cache, const int32_t* block_table, const int32_t* seq_lens,
                                   float scale, int32_t window, void* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* Bytes of the fixed device array pad_decode_attn_noalloc uses as its
+ * workspace, held by each GPU the library runs on until the process ends. */
+#define PAD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the
+ * decode of pad_decode_attn (same arguments, same kernels, same output
+ * bits) with its workspace taken from a fixed array of
+ * PAD_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU,
+ * instead of a caller-supplied buffer.  The caller still owns q, kv_cache,
+ * block_table, seq_lens and out.  It calls no hipMalloc or hipFree and
+ * allocates nothing.  A call whose workspace (pad_decode_attn_workspace_size)
+ * exceeds the array returns PAD_ESCRATCH before anything is enqueued.  On a
+ * device's first call (and on every call until one is made outside graph
+ * capture) a fill kernel clearing the array's 1 MiB control prefix is
+ * enqueued on `stream` ahead of the decode; each decode leaves the prefix
+ * zero again.  Every call on a GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (on different streams, or from different
+ * threads without ordering) race and give undefined results. */
+pad_status pad_decode_attn_noalloc(const pad_shape* shape, const void* q, const void* kv_cache,
+                                   const int32_t* block_table, const int32_t* seq_lens, float scale,
+                                   int32_t window, void* out, void* stream);
 
 /* Bound, in microseconds, on how long a workgroup that shares the split-KV
  * merge waits for the last segment of its unit (process-wide; default 200;

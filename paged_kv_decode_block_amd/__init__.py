@@ -15,7 +15,8 @@ import os
 import torch
 
 __all__ = [
-    "PAD_OK", "PAD_EINVAL", "PAD_EUNSUPPORTED", "PAD_EWORKSPACE", "PAD_EHIP",
+    "PAD_OK", "PAD_EINVAL", "PAD_EUNSUPPORTED", "PAD_EWORKSPACE", "PAD_EHIP", "PAD_ESCRATCH",
+    "PAD_NOALLOC_SCRATCH_BYTES", "pad_decode_attn_noalloc",
     "PAD_F16", "PAD_BF16", "PAD_NHD", "PAD_HND",
     "PAD_PATH_AUTO", "PAD_PATH_MFMA", "PAD_PATH_DOT",
     "PAD_SCHED_AUTO", "PAD_SCHED_GRID", "PAD_SCHED_PERSISTENT",
@@ -27,7 +28,9 @@ __all__ = [
     "make_shape", "Workspace",
 ]
 
-PAD_OK, PAD_EINVAL, PAD_EUNSUPPORTED, PAD_EWORKSPACE, PAD_EHIP = 0, 1, 2, 3, 4
+PAD_OK, PAD_EINVAL, PAD_EUNSUPPORTED, PAD_EWORKSPACE, PAD_EHIP, PAD_ESCRATCH = 0, 1, 2, 3, 4, 5
+# Bytes of the fixed device array pad_decode_attn_noalloc takes its workspace from.
+PAD_NOALLOC_SCRATCH_BYTES = 64 << 20
 PAD_F16, PAD_BF16 = 0, 1
 PAD_NHD, PAD_HND = 0, 1
 PAD_PATH_AUTO, PAD_PATH_MFMA, PAD_PATH_DOT = 0, 1, 2
@@ -112,6 +115,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.pad_decode_attn.argtypes = [
         P(pad_shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+    ]
+    L.pad_decode_attn_noalloc.restype = ctypes.c_int
+    L.pad_decode_attn_noalloc.argtypes = [
+        P(pad_shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
     ]
     L.pad_calib_gather_read.restype = ctypes.c_int
     L.pad_calib_gather_read.argtypes = [
@@ -327,6 +335,43 @@ def pad_decode_attn(
         ctypes.c_float(scale), ctypes.c_int32(window), ctypes.c_void_p(out.data_ptr()),
         ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(_stream_ptr(stream)),
     ), "pad_decode_attn")
+    return out
+
+
+def pad_decode_attn_noalloc(
+    q: torch.Tensor,
+    kv_cache: torch.Tensor,
+    block_table: torch.Tensor,
+    seq_lens: torch.Tensor,
+    scale: float,
+    window: int,
+    out: torch.Tensor,
+    *,
+    layout: int = PAD_HND,
+    max_seq_len: int = 0,
+    num_segments: int = 0,
+    path: int = PAD_PATH_AUTO,
+    schedule: int = PAD_SCHED_AUTO,
+    stream=None,
+) -> torch.Tensor:
+    """``pad_decode_attn`` with its workspace in the library's fixed device
+    array (include/pad_attn.h): nothing is allocated, by the library or
+    here.  Calls that overlap on one GPU race."""
+    _require_device(q=q, kv_cache=kv_cache, block_table=block_table, seq_lens=seq_lens, out=out)
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q's shape and dtype")
+    if seq_lens.shape != (q.shape[0],):
+        raise ValueError("seq_lens must have one entry per sequence")
+    shape = make_shape(q, kv_cache, block_table, layout, max_seq_len=max_seq_len,
+                       num_segments=num_segments, path=path, schedule=schedule)
+    _check(lib.pad_decode_attn_noalloc(
+        ctypes.byref(shape), ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kv_cache.data_ptr()),
+        ctypes.c_void_p(block_table.data_ptr()), ctypes.c_void_p(seq_lens.data_ptr()),
+        ctypes.c_float(scale), ctypes.c_int32(window), ctypes.c_void_p(out.data_ptr()),
+        ctypes.c_void_p(_stream_ptr(stream)),
+    ), "pad_decode_attn_noalloc")
     return out
 
 

@@ -32,7 +32,7 @@ MFMA_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
 # head size, in parallel.
 SOURCES = [("decode_mfma.hip", f"decode_mfma_d{d}", [f"-DPAD_HEAD_SIZE={d}", *MFMA_FLAGS]) for d in (64, 128, 256, 512)] + [
     (src, src.rsplit(".", 1)[0], [])
-    for src in ("launch.hip", "cache_write.hip", "calib.hip", "plan.cpp", "api.cpp")
+    for src in ("launch.hip", "cache_write.hip", "calib.hip", "noalloc.hip", "plan.cpp", "api.cpp")
 ]
 
 # Packed fp32 VALU ops are turned off for every HIP source (the host pass

@@ -67,6 +67,7 @@ const char* pad_status_string(pad_status status) {
     case PAD_EUNSUPPORTED: return "unsupported shape";
     case PAD_EWORKSPACE: return "workspace missing, misaligned or too small";
     case PAD_EHIP: return "HIP runtime error";
+    case PAD_ESCRATCH: return "the call needs more workspace than the library's fixed device array holds";
   }
   return "unknown status";
 }

@@ -38,7 +38,7 @@ def test_abi_version_matches_header():
 
 
 def test_status_strings():
-    for code in range(5):
+    for code in range(6):
         assert pad.pad_status_string(code) and pad.pad_status_string(code) != "unknown status"
     assert pad.pad_status_string(77) == "unknown status"
 
@@ -436,3 +436,36 @@ def test_dot_family_stays_on_the_grid():
         plan(shape(schedule=pad.PAD_SCHED_PERSISTENT, **batch))
     assert e.value.status == pad.PAD_EUNSUPPORTED
 
+
+def test_noalloc_validates_before_launch():
+    """The allocation-free entry point runs the decode's host checks, and
+    rejects a call whose workspace exceeds its fixed array, before it
+    touches the device (fake addresses: nothing here reaches a GPU)."""
+    L = pad.lib
+    P = ctypes.c_void_p
+
+    def call(sh, q=0x1000, kv=0x2000, bt=0x3000, sl=0x4000, scale=0.1, window=0, out=0x5000):
+        return L.pad_decode_attn_noalloc(ctypes.byref(sh) if sh is not None else None, P(q), P(kv), P(bt), P(sl),
+                                         ctypes.c_float(scale), window, P(out), None)
+
+    assert pad.PAD_NOALLOC_SCRATCH_BYTES == 64 << 20
+    m = re.search(r"#define PAD_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == pad.PAD_NOALLOC_SCRATCH_BYTES
+    one_seg = shape(num_segments=1)
+    assert plan(one_seg)["workspace_bytes"] == 0
+    assert call(None) == pad.PAD_EINVAL
+    assert call(one_seg, scale=float("nan")) == pad.PAD_EINVAL
+    assert call(one_seg, q=0) == pad.PAD_EINVAL
+    assert call(one_seg, q=0x1008) == pad.PAD_EINVAL
+    assert call(one_seg, bt=0x3002) == pad.PAD_EINVAL
+    assert call(one_seg, window=-1) == pad.PAD_EINVAL
+    assert call(shape(query_len=257)) == pad.PAD_EUNSUPPORTED
+    # a split call with bad pointers fails on the pointers, not the device
+    assert plan(shape(num_segments=4))["workspace_bytes"] > 0
+    assert call(shape(num_segments=4), out=0) == pad.PAD_EINVAL
+    big = shape(num_seqs=128, num_q_heads=64, num_kv_heads=8, head_size=512, query_len=8, page_size=16,
+                max_blocks_per_seq=2048)
+    assert plan(big)["workspace_bytes"] > pad.PAD_NOALLOC_SCRATCH_BYTES
+    assert call(big) == pad.PAD_ESCRATCH
+    assert call(big, q=0) == pad.PAD_ESCRATCH  # the size bound is checked first
+    assert call(shape(num_seqs=0), q=0, kv=0, bt=0, sl=0, out=0) == pad.PAD_OK
