@@ -105,13 +105,18 @@ typedef enum pad_path {
   PAD_PATH_DOT = 2,
 } pad_path;
 
-/* Work schedule.  AUTO picks the persistent grid for batches whose
- * segments would oversubscribe the device, else one workgroup per item.
- * Both give the same output bits for the same plan. */
+/* Work schedule.  AUTO picks the balanced persistent grid for batches
+ * whose K/V exceeds about 3 MiB per CU, else one workgroup per item.  Each
+ * is deterministic (the same call gives the same bits); the two split the
+ * keys differently, so they agree within rounding, not bit for bit.  On the
+ * balanced grid a sequence's split -- and so the last bits of its output --
+ * depends on the batch's total tile count (sequences of length 0 add none);
+ * num_segments does not apply to it. */
 typedef enum pad_schedule {  /* the dot family runs on the grid schedule only */
   PAD_SCHED_AUTO = 0,
   PAD_SCHED_GRID = 1,        /* one workgroup per (sequence, kv head, segment)  */
-  PAD_SCHED_PERSISTENT = 2,  /* one workgroup per CU taking items from a queue  */
+  PAD_SCHED_PERSISTENT = 2,  /* one workgroup per CU, each taking an equal
+                                contiguous share of the batch's 16-key tiles   */
 } pad_schedule;
 
 /* Shape of one call.  Every field is host data. */
@@ -146,9 +151,9 @@ typedef struct pad_plan {
   int32_t segment_tiles;     /* 16-key tiles per segment (planned)                */
   int32_t grid_x, grid_y;    /* launch grid                                       */
   int32_t merge_slices;      /* workgroups that share the merge of a split unit   */
-  int32_t persistent;        /* 1: grid_x workgroups take the (sequence, kv head,
-                                segment) items from a queue in the workspace;
-                                0: one workgroup per item                        */
+  int32_t persistent;        /* 1: grid_x workgroups (one per CU) each take an
+                                equal share of the batch's tiles (num_segments
+                                is then 1); 0: one workgroup per item            */
   int32_t workspace_segments; /* segment slots per unit the workspace is sized for:
                                  a bound on num_segments over every window, so
                                  workspace_bytes is the same for every window  */
@@ -168,13 +173,13 @@ pad_status pad_decode_attn_plan(const pad_shape* shape, int32_t window, int32_t 
 
 /* Workspace bytes that serve every call of this shape (any window) on the
  * current device.  0 means no workspace is needed (a single segment on a
- * grid of one workgroup per item). The
- * split partials are fp32 (acc[rows][D], m, l per row and segment), as in
- * KernelVariant.scratch_shapes, after a fixed 1 MiB prefix of int32 merge
- * control words (per sequence, kv head and row group: an arrival counter
- * and one hand-over word per merge slice after the first, each in its own
- * 128-byte line; the prefix's last line holds the persistent grid's work
- * queue). */
+ * grid of one workgroup per item).  The split partials are fp32
+ * (acc[rows][D], m, l per row and slot), as in KernelVariant.scratch_shapes,
+ * after a fixed 1 MiB prefix of int32 merge control words (per sequence,
+ * kv head and row group: an arrival counter and one hand-over word per
+ * merge slice after the first, each in its own 128-byte line).  Slots:
+ * segment slots per (sequence, kv head) on the grid schedule, two per CU on
+ * the balanced grid; the size covers every schedule the shape may take. */
 pad_status pad_decode_attn_workspace_size(const pad_shape* shape, size_t* bytes);
 
 /* Zero a workspace of `bytes` bytes (device pointer, 256-byte aligned) on

@@ -174,6 +174,7 @@ pad_status decode(const pad_shape* shape, const void* q, const int32_t* q_start,
   pr.row_groups = p.row_groups;
   pr.group_rows = p.path == PAD_PATH_DOT ? p.rows : p.row_tiles * 16;
   pr.merge_slices = p.merge_slices;
+  pr.slot_rows = p.slot_rows;
   pr.persistent = p.persistent;
   pr.merge_wait_ticks = g_merge_wait_ticks.load();
   pr.scale_log2 = float(double(scale) * 1.4426950408889634);  // log2(e)

@@ -1,6 +1,6 @@
 // Device code shared by the decode-attention kernels (gfx950): MFMA
 // traits, stores, the split-KV merge and its hand-over protocol, segment
-// splits and the persistent grid's work loop.  Included by the kernel
+// splits and the balanced persistent grid's work loop.  Included by the kernel
 // sources only.
 #pragma once
 
@@ -115,31 +115,58 @@ __device__ __forceinline__ T* seq_out(const Params& p, int s, int D) {
 // pass's loads in flight while the current one is consumed.  LN is a
 // run-time value: one compiled body serves every slot count, which keeps
 // this once-per-launch code small (as several unrolled variants it cost
-// the merge about a microsecond of instruction fetch).
+// the merge about a microsecond of instruction fetch; a variant taking
+// several items per thread when n <= 8 -- a quarter of the passes for two
+// partials -- measured no faster on the batch workload and 1.2-1.4 us
+// slower on one sequence of 4k and 32k keys).
 constexpr int kMergeU = 8;
 struct MergeChunk {
   f32x4 acc[kMergeU];
   float2 ml[kMergeU];
 };
 
-// The unit's partial slots start at a wave-uniform 64-bit base; a slot
-// and an item are 32-bit byte offsets from it (a unit's partials span at
-// most 256 segments x 1024 rows x 512 columns x 4 bytes = 512 MiB).
+// Where a unit's n partials live.  Partial j (0 <= j < n) is in slot
+// first + j for j < n - 1 and in slot `last` for j = n - 1: on the grid
+// schedule the unit's slots are consecutive (last = first + n - 1); on the
+// balanced persistent grid the last one may sit in the other half of the
+// slot array.  A slot holds Params::slot_rows rows of (m, l) and of acc;
+// the unit's rows start at row `row0` of each slot.
+struct Parts {
+  int64_t first, last;
+  int n, row0;
+};
+
+// One work item: tiles [ts, te) of one unit's key range, its partial slot
+// and where the unit's other partials and control words are.
+struct Frag {
+  int ts, te;          // 16-key tiles of this item
+  int n_parts;         // partials of the unit (1: the item is the whole unit and writes the output)
+  int merge_slices;    // workgroups sharing the unit's merge
+  int64_t slot;        // this item's partial slot (n_parts > 1)
+  Parts parts;         // the unit's partials, in merge order
+  int* ctl;            // the unit's arrival counter, then one hand-over word per slice
+};
+
+// The unit's first partial slot starts at a wave-uniform 64-bit base; a
+// slot and an item are 32-bit byte offsets from it: below 2^32 for up to
+// 255 consecutive slots of 4096 rows x 512 columns x 4 bytes (grid), or
+// 511 slots of at most 64 rows (balanced grid).
 template <int D, int NT>
 __device__ __forceinline__ void merge_load(const Params& p, MergeChunk& b, const unsigned char* acc_base,
-                                           const unsigned char* ml_base, int row0, int i0, int i1, int n, int lg,
-                                           int pass) {
+                                           const unsigned char* ml_base, uint32_t last_rel, int i0, int i1, int n,
+                                           int lg, int pass) {
   const int it = min(i0 + pass * (NT >> lg) + (int(threadIdx.x) >> lg), i1 - 1);
   const int r = it / (D / 4), d4 = it % (D / 4);
-  const uint32_t acc_item = uint32_t((row0 + r) * D + 4 * d4) * 4u;
-  const uint32_t ml_item = uint32_t(row0 + r) * 8u;
-  const uint32_t acc_slot = uint32_t(p.rows) * uint32_t(D) * 4u, ml_slot = uint32_t(p.rows) * 8u;
+  const uint32_t acc_item = uint32_t(r * D + 4 * d4) * 4u;
+  const uint32_t ml_item = uint32_t(r) * 8u;
+  const uint32_t acc_slot = uint32_t(p.slot_rows) * uint32_t(D) * 4u, ml_slot = uint32_t(p.slot_rows) * 8u;
   const int sub = int(threadIdx.x) & ((1 << lg) - 1);
 #pragma unroll
   for (int u = 0; u < kMergeU; ++u) {
     const uint32_t j = uint32_t(min(sub + (u << lg), n - 1));
-    b.acc[u] = *reinterpret_cast<const f32x4*>(acc_base + (j * acc_slot + acc_item));
-    b.ml[u] = *reinterpret_cast<const float2*>(ml_base + (j * ml_slot + ml_item));
+    const uint32_t jr = j == uint32_t(n - 1) ? last_rel : j;
+    b.acc[u] = *reinterpret_cast<const f32x4*>(acc_base + (jr * acc_slot + acc_item));
+    b.ml[u] = *reinterpret_cast<const float2*>(ml_base + (jr * ml_slot + ml_item));
   }
 }
 
@@ -186,34 +213,37 @@ __device__ __forceinline__ void merge_consume(const Params& p, const MergeChunk&
   }
 }
 
-// Merge slice `slice` of `nslices` of the n partials of a unit (slots
-// slot0 .. slot0 + n - 1, rows row0 .. row0 + wg_rows - 1 of each) into
-// the output.  Lanes per item follow the slot count only, so an item's
-// sums take the same order whatever the slicing and whichever workgroup
-// merges it: the output bits depend on the sequence and the segment split
-// alone.  The caller has acquired the partials.
+// Merge slice `slice` of `nslices` of a unit's partials (rows
+// pt.row0 .. pt.row0 + wg_rows - 1 of each slot) into output rows
+// out_row0 .. out_row0 + wg_rows - 1.  Lanes per item follow the partial
+// count only, so an item's sums take the same order whatever the slicing
+// and whichever workgroup merges it: the output bits depend on the
+// partials alone.  The caller has acquired the partials.
 template <typename T, int D, int NT>
-__device__ __forceinline__ void merge_slice(const Params& p, int64_t slot0, int n, int row0, int wg_rows, int slice,
+__device__ __forceinline__ void merge_slice(const Params& p, const Parts& pt, int out_row0, int wg_rows, int slice,
                                             int nslices, T* out_s, int kvh) {
+  const int n = pt.n;
   const int items = wg_rows * (D / 4);
   const int i0 = slice * items / nslices, i1 = (slice + 1) * items / nslices;
   if (i1 <= i0) return;
   const int lg = n <= 8 ? 0 : (n <= 16 ? 1 : (n <= 32 ? 2 : (n <= 64 ? 3 : (n <= 128 ? 4 : 5))));
   const int ipp = NT >> lg;
   const int W = (i1 - i0 + ipp - 1) / ipp;
-  const unsigned char* acc_base = reinterpret_cast<const unsigned char*>(p.ws_acc + slot0 * p.rows * D);
-  const unsigned char* ml_base = reinterpret_cast<const unsigned char*>(p.ws_ml + slot0 * p.rows * 2);
+  const int64_t row_base = pt.first * p.slot_rows + pt.row0;
+  const unsigned char* acc_base = reinterpret_cast<const unsigned char*>(p.ws_acc + row_base * D);
+  const unsigned char* ml_base = reinterpret_cast<const unsigned char*>(p.ws_ml + row_base * 2);
+  const uint32_t last_rel = uint32_t(pt.last - pt.first);
   MergeChunk b0, b1;
-  merge_load<D, NT>(p, b0, acc_base, ml_base, row0, i0, i1, n, lg, 0);
+  merge_load<D, NT>(p, b0, acc_base, ml_base, last_rel, i0, i1, n, lg, 0);
   if (W == 1) {
-    merge_consume<T, D, NT>(p, b0, i0, i1, n, lg, 0, row0, out_s, kvh);
+    merge_consume<T, D, NT>(p, b0, i0, i1, n, lg, 0, out_row0, out_s, kvh);
     return;
   }
   for (int w = 0; w < W; w += 2) {
-    merge_load<D, NT>(p, b1, acc_base, ml_base, row0, i0, i1, n, lg, min(w + 1, W - 1));
-    merge_consume<T, D, NT>(p, b0, i0, i1, n, lg, w, row0, out_s, kvh);
-    merge_load<D, NT>(p, b0, acc_base, ml_base, row0, i0, i1, n, lg, min(w + 2, W - 1));
-    if (w + 1 < W) merge_consume<T, D, NT>(p, b1, i0, i1, n, lg, w + 1, row0, out_s, kvh);
+    merge_load<D, NT>(p, b1, acc_base, ml_base, last_rel, i0, i1, n, lg, min(w + 1, W - 1));
+    merge_consume<T, D, NT>(p, b0, i0, i1, n, lg, w, out_row0, out_s, kvh);
+    merge_load<D, NT>(p, b0, acc_base, ml_base, last_rel, i0, i1, n, lg, min(w + 2, W - 1));
+    if (w + 1 < W) merge_consume<T, D, NT>(p, b1, i0, i1, n, lg, w + 1, out_row0, out_s, kvh);
   }
 }
 
@@ -271,14 +301,14 @@ __device__ __forceinline__ int helper_wait(int* word, const int* counter, int n,
 // slices) merge one slice of the output each; the rest are done.  `flags`
 // are 16 bytes of LDS (words 0 and 1).
 template <typename T, int D, int NT>
-__device__ __forceinline__ void arrive_and_merge(const Params& p, int* flags, int s, int kvh, int rg, int row0,
-                                                 int wg_rows, int n_live) {
+__device__ __forceinline__ void arrive_and_merge(const Params& p, int* flags, int s, int kvh, int row0, int wg_rows,
+                                                 const Frag& f) {
   const int tid = threadIdx.x;
   T* out_s = seq_out<T>(p, s, D);
-  const int64_t slot0 = (int64_t(s) * p.num_kv_heads + kvh) * p.nseg;
-  int* ctl = p.ws_cnt + ((int64_t(s) * p.num_kv_heads + kvh) * p.row_groups + rg) * p.merge_slices * kCtlStride;
+  int* ctl = f.ctl;
+  const int n_live = f.n_parts;
   int* sm_flag = flags;
-  const int k = min(p.merge_slices, n_live);
+  const int k = min(f.merge_slices, n_live);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
   __syncthreads();
   // Thread 0 of a helper that saw the unit complete still posts "done" on
@@ -321,7 +351,7 @@ __device__ __forceinline__ void arrive_and_merge(const Params& p, int* flags, in
   while (todo != 0) {
     const int sl = __builtin_ctz(todo);
     todo &= todo - 1;
-    merge_slice<T, D, NT>(p, slot0, n_live, row0, wg_rows, sl, k, out_s, kvh);
+    merge_slice<T, D, NT>(p, f.parts, row0, wg_rows, sl, k, out_s, kvh);
     if (!settled) {
       settled = true;
       if (tid < 64) {
@@ -393,63 +423,49 @@ __device__ __forceinline__ SegSplit split_of(const Params& p, int L, int M, int 
   return r;
 }
 
-// Items of a live sequence on the persistent grid: every (row group, kv
-// head, segment).
-__device__ __forceinline__ int seq_items(const Params& p, int L, int M) {
-  int n = 0;
-  for (int rg = 0; rg < p.row_groups; ++rg) n += split_of(p, L, M, rg).n_live;
-  return n * p.num_kv_heads;
-}
-
-// Persistent grid (batched decode): one workgroup per CU takes work items
-// from a queue in the workspace until none are left.  Items are the live
-// segments of every (sequence, kv head, row group), longest sequences
-// first (ties by index; up to kPersistSortSeqs sequences, else in index
-// order) and, within a sequence, unit-major so the segments of a unit run
-// together and its merge helpers wait little.  An item's work does not
-// depend on which workgroup takes it, so results stay bitwise the same.
-// Sequences of length <= 0 get one item per unit (its zero output), those
-// without query tokens none.
-// Every workgroup ends with one failed take; the last of those resets the
-// queue for the next launch.
-template <typename Body>
-__device__ __forceinline__ void persistent_loop(const Params& p, unsigned char* lds, int persist_off, int lds_bytes,
-                                               int nt, Body body) {
+// Balanced persistent grid (batched decode).  The 16-key tiles of every
+// unit -- (sequence, row group, kv head) in that order, each its key range
+// [t_lo, t_hi) of split_of -- are laid end to end, T tiles in all, and
+// workgroup b of the Gs = min(G, T) first of the G = gridDim.x workgroups
+// (one per CU) takes the contiguous share [b T / Gs, (b + 1) T / Gs): every
+// CU reads the same number of tiles, whatever the lengths.  A unit inside one share is computed
+// whole and written directly.  A unit cut by share boundaries is computed
+// as one work item per share it meets; each item publishes a partial and
+// the last to arrive merges them in share order (fixed, so the result is
+// deterministic for a given batch).  A workgroup publishes at most two
+// partials: slot b for the item that reaches its share's end, slot G + b
+// for an item that starts at its share's start and ends inside it
+// (b < Gs <= G, so the two halves never meet).  So a
+// unit met by shares b0..b1 has its partials in slots b0 .. b1 - 1 and
+// then b1 (its end is b1's share end) or G + b1.
+// Sequences of length <= 0 with query tokens get zero rows (written by
+// workgroup s % G); those without query tokens have nothing to do.  The
+// planner keeps T below 2^31.
+template <typename Body, typename Zero>
+__device__ __forceinline__ void balanced_loop(const Params& p, unsigned char* lds, int tables_off, int nt,
+                                              Body body, Zero zero) {
   const int tid = threadIdx.x;
   const int S = p.num_seqs;
-  const int units = p.num_kv_heads * p.row_groups;
-  int* sm_order = reinterpret_cast<int*>(lds + persist_off);  // [S]: sequence of rank r
-  int* sm_pref = sm_order + kPersistMaxSeqs;                   // [S + 1]: first item of rank r
-  // Scratch before the first item (the tile-loop area): lengths and item
-  // counts per rank.
-  int* sm_len = reinterpret_cast<int*>(lds);                   // [S]
-  int* sm_cnt = sm_len + kPersistMaxSeqs;                      // [S]
-  int* sm_take = reinterpret_cast<int*>(lds + lds_bytes - 16) + 2;
-  for (int i = tid; i < S; i += nt) sm_len[i] = clamped_len(p, i);
-  __syncthreads();
-  const bool sort = S <= kPersistSortSeqs;
+  int* sm_len = reinterpret_cast<int*>(lds + tables_off);  // [S]: clamped lengths
+  int* sm_pref = sm_len + kPersistMaxSeqs;                   // [S + 1]: first tile of sequence s
+  // Before the first item the tile-loop area holds the tile counts.
+  int* sm_cnt = reinterpret_cast<int*>(lds);  // [S]
   for (int i = tid; i < S; i += nt) {
-    const int li = sm_len[i];
-    int rank = i;
-    if (sort) {
-      rank = 0;
-      for (int j = 0; j < S; ++j) {
-        const int lj = sm_len[j];
-        rank += (lj > li) || (lj == li && j < i);
+    const int L = clamped_len(p, i);
+    sm_len[i] = L;
+    int n = 0;
+    const int M = seq_queries(p, i).m;
+    if (L > 0 && M > 0) {
+      for (int rg = 0; rg < p.row_groups; ++rg) {
+        const SegSplit sp = split_of(p, L, M, rg);
+        if (sp.n_live > 0) n += sp.t_hi - sp.t_lo;
       }
     }
-    sm_order[rank] = i;
+    sm_cnt[i] = n * p.num_kv_heads;
   }
   __syncthreads();
-  // Items per rank, then an exclusive prefix (wave 0: lanes own
-  // contiguous chunks of ranks).
-  // A sequence with no query token has no item.
-  for (int r = tid; r < S; r += nt) {
-    const int s = sm_order[r];
-    const int L = sm_len[s], M = seq_queries(p, s).m;
-    sm_cnt[r] = M == 0 ? 0 : (L <= 0 ? units : seq_items(p, L, M));
-  }
-  __syncthreads();
+  // Exclusive prefix over the sequences (wave 0: lanes own contiguous
+  // chunks of sequences).
   if (tid < 64) {
     const int chunk = (S + 63) / 64;
     const int r0 = min(S, tid * chunk), r1 = min(S, r0 + chunk);
@@ -469,43 +485,61 @@ __device__ __forceinline__ void persistent_loop(const Params& p, unsigned char* 
     if (tid == 63) sm_pref[S] = incl;
   }
   __syncthreads();
-  const int total = sm_pref[S];
-  int* queue = p.ws_cnt + kQueueWord;
-  for (;;) {
-    if (tid == 0) sm_take[0] = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int item = sm_take[0];
-    __syncthreads();
-    if (item >= total) {
-      if (tid == 0 && item == total + int(gridDim.x) - 1)
-        __hip_atomic_store(queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return;
-    }
-    // Rank holding the item: the last r with sm_pref[r] <= item.
-    int lo = 0, hi = S - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sm_pref[mid] <= item) lo = mid; else hi = mid - 1;
-    }
-    const int s = sm_order[lo];
-    const int local = item - sm_pref[lo];
-    const int L = clamped_len(p, s);
-    if (L <= 0) {
-      body(s, local % p.num_kv_heads, local / p.num_kv_heads, 0);
-    } else {
-      // Row groups last (heaviest) first, then kv heads, then segments.
-      const int M = seq_queries(p, s).m;
-      int rest = local;
-      for (int rg = p.row_groups - 1; rg >= 0; --rg) {
-        const int n = split_of(p, L, M, rg).n_live;
-        if (rest < n * p.num_kv_heads) {
-          body(s, rest / n, rg, rest % n);
-          break;
-        }
-        rest -= n * p.num_kv_heads;
+  const int G = int(gridDim.x), b = int(blockIdx.x);
+  // Zero rows of padded sequences.
+  for (int s = b; s < S; s += G) {
+    if (sm_len[s] > 0) continue;
+    const int M = seq_queries(p, s).m;
+    if (M == 0) continue;
+    for (int rg = 0; rg < p.row_groups; ++rg)
+      for (int kvh = 0; kvh < p.num_kv_heads; ++kvh) zero(s, kvh, rg, M);
+  }
+  const int T = sm_pref[S];
+  // Shares of the first min(G, T) workgroups: each holds at least one tile,
+  // so every share a unit meets has an item that arrives.
+  const int Gs = min(G, T);
+  if (b >= Gs) return;
+  const int start = int(int64_t(b) * T / Gs), end = int(int64_t(b + 1) * T / Gs);
+  // Share holding tile t: the largest b' with floor(b' T / Gs) <= t.
+  auto owner = [&](int t) { return int((int64_t(t + 1) * Gs - 1) / T); };
+  auto share_end = [&](int bb) { return int(int64_t(bb + 1) * T / Gs); };
+  // Sequence holding tile `start`: the last s with sm_pref[s] <= start.
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (sm_pref[mid] <= start) lo = mid; else hi = mid - 1;
+  }
+  int pos = start;
+  for (int s = lo; s < S && pos < end; ++s) {
+    const int L = sm_len[s];
+    const int M = L > 0 ? seq_queries(p, s).m : 0;
+    if (M == 0) continue;
+    int ub = sm_pref[s];  // first tile of the unit being visited
+    for (int rg = 0; rg < p.row_groups && pos < end; ++rg) {
+      const SegSplit sp = split_of(p, L, M, rg);
+      if (sp.n_live == 0) continue;
+      const int nu = sp.t_hi - sp.t_lo;
+      for (int kvh = 0; kvh < p.num_kv_heads && pos < end; ++kvh, ub += nu) {
+        const int ue = ub + nu;
+        if (ue <= pos) continue;
+        const int f0 = max(ub, pos), f1 = min(ue, end);
+        const int b0 = owner(ub), b1 = owner(ue - 1);
+        Frag f;
+        f.ts = sp.t_lo + (f0 - ub);
+        f.te = sp.t_lo + (f1 - ub);
+        f.n_parts = b1 - b0 + 1;
+        f.merge_slices = 1;
+        f.slot = f1 == end ? b : G + b;
+        f.parts.first = b0;
+        f.parts.last = ue == share_end(b1) ? b1 : G + b1;
+        f.parts.n = f.n_parts;
+        f.parts.row0 = 0;
+        f.ctl = p.ws_cnt + ((int64_t(s) * p.num_kv_heads + kvh) * p.row_groups + rg) * kCtlStride;
+        body(s, kvh, rg, f);
+        __syncthreads();  // LDS is reused by the next item
+        pos = f1;
       }
     }
-    __syncthreads();  // LDS is reused by the next item
   }
 }
 

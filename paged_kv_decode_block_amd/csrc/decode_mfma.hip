@@ -92,10 +92,11 @@ struct Shape {
   static constexpr int kIdsBytes = kMaxSegTiles * 4;
   static constexpr int kLoopBytes = kVBytes + kIdsBytes;
   static constexpr int kCombineBytes = Combine<D, RT, NW>::kBytes;
-  // Then the persistent grid's rank order and item prefix.
+  // Then the balanced persistent grid's tables: clamped lengths and the
+  // first tile of each sequence.
   static constexpr int kPersistOff = kLoopBytes > kCombineBytes ? kLoopBytes : kCombineBytes;
   static constexpr int kBytes = kPersistOff + (2 * kPersistMaxSeqs + 1) * 4 + 16;
-  static_assert(kLoopBytes >= 2 * kPersistMaxSeqs * 4, "persistent prologue scratch fits the tile-loop area");
+  static_assert(kLoopBytes >= kPersistMaxSeqs * 4, "the per-sequence tile counts fit the tile-loop area");
 };
 
 // After the waves of a workgroup have left their results in LDS -- per
@@ -105,8 +106,8 @@ struct Shape {
 // order (deterministic) and either write the output (single segment) or
 // publish this segment's partial and take part in the merge.
 template <typename T, int D, int RT, int NW>
-__device__ __forceinline__ void finish(const Params& p, unsigned char* lds, int s, int kvh, int rg, int seg, int row0,
-                                       int wg_rows, int n_live, int lds_bytes) {
+__device__ __forceinline__ void finish(const Params& p, unsigned char* lds, int s, int kvh, int row0, int wg_rows,
+                                       const Frag& f, int lds_bytes) {
   using MF = Mfma<T>;
   using CB = Combine<D, RT, NW>;
   constexpr int NT = NW * 64;
@@ -124,7 +125,7 @@ __device__ __forceinline__ void finish(const Params& p, unsigned char* lds, int 
   };
 
   T* out_s = seq_out<T>(p, s, D);
-  if (n_live == 1) {
+  if (f.n_parts == 1) {
     for (int it = tid; it < wg_rows * (D / 4); it += NT) {
       const int r = it / (D / 4), d4 = it % (D / 4);
       const f32x4 a = combined(r, d4);
@@ -139,21 +140,24 @@ __device__ __forceinline__ void finish(const Params& p, unsigned char* lds, int 
   }
 
   // Publish the partial with device-coherent stores.
-  const int64_t slot0 = (int64_t(s) * p.num_kv_heads + kvh) * p.nseg;
   {
-    const int64_t base = (slot0 + seg) * p.rows + row0;
+    const int64_t base = f.slot * p.slot_rows + f.parts.row0;
     for (int it = tid; it < wg_rows * (D / 4); it += NT) {
       const int r = it / (D / 4), d4 = it % (D / 4);
       store_coherent(p.ws_acc + (base + r) * D + 4 * d4, combined(r, d4));
     }
     for (int r = tid; r < wg_rows; r += NT) store_coherent2(p.ws_ml + (base + r) * 2, sm_ms[r], sm_ls[r]);
   }
-  arrive_and_merge<T, D, NT>(p, reinterpret_cast<int*>(lds + lds_bytes - 16), s, kvh, rg, row0, wg_rows, n_live);
+  arrive_and_merge<T, D, NT>(p, reinterpret_cast<int*>(lds + lds_bytes - 16), s, kvh, row0, wg_rows, f);
 }
 
-// One work item: segment `seg` of (sequence s, kv head kvh, row group rg).
-template <typename T, int D, int RT, bool LEAN>
-__device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds, int s, int kvh, int rg, int seg) {
+// One work item of (sequence s, kv head kvh, row group rg).  On the grid
+// schedule (PERSIST = false) it is segment `seg` of the unit's key range,
+// found once the length is known; on the balanced persistent grid the
+// caller passes the item (its tiles, partial slot and merge layout) in `fr`.
+template <typename T, int D, int RT, bool LEAN, bool PERSIST>
+__device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds, int s, int kvh, int rg, int seg,
+                                            Frag fr) {
   using MF = Mfma<T>;
   using SH = Shape<D, RT, LEAN>;
   constexpr int NW = SH::NW, KC = SH::KC, DT = SH::DT;
@@ -169,23 +173,28 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
   // range for any sequence), so they depend on preloaded arguments only.
   const int L_dev = p.seq_lens[s];
   const int32_t* table = p.block_table + int64_t(s) * p.max_blocks;
-  // The segment's block ids (one per tile) go to LDS once, so a tile's
-  // page address costs an LDS read instead of a scalar load that may miss.
-  // The planner keeps segments within kMaxSegTiles tiles.  Without a
+  // The item's block ids (one per tile) go to LDS, so a tile's page
+  // address costs an LDS read instead of a scalar load that may miss.  At
+  // most kMaxSegTiles ids are staged at a time: a longer item (only a
+  // persistent share can be) is walked in chunks.  On the grid without a
   // window a segment starts at tile seg * seg_tiles whatever the length
   // (unless a length past the planning bound stretches the segments), so
   // its planned tiles are staged before the length is known; entries past
   // the sequence's end are staged but never used.  A thread stages the
   // same slots in both passes, so a second pass needs no barrier first.
   int* sm_ids = reinterpret_cast<int*>(lds + SH::kVBytes);
-  const bool spec_ids = p.window == 0;
-  // The block id of each wave's first tile (without a window) by one
-  // wave-uniform load beside the length, issued before the staging loads:
-  // an in-range read of the table row, used only once the length shows the
-  // tile exists, so the first K/V loads wait neither for the staged ids
-  // nor for the barrier.
+  const bool spec_ids = !PERSIST && p.window == 0;
+  // The block id of each wave's first tile by one wave-uniform load beside
+  // the length, issued before the staging loads: an in-range read of the
+  // table row, used only once the length shows the tile exists, so the
+  // first K/V loads wait neither for the staged ids nor for the barrier.
   int blk_first = 0;
-  if (spec_ids) {
+  if (PERSIST) {
+    const int b = ((fr.ts + wave) * 16) / p.page_size;
+    blk_first = __builtin_amdgcn_readfirstlane(table[min(b, p.max_blocks - 1)]);
+    const int n = min(fr.te - fr.ts, kMaxSegTiles);
+    for (int t = tid; t < n; t += SH::kThreads) sm_ids[t] = table[((fr.ts + t) * 16) / p.page_size];
+  } else if (spec_ids) {
     const int b = ((seg * p.seg_tiles + wave) * 16) / p.page_size;
     blk_first = __builtin_amdgcn_readfirstlane(table[min(b, p.max_blocks - 1)]);
   }
@@ -224,15 +233,35 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
 
   // Lengths past the block table's capacity are clamped to it.
   const int L = min(L_dev, p.max_blocks * p.page_size);
-  if (L <= 0) {
-    if (seg == 0) zero_rows<T, D>(p, s, kvh, row0, wg_rows, SH::kThreads);
-    return;
+  bool early;
+  if constexpr (PERSIST) {
+    early = true;  // the item's first ids are staged and each wave's first block id is known
+  } else {
+    if (L <= 0) {
+      if (seg == 0) zero_rows<T, D>(p, s, kvh, row0, wg_rows, SH::kThreads);
+      return;
+    }
+    const SegSplit sp = split_of(p, L, M, rg);
+    if (seg >= sp.n_live) return;
+    fr.ts = sp.t_lo + seg * sp.seg_tiles;
+    fr.te = min(fr.ts + sp.seg_tiles, sp.t_hi);
+    fr.n_parts = sp.n_live;
+    fr.merge_slices = p.merge_slices;
+    const int64_t slot0 = (int64_t(s) * p.num_kv_heads + kvh) * p.nseg;
+    fr.slot = slot0 + seg;
+    fr.parts.first = slot0;
+    fr.parts.last = slot0 + sp.n_live - 1;
+    fr.parts.n = sp.n_live;
+    fr.parts.row0 = row0;
+    fr.ctl = p.ws_cnt + ((int64_t(s) * p.num_kv_heads + kvh) * p.row_groups + rg) * p.merge_slices * kCtlStride;
+    // Without a window (and unless a length past the planning bound
+    // stretched the segments) the ids staged above are the segment's.
+    early = spec_ids && sp.seg_tiles == p.seg_tiles && fr.ts == seg * p.seg_tiles;
+    if (!early)
+      for (int t = tid; t < fr.te - fr.ts; t += SH::kThreads) sm_ids[t] = table[((fr.ts + t) * 16) / p.page_size];
   }
+  const int ts = fr.ts, te = fr.te;
   const int k_lo = p.window > 0 ? max(0, L - M - p.window + 1) : 0;
-  const SegSplit sp = split_of(p, L, M, rg);
-  const int t_hi = sp.t_hi, seg_tiles = sp.seg_tiles, n_live = sp.n_live;
-  if (seg >= n_live) return;
-  const int ts = sp.t_lo + seg * seg_tiles, te = min(ts + seg_tiles, t_hi);
   // Tiles needing no mask: every key visible to every row.
   const int lo_last = p.window > 0 ? max(0, L - p.window) : 0;
   const int qpos_first = L - M;
@@ -274,12 +303,6 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
     i32x4 v[KC];
   };
 
-  // Without a window (and unless a length past the planning bound
-  // stretched the segments) the ids staged above are the segment's.
-  const bool early = spec_ids && seg_tiles == p.seg_tiles && ts == seg * p.seg_tiles;
-  if (!early)
-    for (int t = tid; t < te - ts; t += SH::kThreads) sm_ids[t] = table[((ts + t) * 16) / p.page_size];
-
   auto issue_tile = [&](Tile& tl, int t, int blk) {
     const int key0 = t * 16;
     const unsigned char* base =
@@ -290,18 +313,6 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) tl.v[kc] = *reinterpret_cast<const i32x4*>(row + 2 * D + 64 * kc);
   };
-
-  // Interleaved tiles per wave: tile i of this wave is ts + wave + i * NW.
-  const int first_t = ts + wave;
-  const int n_w = first_t < te ? (te - first_t + NW - 1) / NW : 0;
-  // The first tile's loads go out before the barrier that publishes the
-  // staged ids when its block id is already known.
-  Tile ring[SH::PF + 1];
-  if (early && n_w > 0) issue_tile(ring[0], first_t, blk_first);
-  __syncthreads();
-  // Physical block of tile t (wave-uniform).
-  auto block_of = [&](int t) { return __builtin_amdgcn_readfirstlane(sm_ids[t - ts]); };
-  if (!early && n_w > 0) issue_tile(ring[0], first_t, block_of(first_t));
 
   // Scores of tile t: stage its V rows in LDS, S^T = K Q^T, mask, online
   // softmax; leaves P (input dtype, MFMA B layout) in pb.  After it the
@@ -381,18 +392,37 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // PF tiles are in flight beyond the one being computed (a ring of PF + 1
-  // register buffers, the first issued above), and each tile's block id is
-  // read one tile before its loads are issued.  The prefetch index is
-  // clamped to the wave's last tile instead of being skipped, so every
-  // iteration has the same loads in flight and the compiler's wait counts
-  // stay exact (the clamped re-reads of the last tile hit in cache).
-  auto tile_at = [&](int i) { return first_t + min(i, n_w - 1) * NW; };
-  if constexpr (SH::PF == 0) {
-    // No register room for a second tile: the next tile's loads go out as
-    // soon as the scores have consumed the current one, so they overlap
-    // the PV product (whose V operand is already in LDS).
-    if (n_w > 0) {
+  // The item's tiles in chunks of at most kMaxSegTiles staged ids (one
+  // chunk on the grid schedule).  Within a chunk, tile i of this wave is
+  // cs + wave + i * NW.
+  Tile ring[SH::PF + 1];
+  int cs = ts;
+  {
+    const int ce = min(te, cs + kMaxSegTiles);
+    // The first tile's loads go out before the barrier that publishes the
+    // staged ids when its block id is already known.
+    if (early && cs + wave < ce) issue_tile(ring[0], cs + wave, blk_first);
+  }
+  __syncthreads();
+  for (;;) {
+    const int ce = min(te, cs + kMaxSegTiles);
+    const int first_t = cs + wave;
+    const int n_w = first_t < ce ? (ce - first_t + NW - 1) / NW : 0;
+    // Physical block of tile t (wave-uniform).
+    auto block_of = [&](int t) { return __builtin_amdgcn_readfirstlane(sm_ids[t - cs]); };
+    if ((!early || cs != ts) && n_w > 0) issue_tile(ring[0], first_t, block_of(first_t));
+
+    // PF tiles are in flight beyond the one being computed (a ring of PF + 1
+    // register buffers, the first issued above), and each tile's block id is
+    // read one tile before its loads are issued.  The prefetch index is
+    // clamped to the wave's last tile instead of being skipped, so every
+    // iteration has the same loads in flight and the compiler's wait counts
+    // stay exact (the clamped re-reads of the last tile hit in cache).
+    auto tile_at = [&](int i) { return first_t + min(i, n_w - 1) * NW; };
+    if constexpr (SH::PF == 0) {
+      // No register room for a second tile: the next tile's loads go out as
+      // soon as the scores have consumed the current one, so they overlap
+      // the PV product (whose V operand is already in LDS).
       Tile& tl = ring[0];
       for (int i = 0; i < n_w; ++i) {
         uint64_t pb[RT];
@@ -400,26 +430,33 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
         if (i + 1 < n_w) issue_tile(tl, first_t + (i + 1) * NW, block_of(first_t + (i + 1) * NW));
         pv_tile(pb);
       }
-    }
-  } else if (n_w > 0) {
-    // (Reloading a tile's registers right after its scores, which keeps
-    // PF + 1 tiles in flight through the PV product, measured slower.)
+    } else if (n_w > 0) {
+      // (Reloading a tile's registers right after its scores, which keeps
+      // PF + 1 tiles in flight through the PV product, measured slower.)
 #pragma unroll
-    for (int u = 1; u < SH::PF; ++u) issue_tile(ring[u], tile_at(u), block_of(tile_at(u)));
-    int blk_next = block_of(tile_at(SH::PF));
-    for (int i = 0;; i += SH::PF + 1) {
+      for (int u = 1; u < SH::PF; ++u) issue_tile(ring[u], tile_at(u), block_of(tile_at(u)));
+      int blk_next = block_of(tile_at(SH::PF));
+      for (int i = 0;; i += SH::PF + 1) {
 #pragma unroll
-      for (int u = 0; u <= SH::PF; ++u) {
-        uint64_t pb[RT];
-        issue_tile(ring[(u + SH::PF) % (SH::PF + 1)], tile_at(i + u + SH::PF), blk_next);
-        blk_next = block_of(tile_at(i + u + SH::PF + 1));
-        score_tile(ring[u], first_t + (i + u) * NW, pb);
-        pv_tile(pb);
-        if (i + u + 1 >= n_w) goto tiles_done;
+        for (int u = 0; u <= SH::PF; ++u) {
+          uint64_t pb[RT];
+          issue_tile(ring[(u + SH::PF) % (SH::PF + 1)], tile_at(i + u + SH::PF), blk_next);
+          blk_next = block_of(tile_at(i + u + SH::PF + 1));
+          score_tile(ring[u], first_t + (i + u) * NW, pb);
+          pv_tile(pb);
+          if (i + u + 1 >= n_w) goto chunk_done;
+        }
       }
     }
+  chunk_done:
+    if (ce >= te) break;
+    // Next chunk: every wave has read its last id of this one.
+    __syncthreads();
+    cs = ce;
+    for (int t = tid; t < min(te - cs, kMaxSegTiles); t += SH::kThreads)
+      sm_ids[t] = table[((cs + t) * 16) / p.page_size];
+    __syncthreads();
   }
-tiles_done:
 
   // ---- combine the waves (one LDS slot per wave, summed in wave order:
   //      deterministic) ----
@@ -463,7 +500,7 @@ tiles_done:
     }
   }
   __syncthreads();
-  finish<T, D, RT, NW>(p, lds, s, kvh, rg, seg, row0, wg_rows, n_live, SH::kBytes);
+  finish<T, D, RT, NW>(p, lds, s, kvh, row0, wg_rows, fr, SH::kBytes);
 }
 
 // PERSIST selects the grid: one workgroup per item, or the persistent
@@ -518,10 +555,15 @@ __global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(
       kvh = unit % p.num_kv_heads;
       rg = unit / p.num_kv_heads;
     }
-    decode_unit<T, D, RT, LEAN>(p, lds, blockIdx.y, kvh, rg, seg);
+    decode_unit<T, D, RT, LEAN, false>(p, lds, blockIdx.y, kvh, rg, seg, Frag{});
   } else {
-    persistent_loop(p, lds, SH::kPersistOff, SH::kBytes, SH::kThreads,
-                    [&](int s, int kvh, int rg, int seg) { decode_unit<T, D, RT, LEAN>(p, lds, s, kvh, rg, seg); });
+    balanced_loop(
+        p, lds, SH::kPersistOff, SH::kThreads,
+        [&](int s, int kvh, int rg, const Frag& f) { decode_unit<T, D, RT, LEAN, true>(p, lds, s, kvh, rg, 0, f); },
+        [&](int s, int kvh, int rg, int M) {
+          const int row0 = rg * RT * 16, n = min(RT * 16, p.group * M - row0);
+          if (n > 0) zero_rows<T, D>(p, s, kvh, row0, n, SH::kThreads);
+        });
   }
 }
 
@@ -780,7 +822,19 @@ tiles_done:
     }
   }
   __syncthreads();
-  finish<T, D, 1, NW>(p, lds, s, kvh, 0, seg, 0, rows, n_live, SH::kBytes);
+  Frag fr;
+  fr.ts = ts;
+  fr.te = te;
+  fr.n_parts = n_live;
+  fr.merge_slices = p.merge_slices;
+  const int64_t slot0 = (int64_t(s) * p.num_kv_heads + kvh) * p.nseg;
+  fr.slot = slot0 + seg;
+  fr.parts.first = slot0;
+  fr.parts.last = slot0 + n_live - 1;
+  fr.parts.n = n_live;
+  fr.parts.row0 = 0;
+  fr.ctl = p.ws_cnt + (int64_t(s) * p.num_kv_heads + kvh) * p.merge_slices * kCtlStride;
+  finish<T, D, 1, NW>(p, lds, s, kvh, 0, rows, fr, SH::kBytes);
 }
 
 // The persistent grid always fills the device and runs the lean loop; a

@@ -17,8 +17,8 @@ struct Params {
   const int32_t* seq_lens;    // [S]
   void* out;                  // same layout as q
   int32_t* ws_cnt;            // merge control [S, Hkv, row_groups, merge_slices]
-  float* ws_ml;               // partial (m, l) [S, Hkv, nseg, rows, 2]
-  float* ws_acc;              // partial acc     [S, Hkv, nseg, rows, D]
+  float* ws_ml;               // partial (m, l) [slots, slot_rows, 2]
+  float* ws_acc;              // partial acc     [slots, slot_rows, D]
   int64_t block_stride;       // elements between physical blocks
   int64_t head_stride;        // elements between kv heads of a block
   int64_t token_stride;       // elements between tokens of a block
@@ -30,8 +30,9 @@ struct Params {
   int32_t row_groups;         // workgroups splitting the rows
   int32_t group_rows;         // query rows per row group (row tiles * 16)
   int32_t merge_slices;       // slices of the merged output (merging workgroups)
+  int32_t slot_rows;          // rows of one partial slot (see Plan::slot_rows)
   uint32_t merge_wait_ticks;  // helpers' wait bound (100 MHz real-time ticks)
-  int32_t persistent;         // 1: workgroups take items from the queue word
+  int32_t persistent;         // 1: balanced persistent grid (one workgroup per CU)
   float scale_log2;           // scale * log2(e): logits are kept in the exp2 domain
 };
 

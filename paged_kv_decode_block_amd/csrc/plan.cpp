@@ -81,29 +81,31 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   // One workgroup per CU: its 4 waves keep enough loads in flight.
   const int64_t slots = num_cus;
   const int64_t tile_bytes = int64_t(kTileKeys) * 2 * sh.head_size * 2;
-  // A batch whose lengths may differ runs on a persistent grid when one
-  // workgroup per planned segment would oversubscribe the device: the
-  // lengths are only known on the device, and a static grid there leaves
-  // CUs idle behind dead or short workgroups.  Its segments hold about
-  // 3 MiB of K/V each: every item pays a fixed prologue, combine, publish
-  // and pipeline-fill cost, which smaller items repeat more often, while
-  // larger ones balance worse over the CUs (measured on 64 bf16 sequences
-  // of 512..16384 keys, 16/2 heads of 256: items of 0.5, 1, 2, 3 and 4 MiB
-  // took 303, 265, 256, 246 and 267 us).
+  // A batch whose lengths may differ runs on the balanced persistent grid
+  // when one round of about 3 MiB per workgroup would not cover its
+  // planned K/V: the lengths are only known on the device, where a static
+  // grid (or a queue of fixed-size items) leaves CUs idle behind short,
+  // dead or late items, while the balanced grid gives every CU the same
+  // number of tiles (64 bf16 sequences of 512..16384 keys, 16/2 heads of
+  // 256: a queue of 3 MiB items took 239 us, with the schedule alone
+  // costing about 50 us over an even split).  It needs the batch's tiles to
+  // count in 32 bits, its sequences to fit the LDS tables and one control
+  // word per unit to fit the counter prefix.
   const int64_t seg_persist = std::max<int64_t>(4, (int64_t(3) << 20) / tile_bytes);
-  if (sh.schedule == PAD_SCHED_PERSISTENT && sh.num_seqs > kPersistMaxSeqs) return PAD_EUNSUPPORTED;
   // The dot family is built for one workgroup per item only.
-  const bool can_persist = p.path != PAD_PATH_DOT;
+  const bool can_persist = p.path != PAD_PATH_DOT && sh.num_seqs <= kPersistMaxSeqs &&
+                           units * (ceil_div(table_keys, kTileKeys) + 1) < (int64_t(1) << 31) &&
+                           units * kCtlWordStride * int64_t(sizeof(int32_t)) <= int64_t(kCounterBytes);
   if (sh.schedule == PAD_SCHED_PERSISTENT && !can_persist) return PAD_EUNSUPPORTED;
   p.persistent = sh.schedule == PAD_SCHED_PERSISTENT ||
-                 (sh.schedule == PAD_SCHED_AUTO && can_persist && sh.num_seqs > 1 && sh.num_seqs <= kPersistMaxSeqs &&
+                 (sh.schedule == PAD_SCHED_AUTO && can_persist && sh.num_seqs > 1 &&
                   units * std::max<int64_t>(1, sh.num_segments > 0 ? sh.num_segments : ceil_div(span_tiles, seg_persist)) >
                       slots);
   int64_t nseg;
   if (sh.num_segments > 0) {
     nseg = sh.num_segments;
   } else if (p.persistent) {
-    nseg = ceil_div(span_tiles, seg_persist);
+    nseg = 1;  // the balanced grid splits units by share, not by segment
   } else {
     // One full round of workgroups for a single sequence; two rounds when a
     // batch's lengths may differ, so short sequences leave no idle CUs.
@@ -169,7 +171,12 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   // splits the tiles it finds over the planned segments).
   int64_t max_tiles = ceil_div(table_keys, kTileKeys);
   if (window > 0) max_tiles = std::min(max_tiles + 1, ceil_div(int64_t(window) + sh.query_len - 1, kTileKeys) + 1);
-  if (ceil_div(max_tiles, p.nseg) > kMaxSegTiles || p.seg_tiles > kMaxSegTiles) {
+  if (p.persistent) {
+    // Items on the balanced grid are shares of the batch's tiles; one
+    // longer than the LDS id area is walked in chunks.
+    p.nseg = 1;
+    p.seg_tiles = int(span_tiles);
+  } else if (ceil_div(max_tiles, p.nseg) > kMaxSegTiles || p.seg_tiles > kMaxSegTiles) {
     const int64_t need = ceil_div(max_tiles, kMaxSegTiles);
     if (need > kMaxSegments) return PAD_EUNSUPPORTED;
     p.nseg = int(std::max<int64_t>(p.nseg, need));
@@ -193,73 +200,70 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   // persistent grid takes the lean loop too (batch workload 246 -> 239 us).
   p.lean = p.persistent || (p.row_tiles == 1 && int64_t(p.grid_x) * p.grid_y >= num_cus);
 
-  // The workspace holds partial slots for a segment count that bounds what
-  // any window plans for this shape (forced, the static grid's fill, the
-  // persistent grid's 3 MiB segments and the LDS block-id bound, all at
-  // the window-free span), so one pad_decode_attn_workspace_size serves
-  // every call of the shape; the slot stride of a call is its own count.
+  // The workspace holds partial slots for whichever schedule the shape
+  // may take under any window, so one pad_decode_attn_workspace_size
+  // serves every call of the shape.  Grid: per unit a segment count that
+  // bounds what any window plans (forced, the static grid's fill and the
+  // LDS block-id bound, all at the window-free span); the slot stride of a
+  // call is its own count.  Balanced grid: two slots per workgroup.
+  const bool may_persist = can_persist && (sh.schedule == PAD_SCHED_PERSISTENT ||
+                                           (sh.schedule == PAD_SCHED_AUTO && sh.num_seqs > 1));
+  const bool may_grid = sh.schedule != PAD_SCHED_PERSISTENT;
   int64_t ws_nseg;
-  {
-    const bool may_persist = can_persist && (sh.schedule == PAD_SCHED_PERSISTENT ||
-                                             (sh.schedule == PAD_SCHED_AUTO && sh.num_seqs > 1 &&
-                                              sh.num_seqs <= kPersistMaxSeqs));
-    const bool may_grid = sh.schedule != PAD_SCHED_PERSISTENT;
-    if (sh.num_segments > 0) {
-      ws_nseg = sh.num_segments;
-    } else {
-      const int64_t target = sh.num_seqs > 1 ? 2 * slots : slots;
-      // A window-free span of at most 64 KiB per unit plans one segment
-      // (and so does every window, which only shortens it).
-      const bool one_seg = all_tiles * tile_bytes <= (int64_t(64) << 10);
-      ws_nseg = may_grid && !one_seg ? std::max<int64_t>(1, target / std::max<int64_t>(1, units)) : 1;
-      if (may_persist) ws_nseg = std::max(ws_nseg, ceil_div(all_tiles, seg_persist));
-    }
-    ws_nseg = std::min(ws_nseg, std::min<int64_t>(all_tiles, kMaxSegments));
-    ws_nseg = std::max<int64_t>(ws_nseg, ceil_div(ceil_div(table_keys, kTileKeys), kMaxSegTiles));
-    ws_nseg = std::max<int64_t>(ws_nseg, p.nseg);
+  if (sh.num_segments > 0) {
+    ws_nseg = sh.num_segments;
+  } else {
+    const int64_t target = sh.num_seqs > 1 ? 2 * slots : slots;
+    // A window-free span of at most 64 KiB per unit plans one segment
+    // (and so does every window, which only shortens it).
+    const bool one_seg = all_tiles * tile_bytes <= (int64_t(64) << 10);
+    ws_nseg = one_seg ? 1 : std::max<int64_t>(1, target / std::max<int64_t>(1, units));
   }
+  ws_nseg = std::min(ws_nseg, std::min<int64_t>(all_tiles, kMaxSegments));
+  ws_nseg = std::max<int64_t>(ws_nseg, ceil_div(ceil_div(table_keys, kTileKeys), kMaxSegTiles));
+  if (!p.persistent) ws_nseg = std::max<int64_t>(ws_nseg, p.nseg);
   p.ws_nseg = int(ws_nseg);
-  // Whether the window-free span plans the persistent grid: a window only
-  // shortens the span, so no window plans it otherwise.
-  const bool persist_any =
-      sh.schedule == PAD_SCHED_PERSISTENT ||
-      (sh.schedule == PAD_SCHED_AUTO && can_persist && sh.num_seqs > 1 && sh.num_seqs <= kPersistMaxSeqs &&
-       units * std::max<int64_t>(1, sh.num_segments > 0 ? sh.num_segments : ceil_div(all_tiles, seg_persist)) > slots);
-  if (ws_nseg > 1 || persist_any) {
-    const size_t S = size_t(sh.num_seqs), H = size_t(sh.num_kv_heads);
-    const size_t slot_rows = S * H * size_t(ws_nseg) * size_t(rows);
+  const size_t S = size_t(sh.num_seqs), H = size_t(sh.num_kv_heads), D = size_t(sh.head_size);
+  const size_t grid_rows = may_grid && ws_nseg > 1 ? S * H * size_t(ws_nseg) * size_t(rows) : 0;
+  const size_t bal_slot_rows = size_t(std::min(rows, p.row_tiles * 16));
+  const size_t bal_rows = may_persist ? 2 * size_t(num_cus) * bal_slot_rows : 0;
+  auto bytes_for = [&](size_t r) { return r ? kCounterBytes + align_up(r * 2 * sizeof(float)) + align_up(r * D * sizeof(float)) : 0; };
+  p.ws_bytes = std::max(bytes_for(grid_rows), bytes_for(bal_rows));
+  p.ws_counters = 0;
+  p.ws_ml = p.ws_bytes ? kCounterBytes : 0;
+  if (p.persistent) {
+    p.slot_rows = int(bal_slot_rows);
+    p.ws_acc = p.ws_ml + align_up(bal_rows * 2 * sizeof(float));
+  } else {
+    p.slot_rows = rows;
+    p.ws_acc = p.ws_ml + align_up(grid_rows * 2 * sizeof(float));
+  }
+  if (p.persistent) {
+    // The last arriving item of a unit merges alone: items start as
+    // workgroups reach them, so a helper could wait for a whole share.
+    p.merge_slices = 1;
+  } else if (p.nseg > 1) {
     // Slices: about kSliceBytes of partial accumulators each, limited by
     // the segments (each merging workgroup must have arrived) and by the
     // control words the counter prefix holds.
     const size_t wg_rows = size_t(std::min(rows, p.row_tiles * 16));
-    const size_t vol = size_t(p.nseg) * wg_rows * size_t(sh.head_size) * sizeof(float);
+    const size_t vol = size_t(p.nseg) * wg_rows * D * sizeof(float);
     // Helpers wait for their unit's last segment, so they are used only
-    // when every workgroup of the grid can be resident at once.  On the
-    // persistent grid, or on a grid larger than one workgroup per CU, the
-    // last segment may only start once a waiting helper's CU frees up
-    // (measured: 48 segments of a 512-wide head with 4 row groups, 384
-    // workgroups, took 425 us with helpers against 73 us at 32 segments):
-    // the last arriver merges alone there.
-    const bool resident = !p.persistent && int64_t(p.grid_x) * p.grid_y <= slots;
+    // when every workgroup of the grid can be resident at once.  On a grid
+    // larger than one workgroup per CU the last segment may only start
+    // once a waiting helper's CU frees up (measured: 48 segments of a
+    // 512-wide head with 4 row groups, 384 workgroups, took 425 us with
+    // helpers against 73 us at 32 segments): the last arriver merges alone
+    // there.
+    const bool resident = int64_t(p.grid_x) * p.grid_y <= slots;
     int64_t k = resident ? int64_t((vol + kSliceBytes - 1) / kSliceBytes) : 1;
     k = std::max<int64_t>(1, std::min<int64_t>(k, std::min(p.nseg, kMaxSlices)));
     const size_t ctl_units = S * H * size_t(p.row_groups);
-    k = std::min<int64_t>(k, int64_t((kCounterBytes - 128) /
-                                     (sizeof(int32_t) * kCtlWordStride * std::max<size_t>(1, ctl_units))));
-    if (p.nseg > 1 && k < 1) return PAD_EUNSUPPORTED;  // more units than the control prefix holds
-    p.merge_slices = int(std::max<int64_t>(1, k));
-    p.ws_counters = 0;
-    p.ws_ml = kCounterBytes;
-    if (ws_nseg > 1) {
-      p.ws_acc = p.ws_ml + align_up(slot_rows * 2 * sizeof(float));
-      p.ws_bytes = p.ws_acc + align_up(slot_rows * size_t(sh.head_size) * sizeof(float));
-    } else {  // the work queue only: a single segment publishes no partial
-      p.ws_acc = p.ws_ml;
-      p.ws_bytes = kCounterBytes;
-    }
+    k = std::min<int64_t>(k, int64_t(kCounterBytes / (sizeof(int32_t) * kCtlWordStride * std::max<size_t>(1, ctl_units))));
+    if (k < 1) return PAD_EUNSUPPORTED;  // more units than the control prefix holds
+    p.merge_slices = int(k);
   } else {
     p.merge_slices = 1;
-    p.ws_counters = p.ws_ml = p.ws_acc = p.ws_bytes = 0;
   }
   *pl = p;
   return PAD_OK;

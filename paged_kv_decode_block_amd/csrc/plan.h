@@ -46,14 +46,11 @@ constexpr int kDotWaveCount = 4;
 // Merge control words live in a fixed-size prefix of the workspace, so
 // calls of different shapes can share one workspace: partials never land
 // where any shape keeps control words, and every call leaves them zero.
-// The prefix's last 128-byte line holds the persistent grid's work queue.
 constexpr size_t kCounterBytes = size_t(1) << 20;
-constexpr int kQueueWord = int((kCounterBytes - 128) / 4);
-// Persistent grid (batched decode): at most this many sequences (its LDS
-// tables), sorted longest first up to kPersistSortSeqs of them.
+// Balanced persistent grid (batched decode): at most this many sequences
+// (its LDS tables).
 constexpr int kPersistMaxSeqs = 1024;
 constexpr int64_t kLdsPerCu = 160 << 10;  // LDS bytes of a gfx950 CU
-constexpr int kPersistSortSeqs = 512;
 
 // Waves per workgroup.  Four for every shape: on one bf16 sequence with
 // 32 query / 8 kv heads of size 128 and 16-key pages, 4 waves with one
@@ -72,14 +69,17 @@ struct Plan {
   int seg_tiles;     // planned tiles per segment
   int merge_slices;  // slices the merged output is cut into (1..kMaxSlices)
   int ws_nseg;       // segment slots the workspace holds (>= nseg, the same for every window)
-  int persistent;    // 1: one workgroup per CU takes items from a queue
+  int persistent;    // 1: one workgroup per CU takes an equal share of the batch's tiles
   int lean;          // 1: the grid fills the device (single-copy tile loop)
   int grid_x, grid_y;
+  int slot_rows;     // rows of one partial slot: G*M (grid) or row_tiles*16 (balanced grid)
   // Workspace layout (byte offsets; all 256-byte aligned): the counter
   // prefix (kCounterBytes; per (unit, row group) merge_slices words, one
   // 128-byte line apart: the arrival counter, then one hand-over word per
-  // slice after the first),
-  // then per unit nseg segment slots of (m, l) and of acc.
+  // slice after the first), then the partial slots of (m, l) and of acc:
+  // per unit nseg slots of all G*M rows on the grid schedule, 2 per
+  // workgroup of row_tiles*16 rows on the balanced grid.  ws_bytes covers
+  // every schedule the shape may take under any window.
   size_t ws_counters, ws_ml, ws_acc, ws_bytes;
 };
 

@@ -84,41 +84,51 @@ def test_plan_invariants(kw):
     assert p["num_segments"] * p["segment_tiles"] >= tiles
     assert (p["num_segments"] - 1) * p["segment_tiles"] < tiles
     assert 1 <= p["num_segments"] <= 256
+    D = sh.head_size
+    if p["persistent"]:
+        # one workgroup per CU, each taking an equal share of the batch's
+        # tiles; two partial slots of one workgroup's rows per workgroup,
+        # after the 1 MiB control prefix, and the last arriver merges alone
+        assert p["grid_y"] == 1 and p["grid_x"] == 256 and p["num_segments"] == 1
+        slot_rows = min(rows, p["row_tiles"] * 16)
+        bal = (1 << 20) + _align(512 * slot_rows * 2 * 4) + _align(512 * slot_rows * D * 4)
+        assert p["workspace_bytes"] >= bal
+        assert p["merge_slices"] == 1
+        return
     # segments stay within 4096 tiles (the LDS block-id stage) for any
     # device length up to the table's capacity
     assert p["segment_tiles"] <= 4096 and -(-tiles // p["num_segments"]) <= 4096
-    if p["persistent"]:
-        # one workgroup per CU;
-        # items come from the queue
-        assert p["grid_y"] == 1 and p["grid_x"] % 256 == 0 and 256 <= p["grid_x"] <= 4 * 256
-        assert p["workspace_bytes"] >= 1 << 20
-    else:
-        assert p["grid_x"] == p["num_segments"] * sh.num_kv_heads * p["row_groups"]
-        assert p["grid_y"] == sh.num_seqs
-    if p["num_segments"] == 1 and not p["persistent"]:
-        assert p["workspace_bytes"] == 0
+    assert p["grid_x"] == p["num_segments"] * sh.num_kv_heads * p["row_groups"]
+    assert p["grid_y"] == sh.num_seqs
+    S, H = sh.num_seqs, sh.num_kv_heads
+    if p["num_segments"] == 1:
         assert p["merge_slices"] == 1
-    elif p["num_segments"] > 1:
+        if S == 1:
+            assert p["workspace_bytes"] == 0
+    else:
         # a fixed 1 MiB prefix of merge control words, then one (m, l) and one
-        # acc slot per segment
-        S, H, n = sh.num_seqs, sh.num_kv_heads, p["num_segments"]
+        # acc slot per segment (or the balanced grid's slots, if larger, for a
+        # batch that another window would put there)
+        n = p["num_segments"]
         nw = p["workspace_segments"]
         assert nw >= n
-        want = (1 << 20) + _align(S * H * nw * rows * 2 * 4) + _align(S * H * nw * rows * sh.head_size * 4)
-        assert p["workspace_bytes"] == want
+        want = (1 << 20) + _align(S * H * nw * rows * 2 * 4) + _align(S * H * nw * rows * D * 4)
+        assert p["workspace_bytes"] >= want
+        if S == 1:
+            assert p["workspace_bytes"] == want
         # about 32 KiB of partial accumulators per merge slice, at most 32
         # slices and no more than segments; control words fit the prefix
         k = p["merge_slices"]
         wg_rows = min(rows, p["row_tiles"] * 16)
-        vol = n * wg_rows * sh.head_size * 4
+        vol = n * wg_rows * D * 4
         assert 1 <= k <= min(32, n)
-        # control words one 128-byte line apart, clear of the queue line
-        # helpers only when the whole grid is resident (one workgroup per CU)
-        resident = not p["persistent"] and p["grid_x"] * p["grid_y"] <= 256
-        want_k = min(-(-vol // (32 << 10)), 32, n, ((1 << 20) - 128) // (128 * S * H * p["row_groups"])) \
+        # control words one 128-byte line apart; helpers only when the
+        # whole grid is resident (one workgroup per CU)
+        resident = p["grid_x"] * p["grid_y"] <= 256
+        want_k = min(-(-vol // (32 << 10)), 32, n, (1 << 20) // (128 * S * H * p["row_groups"])) \
             if resident else 1
         assert k == want_k
-        assert S * H * p["row_groups"] * k * 128 <= (1 << 20) - 128
+        assert S * H * p["row_groups"] * k * 128 <= 1 << 20
 
 
 def test_plan_bounds_segment_length():
@@ -140,16 +150,19 @@ def test_plan_bounds_segment_length():
 def test_schedule_plan():
     batch = dict(num_seqs=65, num_q_heads=16, num_kv_heads=2, head_size=256, page_size=1056, max_blocks_per_seq=16)
     p = plan(shape(**batch))
-    assert p["persistent"] == 1 and p["grid_x"] == 256
+    assert p["persistent"] == 1 and p["grid_x"] == 256 and p["grid_y"] == 1
+    # the balanced grid splits by share: no segment count, the last arriver
+    # merges alone, and a forced segment count does not change it
+    assert p["num_segments"] == 1 and p["merge_slices"] == 1
+    b = plan(shape(num_segments=8, schedule=pad.PAD_SCHED_PERSISTENT, **batch))
+    assert (b["persistent"], b["num_segments"], b["grid_x"]) == (1, 1, 256)
     g = plan(shape(schedule=pad.PAD_SCHED_GRID, **batch))
     assert g["persistent"] == 0 and g["grid_y"] == 65
-    # with the segment count fixed, both schedules split the same way
+    # the automatic schedule's workspace also serves the grid the batch
+    # takes under a window
+    assert p["workspace_bytes"] >= g["workspace_bytes"]
+    # a grid larger than one workgroup per CU: the last arriver merges alone
     a = plan(shape(num_segments=8, schedule=pad.PAD_SCHED_GRID, **batch))
-    b = plan(shape(num_segments=8, schedule=pad.PAD_SCHED_PERSISTENT, **batch))
-    assert (a["num_segments"], a["segment_tiles"]) == (b["num_segments"], b["segment_tiles"])
-    # the persistent grid's last arriver merges alone
-    assert b["merge_slices"] == 1
-    # so does one on a grid larger than one workgroup per CU
     assert a["grid_x"] * a["grid_y"] > 256 and a["merge_slices"] == 1
     wide = dict(num_q_heads=16, num_kv_heads=2, head_size=512, page_size=32, max_blocks_per_seq=1024, query_len=8)
     assert plan(shape(num_segments=32, **wide))["merge_slices"] == 32  # 256 workgroups
@@ -157,7 +170,24 @@ def test_schedule_plan():
     # batch 1 stays on one workgroup per item unless asked
     assert plan(shape())["persistent"] == 0
     one = plan(shape(schedule=pad.PAD_SCHED_PERSISTENT, num_segments=1, max_blocks_per_seq=4))
-    assert one["persistent"] == 1 and one["num_segments"] == 1 and one["workspace_bytes"] == 1 << 20
+    rows = 16
+    assert one["persistent"] == 1 and one["num_segments"] == 1
+    assert one["workspace_bytes"] == (1 << 20) + _align(512 * rows * 8) + _align(512 * rows * 128 * 4)
+    # the balanced grid needs the batch's tiles to count in 32 bits and one
+    # control word per unit in the 1 MiB prefix; otherwise a batch stays on
+    # the grid, and asking for the balanced grid is rejected
+    many = dict(num_seqs=1000, num_q_heads=64, num_kv_heads=16, head_size=128, max_blocks_per_seq=64)
+    assert plan(shape(**many))["persistent"] == 0  # 16000 units of control words
+    with pytest.raises(pad.PadError) as e:
+        plan(shape(schedule=pad.PAD_SCHED_PERSISTENT, **many))
+    assert e.value.status == pad.PAD_EUNSUPPORTED
+    huge = dict(num_seqs=512, num_kv_heads=8, num_q_heads=8, max_blocks_per_seq=600000)
+    assert plan(shape(**huge))["persistent"] == 0  # 4096 units x 600001 tiles >= 2^31
+    # a long share is walked in chunks of staged block ids: no bound on the
+    # tiles per workgroup
+    long_batch = plan(shape(num_seqs=8, num_kv_heads=8, num_q_heads=32, max_blocks_per_seq=60000,
+                            schedule=pad.PAD_SCHED_PERSISTENT))
+    assert long_batch["persistent"] == 1 and long_batch["segment_tiles"] == 60000
 
 
 def test_plan_fills_device():
@@ -463,8 +493,8 @@ def test_noalloc_validates_before_launch():
     # a split call with bad pointers fails on the pointers, not the device
     assert plan(shape(num_segments=4))["workspace_bytes"] > 0
     assert call(shape(num_segments=4), out=0) == pad.PAD_EINVAL
-    big = shape(num_seqs=128, num_q_heads=64, num_kv_heads=8, head_size=512, query_len=8, page_size=16,
-                max_blocks_per_seq=2048)
+    big = shape(num_seqs=64, num_q_heads=64, num_kv_heads=8, head_size=512, query_len=8, page_size=16,
+                max_blocks_per_seq=2048, num_segments=64, schedule=pad.PAD_SCHED_GRID)
     assert plan(big)["workspace_bytes"] > pad.PAD_NOALLOC_SCRATCH_BYTES
     assert call(big) == pad.PAD_ESCRATCH
     assert call(big, q=0) == pad.PAD_ESCRATCH  # the size bound is checked first

@@ -246,29 +246,84 @@ SCHEDULE_CASES = [
 
 
 @pytest.mark.parametrize("cfg,lens,M,window,nseg", SCHEDULE_CASES, ids=[f"sch{i}" for i in range(len(SCHEDULE_CASES))])
-def test_schedules_give_same_bits(cfg, lens, M, window, nseg):
-    """One workgroup per item and the persistent grid compute every item
-    alike: the same output bits, and the workspace's control prefix (merge
-    words and the work queue) is left zero."""
+def test_both_schedules(cfg, lens, M, window, nseg):
+    """One workgroup per item and the balanced persistent grid both match
+    the oracle, each gives the same bits on every call, and each leaves the
+    workspace's control prefix zero."""
     if lens is None:
         c = wl.config_case(cfg, 3000, M, device=DEV)
     else:
         c = _case(wl.CONFIGS[cfg], lens, M, 500 + cfg, window=window)
     ref = oracle_out(c)
-    outs = []
     for sched in (pad.PAD_SCHED_GRID, pad.PAD_SCHED_PERSISTENT):
         shape = pad.make_shape(c.q, c.kv_cache, c.block_tables[0], c.layout, num_segments=nseg, schedule=sched)
         plan = pad.pad_decode_attn_plan(shape, c.window)
         assert plan["persistent"] == (sched == pad.PAD_SCHED_PERSISTENT)
         ws = torch.empty(pad.pad_decode_attn_workspace_size(shape), dtype=torch.uint8, device=DEV)
         pad.pad_decode_attn_workspace_init(ws)
-        for _ in range(2):  # the queue must be reusable
-            out = run_gpu(c, workspace=ws, num_segments=nseg, schedule=sched)
+        outs = [run_gpu(c, workspace=ws, num_segments=nseg, schedule=sched) for _ in range(3)]
         torch.cuda.synchronize()
-        check(out, ref, c.q.dtype, f"schedule {sched}")
+        check(outs[0], ref, c.q.dtype, f"schedule {sched}")
+        assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2]), "deterministic"
         assert int(ws[: 1 << 20].view(torch.int32).abs().sum()) == 0
-        outs.append(out)
-    assert torch.equal(outs[0], outs[1])
+
+
+# Batches for the balanced persistent grid: a unit split over every share,
+# fewer tiles than workgroups, row groups, windows and zero-length
+# sequences.
+BALANCED_CASES = [
+    # spec, lens, M, window
+    (wl.CONFIGS[2], [32768], 4, 0),                      # 8 units over 256 shares
+    (wl.Spec("bf16", 128, 4, 1, 16, wl.HND), [20000], 1, 0),  # one unit in every share: 256 partials
+    (wl.CONFIGS[2], [40, 1, 0, 17], 2, 0),               # 7 tiles per kv head: fewer tiles than workgroups
+    (wl.Spec("bf16", 128, 8, 8, 16, wl.HND), [70000, 65000, 90], 1, 0),  # 264-tile shares over 24 units
+    (wl.CONFIGS[4], [3000, 900, 0, 2500], 8, 0),         # 4 row groups per kv head
+    (wl.CONFIGS[3], [5000, 700, 16384], 4, 512),         # windows, NHD
+]
+
+
+@pytest.mark.parametrize("case", BALANCED_CASES, ids=[f"bal{i}" for i in range(len(BALANCED_CASES))])
+def test_balanced_grid(case):
+    spec, lens, M, window = case
+    c = _case(spec, lens, M, 650 + len(lens) + M, window=window)
+    ref = oracle_out(c)
+    shape = pad.make_shape(c.q, c.kv_cache, c.block_tables[0], c.layout, schedule=pad.PAD_SCHED_PERSISTENT)
+    plan = pad.pad_decode_attn_plan(shape, c.window)
+    assert plan["persistent"] == 1
+    ws = torch.empty(pad.pad_decode_attn_workspace_size(shape), dtype=torch.uint8, device=DEV)
+    pad.pad_decode_attn_workspace_init(ws)
+    for it in range(2):
+        ws[1 << 20:].fill_(0xFF)  # NaN partials: every slot the merge reads must be written first
+        out = run_gpu(c, workspace=ws, schedule=pad.PAD_SCHED_PERSISTENT)
+        torch.cuda.synchronize()
+        check(out, ref, c.q.dtype, f"balanced grid {lens} M={M} call {it}")
+        assert int(ws[: 1 << 20].view(torch.int32).abs().sum()) == 0, "control words left zero"
+
+
+def test_balanced_grid_long_shares_periodic_cache():
+    """Shares longer than the LDS block-id area (4096 tiles) are walked in
+    chunks.  Closed form: a sequence of 20M keys whose block table maps
+    every page to the same physical block holds 1.25M copies of that
+    block's 16 keys, so its softmax gives each copy the same weight and the
+    output equals attention over the single 16-key page (oracle).  One unit
+    spans all shares: its 256 partials take the 32-lane merge."""
+    spec = wl.Spec("bf16", 128, 4, 1, 16, wl.HND)
+    base = _case(spec, [16, 16], 1, 4711)
+    L = 20 * (1 << 20)
+    nb = L // 16
+    blk = int(base.block_tables[0][0, 0])
+    table = torch.full((2, nb), blk, dtype=torch.int32, device=DEV)
+    table[1, 1:] = base.poison_block  # a 16-key sequence beside it
+    table[1, 0] = int(base.block_tables[0][1, 0])
+    lens = torch.tensor([L, 16], dtype=torch.int32, device=DEV)
+    big = wl.Case(spec, base.q, base.kv_cache, [table], lens, base.scale, 0, base.poison_block, base.seed)
+    shape = pad.make_shape(big.q, big.kv_cache, table, big.layout, schedule=pad.PAD_SCHED_PERSISTENT)
+    plan = pad.pad_decode_attn_plan(shape, 0)
+    assert plan["persistent"] == 1 and (nb + 1) // 256 > 4096
+    say(f"periodic cache: {L} keys in one block, shares of {(nb + 1) // 256} tiles")
+    out = run_gpu(big, schedule=pad.PAD_SCHED_PERSISTENT)
+    torch.cuda.synchronize()
+    check(out, oracle_out(base), big.q.dtype, "20M keys of one repeated page")
 
 
 def test_graph_replay():

@@ -1,8 +1,7 @@
 """Prefill chunks (M > 8 query tokens per sequence) on the HIP path against
 the fp64 oracle: each row group reads only the keys its own tokens reach
-(the row-tile work list of plan_prefill on the rdna_hip page), the
-persistent grid takes the heaviest row groups first, and the output bits
-do not depend on the schedule."""
+(the row-tile work list of plan_prefill on the rdna_hip page), on both
+schedules."""
 
 import numpy as np
 import pytest
@@ -38,17 +37,18 @@ def test_prefill_chunk(case):
 
 
 def test_prefill_batch_schedules():
-    """A batch of chunks of different lengths: both schedules give the same
-    bits, and both match the oracle."""
+    """A batch of chunks of different lengths: both schedules match the
+    oracle, and the balanced grid gives the same bits on every call."""
     spec = wl.CONFIGS[2]
     c = wl.make_case(spec, [1500, 300, 0, 2600], 48, seed=8101, device=DEV)
     say("prefill batch: config 2 shapes, lens [1500, 300, 0, 2600], M=48")
-    shape = pad.make_shape(c.q, c.kv_cache, c.block_tables[0], c.layout, num_segments=4)
-    n = pad.pad_decode_attn_plan(shape, c.window)["num_segments"]
-    grid = run_gpu(c, num_segments=n, schedule=pad.PAD_SCHED_GRID)
-    per = run_gpu(c, num_segments=n, schedule=pad.PAD_SCHED_PERSISTENT)
-    check(grid, oracle_out(c), c.q.dtype, "prefill batch")
-    assert torch.equal(grid, per), "schedules give the same bits"
+    ref = oracle_out(c)
+    grid = run_gpu(c, num_segments=4, schedule=pad.PAD_SCHED_GRID)
+    per = run_gpu(c, schedule=pad.PAD_SCHED_PERSISTENT)
+    again = run_gpu(c, schedule=pad.PAD_SCHED_PERSISTENT)
+    check(grid, ref, c.q.dtype, "prefill batch, grid")
+    check(per, ref, c.q.dtype, "prefill batch, balanced grid")
+    assert torch.equal(per, again), "deterministic"
 
 
 def test_mixed_decode_and_prefill_counts():

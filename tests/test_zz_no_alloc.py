@@ -93,12 +93,13 @@ def test_noalloc_graph_replay():
 
 def test_noalloc_rejects_calls_beyond_its_array():
     spec = wl.Spec("bf16", 512, 64, 8, 16, wl.HND)
-    q = torch.zeros((128, 8, 64, 512), dtype=torch.bfloat16, device=DEV)
+    q = torch.zeros((64, 8, 64, 512), dtype=torch.bfloat16, device=DEV)
     kv = torch.zeros((2, 8, 16, 2, 512), dtype=torch.bfloat16, device=DEV)
-    bt = torch.zeros((128, 2048), dtype=torch.int32, device=DEV)
-    lens = torch.zeros(128, dtype=torch.int32, device=DEV)
-    shape = pad.make_shape(q, kv, bt, wl.HND)
+    bt = torch.zeros((64, 2048), dtype=torch.int32, device=DEV)
+    lens = torch.zeros(64, dtype=torch.int32, device=DEV)
+    kw = dict(num_segments=64, schedule=pad.PAD_SCHED_GRID)
+    shape = pad.make_shape(q, kv, bt, wl.HND, **kw)
     assert pad.pad_decode_attn_workspace_size(shape) > pad.PAD_NOALLOC_SCRATCH_BYTES
     with pytest.raises(pad.PadError) as e:
-        pad.pad_decode_attn_noalloc(q, kv, bt, lens, 0.1, 0, torch.empty_like(q), layout=spec.layout)
+        pad.pad_decode_attn_noalloc(q, kv, bt, lens, 0.1, 0, torch.empty_like(q), layout=spec.layout, **kw)
     assert e.value.status == pad.PAD_ESCRATCH
