@@ -5,7 +5,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 and its Python binding) never calls it and shares no code with it.
 
 Everything here is plain fp64 NumPy written from the defining passages of
-the pages (cited per function).  See ``oracle.attention`` for the parity
+the pages (cited per function).  ``oracle.octave`` holds the quantized
+packed-cache codec and attention over it.  See ``oracle.attention`` for the parity
 status of each function; every function is pinned by ``tests/test_oracle*.py``
 against closed forms, brute force, a library routine or hand-computed
 fixtures under ``tests/golden/``.
