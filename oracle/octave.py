@@ -34,13 +34,13 @@ the rest supports:
   one per head when compact), V has one scale per head;
 * sign bits: bit ``i % 32`` of word ``i // 32`` set means element i is
   negated;
-* slot layout (bytes, head size D, b_K = 3, b_V = 4 or 3): the K codes as
-  bit planes, then the V codes as bit planes, then the K scales and the V
-  scale as fp16, zero-padded to a multiple of 16.  Element
-  ``d = 32 kc + 8 g + e`` (kc < D/32, g < 4, e < 8) of a code vector sits
-  at bit e of byte ``(g * b + k) * D/32 + kc`` for plane k (bit k of the
-  code): each of the four 16-lane groups of an MFMA tile finds the bits of
-  its elements in its own contiguous bytes.
+* slot layout (bytes, head size D, b_K = 3, b_V = 4 or 3): the K codes,
+  then the V codes, then the K scales and the V scale as fp16, zero-padded
+  to a multiple of 16.  Codes go in groups of 8 elements packed into b
+  bytes, little-endian, code e of a group at bits ``b e .. b e + b - 1``;
+  element ``d = 32 kc + 8 g + e`` (kc < D/32, g < 4, e < 8) is code e of
+  group ``g * D/32 + kc``: each of the four 16-lane groups of an MFMA tile
+  finds its elements in its own contiguous bytes.
 
 Parity status: every function here is pinned in tests/test_oracle_octave.py
 (closed forms, brute force, exactly representable caches, hand-checked
@@ -139,31 +139,25 @@ def slot_bytes(fmt: str, D: int = HEAD_SIZE) -> int:
 
 
 def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
-    """Bit planes of code vectors (last axis D): byte (g * bits + k) * D/32
-    + kc holds bit k of element 32 kc + 8 g + e at bit e."""
+    """Codes (last axis D) packed in groups of 8 into ``bits`` bytes each:
+    element 32 kc + 8 g + e is code e (bits bits*e ..) of group g * D/32 + kc."""
     codes = np.asarray(codes, dtype=np.int64)
     D = codes.shape[-1]
     nkc = D // 32
     c = codes.reshape(codes.shape[:-1] + (nkc, 4, 8))  # [..., kc, g, e]
-    weights = 1 << np.arange(8)
-    planes = []
-    for k in range(bits):
-        byte = (((c >> k) & 1) * weights).sum(axis=-1)  # [..., kc, g]
-        planes.append(np.swapaxes(byte, -1, -2))  # [..., g, kc]
-    out = np.stack(planes, axis=-2)  # [..., g, k, kc]
+    c = np.swapaxes(c, -2, -3)  # [..., g, kc, e]: groups in g-major order
+    word = (c << (bits * np.arange(8))).sum(axis=-1)  # [..., g, kc]: 8 codes in 8 * bits bits
+    out = (word[..., None] >> (8 * np.arange(bits))) & 0xFF  # little-endian bytes
     return out.reshape(codes.shape[:-1] + (bits * D // 8,)).astype(np.uint8)
 
 
 def unpack_codes(raw: np.ndarray, bits: int, D: int) -> np.ndarray:
     raw = np.asarray(raw, dtype=np.uint8).astype(np.int64)
     nkc = D // 32
-    r = raw.reshape(raw.shape[:-1] + (4, bits, nkc))  # [..., g, k, kc]
-    e = np.arange(8)
-    codes = np.zeros(raw.shape[:-1] + (nkc, 4, 8), dtype=np.int64)
-    for k in range(bits):
-        byte = np.swapaxes(r[..., :, k, :], -1, -2)  # [..., kc, g]
-        codes |= ((byte[..., None] >> e) & 1) << k
-    return codes.reshape(raw.shape[:-1] + (D,))
+    r = raw.reshape(raw.shape[:-1] + (4, nkc, bits))  # [..., g, kc, byte]
+    word = (r << (8 * np.arange(bits))).sum(axis=-1)  # [..., g, kc]
+    c = (word[..., None] >> (bits * np.arange(8))) & ((1 << bits) - 1)  # [..., g, kc, e]
+    return np.swapaxes(c, -2, -3).reshape(raw.shape[:-1] + (D,))
 
 
 def encode_rows(k: np.ndarray, v: np.ndarray, k_signs: np.ndarray, v_signs: np.ndarray, fmt: str) -> np.ndarray:

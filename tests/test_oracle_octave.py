@@ -24,7 +24,9 @@ MUTATIONS = [
     ("round_not_floor", "np.floor(x / safe)", "np.round(x / safe)"),
     ("no_half_step", "- half + 0.5)", "- half)"),
     ("step_not_fp16", "delta = fp16_round(np.abs(x).max(axis=-1) / half)", "delta = np.abs(x).max(axis=-1) / half"),
-    ("planes_in_wrong_order", "out = np.stack(planes, axis=-2)  # [..., g, k, kc]", "out = np.stack(planes, axis=-3)"),
+    ("groups_kc_major", "c = np.swapaxes(c, -2, -3)  # [..., g, kc, e]: groups in g-major order", "c = c"),
+    ("codes_big_endian", "out = (word[..., None] >> (8 * np.arange(bits))) & 0xFF  # little-endian bytes",
+     "out = (word[..., None] >> (8 * np.arange(bits)[::-1])) & 0xFF"),
     ("k_whole_head", "k_group = D if compact else ROPE_DIM", "k_group = D"),
     ("v_with_k_signs", "vr = rotate(v, v_signs, D)", "vr = rotate(v, k_signs, D)"),
     ("query_not_rotated", "q_rot = rotate(q, k_signs, k_group)", "q_rot = q"),
