@@ -417,6 +417,87 @@ def cache_write_main(args) -> int:
     return 0
 
 
+def octave_main(args) -> int:
+    """Decode over a quantized (octave) packed cache on the batch workload's
+    shapes: 64 sequences of 512..16384 keys plus one padded, 16/2 heads of
+    256, page 1056, M = 4, q/out bf16.  The cache is written from seeded
+    N(0,1) rows by the library's store kernel before timing.  Effective
+    bytes: the packed slots of the attended keys, plus Q and O."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+
+    import paged_kv_decode_block_amd as pad
+
+    fmt = pad.OCTAVE_FORMATS[args.octave]
+    cfg, ctx, M = 5, 16384, 4
+    spec = wl.CONFIGS[cfg]
+    case = wl.config_case(cfg, ctx, M, device="cuda")
+    nb, Hkv, P = case.kv_cache.shape[0], spec.num_kv_heads, spec.page_size
+    sb = pad.pad_octave_slot_bytes(fmt)
+    cache = torch.zeros((nb, Hkv, P, sb), dtype=torch.uint8, device="cuda")
+    ks, vs = wl.sign_words(20261203).to("cuda"), wl.sign_words(20261204).to("cuda")
+    # write the pool token by token (a block's slots are block * P + offset)
+    rows = case.kv_cache.permute(0, 2, 1, 3, 4).reshape(nb * P, Hkv, 2, spec.head_size)
+    chunk = 1 << 16
+    for t0 in range(0, nb * P, chunk):
+        part = rows[t0:t0 + chunk]
+        slots = torch.arange(t0, t0 + part.shape[0], dtype=torch.int64, device="cuda")
+        pad.pad_octave_cache_write(part[:, :, 0].contiguous(), part[:, :, 1].contiguous(), cache, slots, ks, vs, fmt)
+    torch.cuda.synchronize()
+    del rows
+    lens = case.seq_lens.tolist()
+    eb = case.q.element_size()
+    nbytes = sum(L * Hkv * sb + 2 * M * spec.num_q_heads * spec.head_size * eb for L in lens if L > 0)
+    out = torch.empty_like(case.q)
+    bt = case.block_tables[0]
+
+    def call(i):
+        pad.pad_decode_attn_octave(case.q, cache, bt, case.seq_lens, ks, vs, case.scale, out, fmt)
+
+    ms = _event_time(call, args.warmup, args.steps)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu:
+        from oracle import octave as oc
+
+        name = args.octave
+        s_k = oc.signs_from_bits(ks.cpu().numpy().view(np.uint32), spec.head_size)
+        s_v = oc.signs_from_bits(vs.cpu().numpy().view(np.uint32), spec.head_size)
+        bt_np = bt.cpu().numpy()
+        t0, done, moved = time.perf_counter(), 0, 0
+        while done < len(lens) and time.perf_counter() - t0 < 12.0:
+            L = lens[done]
+            if L > 0:
+                used = np.unique(bt_np[done, : -(-L // P)])
+                packed = cache[torch.as_tensor(used, device="cuda")].cpu().numpy()
+                table = np.arange(len(used))[None, :]
+                q64 = case.q[done:done + 1].to(torch.float64).cpu().numpy()
+                oc.decode_attention_quant(q64, packed, table, [L], case.scale, wl.HND, name, s_k, s_v)
+                moved += L * Hkv * sb + 2 * M * spec.num_q_heads * spec.head_size * eb
+            done += 1
+        el = time.perf_counter() - t0
+        cpu = {"value": round(moved / el / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(), "host_cpus": os.cpu_count(),
+               "kind": "oracle", "sample": f"{done} of {len(lens)} sequences, one oracle call each, {el:.1f} s"}
+    line = {
+        "metric": "packed-cache decode effective HBM GB/s (packed K+V slots read + Q + O) and fraction of 8 TB/s",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 q/out, fp16 products over " + args.octave + " codes", "data": "synthetic",
+        "config": {"workload": f"{args.octave} cache, batch {case.num_seqs} ({case.num_seqs - 1} sequences of "
+                               f"512..{ctx} keys + 1 padded), D={spec.head_size}, {spec.num_q_heads}/{Hkv} heads, "
+                               f"page {P}, HND, M={M}, {sb}-byte slots",
+                   "bytes_per_step": nbytes,
+                   "bf16_cache_bytes_per_step": int(sum(L * Hkv * 2 * spec.head_size * 2 for L in lens if L > 0))},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def prefill_main(args) -> int:
     """A prefill chunk through the same entry point: 256 new tokens over a
     4096-key context, the default workload's shapes (1024 GQA-packed rows
@@ -492,6 +573,8 @@ def main() -> int:
                     help="time the KV-cache write with rotation (the step before decode) instead")
     ap.add_argument("--varlen", action="store_true",
                     help="time a mixed decode/verify batch through the per-sequence-count entry point instead")
+    ap.add_argument("--octave", choices=["octave_k3v4", "octave_k3v3", "octave_k3v3_compact"], default=None,
+                    help="time decode over a quantized packed cache of this format instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the decode-attention path has no multi-GPU mode "
@@ -500,6 +583,8 @@ def main() -> int:
 
     if args.varlen:
         return varlen_main(args)
+    if args.octave:
+        return octave_main(args)
     if args.cache_write:
         return cache_write_main(args)
     if args.prefill:

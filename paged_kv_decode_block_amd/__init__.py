@@ -17,6 +17,9 @@ import torch
 __all__ = [
     "PAD_OK", "PAD_EINVAL", "PAD_EUNSUPPORTED", "PAD_EWORKSPACE", "PAD_EHIP", "PAD_ESCRATCH",
     "PAD_NOALLOC_SCRATCH_BYTES", "pad_decode_attn_noalloc",
+    "PAD_KV_OCTAVE_K3V4", "PAD_KV_OCTAVE_K3V3", "PAD_KV_OCTAVE_K3V3_COMPACT", "OCTAVE_FORMATS",
+    "pad_octave_cache_shape", "pad_octave_slot_bytes", "pad_octave_cache_write",
+    "pad_decode_attn_octave_workspace_size", "pad_decode_attn_octave",
     "PAD_F16", "PAD_BF16", "PAD_NHD", "PAD_HND",
     "PAD_PATH_AUTO", "PAD_PATH_MFMA", "PAD_PATH_DOT",
     "PAD_SCHED_AUTO", "PAD_SCHED_GRID", "PAD_SCHED_PERSISTENT",
@@ -35,6 +38,9 @@ PAD_F16, PAD_BF16 = 0, 1
 PAD_NHD, PAD_HND = 0, 1
 PAD_PATH_AUTO, PAD_PATH_MFMA, PAD_PATH_DOT = 0, 1, 2
 PAD_SCHED_AUTO, PAD_SCHED_GRID, PAD_SCHED_PERSISTENT = 0, 1, 2
+PAD_KV_OCTAVE_K3V4, PAD_KV_OCTAVE_K3V3, PAD_KV_OCTAVE_K3V3_COMPACT = 1, 2, 3
+OCTAVE_FORMATS = {"octave_k3v4": PAD_KV_OCTAVE_K3V4, "octave_k3v3": PAD_KV_OCTAVE_K3V3,
+                  "octave_k3v3_compact": PAD_KV_OCTAVE_K3V3_COMPACT}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpad_attn.so")
 
@@ -90,6 +96,19 @@ class pad_cache_shape(ctypes.Structure):
     ]
 
 
+class pad_octave_cache_shape(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_size", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
+        ("format", ctypes.c_int32),
+    ]
+
+
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     """Open a build of the library and declare its C signatures."""
     if not os.path.exists(path):
@@ -120,6 +139,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.pad_decode_attn_noalloc.argtypes = [
         P(pad_shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    L.pad_octave_slot_bytes.restype = ctypes.c_int
+    L.pad_octave_slot_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, P(ctypes.c_int32)]
+    L.pad_octave_cache_write.restype = ctypes.c_int
+    L.pad_octave_cache_write.argtypes = [P(pad_octave_cache_shape)] + [ctypes.c_void_p] * 7
+    L.pad_decode_attn_octave_workspace_size.restype = ctypes.c_int
+    L.pad_decode_attn_octave_workspace_size.argtypes = [P(pad_shape), ctypes.c_int32, P(ctypes.c_size_t)]
+    L.pad_decode_attn_octave.restype = ctypes.c_int
+    L.pad_decode_attn_octave.argtypes = [
+        P(pad_shape), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+        ctypes.c_void_p,
     ]
     L.pad_calib_gather_read.restype = ctypes.c_int
     L.pad_calib_gather_read.argtypes = [
@@ -502,3 +533,107 @@ def pad_calib_stream_read(src: torch.Tensor, sink: torch.Tensor, *, blocks: int 
         ctypes.c_void_p(src.data_ptr()), src.numel() * src.element_size(), int(blocks), int(threads),
         int(loads_in_flight), ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(_stream_ptr(stream))),
         "pad_calib_stream_read")
+
+
+def pad_octave_slot_bytes(fmt: int, head_size: int = 256) -> int:
+    """Bytes of one packed slot (include/pad_octave.h)."""
+    n = ctypes.c_int32(0)
+    _check(lib.pad_octave_slot_bytes(int(fmt), int(head_size), ctypes.byref(n)), "pad_octave_slot_bytes")
+    return int(n.value)
+
+
+def _octave_cache_dims(cache: torch.Tensor, layout: int):
+    if cache.dim() != 4 or cache.dtype != torch.uint8:
+        raise ValueError("a packed cache is uint8 [blocks, kv_heads, page, slot] (HND) or [blocks, page, kv_heads, slot]")
+    if layout == PAD_HND:
+        nb, Hkv, P, sb = cache.shape
+    elif layout == PAD_NHD:
+        nb, P, Hkv, sb = cache.shape
+    else:
+        raise ValueError(f"unknown layout {layout}")
+    return nb, Hkv, P, sb
+
+
+def pad_octave_cache_write(key: torch.Tensor, value: torch.Tensor, cache: torch.Tensor, slot_mapping: torch.Tensor,
+                           k_signs: torch.Tensor, v_signs: torch.Tensor, fmt: int, *, layout: int = PAD_HND,
+                           stream=None) -> None:
+    """Rotate, quantize and pack new tokens' K and V rows ``[T, Hkv, 256]``
+    into their slots of a packed cache (include/pad_octave.h)."""
+    _require_device(key=key, value=value, cache=cache, slot_mapping=slot_mapping, k_signs=k_signs, v_signs=v_signs)
+    nb, Hkv, P, sb = _octave_cache_dims(cache, layout)
+    if key.dim() != 3 or value.shape != key.shape or key.dtype not in _DTYPE_CODE or value.dtype != key.dtype:
+        raise ValueError("key and value must be [T, Hkv, 256] of one dtype (float16 or bfloat16)")
+    if key.shape[1] != Hkv or sb != pad_octave_slot_bytes(fmt, key.shape[2]):
+        raise ValueError("the cache's kv heads and slot size must match key and the format")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (key.shape[0],):
+        raise ValueError("slot_mapping must be int64 [T]")
+    for n, t in (("k_signs", k_signs), ("v_signs", v_signs)):
+        if t.dtype not in (torch.int32, torch.uint32) or t.numel() != key.shape[2] // 32:
+            raise ValueError(f"{n} must hold head_size / 32 32-bit words")
+    shape = pad_octave_cache_shape(num_tokens=key.shape[0], num_kv_heads=Hkv, head_size=key.shape[2], page_size=P,
+                                   num_blocks=nb, dtype=_DTYPE_CODE[key.dtype], layout=layout, format=int(fmt))
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    _check(lib.pad_octave_cache_write(ctypes.byref(shape), ptr(key), ptr(value), ptr(slot_mapping), ptr(k_signs),
+                                      ptr(v_signs), ptr(cache), ctypes.c_void_p(_stream_ptr(stream))),
+           "pad_octave_cache_write")
+
+
+def _octave_shape(q, cache, block_table, layout, fmt, **kw) -> pad_shape:
+    nb, Hkv, P, sb = _octave_cache_dims(cache, layout)
+    if q.dim() != 4 or q.dtype not in _DTYPE_CODE:
+        raise ValueError("q must be [S, M, Hq, D] of float16 or bfloat16")
+    S, M, Hq, D = q.shape
+    if sb != pad_octave_slot_bytes(fmt, D):
+        raise ValueError("the cache's slot size does not match the format")
+    if block_table.shape[0] != S:
+        raise ValueError("block_table must have one row per sequence")
+    return pad_shape(num_seqs=S, query_len=M, num_q_heads=Hq, num_kv_heads=Hkv, head_size=D, page_size=P,
+                     max_blocks_per_seq=block_table.shape[1], max_seq_len=kw.get("max_seq_len", 0),
+                     dtype=_DTYPE_CODE[q.dtype], layout=layout, num_segments=kw.get("num_segments", 0),
+                     path=kw.get("path", PAD_PATH_AUTO), schedule=kw.get("schedule", PAD_SCHED_AUTO))
+
+
+def pad_decode_attn_octave_workspace_size(shape: pad_shape, fmt: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.pad_decode_attn_octave_workspace_size(ctypes.byref(shape), int(fmt), ctypes.byref(n)),
+           "pad_decode_attn_octave_workspace_size")
+    return int(n.value)
+
+
+def pad_decode_attn_octave(q: torch.Tensor, cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                           k_signs: torch.Tensor, v_signs: torch.Tensor, scale: float, out: torch.Tensor, fmt: int, *,
+                           layout: int = PAD_HND, workspace: torch.Tensor | None = None, max_seq_len: int = 0,
+                           num_segments: int = 0, path: int = PAD_PATH_AUTO, schedule: int = PAD_SCHED_AUTO,
+                           stream=None) -> torch.Tensor:
+    """Decode attention over a packed quantized cache into ``out``
+    (include/pad_octave.h): q and out in the model's space, no window."""
+    _require_device(q=q, cache=cache, block_table=block_table, seq_lens=seq_lens, k_signs=k_signs, v_signs=v_signs,
+                    out=out)
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or seq_lens.shape != (q.shape[0],):
+        raise ValueError("block_table and seq_lens must be int32, one row / entry per sequence")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q's shape and dtype")
+    shape = _octave_shape(q, cache, block_table, layout, fmt, max_seq_len=max_seq_len, num_segments=num_segments,
+                          path=path, schedule=schedule)
+    if workspace is None:
+        key = (q.device.index, _stream_ptr(stream), "octave")
+        ws_obj = _default_ws.get(key)
+        if ws_obj is None:
+            ws_obj = _default_ws[key] = Workspace(q.device)
+        need = pad_decode_attn_octave_workspace_size(shape, fmt)
+        if need and (ws_obj.buf is None or ws_obj.buf.numel() < need):
+            buf = torch.empty(need, dtype=torch.uint8, device=q.device)
+            _record_on(buf, stream)
+            pad_decode_attn_workspace_init(buf, stream)
+            ws_obj.buf = buf
+        ws = ws_obj.buf
+    else:
+        ws = workspace
+    ws_ptr = ws.data_ptr() if ws is not None else 0
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    _check(lib.pad_decode_attn_octave(
+        ctypes.byref(shape), int(fmt), ptr(q), ptr(cache), ptr(block_table), ptr(seq_lens), ptr(k_signs), ptr(v_signs),
+        ctypes.c_float(scale), ptr(out), ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes),
+        ctypes.c_void_p(_stream_ptr(stream))), "pad_decode_attn_octave")
+    return out

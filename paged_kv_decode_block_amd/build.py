@@ -31,8 +31,11 @@ MFMA_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
 # (source, object name, extra flags): the decode kernels build once per
 # head size, in parallel.
 SOURCES = [("decode_mfma.hip", f"decode_mfma_d{d}", [f"-DPAD_HEAD_SIZE={d}", *MFMA_FLAGS]) for d in (64, 128, 256, 512)] + [
+    # the packed (quantized) cache's kernels: a further build at head size 256
+    ("decode_mfma.hip", "decode_octave_d256", ["-DPAD_HEAD_SIZE=256", "-DPAD_OCTAVE=1", *MFMA_FLAGS]),
+] + [
     (src, src.rsplit(".", 1)[0], [])
-    for src in ("launch.hip", "cache_write.hip", "calib.hip", "noalloc.hip", "plan.cpp", "api.cpp")
+    for src in ("launch.hip", "cache_write.hip", "octave_store.hip", "calib.hip", "noalloc.hip", "plan.cpp", "api.cpp")
 ]
 
 # Packed fp32 VALU ops are turned off for every HIP source (the host pass

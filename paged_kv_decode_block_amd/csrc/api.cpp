@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "../../include/pad_attn.h"
+#include "../../include/pad_octave.h"
 #include "entry.h"
 #include "kernels.h"
 #include "plan.h"
@@ -126,13 +127,33 @@ pad_status check_buffers(const pad_shape* shape, const void* q, const void* kv_c
 }
 
 // One decode launch; q_start is null for the uniform [S, M, Hq, D] layout.
+int octave_slot_bytes(int format, int head_size) {
+  if (head_size != 256) return 0;
+  switch (format) {
+    case PAD_KV_OCTAVE_K3V4: return 240;                // 96 + 128 + 10 -> 240
+    case PAD_KV_OCTAVE_K3V3:                            // 96 + 96 + 10 -> 208
+    case PAD_KV_OCTAVE_K3V3_COMPACT: return 208;        // 96 + 96 + 4 -> 208
+  }
+  return 0;
+}
+
 pad_status decode(const pad_shape* shape, const void* q, const int32_t* q_start, const void* kv_cache,
                   const int32_t* block_table, const int32_t* seq_lens, float scale, int32_t window, void* out,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+                  void* workspace, size_t workspace_bytes, void* stream, int format, const uint32_t* k_signs,
+                  const uint32_t* v_signs) {
   if (!shape) return PAD_EINVAL;
+  int key_bytes = 0;
+  if (format != 0) {
+    if (format < PAD_KV_OCTAVE_K3V4 || format > PAD_KV_OCTAVE_K3V3_COMPACT) return PAD_EINVAL;
+    if (shape->head_size != PAD_OCTAVE_HEAD_SIZE || shape->path == PAD_PATH_DOT) return PAD_EUNSUPPORTED;
+    key_bytes = octave_slot_bytes(format, shape->head_size);
+  }
   pad::Plan p;
-  const pad_status st = pad::make_plan(*shape, window, device_cus(), &p);
+  const pad_status st = pad::make_plan(*shape, window, device_cus(), &p, key_bytes);
   if (st != PAD_OK) return st;
+  if (format != 0 && shape->num_seqs > 0 &&
+      (!k_signs || !v_signs || !aligned(k_signs, 4) || !aligned(v_signs, 4)))
+    return PAD_EINVAL;
   const pad_status vb = check_buffers(shape, q, kv_cache, block_table, seq_lens, scale, out);
   if (vb != PAD_OK) return vb;
   if (shape->num_seqs == 0) return PAD_OK;
@@ -151,15 +172,20 @@ pad_status decode(const pad_shape* shape, const void* q, const int32_t* q_start,
   pr.ws_cnt = p.ws_bytes ? reinterpret_cast<int32_t*>(ws + p.ws_counters) : nullptr;
   pr.ws_ml = p.ws_bytes ? reinterpret_cast<float*>(ws + p.ws_ml) : nullptr;
   pr.ws_acc = p.ws_bytes ? reinterpret_cast<float*>(ws + p.ws_acc) : nullptr;
+  // Strides in 16-bit elements: a slot is 2 D elements, or the packed
+  // slot's bytes / 2.
+  const int64_t slot = format ? key_bytes / 2 : 2 * D;
   if (shape->layout == PAD_HND) {
-    pr.token_stride = 2 * D;
-    pr.head_stride = P * 2 * D;
-    pr.block_stride = H * P * 2 * D;
+    pr.token_stride = slot;
+    pr.head_stride = P * slot;
+    pr.block_stride = H * P * slot;
   } else {
-    pr.head_stride = 2 * D;
-    pr.token_stride = H * 2 * D;
-    pr.block_stride = P * H * 2 * D;
+    pr.head_stride = slot;
+    pr.token_stride = H * slot;
+    pr.block_stride = P * H * slot;
   }
+  pr.k_signs = k_signs;
+  pr.v_signs = v_signs;
   pr.num_seqs = shape->num_seqs;
   pr.query_len = shape->query_len;
   pr.num_q_heads = shape->num_q_heads;
@@ -178,7 +204,9 @@ pad_status decode(const pad_shape* shape, const void* q, const int32_t* q_start,
   pr.persistent = p.persistent;
   pr.merge_wait_ticks = g_merge_wait_ticks.load();
   pr.scale_log2 = float(double(scale) * 1.4426950408889634);  // log2(e)
-  return pad::launch_decode(p, pr, shape->dtype, shape->head_size, stream) == 0 ? PAD_OK : PAD_EHIP;
+  const int rc = format ? pad::launch_decode_octave(p, pr, shape->dtype, format, stream)
+                        : pad::launch_decode(p, pr, shape->dtype, shape->head_size, stream);
+  return rc == 0 ? PAD_OK : PAD_EHIP;
 }
 
 }  // namespace pad
@@ -202,6 +230,40 @@ pad_status pad_decode_attn_varlen(const pad_shape* shape, const void* q, const i
   if (shape && shape->num_seqs > 0 && (!q_start || !aligned(q_start, 4))) return PAD_EINVAL;
   return decode(shape, q, q_start, kv_cache, block_table, seq_lens, scale, window, out, workspace,
                 workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+pad_status pad_octave_slot_bytes(int32_t format, int32_t head_size, int32_t* bytes) {
+  if (!bytes) return PAD_EINVAL;
+  if (format < PAD_KV_OCTAVE_K3V4 || format > PAD_KV_OCTAVE_K3V3_COMPACT) return PAD_EINVAL;
+  const int b = pad::octave_slot_bytes(format, head_size);
+  if (b == 0) return PAD_EUNSUPPORTED;
+  *bytes = b;
+  return PAD_OK;
+}
+
+pad_status pad_decode_attn_octave_workspace_size(const pad_shape* shape, int32_t format, size_t* bytes) {
+  if (!shape || !bytes) return PAD_EINVAL;
+  if (format < PAD_KV_OCTAVE_K3V4 || format > PAD_KV_OCTAVE_K3V3_COMPACT) return PAD_EINVAL;
+  if (shape->head_size != PAD_OCTAVE_HEAD_SIZE || shape->path == PAD_PATH_DOT) return PAD_EUNSUPPORTED;
+  pad::Plan p;
+  const pad_status st = pad::make_plan(*shape, 0, device_cus(), &p, pad::octave_slot_bytes(format, shape->head_size));
+  if (st != PAD_OK) return st;
+  *bytes = p.ws_bytes;
+  return PAD_OK;
+}
+
+pad_status pad_decode_attn_octave(const pad_shape* shape, int32_t format, const void* q, const void* cache,
+                                  const int32_t* block_table, const int32_t* seq_lens, const uint32_t* k_signs,
+                                  const uint32_t* v_signs, float scale, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!shape) return PAD_EINVAL;
+  if (format < PAD_KV_OCTAVE_K3V4 || format > PAD_KV_OCTAVE_K3V3_COMPACT) return PAD_EINVAL;
+  return decode(shape, q, nullptr, cache, block_table, seq_lens, scale, 0, out, workspace, workspace_bytes, stream,
+                format, k_signs, v_signs);
 }
 
 }  // extern "C"

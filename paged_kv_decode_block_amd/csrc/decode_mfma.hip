@@ -35,9 +35,11 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "decode_common.h"
 #include "kernels.h"
+#include "octave_dev.h"
 
 #ifndef PAD_HEAD_SIZE
 #error "compile once per head size with -DPAD_HEAD_SIZE=64|128|256|512"
@@ -104,8 +106,9 @@ struct Shape {
 // rows, already rescaled to the workgroup maximum, in slot w of sm_acc; and
 // the workgroup's merged max/sum in sm_ms/sm_ls -- sum the slots in wave
 // order (deterministic) and either write the output (single segment) or
-// publish this segment's partial and take part in the merge.
-template <typename T, int D, int RT, int NW>
+// publish this segment's partial and take part in the merge.  NSUM slots
+// are summed (1 when the rows were already summed and rotated into slot 0).
+template <typename T, int D, int RT, int NW, int NSUM = NW>
 __device__ __forceinline__ void finish(const Params& p, unsigned char* lds, int s, int kvh, int row0, int wg_rows,
                                        const Frag& f, int lds_bytes) {
   using MF = Mfma<T>;
@@ -120,7 +123,7 @@ __device__ __forceinline__ void finish(const Params& p, unsigned char* lds, int 
     const float* col = sm_acc + r * CB::kAccStride + 4 * d4;
     f32x4 a = *reinterpret_cast<const f32x4*>(col);
 #pragma unroll
-    for (int w = 1; w < NW; ++w) a += *reinterpret_cast<const f32x4*>(col + w * CB::kRows * CB::kAccStride);
+    for (int w = 1; w < NSUM; ++w) a += *reinterpret_cast<const f32x4*>(col + w * CB::kRows * CB::kAccStride);
     return a;
   };
 
@@ -151,16 +154,36 @@ __device__ __forceinline__ void finish(const Params& p, unsigned char* lds, int 
   arrive_and_merge<T, D, NT>(p, reinterpret_cast<int*>(lds + lds_bytes - 16), s, kvh, row0, wg_rows, f);
 }
 
+// The tile a lane holds: its key's K and V rows (eight elements of every
+// 32-wide chunk, per its lane group), or its share of a packed slot.
+template <int KC>
+struct PlainTile {
+  i32x4 k[KC];
+  i32x4 v[KC];
+};
+
 // One work item of (sequence s, kv head kvh, row group rg).  On the grid
 // schedule (PERSIST = false) it is segment `seg` of the unit's key range,
 // found once the length is known; on the balanced persistent grid the
 // caller passes the item (its tiles, partial slot and merge layout) in `fr`.
-template <typename T, int D, int RT, bool LEAN, bool PERSIST>
+// FMT: 0 for an fp16/bf16 cache, else the packed format (pad_kv_format) of
+// a quantized cache (head size 256): the products then run on codes in the
+// rotated space (octave_dev.h).
+template <typename T, int D, int RT, bool LEAN, bool PERSIST, int FMT = 0>
 __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds, int s, int kvh, int rg, int seg,
                                             Frag fr) {
-  using MF = Mfma<T>;
+  // The products' element type: the input's, or fp16 for a packed cache
+  // (codes as 1024 + c, the rotated queries and the step-scaled weights in
+  // fp16, whatever the type of q and out -- the octave page's kernels run
+  // in fp16).
+  using MF = std::conditional_t<FMT == 0, Mfma<T>, Mfma<_Float16>>;
   using SH = Shape<D, RT, LEAN>;
   constexpr int NW = SH::NW, KC = SH::KC, DT = SH::DT;
+  static_assert(FMT == 0 || D == kOctD, "packed formats are built for head size 256");
+  // Tiles in flight beyond the one computed: a packed tile carries a
+  // quarter of the bytes of a bf16 one in a few registers per lane, so the
+  // packed path keeps a deeper ring.
+  constexpr int PF = FMT ? kOctRing : SH::PF;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -231,6 +254,88 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
     }
   }
 
+  // Packed cache: the query rows go to the rotated space of the keys,
+  // q' = H (s * q) / sqrt(n) over each K block (64 dims, or 256 when
+  // compact), in fp32, rounded back to T for the MFMA; qsum[rt][b] is the
+  // sum of the rounded q' over K block b of the lane's row (the offset of
+  // the code operand is taken off with it).  Element 32 kc + 8 g + e has
+  // index bits e (this lane), g (lane groups: lane bits 4 and 5) and kc.
+  constexpr int KG = FMT ? Oct<FMT>::KG : 1;
+  float qsum[RT][KG];
+  if constexpr (FMT != 0) {
+    using OT = OctType<T>;     // the input queries
+    using OF = OctType<_Float16>;  // the rotated ones
+    uint32_t ksw[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) ksw[kc] = p.k_signs[kc];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float f[KC][8];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const uint32_t w = uint32_t(qop[rt][kc][q4]);
+          f[kc][2 * q4] = OT::lo(w);
+          f[kc][2 * q4 + 1] = OT::hi(w);
+        }
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if ((ksw[kc] >> (8 * g + e)) & 1u) f[kc][e] = -f[kc][e];
+#pragma unroll
+      for (int st = 1; st < 8; st <<= 1)  // index bits 0-2: e
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (!(e & st)) {
+              const float a = f[kc][e], b = f[kc][e | st];
+              f[kc][e] = a + b;
+              f[kc][e | st] = a - b;
+            }
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)  // index bits 3-4: g
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          f[kc][e] = wht_lane_stage(f[kc][e], 16, (g & 1) != 0);
+          f[kc][e] = wht_lane_stage(f[kc][e], 32, (g & 2) != 0);
+        }
+      constexpr int kSpan = KG == 4 ? 2 : KC;  // chunks per K block
+#pragma unroll
+      for (int st = 1; st < kSpan; st <<= 1)  // index bits from 5 on: kc within the block
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          if (!(kc & st))
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float a = f[kc][e], b = f[kc | st][e];
+              f[kc][e] = a + b;
+              f[kc | st][e] = a - b;
+            }
+      constexpr float kNorm = KG == 4 ? 0.125f : 0.0625f;  // 1 / sqrt(block)
+      float qs[KG];
+#pragma unroll
+      for (int b = 0; b < KG; ++b) qs[b] = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const uint32_t lo = MF::bits(f[kc][2 * q4] * kNorm), hi = MF::bits(f[kc][2 * q4 + 1] * kNorm);
+          const uint32_t w = lo | (hi << 16);
+          qop[rt][kc][q4] = int(w);
+          qs[kc / kSpan] += OF::lo(w) + OF::hi(w);
+        }
+#pragma unroll
+      for (int b = 0; b < KG; ++b) {
+        qs[b] += __shfl_xor(qs[b], 16);
+        qs[b] += __shfl_xor(qs[b], 32);
+        qsum[rt][b] = qs[b];
+      }
+    }
+  }
+
   // Lengths past the block table's capacity are clamped to it.
   const int L = min(L_dev, p.max_blocks * p.page_size);
   bool early;
@@ -290,28 +395,68 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
       static_cast<const unsigned char*>(p.kv) + int64_t(kvh) * p.head_stride * int64_t(sizeof(T));
   // Byte offset of this lane's 16-byte chunk inside a tile: key row c,
   // head-dim elements 8g..8g+7 of chunk 0 (32-bit, per lane); the tile base
-  // itself is wave-uniform, so the loads take a scalar base address.
-  const uint32_t lane_off = uint32_t(c * p.token_stride + 8 * g) * uint32_t(sizeof(T));
+  // itself is wave-uniform, so the loads take a scalar base address.  A
+  // packed slot is read as this lane group's K and V codes and the key's
+  // step area.
+  const uint32_t lane_off = FMT ? uint32_t(c * p.token_stride) * uint32_t(sizeof(T))
+                                : uint32_t(c * p.token_stride + 8 * g) * uint32_t(sizeof(T));
   uint16_t* vs = reinterpret_cast<uint16_t*>(lds) + wave * 16 * SH::kVStride;
   // Transposed-read address of this lane: row 4g + c/4, columns 4(c%4).. of
   // each 16-column tile (ds_read_b64_tr_b16 returns column c of the 4x16
   // block its 16-lane group addresses, i.e. 4 keys of one head-dim column).
   const uint16_t* vtr = vs + (4 * g + (c >> 2)) * SH::kVStride + 4 * (c & 3);
 
-  struct Tile {
-    i32x4 k[KC];
-    i32x4 v[KC];
-  };
+  using Tile = std::conditional_t<FMT == 0, PlainTile<KC>, OctTile>;
+  // Running sum, per lane, of the rounded step-scaled softmax weights that
+  // multiply the V codes (packed cache): the V offset is taken off the
+  // accumulator with it after the last tile.
+  float psum[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) psum[rt] = 0.f;
 
   auto issue_tile = [&](Tile& tl, int t, int blk) {
     const int key0 = t * 16;
     const unsigned char* base =
         KVh + (int64_t(blk) * p.block_stride + int64_t(key0 % p.page_size) * p.token_stride) * int64_t(sizeof(T));
     const unsigned char* row = base + lane_off;
+    if constexpr (FMT == 0) {
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) tl.k[kc] = *reinterpret_cast<const i32x4*>(row + 64 * kc);
+      for (int kc = 0; kc < KC; ++kc) tl.k[kc] = *reinterpret_cast<const i32x4*>(row + 64 * kc);
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) tl.v[kc] = *reinterpret_cast<const i32x4*>(row + 2 * D + 64 * kc);
+      for (int kc = 0; kc < KC; ++kc) tl.v[kc] = *reinterpret_cast<const i32x4*>(row + 2 * D + 64 * kc);
+    } else {
+      using SL = OctSlot<FMT>;
+      const unsigned char* kp = row + SL::kKBytesPerGroup * g;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const uint2 w = *reinterpret_cast<const uint2*>(kp + 8 * i);
+        tl.k[2 * i] = w.x;
+        tl.k[2 * i + 1] = w.y;
+      }
+      const unsigned char* vp = row + SL::kVOff + SL::kVBytesPerGroup * g;
+      if constexpr (Oct<FMT>::VB == 4) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint4 w = *reinterpret_cast<const uint4*>(vp + 16 * i);
+          tl.v[4 * i] = w.x;
+          tl.v[4 * i + 1] = w.y;
+          tl.v[4 * i + 2] = w.z;
+          tl.v[4 * i + 3] = w.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          const uint2 w = *reinterpret_cast<const uint2*>(vp + 8 * i);
+          tl.v[2 * i] = w.x;
+          tl.v[2 * i + 1] = w.y;
+        }
+      }
+      const uint4 sw = *reinterpret_cast<const uint4*>(row + SL::kSOff);
+      tl.sc[0] = sw.x;
+      tl.sc[1] = sw.y;
+      tl.sc[2] = sw.z;
+      tl.sc[3] = sw.w;
+    }
   };
 
   // Scores of tile t: stage its V rows in LDS, S^T = K Q^T, mask, online
@@ -320,28 +465,88 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
   auto score_tile = [&](Tile& tl, int t, uint64_t (&pb)[RT]) {
     const int key0 = t * 16;
     const bool edge = !(key0 >= lo_last && key0 + 15 <= qpos_first);
-    if (edge) {
-      // Keys outside [k_lo, L) may hold anything (even NaN); they must not
-      // reach the PV product, where 0 * NaN would poison the sum.
-      const int key = key0 + c;
-      if (key < k_lo || key >= L) {
+    // Packed cache: each lane's four scores belong to keys 4g + j; their
+    // K steps (one per K block) and V step come from the lanes that loaded
+    // those keys' step areas (lane 4g + j).
+    float kstep[KG][4], vstep[4];
+    i32x4 kop[FMT ? KC : 1];
+    if constexpr (FMT == 0) {
+      if (edge) {
+        // Keys outside [k_lo, L) may hold anything (even NaN); they must not
+        // reach the PV product, where 0 * NaN would poison the sum.
+        const int key = key0 + c;
+        if (key < k_lo || key >= L) {
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) tl.v[kc] = i32x4{0, 0, 0, 0};
+          for (int kc = 0; kc < KC; ++kc) tl.v[kc] = i32x4{0, 0, 0, 0};
+        }
+      }
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        *reinterpret_cast<i32x4*>(vs + c * SH::kVStride + 32 * kc + 8 * g) = tl.v[kc];
+    } else {
+      // V codes as operand values (finite whatever the slot holds: keys
+      // outside [k_lo, L) get a weight of exactly 0 below).
+      constexpr uint32_t magic2 = OctType<_Float16>::kMagic | (OctType<_Float16>::kMagic << 16);
+      constexpr int VB = Oct<FMT>::VB;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        i32x4 vv;
+        if constexpr (VB == 4)
+          vv = codes8<4>(tl.v[kc], magic2);
+        else
+          vv = codes8<3>(bits_window(tl.v, 24 * kc), magic2);
+        *reinterpret_cast<i32x4*>(vs + c * SH::kVStride + 32 * kc + 8 * g) = vv;
+      }
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) kop[kc] = codes8<3>(bits_window(tl.k, 24 * kc), magic2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int src = 4 * g + j;
+        if constexpr (KG == 4) {
+          const uint32_t w0 = uint32_t(__shfl(int(tl.sc[0]), src)), w1 = uint32_t(__shfl(int(tl.sc[1]), src));
+          const uint32_t w2 = uint32_t(__shfl(int(tl.sc[2]), src));
+          kstep[0][j] = half_bits_to_float(w0);
+          kstep[1][j] = half_bits_to_float(w0 >> 16);
+          kstep[2][j] = half_bits_to_float(w1);
+          kstep[3][j] = half_bits_to_float(w1 >> 16);
+          vstep[j] = half_bits_to_float(w2);
+        } else {
+          const uint32_t w0 = uint32_t(__shfl(int(tl.sc[0]), src));
+          kstep[0][j] = half_bits_to_float(w0);
+          vstep[j] = half_bits_to_float(w0 >> 16);
+        }
       }
     }
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-      *reinterpret_cast<i32x4*>(vs + c * SH::kVStride + 32 * kc + 8 * g) = tl.v[kc];
 
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) sc = MF::qk(tl.k[kc], qop[rt][kc], sc);
       float x[4];
+      if constexpr (FMT == 0) {
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) sc = MF::qk(tl.k[kc], qop[rt][kc], sc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = sc[j] * p.scale_log2;
+      } else {
+        // Per K block: codes x q', then the block's step times (sum - the
+        // operand offset times the block's q' sum).
+        constexpr float kOff = OctType<_Float16>::kMagicValue + float(1 << (Oct<FMT>::KB - 1)) - 0.5f;
+        constexpr int kSpan = KC / KG;
+        float sj[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < KG; ++b) {
+          f32x4 sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = b * kSpan; kc < (b + 1) * kSpan; ++kc) sb = MF::qk(kop[kc], qop[rt][kc], sb);
+          const float corr = kOff * qsum[rt][b];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sj[j] += kstep[b][j] * (sb[j] - corr);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = sj[j] * p.scale_log2;
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        x[j] = sc[j] * p.scale_log2;
         if (edge) {
           const int key = key0 + 4 * g + j;
           if (key < lo_r[rt] || key > qpos_r[rt]) x[j] = kNegInf;
@@ -367,8 +572,26 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
       if (__builtin_amdgcn_ballot_w64(move) != 0) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
+        psum[rt] *= alpha;
       }
-      pb[rt] = pack4(MF::bits(pj[0]), MF::bits(pj[1]), MF::bits(pj[2]), MF::bits(pj[3]));
+      if constexpr (FMT == 0) {
+        pb[rt] = pack4(MF::bits(pj[0]), MF::bits(pj[1]), MF::bits(pj[2]), MF::bits(pj[3]));
+      } else {
+        // The V step goes into the weight; keys outside [k_lo, L) weigh
+        // exactly 0 (their step may be anything).
+        uint16_t pbits[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = key0 + 4 * g + j;
+          const float w = key >= k_lo && key < L ? pj[j] * vstep[j] : 0.f;
+          pbits[j] = MF::bits(w);
+        }
+        pb[rt] = pack4(pbits[0], pbits[1], pbits[2], pbits[3]);
+        const uint32_t p01 = uint32_t(pbits[0]) | (uint32_t(pbits[1]) << 16);
+        const uint32_t p23 = uint32_t(pbits[2]) | (uint32_t(pbits[3]) << 16);
+        using OF = OctType<_Float16>;
+        psum[rt] += (OF::lo(p01) + OF::hi(p01)) + (OF::lo(p23) + OF::hi(p23));
+      }
     }
   };
 
@@ -395,7 +618,7 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
   // The item's tiles in chunks of at most kMaxSegTiles staged ids (one
   // chunk on the grid schedule).  Within a chunk, tile i of this wave is
   // cs + wave + i * NW.
-  Tile ring[SH::PF + 1];
+  Tile ring[PF + 1];
   int cs = ts;
   {
     const int ce = min(te, cs + kMaxSegTiles);
@@ -419,7 +642,7 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
     // iteration has the same loads in flight and the compiler's wait counts
     // stay exact (the clamped re-reads of the last tile hit in cache).
     auto tile_at = [&](int i) { return first_t + min(i, n_w - 1) * NW; };
-    if constexpr (SH::PF == 0) {
+    if constexpr (PF == 0) {
       // No register room for a second tile: the next tile's loads go out as
       // soon as the scores have consumed the current one, so they overlap
       // the PV product (whose V operand is already in LDS).
@@ -434,14 +657,14 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
       // (Reloading a tile's registers right after its scores, which keeps
       // PF + 1 tiles in flight through the PV product, measured slower.)
 #pragma unroll
-      for (int u = 1; u < SH::PF; ++u) issue_tile(ring[u], tile_at(u), block_of(tile_at(u)));
-      int blk_next = block_of(tile_at(SH::PF));
-      for (int i = 0;; i += SH::PF + 1) {
+      for (int u = 1; u < PF; ++u) issue_tile(ring[u], tile_at(u), block_of(tile_at(u)));
+      int blk_next = block_of(tile_at(PF));
+      for (int i = 0;; i += PF + 1) {
 #pragma unroll
-        for (int u = 0; u <= SH::PF; ++u) {
+        for (int u = 0; u <= PF; ++u) {
           uint64_t pb[RT];
-          issue_tile(ring[(u + SH::PF) % (SH::PF + 1)], tile_at(i + u + SH::PF), blk_next);
-          blk_next = block_of(tile_at(i + u + SH::PF + 1));
+          issue_tile(ring[(u + PF) % (PF + 1)], tile_at(i + u + PF), blk_next);
+          blk_next = block_of(tile_at(i + u + PF + 1));
           score_tile(ring[u], first_t + (i + u) * NW, pb);
           pv_tile(pb);
           if (i + u + 1 >= n_w) goto chunk_done;
@@ -456,6 +679,21 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
     for (int t = tid; t < min(te - cs, kMaxSegTiles); t += SH::kThreads)
       sm_ids[t] = table[((cs + t) * 16) / p.page_size];
     __syncthreads();
+  }
+
+  // Packed cache: the V codes entered the products as offset + code, with
+  // the step in the weight; the offset times the row's sum of the rounded
+  // weights comes off every column.
+  if constexpr (FMT != 0) {
+    constexpr float kOff = OctType<_Float16>::kMagicValue + float(1 << (Oct<FMT>::VB - 1)) - 0.5f;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float ps = psum[rt];
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[rt][dt] -= kOff * ps;
+    }
   }
 
   // ---- combine the waves (one LDS slot per wave, summed in wave order:
@@ -500,7 +738,34 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
     }
   }
   __syncthreads();
-  finish<T, D, RT, NW>(p, lds, s, kvh, row0, wg_rows, fr, SH::kBytes);
+  if constexpr (FMT != 0) {
+    // Packed cache: the summed rows leave the rotated space of the values,
+    // o = s * (H o') / 16, before they are written or published (the merge
+    // is linear, so it may combine rotated-back partials).  A wave takes a
+    // row at a time, four consecutive columns per lane: index bits 0-1 in
+    // the lane, bits 2-7 across lanes.
+    const uint32_t vsw = p.v_signs[lane >> 3];
+    for (int r = wave; r < wg_rows; r += NW) {
+      float* rowp = sm_acc + r * CB::kAccStride + 4 * lane;
+      f32x4 a = *reinterpret_cast<const f32x4*>(rowp);
+#pragma unroll
+      for (int w = 1; w < NW; ++w) a += *reinterpret_cast<const f32x4*>(rowp + w * CB::kRows * CB::kAccStride);
+      float v[4] = {a[0] + a[1], a[0] - a[1], a[2] + a[3], a[2] - a[3]};
+      float u[4] = {v[0] + v[2], v[1] + v[3], v[0] - v[2], v[1] - v[3]};
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = wht_lane_stage(u[i], o, (lane & o) != 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = u[i] * 0.0625f;
+        a[i] = ((vsw >> ((4 * lane + i) & 31)) & 1u) ? -x : x;
+      }
+      *reinterpret_cast<f32x4*>(rowp) = a;
+    }
+    __syncthreads();
+  }
+  finish<T, D, RT, NW, FMT ? 1 : NW>(p, lds, s, kvh, row0, wg_rows, fr, SH::kBytes);
 }
 
 // PERSIST selects the grid: one workgroup per item, or the persistent
@@ -515,7 +780,7 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
 // for no kernel-argument fetch.  The other fields stay in the Params block; the
 // host keeps the three strides within 32 bits.  (One sequence of 32k
 // keys: 31.35 -> 31.03 us; 4k keys: 12.89 -> 12.65 us.)
-template <typename T, int D, int RT, bool PERSIST, bool LEAN>
+template <typename T, int D, int RT, bool PERSIST, bool LEAN, int FMT = 0>
 __global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(
     const int32_t* seq_lens, const int32_t* block_table, const void* kv, int32_t row_groups, int32_t num_kv_heads,
     int32_t max_blocks, int32_t seg_tiles, int32_t page_size, int32_t window, int32_t block_stride,
@@ -555,11 +820,11 @@ __global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(
       kvh = unit % p.num_kv_heads;
       rg = unit / p.num_kv_heads;
     }
-    decode_unit<T, D, RT, LEAN, false>(p, lds, blockIdx.y, kvh, rg, seg, Frag{});
+    decode_unit<T, D, RT, LEAN, false, FMT>(p, lds, blockIdx.y, kvh, rg, seg, Frag{});
   } else {
     balanced_loop(
         p, lds, SH::kPersistOff, SH::kThreads,
-        [&](int s, int kvh, int rg, const Frag& f) { decode_unit<T, D, RT, LEAN, true>(p, lds, s, kvh, rg, 0, f); },
+        [&](int s, int kvh, int rg, const Frag& f) { decode_unit<T, D, RT, LEAN, true, FMT>(p, lds, s, kvh, rg, 0, f); },
         [&](int s, int kvh, int rg, int M) {
           const int row0 = rg * RT * 16, n = min(RT * 16, p.group * M - row0);
           if (n > 0) zero_rows<T, D>(p, s, kvh, row0, n, SH::kThreads);
@@ -840,13 +1105,15 @@ tiles_done:
 // The persistent grid always fills the device and runs the lean loop; a
 // grid of one workgroup per item takes it when the plan says it fills the
 // device.  Where the ring has one tile anyway, one variant serves both.
-template <typename T, int D, int RT>
+// A packed cache (FMT > 0) keeps the two-tile ring on both schedules: its
+// tiles take a few registers per lane.
+template <typename T, int D, int RT, int FMT = 0>
 int launch_t(const Plan& pl, const Params& pr, hipStream_t st) {
-  constexpr bool kTwo = Shape<D, RT, false>::PF != Shape<D, RT, true>::PF;
+  constexpr bool kTwo = FMT == 0 && Shape<D, RT, false>::PF != Shape<D, RT, true>::PF;
   const dim3 grid(pl.grid_x, pl.grid_y), block(Shape<D, RT>::kThreads);
-  const auto kernel = pl.persistent      ? decode_mfma_kernel<T, D, RT, true, kTwo>
-                      : kTwo && pl.lean ? decode_mfma_kernel<T, D, RT, false, kTwo>
-                                        : decode_mfma_kernel<T, D, RT, false, false>;
+  const auto kernel = pl.persistent      ? decode_mfma_kernel<T, D, RT, true, kTwo, FMT>
+                      : kTwo && pl.lean ? decode_mfma_kernel<T, D, RT, false, kTwo, FMT>
+                                        : decode_mfma_kernel<T, D, RT, false, false, FMT>;
   // The strides fit in 32 bits (checked by the planner).
   hipLaunchKernelGGL(kernel, grid, block, 0, st, pr.seq_lens, pr.block_table, pr.kv, pr.row_groups, pr.num_kv_heads,
                      pr.max_blocks, pr.seg_tiles, pr.page_size, pr.window, int32_t(pr.block_stride),
@@ -854,6 +1121,7 @@ int launch_t(const Plan& pl, const Params& pr, hipStream_t st) {
   return int(hipGetLastError());
 }
 
+#ifndef PAD_OCTAVE
 template <typename T, int D>
 int launch_d(const Plan& pl, const Params& pr, hipStream_t st) {
   switch (pl.row_tiles) {
@@ -877,9 +1145,30 @@ int launch_dtype(const Plan& pl, const Params& pr, hipStream_t st) {
   }
   return launch_d<T, D>(pl, pr, st);
 }
+#else
+template <typename T, int FMT>
+int launch_octave_t(const Plan& pl, const Params& pr, hipStream_t st) {
+  switch (pl.row_tiles) {
+    case 1: return launch_t<T, kOctD, 1, FMT>(pl, pr, st);
+    case 2: return launch_t<T, kOctD, 2, FMT>(pl, pr, st);
+  }
+  return int(hipErrorInvalidValue);
+}
+
+template <typename T>
+int launch_octave_dtype(const Plan& pl, const Params& pr, int format, hipStream_t st) {
+  switch (format) {
+    case PAD_KV_OCTAVE_K3V4: return launch_octave_t<T, PAD_KV_OCTAVE_K3V4>(pl, pr, st);
+    case PAD_KV_OCTAVE_K3V3: return launch_octave_t<T, PAD_KV_OCTAVE_K3V3>(pl, pr, st);
+    case PAD_KV_OCTAVE_K3V3_COMPACT: return launch_octave_t<T, PAD_KV_OCTAVE_K3V3_COMPACT>(pl, pr, st);
+  }
+  return int(hipErrorInvalidValue);
+}
+#endif
 
 }  // namespace
 
+#ifndef PAD_OCTAVE
 // This source is compiled once per head size (PAD_HEAD_SIZE), so the
 // instantiations of the four sizes build in parallel.
 template <>
@@ -888,5 +1177,14 @@ int launch_decode_hs<PAD_HEAD_SIZE>(const Plan& plan, const Params& params, int 
   if (dtype == PAD_BF16) return launch_dtype<__bf16, PAD_HEAD_SIZE>(plan, params, st);
   return launch_dtype<_Float16, PAD_HEAD_SIZE>(plan, params, st);
 }
+#else
+// A further build of this source (head size 256, PAD_OCTAVE) holds the
+// packed-cache kernels only.
+int launch_decode_octave(const Plan& plan, const Params& params, int dtype, int format, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == PAD_BF16) return launch_octave_dtype<__bf16>(plan, params, format, st);
+  return launch_octave_dtype<_Float16>(plan, params, format, st);
+}
+#endif
 
 }  // namespace pad

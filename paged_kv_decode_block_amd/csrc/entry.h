@@ -19,9 +19,14 @@ pad_status check_buffers(const pad_shape* shape, const void* q, const void* kv_c
                          const int32_t* seq_lens, float scale, const void* out);
 
 // Validate, plan and enqueue one decode launch on `stream` (the body of
-// pad_decode_attn, and of pad_decode_attn_varlen when q_start is not null).
+// pad_decode_attn, of pad_decode_attn_varlen when q_start is not null, and
+// of pad_decode_attn_octave when format is a pad_kv_format).
 pad_status decode(const pad_shape* shape, const void* q, const int32_t* q_start, const void* kv_cache,
                   const int32_t* block_table, const int32_t* seq_lens, float scale, int32_t window, void* out,
-                  void* workspace, size_t workspace_bytes, void* stream);
+                  void* workspace, size_t workspace_bytes, void* stream, int format = 0,
+                  const uint32_t* k_signs = nullptr, const uint32_t* v_signs = nullptr);
+
+// Bytes of one packed slot of `format` at `head_size` (0: not built).
+int octave_slot_bytes(int format, int head_size);
 
 }  // namespace pad

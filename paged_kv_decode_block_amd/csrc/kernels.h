@@ -34,6 +34,8 @@ struct Params {
   uint32_t merge_wait_ticks;  // helpers' wait bound (100 MHz real-time ticks)
   int32_t persistent;         // 1: balanced persistent grid (one workgroup per CU)
   float scale_log2;           // scale * log2(e): logits are kept in the exp2 domain
+  const uint32_t* k_signs;    // packed cache: sign bits of the K rotation [8]
+  const uint32_t* v_signs;    // packed cache: sign bits of the V rotation [8]
 };
 
 // Enqueue the decode kernel the plan selects.  Returns a HIP error code
@@ -43,6 +45,10 @@ int launch_decode(const Plan& plan, const Params& params, int dtype, int head_si
 // The same for one head size D (64, 128, 256 or 512).
 template <int D>
 int launch_decode_hs(const Plan& plan, const Params& params, int dtype, void* stream);
+
+// Enqueue the packed-cache decode kernel (head size 256) for `format`
+// (pad_kv_format).  Returns a HIP error code.
+int launch_decode_octave(const Plan& plan, const Params& params, int dtype, int format, void* stream);
 
 // Enqueue a fill of `words` 32-bit zeros at `ptr`.
 int launch_zero(void* ptr, size_t words, void* stream);

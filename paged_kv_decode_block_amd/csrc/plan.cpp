@@ -22,7 +22,7 @@ int max_row_tiles(int head_size) {
   return std::max(1, std::min(4, 512 / head_size));
 }
 
-pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
+pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int key_bytes) {
   if (sh.num_seqs < 0 || sh.query_len < 1 || sh.num_q_heads < 1 || sh.num_kv_heads < 1 ||
       sh.head_size < 1 || sh.page_size < 1 || sh.max_blocks_per_seq < 1 || sh.max_seq_len < 0 ||
       sh.num_segments < 0 || window < 0 || num_cus < 1)
@@ -80,7 +80,9 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl) {
   const int64_t units = int64_t(sh.num_seqs) * sh.num_kv_heads * p.row_groups;
   // One workgroup per CU: its 4 waves keep enough loads in flight.
   const int64_t slots = num_cus;
-  const int64_t tile_bytes = int64_t(kTileKeys) * 2 * sh.head_size * 2;
+  // K/V bytes of one 16-key tile of one kv head: two fp16/bf16 rows per key,
+  // or the packed slot of a quantized cache.
+  const int64_t tile_bytes = int64_t(kTileKeys) * (key_bytes > 0 ? key_bytes : 2 * sh.head_size * 2);
   // A batch whose lengths may differ runs on the balanced persistent grid
   // when one round of about 3 MiB per workgroup would not cover its
   // planned K/V: the lengths are only known on the device, where a static

@@ -83,8 +83,10 @@ struct Plan {
   size_t ws_counters, ws_ml, ws_acc, ws_bytes;
 };
 
-// Validates the shape fields (not pointers) and fills `plan`.
-pad_status make_plan(const pad_shape& shape, int window, int num_cus, Plan* plan);
+// Validates the shape fields (not pointers) and fills `plan`.  key_bytes:
+// K/V bytes per key of one kv head that the segment sizing assumes (0: the
+// 2 * head_size elements of an fp16/bf16 cache).
+pad_status make_plan(const pad_shape& shape, int window, int num_cus, Plan* plan, int key_bytes = 0);
 
 // Largest row tiles per wave that fit the accumulator budget at head size D.
 int max_row_tiles(int head_size);

@@ -499,3 +499,50 @@ def test_noalloc_validates_before_launch():
     assert call(big) == pad.PAD_ESCRATCH
     assert call(big, q=0) == pad.PAD_ESCRATCH  # the size bound is checked first
     assert call(shape(num_seqs=0), q=0, kv=0, bt=0, sl=0, out=0) == pad.PAD_OK
+
+
+def test_octave_validation():
+    """Host checks of the packed-cache entry points (no GPU: every call
+    fails or returns before a launch)."""
+    L = pad.lib
+    P = ctypes.c_void_p
+    for fmt, want in ((pad.PAD_KV_OCTAVE_K3V4, 240), (pad.PAD_KV_OCTAVE_K3V3, 208),
+                      (pad.PAD_KV_OCTAVE_K3V3_COMPACT, 208)):
+        assert pad.pad_octave_slot_bytes(fmt) == want
+    n = ctypes.c_int32(0)
+    assert L.pad_octave_slot_bytes(0, 256, ctypes.byref(n)) == pad.PAD_EINVAL
+    assert L.pad_octave_slot_bytes(4, 256, ctypes.byref(n)) == pad.PAD_EINVAL
+    assert L.pad_octave_slot_bytes(1, 128, ctypes.byref(n)) == pad.PAD_EUNSUPPORTED
+    assert L.pad_octave_slot_bytes(1, 256, None) == pad.PAD_EINVAL
+
+    def dec(sh, fmt=1, q=0x1000, cache=0x2000, bt=0x3000, sl=0x4000, ks=0x5000, vs=0x6000, out=0x7000):
+        return L.pad_decode_attn_octave(ctypes.byref(sh), fmt, P(q), P(cache), P(bt), P(sl), P(ks), P(vs),
+                                        ctypes.c_float(0.1), P(out), P(0), ctypes.c_size_t(0), None)
+
+    base = dict(num_q_heads=16, num_kv_heads=2, head_size=256, num_segments=1)
+    assert dec(shape(**base), fmt=0) == pad.PAD_EINVAL
+    assert dec(shape(**base), fmt=4) == pad.PAD_EINVAL
+    assert dec(shape(num_q_heads=16, num_kv_heads=2, head_size=128)) == pad.PAD_EUNSUPPORTED
+    assert dec(shape(path=pad.PAD_PATH_DOT, **base)) == pad.PAD_EUNSUPPORTED
+    assert dec(shape(**base), ks=0) == pad.PAD_EINVAL
+    assert dec(shape(**base), vs=0x6002) == pad.PAD_EINVAL
+    assert dec(shape(**base), q=0) == pad.PAD_EINVAL
+    assert dec(shape(num_seqs=0, **base), q=0, cache=0, bt=0, sl=0, ks=0, vs=0, out=0) == pad.PAD_OK
+    # a split plan needs a workspace
+    split = shape(num_q_heads=16, num_kv_heads=2, head_size=256, num_segments=4)
+    assert dec(split) == pad.PAD_EWORKSPACE
+    # the packed format's bytes per key shrink the planned workspace's K/V
+    # span, never below the control prefix
+    assert pad.pad_decode_attn_octave_workspace_size(split, 1) >= 1 << 20
+
+    def wr(fmt=1, head_size=256, tokens=4, key=0x1000, ks=0x2000, cache=0x3000):
+        sh = pad.pad_octave_cache_shape(num_tokens=tokens, num_kv_heads=2, head_size=head_size, page_size=16,
+                                        num_blocks=4, dtype=pad.PAD_BF16, layout=pad.PAD_HND, format=fmt)
+        return L.pad_octave_cache_write(ctypes.byref(sh), P(key), P(key), P(0x4000), P(ks), P(ks), P(cache), None)
+
+    assert wr(tokens=0, key=0) == pad.PAD_OK
+    assert wr(fmt=0) == pad.PAD_EINVAL
+    assert wr(head_size=128) == pad.PAD_EUNSUPPORTED
+    assert wr(key=0) == pad.PAD_EINVAL
+    assert wr(ks=0x2002) == pad.PAD_EINVAL
+    assert wr(cache=0x3008) == pad.PAD_EINVAL

@@ -1,0 +1,207 @@
+"""The quantized ("octave") packed cache on the HIP path, through the C ABI,
+against the fp64 oracle (oracle/octave.py) on seeded inputs.
+
+* Decode over a packed cache the oracle encoded: every format, both
+  dtypes of q/out, both layouts, both schedules, forced segment counts,
+  row groups, padded and short sequences (rows with no key).  Slots past a
+  sequence's end and the never-read block hold NaN steps: they must not
+  reach the output.
+* The store kernel against the oracle's encoder: steps and codes equal,
+  except where the value sits within rounding of a decision boundary
+  (either neighbour is correct there); skipped and other slots untouched.
+* Store then decode on the GPU against encode then decode in the oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_decode_block_amd as pad
+import workloads as wl
+from gpu_check import check, say
+from oracle import octave as oc
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+NAMES = {pad.PAD_KV_OCTAVE_K3V4: "octave_k3v4", pad.PAD_KV_OCTAVE_K3V3: "octave_k3v3",
+         pad.PAD_KV_OCTAVE_K3V3_COMPACT: "octave_k3v3_compact"}
+
+
+def _signs(seed):
+    w = wl.sign_words(seed)
+    return w, oc.signs_from_bits(w.numpy().view(np.uint32), 256)
+
+
+def _packed_case(fmt, dtype, layout, lens, M, Hq, Hkv, P, seed, **kw):
+    """Host case, its cache encoded by the oracle, slots of NaN rows set to
+    all-ones bytes (NaN steps)."""
+    spec = wl.Spec(dtype, 256, Hq, Hkv, P, layout)
+    c = wl.make_case(spec, lens, M, seed=seed, device="cpu", **kw)
+    kw_, sk = _signs(seed + 1)
+    vw_, sv = _signs(seed + 2)
+    kv = c.kv_cache.to(torch.float64).numpy()
+    bad = np.isnan(kv).any(axis=(-1, -2))
+    with np.errstate(invalid="ignore"):
+        packed = oc.encode_rows(np.nan_to_num(kv[..., 0, :]), np.nan_to_num(kv[..., 1, :]), sk, sv, NAMES[fmt])
+    packed[bad] = 0xFF
+    return c, packed, kw_, vw_, sk, sv
+
+
+def _oracle(c, packed, fmt, sk, sv, seqs=None):
+    bt = c.block_tables[0].numpy()
+    idx = list(range(c.num_seqs)) if seqs is None else list(seqs)
+    sub = bt[idx]
+    used = np.unique(sub)
+    remap = {int(b): i for i, b in enumerate(used)}
+    table = np.vectorize(lambda b: remap[int(b)], otypes=[np.int64])(sub)
+    lens = c.seq_lens.numpy()[idx]
+    q64 = c.q[idx].to(torch.float64).numpy()
+    with np.errstate(invalid="ignore"):
+        return oc.decode_attention_quant(q64, packed[used], table, lens, c.scale, c.layout, NAMES[fmt], sk, sv)
+
+
+def _run(c, packed, fmt, kw_, vw_, **kw):
+    q = c.q.to(DEV)
+    out = torch.full_like(q, float("nan"))
+    pad.pad_decode_attn_octave(q, torch.from_numpy(packed).to(DEV), c.block_tables[0].to(DEV), c.seq_lens.to(DEV),
+                               kw_.to(DEV), vw_.to(DEV), c.scale, out, fmt, layout=c.layout, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+CASES = [
+    # fmt, dtype, layout, lens, M, Hq, Hkv, P, run kwargs
+    (1, "bf16", wl.HND, [3000, 17, 0, 1200], 4, 16, 2, 32, {}),
+    (2, "fp16", wl.NHD, [2100], 1, 8, 2, 16, {}),
+    (3, "bf16", wl.HND, [1500, 800], 8, 16, 2, 1056, {}),           # 64 rows: two row groups
+    (1, "fp16", wl.HND, [5, 3, 40], 4, 8, 2, 16, {}),               # L < M: rows with no key
+    (1, "bf16", wl.NHD, [2500], 2, 16, 2, 32, {"num_segments": 1}),
+    (2, "bf16", wl.HND, [2500], 2, 16, 2, 32, {"num_segments": 17}),
+    (3, "fp16", wl.HND, [4000, 900, 0, 2000], 4, 16, 2, 544, {"schedule": pad.PAD_SCHED_PERSISTENT}),
+    (1, "bf16", wl.HND, [4000, 900, 0, 2000], 4, 16, 2, 544, {"schedule": pad.PAD_SCHED_GRID, "num_segments": 5}),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"o{i}" for i in range(len(CASES))])
+def test_decode_matches_oracle(case):
+    fmt, dt, layout, lens, M, Hq, Hkv, P, kw = case
+    say(f"octave decode: {NAMES[fmt]} {dt} layout={layout} lens={lens} M={M} {Hq}/{Hkv} P={P} {kw}")
+    c, packed, kw_, vw_, sk, sv = _packed_case(fmt, dt, layout, lens, M, Hq, Hkv, P, 900 + fmt + M + len(lens))
+    out = _run(c, packed, fmt, kw_, vw_, **kw)
+    check(out, _oracle(c, packed, fmt, sk, sv), c.q.dtype, f"octave {NAMES[fmt]} {dt}")
+    if 0 in lens:
+        assert torch.all(out[lens.index(0)] == 0)
+
+
+def test_decode_batch_workload_shapes():
+    """64 sequences of 512..4000 keys plus a padded one, the batch
+    workload's heads and page size (16/2 heads of 256, page 1056, M=4),
+    k3v4 bf16: the balanced persistent grid."""
+    g = torch.Generator().manual_seed(77)
+    lens = torch.randint(512, 4001, (64,), generator=g).tolist() + [0]
+    c, packed, kw_, vw_, sk, sv = _packed_case(1, "bf16", wl.HND, lens, 4, 16, 2, 1056, 4242)
+    say("octave decode: batch of 64 + 1 padded, k3v4 bf16, page 1056")
+    out = _run(c, packed, 1, kw_, vw_)
+    assert torch.all(out[64] == 0)
+    pick = [0, 13, 31, 47, 63]
+    check(out[pick], _oracle(c, packed, 1, sk, sv, seqs=pick), c.q.dtype, "octave batch (5 sequences)")
+
+
+def _ambiguous(x, step):
+    r = x / np.where(step > 0, step, 1.0)
+    return np.abs(r - np.round(r)) < 1e-4
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+@pytest.mark.parametrize("dtype,layout", [("bf16", wl.HND), ("fp16", wl.NHD)])
+def test_cache_write_matches_encoder(fmt, dtype, layout):
+    T, Hkv, P, nb = 300, 2, 16, 40
+    say(f"octave store: {NAMES[fmt]} {dtype} layout={layout} T={T}")
+    g = torch.Generator().manual_seed(31 + fmt)
+    tdt = wl._DTYPES[dtype]
+    key = torch.randn((T, Hkv, 256), generator=g).to(tdt)
+    value = (torch.randn((T, Hkv, 256), generator=g) * 0.5).to(tdt)
+    slots = torch.randperm(nb * P, generator=g)[:T].to(torch.int64)
+    slots[5] = -1                 # padding token: skipped
+    slots[7] = nb * P             # past the cache: skipped
+    kw_, sk = _signs(500 + fmt)
+    vw_, sv = _signs(600 + fmt)
+    sb = pad.pad_octave_slot_bytes(fmt)
+    shape = (nb, Hkv, P, sb) if layout == wl.HND else (nb, P, Hkv, sb)
+    cache = torch.full(shape, 0xAB, dtype=torch.uint8, device=DEV)
+    pad.pad_octave_cache_write(key.to(DEV), value.to(DEV), cache, slots.to(DEV), kw_.to(DEV), vw_.to(DEV), fmt,
+                               layout=layout)
+    torch.cuda.synchronize()
+    got_all = cache.cpu().numpy()
+    name = NAMES[fmt]
+    kb, vb, compact = oc.FORMATS[name]
+    gk = 256 if compact else 64
+    k64, v64 = key.to(torch.float64).numpy(), value.to(torch.float64).numpy()
+    want = oc.encode_rows(k64, v64, sk, sv, name)
+    kr = oc.rotate(k64, sk, gk)
+    vr = oc.rotate(v64, sv, 256)
+    written = np.zeros(got_all.shape[:-1], dtype=bool)
+    n_codes = n_equal = 0
+    for t in range(T):
+        s = int(slots[t])
+        if s < 0 or s >= nb * P:
+            continue
+        blk, off = divmod(s, P)
+        for h in range(Hkv):
+            got = got_all[blk, h, off] if layout == wl.HND else got_all[blk, off, h]
+            written[(blk, h, off) if layout == wl.HND else (blk, off, h)] = True
+            w = want[t, h]
+            nk, nv = kb * 32, vb * 32
+            ng = 256 // gk
+            st_got = got[nk + nv: nk + nv + 2 * (ng + 1)].view(np.float16).astype(np.float64)
+            st_want = w[nk + nv: nk + nv + 2 * (ng + 1)].view(np.float16).astype(np.float64)
+            assert np.all(got[nk + nv + 2 * (ng + 1):] == 0), "padding bytes are zero"
+            kc_got, kc_want = oc.unpack_codes(got[:nk], kb, 256), oc.unpack_codes(w[:nk], kb, 256)
+            vc_got, vc_want = oc.unpack_codes(got[nk:nk + nv], vb, 256), oc.unpack_codes(w[nk:nk + nv], vb, 256)
+            # a step may differ only where absmax / 2^(b-1) is within rounding of an fp16 midpoint
+            for i in range(ng + 1):
+                if st_got[i] != st_want[i]:
+                    a = np.abs(kr[t, h, i * gk:(i + 1) * gk]).max() / 4 if i < ng else np.abs(vr[t, h]).max() / (1 << (vb - 1))
+                    assert abs(st_got[i] - st_want[i]) <= 2 ** -10 * a and abs(a - (st_got[i] + st_want[i]) / 2) < 1e-6 * a
+            for codes_g, codes_w, x, steps, groups in ((kc_got, kc_want, kr[t, h], st_got[:ng], ng),
+                                                        (vc_got, vc_want, vr[t, h], st_got[ng:], 1)):
+                step = np.repeat(steps, 256 // groups)
+                diff = codes_g != codes_w
+                n_codes += codes_g.size
+                n_equal += int((~diff).sum())
+                assert np.all(~diff | _ambiguous(x, step) | (np.repeat(st_got[:ng] if groups == ng else st_got[ng:], 256 // groups) != np.repeat(st_want[:ng] if groups == ng else st_want[ng:], 256 // groups)))
+                assert np.all(np.abs(codes_g - codes_w) <= 1)
+    assert np.all(got_all[~written] == 0xAB), "slots of skipped tokens and unused slots are untouched"
+    assert n_equal >= 0.999 * n_codes
+    say(f"  codes equal: {n_equal}/{n_codes}")
+
+
+@pytest.mark.parametrize("fmt,dtype", [(1, "bf16"), (3, "fp16")])
+def test_store_then_decode(fmt, dtype):
+    """New tokens stored by the GPU, then decoded by the GPU, against the
+    oracle's encode-then-decode of the same rows (a code taken on the
+    other side of a decision boundary moves an output by far less than
+    the tolerance at these lengths)."""
+    spec = wl.Spec(dtype, 256, 16, 2, 32, wl.HND)
+    lens, M = [900, 600], 4
+    c = wl.make_case(spec, lens, M, seed=71 + fmt, device="cpu", poison_tail=False)
+    kw_, sk = _signs(81 + fmt)
+    vw_, sv = _signs(91 + fmt)
+    nb = c.kv_cache.shape[0]
+    # token rows in the order of their slots: slot = block * P + offset
+    kv = c.kv_cache.permute(0, 2, 1, 3, 4).reshape(nb * 32, 2, 2, 256)  # [slot, Hkv, 2, D]
+    slots = torch.arange(nb * 32, dtype=torch.int64)
+    sb = pad.pad_octave_slot_bytes(fmt)
+    cache = torch.zeros((nb, 2, 32, sb), dtype=torch.uint8, device=DEV)
+    say(f"octave store then decode: {NAMES[fmt]} {dtype}")
+    pad.pad_octave_cache_write(kv[:, :, 0].contiguous().to(DEV), kv[:, :, 1].contiguous().to(DEV), cache,
+                               slots.to(DEV), kw_.to(DEV), vw_.to(DEV), fmt)
+    q = c.q.to(DEV)
+    out = torch.empty_like(q)
+    pad.pad_decode_attn_octave(q, cache, c.block_tables[0].to(DEV), c.seq_lens.to(DEV), kw_.to(DEV), vw_.to(DEV),
+                               c.scale, out, fmt)
+    torch.cuda.synchronize()
+    kv64 = c.kv_cache.to(torch.float64).numpy()
+    with np.errstate(invalid="ignore"):
+        packed = oc.encode_rows(np.nan_to_num(kv64[..., 0, :]), np.nan_to_num(kv64[..., 1, :]), sk, sv, NAMES[fmt])
+    check(out, _oracle(c, packed, fmt, sk, sv), c.q.dtype, f"store then decode {NAMES[fmt]}")

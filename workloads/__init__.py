@@ -326,3 +326,12 @@ def compact(case: Case, instance: int = 0, seqs: Sequence[int] | None = None):
     idx = torch.as_tensor(used, dtype=torch.int64, device=case.kv_cache.device)
     kv64 = as_f64(case.kv_cache.index_select(0, idx))
     return kv64, table, lens[seqs].astype(np.int64)
+
+
+def sign_words(seed: int, head_size: int = 256) -> torch.Tensor:
+    """Seeded sign bits of a rotation, ``head_size // 32`` 32-bit words as an
+    int32 tensor (the random draw of the octave page's ``sign_bits``, handed
+    to both sides as an input; bit i % 32 of word i // 32 set = element i
+    negated)."""
+    g = torch.Generator().manual_seed(seed)
+    return torch.randint(-(1 << 31), 1 << 31, (head_size // 32,), generator=g, dtype=torch.int64).to(torch.int32)
