@@ -407,12 +407,13 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
   const uint16_t* vtr = vs + (4 * g + (c >> 2)) * SH::kVStride + 4 * (c & 3);
 
   using Tile = std::conditional_t<FMT == 0, PlainTile<KC>, OctTile>;
-  // Running sum, per lane, of the rounded step-scaled softmax weights that
-  // multiply the V codes (packed cache): the V offset is taken off the
-  // accumulator with it after the last tile.
-  float psum[RT];
+  // Packed cache: the row sums of the rounded step-scaled weights that
+  // multiply the V codes, as one more PV product against an operand of
+  // ones (every lane of the row holds its row's sum); the V offset is taken
+  // off the accumulator with them after the last tile.
+  f32x4 psum[RT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) psum[rt] = 0.f;
+  for (int rt = 0; rt < RT; ++rt) psum[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto issue_tile = [&](Tile& tl, int t, int blk) {
     const int key0 = t * 16;
@@ -484,21 +485,20 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
       for (int kc = 0; kc < KC; ++kc)
         *reinterpret_cast<i32x4*>(vs + c * SH::kVStride + 32 * kc + 8 * g) = tl.v[kc];
     } else {
-      // V codes as operand values (finite whatever the slot holds: keys
-      // outside [k_lo, L) get a weight of exactly 0 below).
-      constexpr uint32_t magic2 = OctType<_Float16>::kMagic | (OctType<_Float16>::kMagic << 16);
+      // V codes as operands (finite whatever the slot holds: keys outside
+      // [k_lo, L) get a weight of exactly 0 below).
       constexpr int VB = Oct<FMT>::VB;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         i32x4 vv;
         if constexpr (VB == 4)
-          vv = codes8<4>(tl.v[kc], magic2);
+          vv = codes8_nibbles(tl.v[kc]);
         else
-          vv = codes8<3>(bits_window(tl.v, 24 * kc), magic2);
+          vv = codes8<3>(bits_window(tl.v, 24 * kc));
         *reinterpret_cast<i32x4*>(vs + c * SH::kVStride + 32 * kc + 8 * g) = vv;
       }
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) kop[kc] = codes8<3>(bits_window(tl.k, 24 * kc), magic2);
+      for (int kc = 0; kc < KC; ++kc) kop[kc] = codes8<3>(bits_window(tl.k, 24 * kc));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int src = 4 * g + j;
@@ -528,9 +528,9 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
 #pragma unroll
         for (int j = 0; j < 4; ++j) x[j] = sc[j] * p.scale_log2;
       } else {
-        // Per K block: codes x q', then the block's step times (sum - the
-        // operand offset times the block's q' sum).
-        constexpr float kOff = OctType<_Float16>::kMagicValue + float(1 << (Oct<FMT>::KB - 1)) - 0.5f;
+        // Per K block: codes x q' (scaled back by 2^24), minus the level
+        // offset times the block's q' sum, times the block's step.
+        constexpr float kOff = float(1 << (Oct<FMT>::KB - 1)) - 0.5f;
         constexpr int kSpan = KC / KG;
         float sj[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -540,7 +540,7 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
           for (int kc = b * kSpan; kc < (b + 1) * kSpan; ++kc) sb = MF::qk(kop[kc], qop[rt][kc], sb);
           const float corr = kOff * qsum[rt][b];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) sj[j] += kstep[b][j] * (sb[j] - corr);
+          for (int j = 0; j < 4; ++j) sj[j] += kstep[b][j] * fmaf(sb[j], kCodeScale, -corr);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) x[j] = sj[j] * p.scale_log2;
@@ -572,30 +572,30 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
       if (__builtin_amdgcn_ballot_w64(move) != 0) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
-        psum[rt] *= alpha;
+        if constexpr (FMT != 0) psum[rt] *= alpha;
       }
       if constexpr (FMT == 0) {
         pb[rt] = pack4(MF::bits(pj[0]), MF::bits(pj[1]), MF::bits(pj[2]), MF::bits(pj[3]));
       } else {
-        // The V step goes into the weight; keys outside [k_lo, L) weigh
-        // exactly 0 (their step may be anything).
-        uint16_t pbits[4];
+        // The V step goes into the weight; on edge tiles keys outside
+        // [k_lo, L) weigh exactly 0 (their step may be anything).
+        float w[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = key0 + 4 * g + j;
-          const float w = key >= k_lo && key < L ? pj[j] * vstep[j] : 0.f;
-          pbits[j] = MF::bits(w);
+        for (int j = 0; j < 4; ++j) w[j] = pj[j] * vstep[j];
+        if (edge) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int key = key0 + 4 * g + j;
+            if (key < k_lo || key >= L) w[j] = 0.f;
+          }
         }
-        pb[rt] = pack4(pbits[0], pbits[1], pbits[2], pbits[3]);
-        const uint32_t p01 = uint32_t(pbits[0]) | (uint32_t(pbits[1]) << 16);
-        const uint32_t p23 = uint32_t(pbits[2]) | (uint32_t(pbits[3]) << 16);
-        using OF = OctType<_Float16>;
-        psum[rt] += (OF::lo(p01) + OF::hi(p01)) + (OF::lo(p23) + OF::hi(p23));
+        pb[rt] = pack4(MF::bits(w[0]), MF::bits(w[1]), MF::bits(w[2]), MF::bits(w[3]));
       }
     }
   };
 
   // O^T += V^T P^T from the V rows staged in LDS.
+  constexpr int kPvAhead = DT < 4 ? DT : 4;
   auto pv_tile = [&](const uint64_t (&pb)[RT]) {
     // The staged V rows were written by other lanes of this wave; LDS
     // operations of a wave complete in order, the fences keep the compiler
@@ -603,13 +603,29 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint64_t va[DT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint64_t va = __builtin_bit_cast(
+    for (int dt = 0; dt < DT; ++dt)
+      va[dt] = __builtin_bit_cast(
           uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vtr + 16 * dt)));
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) acc[rt][dt] = MF::pv(va, pb[rt], acc[rt][dt]);
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt][dt] = MF::pv(va[dt], pb[rt], acc[rt][dt]);
+    if constexpr (FMT != 0) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) psum[rt] = MF::pv(kOnes4, pb[rt], psum[rt]);
     }
+    // Order: kPvAhead reads, then per column the RT products and the read
+    // kPvAhead columns on, so several LDS round trips overlap instead of
+    // one read waiting before each column's products.
+    __builtin_amdgcn_sched_group_barrier(0x100, kPvAhead, 0);
+#pragma unroll
+    for (int dt = 0; dt < DT - kPvAhead; ++dt) {
+      __builtin_amdgcn_sched_group_barrier(0x008, RT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, RT * kPvAhead + (FMT != 0 ? RT : 0), 0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -685,14 +701,14 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
   // the step in the weight; the offset times the row's sum of the rounded
   // weights comes off every column.
   if constexpr (FMT != 0) {
-    constexpr float kOff = OctType<_Float16>::kMagicValue + float(1 << (Oct<FMT>::VB - 1)) - 0.5f;
+    constexpr float kOff = float(1 << (Oct<FMT>::VB - 1)) - 0.5f;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      float ps = psum[rt];
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
+      const float corr = kOff * psum[rt][0];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[rt][dt] -= kOff * ps;
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[rt][dt][e] = fmaf(acc[rt][dt][e], kCodeScale, -corr);
     }
   }
 

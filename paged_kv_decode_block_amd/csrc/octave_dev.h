@@ -13,10 +13,10 @@
 // is code e of group g * 8 + kc, so the 16 lanes of MFMA lane group g (the
 // lanes that hold elements 32 kc + 8 g .. + 7 of every chunk kc) read the
 // lane-group's own 3 (K) or VB (V) bytes per chunk, 24 or 8 VB contiguous
-// bytes.  A code c is turned into the exact MFMA operand value 128 + c
-// (bf16) or 1024 + c (fp16) by an OR with the value's bit pattern: the
-// products run on codes, and the steps and the offset of the level
-// (c - 2^(B-1) + 1/2) * step are applied afterwards.
+// bytes.  A code c is used as the fp16 operand whose bits are c, the exact
+// subnormal c * 2^-24: the products run on codes, and 2^24, the steps and
+// the offset of the level (c - 2^(B-1) + 1/2) * step are applied
+// afterwards.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -76,37 +76,48 @@ __device__ __forceinline__ uint32_t bits_window(const uint32_t (&w)[N], int lo) 
   return __builtin_amdgcn_alignbit(w[i + 1 < N ? i + 1 : N - 1], w[i], uint32_t(sh));
 }
 
-// Eight B-bit codes (code e at bits B e of x) as an MFMA operand: four
-// dwords of two 16-bit values each, value bits = magic | code.
+// Eight B-bit codes (code e at bits B e of x) as an fp16 MFMA operand:
+// four dwords of two 16-bit values each whose bits are the code, i.e. the
+// fp16 subnormal c * 2^-24 (exact; the products scale back by 2^24).
 template <int B>
-__device__ __forceinline__ i32x4 codes8(uint32_t x, uint32_t magic2) {
+__device__ __forceinline__ i32x4 codes8(uint32_t x) {
   i32x4 r;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    r[q] = int(magic2 | __builtin_amdgcn_ubfe(x, 2 * q * B, B) | (__builtin_amdgcn_ubfe(x, (2 * q + 1) * B, B) << 16));
+    r[q] = int(__builtin_amdgcn_ubfe(x, 2 * q * B, B) | (__builtin_amdgcn_ubfe(x, (2 * q + 1) * B, B) << 16));
   return r;
 }
+
+// The same for eight 4-bit codes: the even codes' nibbles and the odd
+// codes' nibbles as bytes, interleaved with zero bytes by byte permutes.
+__device__ __forceinline__ i32x4 codes8_nibbles(uint32_t x) {
+  const uint32_t ev = x & 0x0f0f0f0fu, od = (x >> 4) & 0x0f0f0f0fu;
+  i32x4 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)  // bytes: even code q, 0, odd code q, 0
+    r[q] = int(__builtin_amdgcn_perm(od, ev, 0x0c040c00u + 0x00010001u * uint32_t(q)));
+  return r;
+}
+
+// An fp16 MFMA operand of four ones.
+constexpr uint64_t kOnes4 = 0x3c003c003c003c00ull;
+// Scale of the products of subnormal code operands.
+constexpr float kCodeScale = 16777216.f;  // 2^24
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return float(__builtin_bit_cast(_Float16, uint16_t(h & 0xffffu)));
 }
 
-// The 16-bit element type's code operand: value bits kMagic | c stand for
-// kMagicValue + c exactly (a 7- or 10-bit mantissa holds any code), and the
-// two 16-bit halves of a dword as fp32.
+// The two 16-bit halves of a dword of the element type as fp32.
 template <typename T>
 struct OctType;
 template <>
 struct OctType<__bf16> {
-  static constexpr uint32_t kMagic = 0x4300u;  // 128
-  static constexpr float kMagicValue = 128.f;
   static __device__ __forceinline__ float lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
   static __device__ __forceinline__ float hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 };
 template <>
 struct OctType<_Float16> {
-  static constexpr uint32_t kMagic = 0x6400u;  // 1024
-  static constexpr float kMagicValue = 1024.f;
   static __device__ __forceinline__ float lo(uint32_t w) { return float(__builtin_bit_cast(_Float16, uint16_t(w))); }
   static __device__ __forceinline__ float hi(uint32_t w) {
     return float(__builtin_bit_cast(_Float16, uint16_t(w >> 16)));
