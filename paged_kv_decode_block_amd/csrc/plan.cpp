@@ -171,8 +171,11 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
   // exceed kMaxSegTiles tiles -- also for device lengths beyond
   // max_seq_len, up to the table's capacity (the kernel clamps to it and
   // splits the tiles it finds over the planned segments).
+  // A window's span may straddle one more tile than its keys fill, but no
+  // unit reads more tiles than the table holds (so every window plans
+  // within the window-free bound the workspace is sized for).
   int64_t max_tiles = ceil_div(table_keys, kTileKeys);
-  if (window > 0) max_tiles = std::min(max_tiles + 1, ceil_div(int64_t(window) + sh.query_len - 1, kTileKeys) + 1);
+  if (window > 0) max_tiles = std::min(max_tiles, ceil_div(int64_t(window) + sh.query_len - 1, kTileKeys) + 1);
   if (p.persistent) {
     // Items on the balanced grid are shares of the batch's tiles; one
     // longer than the LDS id area is walked in chunks.

@@ -546,3 +546,19 @@ def test_octave_validation():
     assert wr(key=0) == pad.PAD_EINVAL
     assert wr(ks=0x2002) == pad.PAD_EINVAL
     assert wr(cache=0x3008) == pad.PAD_EINVAL
+
+
+@pytest.mark.parametrize("window", [0, 1, 512, 65535, 65536, 100000])
+@pytest.mark.parametrize("nseg", [0, 1, 3])
+def test_workspace_covers_every_window(window, nseg):
+    """The window-independent workspace size covers the plan of any window,
+    also where the table holds exactly as many tiles as one segment may
+    stage (a windowed plan once counted one tile more than the table and
+    split such a unit, needing a workspace the size query never reported)."""
+    sh = shape(num_seqs=65, query_len=256, num_q_heads=4, num_kv_heads=4, head_size=256, page_size=32,
+               max_blocks_per_seq=2048, num_segments=nseg, schedule=pad.PAD_SCHED_GRID)
+    ws = pad.pad_decode_attn_workspace_size(sh)
+    p = pad.pad_decode_attn_plan(sh, window, 256)
+    assert p["workspace_bytes"] <= ws, (window, nseg, p)
+    if nseg:
+        assert p["num_segments"] == nseg
