@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define PAD_ABI_VERSION 6
+#define PAD_ABI_VERSION 7
 
 typedef enum pad_status {
   PAD_OK = 0,
@@ -98,11 +98,17 @@ typedef enum pad_layout { PAD_NHD = 0, PAD_HND = 1 } pad_layout;
 /* Which kernel family serves a call.  AUTO lets the planner choose; the
  * others force a family (tuning and tests).  MFMA: the waves of a workgroup
  * split a segment's keys and are combined at the end.  DOT: per-head dot
- * products (G*M <= 4, head size <= 128). */
+ * products (G*M <= 4, head size <= 128).  PREFILL: prefill chunks (head
+ * size 64 or 128, one workgroup per item): 128 query rows of a kv head per
+ * workgroup share each 64-key tile through LDS (the prefill work items of
+ * plan_prefill on the rocm_rdna_hip page); AUTO takes it for chunks of at
+ * least 128 rows per kv head whose row blocks fill a quarter of the device,
+ * over at least 1024 keys. */
 typedef enum pad_path {
   PAD_PATH_AUTO = 0,
   PAD_PATH_MFMA = 1,
   PAD_PATH_DOT = 2,
+  PAD_PATH_PREFILL = 3,
 } pad_path;
 
 /* Work schedule.  AUTO picks the balanced persistent grid for batches
@@ -122,8 +128,8 @@ typedef enum pad_schedule {  /* the dot family runs on the grid schedule only */
 /* Shape of one call.  Every field is host data. */
 typedef struct pad_shape {
   int32_t num_seqs;           /* S >= 0 (0: the call does nothing)                 */
-  int32_t query_len;          /* M, 1..256 query tokens per sequence; at most
-                                 4096 rows G * M per kv head                     */
+  int32_t query_len;          /* M, 1..4096 query tokens per sequence; at most
+                                 32768 rows G * M per kv head                    */
   int32_t num_q_heads;        /* Hq >= 1                                         */
   int32_t num_kv_heads;       /* Hkv >= 1, divides Hq                            */
   int32_t head_size;          /* D in {64, 128, 256, 512}                        */
@@ -142,7 +148,7 @@ typedef struct pad_shape {
 
 /* The launch the planner chose (introspection, tests and tuning). */
 typedef struct pad_plan {
-  int32_t path;              /* PAD_PATH_MFMA or PAD_PATH_DOT                     */
+  int32_t path;              /* PAD_PATH_MFMA, PAD_PATH_DOT or PAD_PATH_PREFILL   */
   int32_t rows;              /* query rows per (sequence, kv head) = G * M        */
   int32_t row_tiles;         /* rows of one workgroup in 16-row tiles             */
   int32_t row_groups;        /* workgroups splitting a kv head's rows             */

@@ -21,7 +21,7 @@ __all__ = [
     "pad_octave_cache_shape", "pad_octave_slot_bytes", "pad_octave_cache_write",
     "pad_decode_attn_octave_workspace_size", "pad_decode_attn_octave",
     "PAD_F16", "PAD_BF16", "PAD_NHD", "PAD_HND",
-    "PAD_PATH_AUTO", "PAD_PATH_MFMA", "PAD_PATH_DOT",
+    "PAD_PATH_AUTO", "PAD_PATH_MFMA", "PAD_PATH_DOT", "PAD_PATH_PREFILL",
     "PAD_SCHED_AUTO", "PAD_SCHED_GRID", "PAD_SCHED_PERSISTENT",
     "PadError", "pad_shape", "pad_plan", "lib", "LIB_PATH", "load_library",
     "pad_abi_version", "pad_status_string", "pad_decode_attn_plan",
@@ -36,7 +36,7 @@ PAD_OK, PAD_EINVAL, PAD_EUNSUPPORTED, PAD_EWORKSPACE, PAD_EHIP, PAD_ESCRATCH = 0
 PAD_NOALLOC_SCRATCH_BYTES = 64 << 20
 PAD_F16, PAD_BF16 = 0, 1
 PAD_NHD, PAD_HND = 0, 1
-PAD_PATH_AUTO, PAD_PATH_MFMA, PAD_PATH_DOT = 0, 1, 2
+PAD_PATH_AUTO, PAD_PATH_MFMA, PAD_PATH_DOT, PAD_PATH_PREFILL = 0, 1, 2, 3
 PAD_SCHED_AUTO, PAD_SCHED_GRID, PAD_SCHED_PERSISTENT = 0, 1, 2
 PAD_KV_OCTAVE_K3V4, PAD_KV_OCTAVE_K3V3, PAD_KV_OCTAVE_K3V3_COMPACT = 1, 2, 3
 OCTAVE_FORMATS = {"octave_k3v4": PAD_KV_OCTAVE_K3V4, "octave_k3v3": PAD_KV_OCTAVE_K3V3,

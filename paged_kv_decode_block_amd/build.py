@@ -33,6 +33,8 @@ MFMA_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
 SOURCES = [("decode_mfma.hip", f"decode_mfma_d{d}", [f"-DPAD_HEAD_SIZE={d}", *MFMA_FLAGS]) for d in (64, 128, 256, 512)] + [
     # the packed (quantized) cache's kernels: a further build at head size 256
     ("decode_mfma.hip", "decode_octave_d256", ["-DPAD_HEAD_SIZE=256", "-DPAD_OCTAVE=1", *MFMA_FLAGS]),
+    # the prefill kernels (head sizes 64 and 128)
+    ("prefill_mfma.hip", "prefill_mfma", [*MFMA_FLAGS]),
 ] + [
     (src, src.rsplit(".", 1)[0], [])
     for src in ("launch.hip", "cache_write.hip", "octave_store.hip", "calib.hip", "noalloc.hip", "plan.cpp", "api.cpp")

@@ -543,5 +543,72 @@ __device__ __forceinline__ void balanced_loop(const Params& p, unsigned char* ld
   }
 }
 
+// LDS layout of the wave combine: per wave its running max and sum per row
+// and its rescaled accumulator rows, plus the workgroup's merged max/sum.
+template <int D, int RT, int NW>
+struct Combine {
+  static constexpr int kRows = RT * 16;
+  static constexpr int kAccStride = D + 4;
+  static constexpr int kBytes = (2 * NW * kRows + 2 * kRows) * 4 + NW * kRows * kAccStride * 4;
+  static __device__ float* m(unsigned char* lds) { return reinterpret_cast<float*>(lds); }
+  static __device__ float* l(unsigned char* lds) { return m(lds) + NW * kRows; }
+  static __device__ float* ms(unsigned char* lds) { return l(lds) + NW * kRows; }
+  static __device__ float* ls(unsigned char* lds) { return ms(lds) + kRows; }
+  static __device__ float* acc(unsigned char* lds) { return ls(lds) + kRows; }
+};
+
+// After the waves of a workgroup have left their results in LDS -- per
+// wave w: sm_m/sm_l[w][row] (running max and sum) and the accumulator
+// rows, already rescaled to the workgroup maximum, in slot w of sm_acc; and
+// the workgroup's merged max/sum in sm_ms/sm_ls -- sum the slots in wave
+// order (deterministic) and either write the output (single segment) or
+// publish this segment's partial and take part in the merge.  NSUM slots
+// are summed (1 when the rows were already summed and rotated into slot 0).
+// NT threads take part (NW * 64 by default).
+template <typename T, int D, int RT, int NW, int NSUM = NW, int NT = NW * 64>
+__device__ __forceinline__ void finish(const Params& p, unsigned char* lds, int s, int kvh, int row0, int wg_rows,
+                                       const Frag& f, int lds_bytes) {
+  using MF = Mfma<T>;
+  using CB = Combine<D, RT, NW>;
+  const int tid = threadIdx.x;
+  const float* sm_acc = CB::acc(lds);
+  const float* sm_ms = CB::ms(lds);
+  const float* sm_ls = CB::ls(lds);
+  // Thread-distributed result: item (row r, 4 head-dim columns d4).
+  auto combined = [&](int r, int d4) {
+    const float* col = sm_acc + r * CB::kAccStride + 4 * d4;
+    f32x4 a = *reinterpret_cast<const f32x4*>(col);
+#pragma unroll
+    for (int w = 1; w < NSUM; ++w) a += *reinterpret_cast<const f32x4*>(col + w * CB::kRows * CB::kAccStride);
+    return a;
+  };
+
+  T* out_s = seq_out<T>(p, s, D);
+  if (f.n_parts == 1) {
+    for (int it = tid; it < wg_rows * (D / 4); it += NT) {
+      const int r = it / (D / 4), d4 = it % (D / 4);
+      const f32x4 a = combined(r, d4);
+      const float ls = sm_ls[r];
+      const float inv = ls > 0.f ? 1.f / ls : 0.f;
+      uint2 o;
+      o.x = uint32_t(MF::bits(a[0] * inv)) | (uint32_t(MF::bits(a[1] * inv)) << 16);
+      o.y = uint32_t(MF::bits(a[2] * inv)) | (uint32_t(MF::bits(a[3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(out_row(p, out_s, kvh, row0 + r, D) + 4 * d4) = o;
+    }
+    return;
+  }
+
+  // Publish the partial with device-coherent stores.
+  {
+    const int64_t base = f.slot * p.slot_rows + f.parts.row0;
+    for (int it = tid; it < wg_rows * (D / 4); it += NT) {
+      const int r = it / (D / 4), d4 = it % (D / 4);
+      store_coherent(p.ws_acc + (base + r) * D + 4 * d4, combined(r, d4));
+    }
+    for (int r = tid; r < wg_rows; r += NT) store_coherent2(p.ws_ml + (base + r) * 2, sm_ms[r], sm_ls[r]);
+  }
+  arrive_and_merge<T, D, NT>(p, reinterpret_cast<int*>(lds + lds_bytes - 16), s, kvh, row0, wg_rows, f);
+}
+
 }  // namespace dev
 }  // namespace pad

@@ -46,6 +46,9 @@ int launch_decode(const Plan& plan, const Params& params, int dtype, int head_si
 template <int D>
 int launch_decode_hs(const Plan& plan, const Params& params, int dtype, void* stream);
 
+// Enqueue the prefill kernel (head size 64 or 128; path PAD_PATH_PREFILL).
+int launch_prefill(const Plan& plan, const Params& params, int dtype, int head_size, void* stream);
+
 // Enqueue the packed-cache decode kernel (head size 256) for `format`
 // (pad_kv_format).  Returns a HIP error code.
 int launch_decode_octave(const Plan& plan, const Params& params, int dtype, int format, void* stream);

@@ -30,6 +30,7 @@ int launch_zero(void* ptr, size_t words, void* stream) {
 // The decode kernels of each head size live in their own build of
 // decode_mfma.hip.
 int launch_decode(const Plan& plan, const Params& params, int dtype, int head_size, void* stream) {
+  if (plan.path == PAD_PATH_PREFILL) return launch_prefill(plan, params, dtype, head_size, stream);
   switch (head_size) {
     case 64: return launch_decode_hs<64>(plan, params, dtype, stream);
     case 128: return launch_decode_hs<128>(plan, params, dtype, stream);

@@ -30,7 +30,7 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
   if (sh.num_q_heads % sh.num_kv_heads != 0) return PAD_EINVAL;
   if (sh.dtype != PAD_F16 && sh.dtype != PAD_BF16) return PAD_EINVAL;
   if (sh.layout != PAD_NHD && sh.layout != PAD_HND) return PAD_EINVAL;
-  if (sh.path < PAD_PATH_AUTO || sh.path > PAD_PATH_DOT) return PAD_EINVAL;
+  if (sh.path < PAD_PATH_AUTO || sh.path > PAD_PATH_PREFILL) return PAD_EINVAL;
   if (sh.schedule < PAD_SCHED_AUTO || sh.schedule > PAD_SCHED_PERSISTENT) return PAD_EINVAL;
   const int64_t table_keys = int64_t(sh.max_blocks_per_seq) * sh.page_size;
   if (sh.max_seq_len > table_keys) return PAD_EINVAL;
@@ -50,17 +50,40 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
   if (rows > kMaxRows) return PAD_EUNSUPPORTED;
   const bool dot_ok = rows <= kDotMaxRows && sh.head_size <= kDotMaxHeadSize;
   if (sh.path == PAD_PATH_DOT && !dot_ok) return PAD_EUNSUPPORTED;
+  // The prefill family: head sizes 64 and 128, one workgroup per item.
+  const bool prefill_ok = (sh.head_size == 64 || sh.head_size == 128) && sh.schedule != PAD_SCHED_PERSISTENT;
+  if (sh.path == PAD_PATH_PREFILL && !prefill_ok) return PAD_EUNSUPPORTED;
   const int tiles_total = int(ceil_div(rows, 16));
 
   Plan p{};
   // The key-split MFMA family serves every shape and is the automatic
-  // choice; the per-head dot-product family is used when asked for.
-  p.path = sh.path == PAD_PATH_AUTO ? PAD_PATH_MFMA : sh.path;
+  // choice up to kPrefillMinRows rows per kv head; from there on (prefill
+  // chunks) the prefill family, whose workgroups share each K/V tile among
+  // 128 rows.  The per-head dot-product family is used when asked for.
+  // AUTO takes it where its 128-row blocks fill a quarter of the device
+  // without splitting the keys into many segments, over at least 1024 keys
+  // (16/8 heads of 128, bf16: 256 tokens over 4096 keys 56.8 against 65.3
+  // us, a 2048-token prompt 91 against 164 us; 64 tokens over 8192 keys
+  // 86.8 against 38.9 us and a 512-token prompt 26.5 against 22.5 us stay
+  // with the key-split family).
+  {
+    const int64_t pf_units = int64_t(std::max(1, sh.num_seqs)) * sh.num_kv_heads * ceil_div(rows, kPrefillRows);
+    const int64_t keys = sh.max_seq_len ? sh.max_seq_len : int64_t(sh.max_blocks_per_seq) * sh.page_size;
+    const bool pf_wins = rows >= kPrefillMinRows && 4 * pf_units >= num_cus && keys >= kPrefillMinKeys;
+    if (sh.path == PAD_PATH_AUTO)
+      p.path = prefill_ok && pf_wins ? PAD_PATH_PREFILL : PAD_PATH_MFMA;
+    else
+      p.path = sh.path;
+  }
   p.rows = rows;
   if (p.path == PAD_PATH_DOT) {
     p.row_tiles = 1;
     p.row_groups = 1;
     p.waves = kDotWaveCount;
+  } else if (p.path == PAD_PATH_PREFILL) {
+    p.row_tiles = kPrefillRows / 16;
+    p.row_groups = int(ceil_div(rows, kPrefillRows));
+    p.waves = kPrefillWaves;
   } else {
     int rt = std::min(tiles_total, max_row_tiles(sh.head_size));
     p.row_groups = int(ceil_div(tiles_total, rt));
@@ -94,8 +117,8 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
   // count in 32 bits, its sequences to fit the LDS tables and one control
   // word per unit to fit the counter prefix.
   const int64_t seg_persist = std::max<int64_t>(4, (int64_t(3) << 20) / tile_bytes);
-  // The dot family is built for one workgroup per item only.
-  const bool can_persist = p.path != PAD_PATH_DOT && sh.num_seqs <= kPersistMaxSeqs &&
+  // The dot and prefill families are built for one workgroup per item only.
+  const bool can_persist = p.path == PAD_PATH_MFMA && sh.num_seqs <= kPersistMaxSeqs &&
                            units * (ceil_div(table_keys, kTileKeys) + 1) < (int64_t(1) << 31) &&
                            units * kCtlWordStride * int64_t(sizeof(int32_t)) <= int64_t(kCounterBytes);
   if (sh.schedule == PAD_SCHED_PERSISTENT && !can_persist) return PAD_EUNSUPPORTED;
@@ -103,9 +126,20 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
                  (sh.schedule == PAD_SCHED_AUTO && can_persist && sh.num_seqs > 1 &&
                   units * std::max<int64_t>(1, sh.num_segments > 0 ? sh.num_segments : ceil_div(span_tiles, seg_persist)) >
                       slots);
+  // Prefill: about one workgroup per CU (one fits: 300 registers per
+  // lane; 256 tokens over 4096 keys in 4 segments 56.8 us, in 8 81.2 us)
+  // over the units' row blocks, segments of at least 4 tiles (one 64-key
+  // LDS tile) and a multiple of 4 tiles.  Computed from the window-free
+  // span as well, so the workspace bound below covers every window.
+  auto prefill_nseg = [&](int64_t tiles) {
+    const int64_t want = ceil_div(slots, std::max<int64_t>(1, units));
+    return std::max<int64_t>(1, std::min(want, ceil_div(tiles, 4)));
+  };
   int64_t nseg;
   if (sh.num_segments > 0) {
     nseg = sh.num_segments;
+  } else if (p.path == PAD_PATH_PREFILL) {
+    nseg = prefill_nseg(span_tiles);
   } else if (p.persistent) {
     nseg = 1;  // the balanced grid splits units by share, not by segment
   } else {
@@ -150,13 +184,15 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
   nseg = std::min<int64_t>(nseg, kMaxSegments);
   nseg = std::max<int64_t>(1, nseg);
   p.seg_tiles = int(ceil_div(span_tiles, nseg));
+  if (p.path == PAD_PATH_PREFILL && sh.num_segments == 0) p.seg_tiles = int(ceil_div(p.seg_tiles, 4) * 4);
   p.nseg = int(ceil_div(span_tiles, p.seg_tiles));
   // The row groups of one (kv head, segment) read the same tiles; the
   // kernel places them on one XCD (sharing its L2) when segments x kv
   // heads is a multiple of the 8 XCDs.  An automatic count keeps that
   // (measured at head size 512, M = 5, three row groups, 16k keys: 41
   // segments 45.0 us, 32 segments 41.6 us).
-  if (sh.num_segments == 0 && !p.persistent && p.row_groups > 1 && (int64_t(p.nseg) * sh.num_kv_heads) % 8 != 0) {
+  if (sh.num_segments == 0 && !p.persistent && p.path == PAD_PATH_MFMA && p.row_groups > 1 &&
+      (int64_t(p.nseg) * sh.num_kv_heads) % 8 != 0) {
     for (int64_t n = p.nseg - 1; n >= 1; --n) {
       const int64_t st = ceil_div(span_tiles, n);
       const int64_t n2 = ceil_div(span_tiles, st);
@@ -174,6 +210,8 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
   // A window's span may straddle one more tile than its keys fill, but no
   // unit reads more tiles than the table holds (so every window plans
   // within the window-free bound the workspace is sized for).
+  // (The prefill family's id area holds kPrefillMaxSegTiles.)
+  const int64_t seg_cap = p.path == PAD_PATH_PREFILL ? kPrefillMaxSegTiles : kMaxSegTiles;
   int64_t max_tiles = ceil_div(table_keys, kTileKeys);
   if (window > 0) max_tiles = std::min(max_tiles, ceil_div(int64_t(window) + sh.query_len - 1, kTileKeys) + 1);
   if (p.persistent) {
@@ -181,8 +219,8 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
     // longer than the LDS id area is walked in chunks.
     p.nseg = 1;
     p.seg_tiles = int(span_tiles);
-  } else if (ceil_div(max_tiles, p.nseg) > kMaxSegTiles || p.seg_tiles > kMaxSegTiles) {
-    const int64_t need = ceil_div(max_tiles, kMaxSegTiles);
+  } else if (ceil_div(max_tiles, p.nseg) > seg_cap || p.seg_tiles > seg_cap) {
+    const int64_t need = ceil_div(max_tiles, seg_cap);
     if (need > kMaxSegments) return PAD_EUNSUPPORTED;
     p.nseg = int(std::max<int64_t>(p.nseg, need));
     p.seg_tiles = int(ceil_div(span_tiles, p.nseg));
@@ -217,6 +255,8 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
   int64_t ws_nseg;
   if (sh.num_segments > 0) {
     ws_nseg = sh.num_segments;
+  } else if (p.path == PAD_PATH_PREFILL) {
+    ws_nseg = prefill_nseg(all_tiles);
   } else {
     const int64_t target = sh.num_seqs > 1 ? 2 * slots : slots;
     // A window-free span of at most 64 KiB per unit plans one segment
@@ -225,7 +265,7 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
     ws_nseg = one_seg ? 1 : std::max<int64_t>(1, target / std::max<int64_t>(1, units));
   }
   ws_nseg = std::min(ws_nseg, std::min<int64_t>(all_tiles, kMaxSegments));
-  ws_nseg = std::max<int64_t>(ws_nseg, ceil_div(ceil_div(table_keys, kTileKeys), kMaxSegTiles));
+  ws_nseg = std::max<int64_t>(ws_nseg, ceil_div(ceil_div(table_keys, kTileKeys), seg_cap));
   if (!p.persistent) ws_nseg = std::max<int64_t>(ws_nseg, p.nseg);
   p.ws_nseg = int(ws_nseg);
   const size_t S = size_t(sh.num_seqs), H = size_t(sh.num_kv_heads), D = size_t(sh.head_size);

@@ -26,8 +26,8 @@ constexpr int kTileKeys = 16;    // keys per MFMA tile (page sizes are multiples
 // call: decode and speculative verify use M <= 8; longer prefill chunks
 // take one row group per 16-row tiles of a workgroup, each reading only
 // the keys its own tokens reach.
-constexpr int kMaxQueryLen = 256;
-constexpr int kMaxRows = 4096;
+constexpr int kMaxQueryLen = 4096;
+constexpr int kMaxRows = 32768;
 constexpr int kMaxSegments = 256;
 // Longest segment in tiles: a workgroup stages its segment's block ids
 // (one int32 per tile) in LDS.
@@ -43,6 +43,18 @@ constexpr int kCtlWordStride = 32;
 constexpr int kDotMaxRows = 4;
 constexpr int kDotMaxHeadSize = 128;
 constexpr int kDotWaveCount = 4;
+// The prefill family (head sizes 64 and 128): workgroups of kPrefillWaves
+// waves take kPrefillRows GQA-packed query rows of a kv head and stream
+// its keys in LDS tiles of kPrefillKeys; a segment spans at most
+// kPrefillMaxSegTiles 16-key tiles (its block ids are staged in LDS).  The
+// planner picks the family for at least kPrefillMinRows rows per kv head
+// and kPrefillMinKeys keys (see make_plan).
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRows = 128;
+constexpr int kPrefillKeys = 64;
+constexpr int kPrefillMaxSegTiles = 1024;
+constexpr int kPrefillMinRows = 128;
+constexpr int kPrefillMinKeys = 1024;
 // Merge control words live in a fixed-size prefix of the workspace, so
 // calls of different shapes can share one workspace: partials never land
 // where any shape keeps control words, and every call leaves them zero.
@@ -60,7 +72,7 @@ constexpr int64_t kLdsPerCu = 160 << 10;  // LDS bytes of a gfx950 CU
 constexpr int waves_for(int head_size, int row_tiles) { return (void)head_size, (void)row_tiles, 4; }
 
 struct Plan {
-  int path;          // PAD_PATH_MFMA / PAD_PATH_DOT
+  int path;          // PAD_PATH_MFMA / PAD_PATH_DOT / PAD_PATH_PREFILL
   int rows;          // G*M rows per unit
   int row_tiles;     // 16-row tiles handled by each workgroup (per wave)
   int row_groups;    // workgroups splitting a unit's rows

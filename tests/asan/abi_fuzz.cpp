@@ -58,7 +58,13 @@ void check_launch(const pad::Plan& pl, const pad::Params& pr) {
   expect(pl.grid_x >= 1 && pl.grid_y >= 1 && pl.grid_y <= 65535, "grid within the launch limits");
   expect(pr.rows == sh.num_q_heads / sh.num_kv_heads * sh.query_len, "rows = G * M");
   expect(int64_t(pr.group_rows) * pr.row_groups >= pr.rows, "row groups cover the rows");
-  expect(pl.row_tiles >= 1 && pl.row_tiles <= 4, "row tiles per wave");
+  if (pl.path == PAD_PATH_PREFILL) {
+    expect(pl.row_tiles * 16 == pad::kPrefillRows && (sh.head_size == 64 || sh.head_size == 128),
+           "prefill: 128-row blocks at head size 64 or 128");
+    expect(!pl.persistent && pl.seg_tiles <= pad::kPrefillMaxSegTiles, "prefill: grid, segments within the id area");
+  } else {
+    expect(pl.row_tiles >= 1 && pl.row_tiles <= 4, "row tiles per wave");
+  }
   expect(pr.block_stride > 0 && pr.block_stride <= INT32_MAX && pr.head_stride <= INT32_MAX &&
              pr.token_stride <= INT32_MAX,
          "strides fit the kernel's 32-bit arguments");
@@ -124,7 +130,7 @@ int main(int argc, char** argv) {
     // or extreme.
     pad_shape sh{};
     sh.num_seqs = pick({0, 1, 2, 3, 65, 200, 1024, uni(1, 3000)});
-    sh.query_len = pick({1, 1, 2, 4, 8, 16, 64, 256});
+    sh.query_len = pick({1, 1, 2, 4, 8, 16, 64, 256, 2048, 4096});
     sh.num_kv_heads = pick({1, 2, 4, 8, 64});
     sh.num_q_heads = sh.num_kv_heads * pick({1, 2, 4, 8, 16, 3});
     sh.head_size = pick({64, 128, 256, 512});
@@ -135,14 +141,14 @@ int main(int argc, char** argv) {
     sh.dtype = pick({PAD_F16, PAD_BF16});
     sh.layout = pick({PAD_NHD, PAD_HND});
     sh.num_segments = pick({0, 0, 0, 1, 7, 256});
-    sh.path = pick({PAD_PATH_AUTO, PAD_PATH_AUTO, PAD_PATH_MFMA, PAD_PATH_DOT});
+    sh.path = pick({PAD_PATH_AUTO, PAD_PATH_AUTO, PAD_PATH_MFMA, PAD_PATH_DOT, PAD_PATH_PREFILL});
     sh.schedule = pick({PAD_SCHED_AUTO, PAD_SCHED_AUTO, PAD_SCHED_GRID, PAD_SCHED_PERSISTENT});
     int32_t window = pick({0, 0, 1, 100, 512, 4096, 100000});
     int32_t cus = pick({1, 80, 256, 304});
     if (uni(0, 4) == 0) {
       switch (uni(0, 13)) {
         case 0: sh.num_seqs = pick({-1, 65536, 70000}); break;
-        case 1: sh.query_len = pick({0, -3, 257, 4096}); break;
+        case 1: sh.query_len = pick({0, -3, 4097, 100000}); break;
         case 2: sh.num_kv_heads = pick({0, -1}); break;
         case 3: sh.num_q_heads += pick({1, -1}); break;
         case 4: sh.head_size = pick({0, 96, 1024}); break;

@@ -267,8 +267,8 @@ def test_window_plan_is_smaller():
     "kw,status",
     [
         (dict(query_len=0), pad.PAD_EINVAL),
-        (dict(query_len=257), pad.PAD_EUNSUPPORTED),
-        (dict(query_len=256, num_q_heads=256, num_kv_heads=8), pad.PAD_EUNSUPPORTED),  # 8192 rows
+        (dict(query_len=4097), pad.PAD_EUNSUPPORTED),
+        (dict(query_len=2048, num_q_heads=256, num_kv_heads=8), pad.PAD_EUNSUPPORTED),  # 65536 rows
         (dict(head_size=96), pad.PAD_EUNSUPPORTED),
         (dict(head_size=0), pad.PAD_EINVAL),
         (dict(page_size=8), pad.PAD_EUNSUPPORTED),
@@ -279,8 +279,10 @@ def test_window_plan_is_smaller():
         (dict(layout=5), pad.PAD_EINVAL),
         (dict(max_seq_len=2048 * 16 + 1), pad.PAD_EINVAL),
         (dict(num_segments=-1), pad.PAD_EINVAL),
-        (dict(path=3), pad.PAD_EINVAL),
         (dict(path=4), pad.PAD_EINVAL),
+        (dict(path=-1), pad.PAD_EINVAL),
+        (dict(path=pad.PAD_PATH_PREFILL, head_size=256), pad.PAD_EUNSUPPORTED),
+        (dict(path=pad.PAD_PATH_PREFILL, schedule=pad.PAD_SCHED_PERSISTENT), pad.PAD_EUNSUPPORTED),
         (dict(schedule=3), pad.PAD_EINVAL),
         (dict(schedule=-1), pad.PAD_EINVAL),
         (dict(schedule=pad.PAD_SCHED_PERSISTENT, num_seqs=1025), pad.PAD_EUNSUPPORTED),
@@ -335,7 +337,7 @@ def test_decode_validates_before_launch():
     assert _call(one_seg, out=0x5002) == pad.PAD_EINVAL
     assert _call(one_seg, bt=0x3002) == pad.PAD_EINVAL  # 4-byte alignment
     assert _call(one_seg, window=-3) == pad.PAD_EINVAL
-    assert _call(shape(query_len=257)) == pad.PAD_EUNSUPPORTED
+    assert _call(shape(query_len=4097)) == pad.PAD_EUNSUPPORTED
     split = shape(num_segments=4)
     need = plan(split)["workspace_bytes"]
     assert need > 0
@@ -402,7 +404,7 @@ def test_varlen_validation():
     assert v(shape(num_seqs=0), 0) == pad.PAD_OK
     assert v(shape(), 0) == pad.PAD_EINVAL  # missing q_start
     assert v(shape(), 0x1002) == pad.PAD_EINVAL  # misaligned q_start
-    assert v(shape(query_len=257), 0x1000) == pad.PAD_EUNSUPPORTED  # bound on the per-sequence counts
+    assert v(shape(query_len=4097), 0x1000) == pad.PAD_EUNSUPPORTED  # bound on the per-sequence counts
 
 
 def test_workspace_serves_every_window():
@@ -489,7 +491,7 @@ def test_noalloc_validates_before_launch():
     assert call(one_seg, q=0x1008) == pad.PAD_EINVAL
     assert call(one_seg, bt=0x3002) == pad.PAD_EINVAL
     assert call(one_seg, window=-1) == pad.PAD_EINVAL
-    assert call(shape(query_len=257)) == pad.PAD_EUNSUPPORTED
+    assert call(shape(query_len=4097)) == pad.PAD_EUNSUPPORTED
     # a split call with bad pointers fails on the pointers, not the device
     assert plan(shape(num_segments=4))["workspace_bytes"] > 0
     assert call(shape(num_segments=4), out=0) == pad.PAD_EINVAL
@@ -562,3 +564,36 @@ def test_workspace_covers_every_window(window, nseg):
     assert p["workspace_bytes"] <= ws, (window, nseg, p)
     if nseg:
         assert p["num_segments"] == nseg
+
+
+@pytest.mark.parametrize("M", [1, 8, 31, 32, 33, 256, 2048])
+@pytest.mark.parametrize("head_size", [64, 128, 256])
+def test_plan_prefill_family(M, head_size):
+    """AUTO takes the prefill family (head sizes 64 and 128) for at least
+    128 GQA-packed rows per kv head when its 128-row blocks fill a quarter
+    of the device, over at least 1024 keys: 128-row blocks of one workgroup
+    each, segments of a multiple of 4 tiles within the LDS id area, about
+    one workgroup per CU; batches keep it on the grid schedule."""
+    sh = shape(num_q_heads=32, num_kv_heads=8, head_size=head_size, query_len=M, max_blocks_per_seq=512)
+    p = plan(sh)
+    rows = 4 * M
+    units = 8 * -(-rows // 128)
+    if rows >= 128 and head_size in (64, 128) and 4 * units >= 256:
+        assert p["path"] == pad.PAD_PATH_PREFILL
+        assert p["row_tiles"] == 8 and p["row_groups"] == -(-rows // 128) and p["waves"] == 4
+        assert p["persistent"] == 0
+        assert p["segment_tiles"] <= 1024
+        assert p["num_segments"] == 1 or p["segment_tiles"] % 4 == 0
+        assert p["grid_x"] == p["num_segments"] * 8 * p["row_groups"]
+        assert p["workspace_bytes"] >= 0
+    else:
+        assert p["path"] == pad.PAD_PATH_MFMA
+    # the window-free workspace covers every window
+    ws = pad.pad_decode_attn_workspace_size(sh)
+    for w in (1, 100, 4096):
+        assert plan(sh, w)["workspace_bytes"] <= ws
+    # a batch of prompts stays on the grid with the prefill family
+    if rows >= 128 and head_size in (64, 128):
+        b = plan(shape(num_seqs=16, num_q_heads=32, num_kv_heads=8, head_size=head_size, query_len=M,
+                       max_blocks_per_seq=512))
+        assert b["path"] == pad.PAD_PATH_PREFILL and b["persistent"] == 0

@@ -68,3 +68,80 @@ def test_mixed_decode_and_prefill_counts():
     kv64, table, lens64 = wl.compact(c)
     ref = oracle.decode_attention_varlen(wl.as_f64(q), starts, kv64, table, lens64, c.scale, c.window, c.layout)
     check(out, ref, c.q.dtype, "mixed counts")
+
+
+# ------------------------------------------------- the prefill family
+
+PREFILL = pad.PAD_PATH_PREFILL
+FAMILY_SHAPES = [
+    # D, Hq, Hkv, P, dtype, layout
+    (128, 32, 8, 16, "bf16", wl.HND),
+    (64, 8, 2, 32, "fp16", wl.NHD),
+    (128, 12, 4, 48, "fp16", wl.HND),
+]
+FAMILY_CASES = [
+    # lens, M, window, nseg
+    ([1], 1, 0, 0),                  # one key, one row of 128
+    ([40, 1, 0, 77], 33, 0, 0),      # ragged, a padded sequence, L < M rows with no key
+    ([1000], 100, 0, 3),             # forced segments
+    ([700], 64, 50, 0),              # window shorter than the chunk
+    ([300, 513], 130, 1, 7),         # window 1: each row sees its own key only
+    ([5, 3], 8, 0, 0),               # every row past the keys for some tokens
+]
+
+
+@pytest.mark.parametrize("shape", FAMILY_SHAPES, ids=[f"d{s[0]}g{s[1] // s[2]}" for s in FAMILY_SHAPES])
+@pytest.mark.parametrize("case", FAMILY_CASES, ids=[f"c{i}" for i in range(len(FAMILY_CASES))])
+def test_prefill_family(shape, case):
+    """The prefill family forced on small, ragged and degenerate chunks
+    (NaN-poisoned page tails, empty rows of a 128-row block, windows,
+    forced segments) against the oracle."""
+    D, Hq, Hkv, P, dt, layout = shape
+    lens, M, window, nseg = case
+    spec = wl.Spec(dt, D, Hq, Hkv, P, layout, window=window)
+    say(f"prefill family: D={D} Hq={Hq} Hkv={Hkv} P={P} {dt} layout={layout} lens={lens} M={M} W={window} "
+        f"nseg={nseg}")
+    c = wl.make_case(spec, lens, M, seed=8300 + D + M + sum(lens), device=DEV, window=window)
+    out = run_gpu(c, path=PREFILL, num_segments=nseg, schedule=pad.PAD_SCHED_GRID)
+    for s, L in enumerate(lens):
+        if L == 0:
+            assert torch.all(out[s] == 0), "padded sequence must be zero"
+    check(out, oracle_out(c), c.q.dtype, "prefill family")
+
+
+def test_prefill_bench_chunk_full():
+    """The benchmark's chunk at full size (256 tokens over a 4096-key
+    context, 32/8 heads of 128, bf16) through the automatic plan, which is
+    the prefill family, against the oracle on every row."""
+    spec = wl.CONFIGS[2]
+    c = wl.make_case(spec, [4096 + 256], 256, seed=20261202 + 7, device=DEV)
+    sh = pad.make_shape(c.q, c.kv_cache, c.block_tables[0], c.layout)
+    assert pad.pad_decode_attn_plan(sh)["path"] == PREFILL
+    say("prefill bench chunk: 256 tokens over 4096 keys, config 2 shapes")
+    check(run_gpu(c), oracle_out(c), c.q.dtype, "prefill bench chunk")
+
+
+def test_prefill_2048_token_prompt():
+    """A 2048-token prompt (no earlier context) in one call: 8192 GQA-packed
+    rows per kv head, 64 row blocks.  Sampled tokens (the first, the last
+    and 62 spread between) of every head against the oracle's own
+    gather-and-softmax steps."""
+    spec = wl.CONFIGS[2]
+    M = 2048
+    c = wl.make_case(spec, [M], M, seed=8400, device=DEV)
+    say("prefill prompt: 2048 tokens, config 2 shapes")
+    out = run_gpu(c)
+    assert torch.isfinite(out).all()
+    kv64, table, lens = wl.compact(c)
+    q64 = wl.as_f64(c.q)
+    G = spec.num_q_heads // spec.num_kv_heads
+    toks = sorted(set([0, M - 1] + list(np.linspace(1, M - 2, 62).astype(int))))
+    ref = np.zeros((len(toks), spec.num_q_heads, spec.head_size))
+    for kvh in range(spec.num_kv_heads):
+        K_all, V_all = oracle.gather_kv(kv64, c.layout, table[0], kvh, range(M))
+        for i, m in enumerate(toks):
+            lo, hi = oracle.key_bounds(M, M, m, 0)
+            for g in range(G):
+                h = kvh * G + g
+                ref[i, h] = oracle.attention._softmax_attend(q64[0, m, h], K_all[lo:hi + 1], V_all[lo:hi + 1], c.scale)
+    check(out[0, toks], ref, c.q.dtype, "2048-token prompt, sampled tokens")
