@@ -44,12 +44,13 @@ constexpr int kDotMaxRows = 4;
 constexpr int kDotMaxHeadSize = 128;
 constexpr int kDotWaveCount = 4;
 // The prefill family (head sizes 64 and 128): workgroups of kPrefillWaves
-// waves take kPrefillRows GQA-packed query rows of a kv head and stream
-// its keys in LDS tiles of kPrefillKeys; a segment spans at most
+// waves (two per 32-row slab) take kPrefillRows GQA-packed query rows of a
+// kv head and stream its keys in LDS tiles of kPrefillKeys; a segment
+// spans at most
 // kPrefillMaxSegTiles 16-key tiles (its block ids are staged in LDS).  The
 // planner picks the family for at least kPrefillMinRows rows per kv head
 // and kPrefillMinKeys keys (see make_plan).
-constexpr int kPrefillWaves = 4;
+constexpr int kPrefillWaves = 8;
 constexpr int kPrefillRows = 128;
 constexpr int kPrefillKeys = 64;
 constexpr int kPrefillMaxSegTiles = 1024;

@@ -7,10 +7,12 @@
 //
 // One workgroup serves one (sequence, kv head, 128-row block, key
 // segment): the kv head's G * M query rows are GQA-packed (row = token * G
-// + head) and cut into blocks of 128; each of its four waves owns 32 rows.
-// Per 64-key tile, staged once in LDS for all four waves (double-buffered:
-// the next tile's loads are in registers while the current one is
-// computed), a wave
+// + head) and cut into blocks of 128.  Its eight waves form four slabs of
+// 32 rows; the two waves of a slab take the two 32-key halves of every
+// 64-key tile (two independent waves per SIMD, so one's softmax overlaps
+// the other's products) and are combined at the end.  Per tile, staged
+// once in LDS for all eight waves (double-buffered, its loads issued two
+// tiles ahead into registers), a wave
 //   * forms S^T = K Q^T with v_mfma_f32_32x32x16 (K rows from LDS as the A
 //     operand, its query rows as the B operand, kept in registers), which
 //     leaves each lane 16 keys of one query row per 32-key block -- the row
@@ -60,7 +62,10 @@ struct Mfma32<_Float16> {
 
 template <int D>
 struct PfShape {
-  static constexpr int kThreads = kPrefillWaves * 64;
+  static constexpr int NW = kPrefillWaves;
+  static constexpr int kThreads = NW * 64;
+  static constexpr int kHalves = NW / 4;   // waves per 32-row slab (key halves of a tile)
+  static constexpr int KB = 2 / kHalves;   // 32-key blocks of a tile per wave
   static constexpr int kRows = kPrefillRows;   // query rows of a workgroup
   static constexpr int kKeys = kPrefillKeys;   // keys of an LDS tile
   static constexpr int kStride = D + 8;        // elements per LDS row (16-byte pad: spreads the banks)
@@ -75,6 +80,10 @@ struct PfShape {
   static constexpr int kChunksPerKey = 2 * D / 8;  // 16-byte chunks of a key's K and V rows
   static constexpr int kPerThread = kKeys * kChunksPerKey / kThreads;
   static_assert(kPerThread * kThreads == kKeys * kChunksPerKey, "tile chunks split evenly over the threads");
+  static_assert(NW == 4 || NW == 8, "four slabs of 32 rows, one or two waves each");
+  // The pair exchange (running max and sum of each half) after the loop
+  // uses the block-id area, past the combine area.
+  static_assert(kIdsOff >= CB::kBytes && kPrefillMaxSegTiles >= 4 * kRows, "exchange area");
 };
 
 template <typename T, int D>
@@ -89,6 +98,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(Params p
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;  // this lane's query row in the wave, its lane half
+  const int slab = wave & 3, half = wave >> 2;  // the wave's 32 rows, its 32-key blocks of a tile
 
   // Work item: the row blocks of the latest tokens (the longest key ranges)
   // first.
@@ -132,7 +142,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(Params p
 
   // This lane's query row: its B operand chunks (head-dim 16 st + 8 h ..
   // + 7 of step st), position and window start; rows past G*M see nothing.
-  const int r = row0 + wave * 32 + n;
+  const int r = row0 + slab * 32 + n;
   i32x4 qop[DS];
   if (r < rows) {
     const T* qrow = static_cast<const T*>(p.q) +
@@ -164,6 +174,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(Params p
   // wave-uniform (the block id of a group outside the segment is clamped
   // to one inside it; such keys are zeroed when the tile is stored).
   constexpr int kKeysPerU = NT / (D / 4);
+  static_assert(kKeysPerU == 16 || kKeysPerU == 32, "a thread's chunk u covers one or two 16-key groups");
   const int key_t = tid / (D / 4), part = (tid / (D / 8)) & 1, col = tid % (D / 8);
   // Two register stages: a tile's loads go out two tiles ahead of its
   // products, every chunk loaded (a fixed count per tile keeps the
@@ -181,9 +192,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(Params p
 #pragma unroll
     for (int u = 0; u < SH::kPerThread; ++u) {
       const int key = kKeysPerU * u + key_t;
+      // the key's 16-key group: u (16 keys per u) or one of u's two groups
+      const int64_t gb =
+          kKeysPerU == 16 ? gbase[u & 3] : ((key_t & 16) ? gbase[(2 * u + 1) & 3] : gbase[(2 * u) & 3]);
       stage[sl][u] = *reinterpret_cast<const i32x4*>(
-          KVh + (gbase[(kKeysPerU * u) >> 4] + int64_t(key & 15) * p.token_stride + part * D) * int64_t(sizeof(T)) +
-          16 * col);
+          KVh + (gb + int64_t(key & 15) * p.token_stride + part * D) * int64_t(sizeof(T)) + 16 * col);
     }
   };
   // Keys outside [key_lo, key_hi) may hold anything (even NaN): zeros go to
@@ -223,29 +236,31 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(Params p
     const uint16_t* kt_lds = kbuf(b);
     const uint16_t* vt_lds = kbuf(b) + SH::kTileElems;
     const int key0 = kt * SH::kKeys;
-    // S^T of the two 32-key blocks (independent product chains).
-    f32x16 sc[2];
+    // S^T of this wave's 32-key blocks kb = half * KB + j (independent
+    // product chains).
+    constexpr int KB = SH::KB;
+    f32x16 sc[KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int j = 0; j < KB; ++j) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sc[kb][v] = 0.f;
-      const uint16_t* kr = kt_lds + (kb * 32 + n) * SH::kStride + 8 * h;
+      for (int v = 0; v < 16; ++v) sc[j][v] = 0.f;
+      const uint16_t* kr = kt_lds + ((half * KB + j) * 32 + n) * SH::kStride + 8 * h;
 #pragma unroll
-      for (int st = 0; st < DS; ++st) sc[kb] = MM::mma(*reinterpret_cast<const i32x4*>(kr + 16 * st), qop[st], sc[kb]);
+      for (int st = 0; st < DS; ++st) sc[j] = MM::mma(*reinterpret_cast<const i32x4*>(kr + 16 * st), qop[st], sc[j]);
     }
     // Value v of block kb is key key0 + 32 kb + 8 (v / 4) + 4 h + v % 4.
     const bool edge = !(key0 >= full_lo && key0 + SH::kKeys - 1 <= full_hi);
     float tmax = kNegInf;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int j = 0; j < KB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float x = sc[kb][v] * p.scale_log2;
+        float x = sc[j][v] * p.scale_log2;
         if (edge) {
-          const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
+          const int key = key0 + 32 * (half * KB + j) + 8 * (v >> 2) + 4 * h + (v & 3);
           if (key < lo_r || key > qpos || key < key_lo || key >= key_hi) x = kNegInf;
         }
-        sc[kb][v] = x;
+        sc[j][v] = x;
         tmax = fmaxf(tmax, x);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
@@ -254,17 +269,17 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(Params p
     const float m_use = m_new == kNegInf ? 0.f : m_new;
     const float alpha = move ? fast_exp2(m_run - m_use) : 1.f;
     float psum = 0.f;
-    i32x4 pb[2][2];
+    i32x4 pb[KB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int j = 0; j < KB; ++j)
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p0 = fast_exp2(sc[kb][8 * sub + 2 * j] - m_use);
-          const float p1 = fast_exp2(sc[kb][8 * sub + 2 * j + 1] - m_use);
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(sc[j][8 * sub + 2 * e] - m_use);
+          const float p1 = fast_exp2(sc[j][8 * sub + 2 * e + 1] - m_use);
           psum += p0 + p1;
-          pb[kb][sub][j] = int(uint32_t(MF::bits(p0)) | (uint32_t(MF::bits(p1)) << 16));
+          pb[j][sub][e] = int(uint32_t(MF::bits(p0)) | (uint32_t(MF::bits(p1)) << 16));
         }
     l_run = l_run * alpha + psum;
     m_run = m_new;
@@ -279,19 +294,19 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(Params p
     const int g4 = lane >> 4, i16 = lane & 15;
     const uint16_t* vtr = vt_lds + (4 * h + (i16 >> 2)) * SH::kStride + 16 * (g4 & 1) + 4 * (i16 & 3);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int j = 0; j < KB; ++j)
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const uint16_t* a = vtr + (32 * kb + 16 * sub) * SH::kStride + 32 * db;
+          const uint16_t* a = vtr + (32 * (half * KB + j) + 16 * sub) * SH::kStride + 32 * db;
           const uint64_t lo = __builtin_bit_cast(
               uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a)));
           const uint64_t hi = __builtin_bit_cast(
               uint64_t,
               __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a + 8 * SH::kStride)));
           const i32x4 va = {int(uint32_t(lo)), int(uint32_t(lo >> 32)), int(uint32_t(hi)), int(uint32_t(hi >> 32))};
-          acc[db] = MM::mma(va, pb[kb][sub], acc[db]);
+          acc[db] = MM::mma(va, pb[j][sub], acc[db]);
         }
     if (kt + 1 < kt1) store_tile(kt + 1, b ^ 1, b ^ 1);
     __syncthreads();
@@ -302,22 +317,61 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(Params p
     step(kt + 1, 1);
   }
 
-  // Rows of this wave: the running sum over both lane halves, then the
-  // accumulator columns (value v of block db is column 32 db + 8 (v / 4) +
-  // 4 h + v % 4) into slot 0 of the combine area, which overlays the tile
-  // buffers.
+  // Rows of this wave: the running sum over both lane halves; with two key
+  // halves per slab, the pair's maxima and sums meet in the block-id area
+  // (dead now) and each wave rescales its accumulator to the pair's
+  // maximum.  Then the accumulator columns (value v of block db is column
+  // 32 db + 8 (v / 4) + 4 h + v % 4) go to slot 0 of the combine area,
+  // which overlays the tile buffers: the second half's rows first, added
+  // into the first half's in fixed order.
   l_run += __shfl_xor(l_run, 32);
-  const int rr = wave * 32 + n;
+  const int rr = slab * 32 + n;
   float* slot = CB::acc(lds) + rr * CB::kAccStride + 4 * h;
+  auto put = [&]() {
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      *reinterpret_cast<f32x4*>(slot + 32 * db + 8 * q4) =
-          f32x4{acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2], acc[db][4 * q4 + 3]};
-  if (h == 0) {
-    CB::ms(lds)[rr] = m_run;
-    CB::ls(lds)[rr] = l_run;
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(slot + 32 * db + 8 * q4) =
+            f32x4{acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2], acc[db][4 * q4 + 3]};
+  };
+  if constexpr (SH::kHalves == 1) {
+    put();
+    if (h == 0) {
+      CB::ms(lds)[rr] = m_run;
+      CB::ls(lds)[rr] = l_run;
+    }
+  } else {
+    float* xm = reinterpret_cast<float*>(lds + SH::kIdsOff);  // [2][kRows]
+    float* xl = xm + 2 * SH::kRows;                          // [2][kRows]
+    if (h == 0) {
+      xm[half * SH::kRows + rr] = m_run;
+      xl[half * SH::kRows + rr] = l_run;
+    }
+    __syncthreads();
+    const float m0 = xm[rr], m1 = xm[SH::kRows + rr];
+    const float ms = fmaxf(m0, m1);
+    const float mu = ms == kNegInf ? 0.f : ms;
+    const float f = fast_exp2(m_run - mu);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] *= f;
+    if (half == 0 && h == 0) {
+      CB::ms(lds)[rr] = ms;
+      CB::ls(lds)[rr] = xl[rr] * fast_exp2(m0 - mu) + xl[SH::kRows + rr] * fast_exp2(m1 - mu);
+    }
+    if (half == 1) put();
+    __syncthreads();
+    if (half == 0) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 o = *reinterpret_cast<const f32x4*>(slot + 32 * db + 8 * q4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[db][4 * q4 + e] += o[e];
+        }
+      put();
+    }
   }
   __syncthreads();
   finish<T, D, SH::kRows / 16, 1, 1, NT>(p, lds, s, kvh, row0, wg_rows, fr, SH::kBytes);
