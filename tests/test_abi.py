@@ -580,7 +580,7 @@ def test_plan_prefill_family(M, head_size):
     units = 8 * -(-rows // 128)
     if rows >= 128 and head_size in (64, 128) and 4 * units >= 256:
         assert p["path"] == pad.PAD_PATH_PREFILL
-        assert p["row_tiles"] == 8 and p["row_groups"] == -(-rows // 128) and p["waves"] == 4
+        assert p["row_tiles"] == 8 and p["row_groups"] == -(-rows // 128) and p["waves"] == 8
         assert p["persistent"] == 0
         assert p["segment_tiles"] <= 1024
         assert p["num_segments"] == 1 or p["segment_tiles"] % 4 == 0
