@@ -501,9 +501,10 @@ def octave_main(args) -> int:
 def prefill_main(args) -> int:
     """A prefill chunk through the same entry point: 256 new tokens over a
     4096-key context, the default workload's shapes (1024 GQA-packed rows
-    per kv head in 16 row groups, each reading only the keys its tokens
-    reach).  Arithmetic intensity ~1000 flop/byte: bound by the matrix
-    cores, reported against the dense bf16 MFMA peak."""
+    per kv head; the planner takes the prefill family: eight 128-row
+    blocks, each reading only the keys its tokens reach).  Arithmetic
+    intensity ~1000 flop/byte: bound by the matrix cores, reported against
+    the dense bf16 MFMA peak."""
     import torch
 
     import workloads as wl
