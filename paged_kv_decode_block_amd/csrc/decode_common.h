@@ -423,12 +423,15 @@ __device__ __forceinline__ SegSplit split_of(const Params& p, int L, int M, int 
   return r;
 }
 
-// Balanced persistent grid (batched decode).  The 16-key tiles of every
-// unit -- (sequence, row group, kv head) in that order, each its key range
-// [t_lo, t_hi) of split_of -- are laid end to end, T tiles in all, and
-// workgroup b of the Gs = min(G, T) first of the G = gridDim.x workgroups
-// (one per CU) takes the contiguous share [b T / Gs, (b + 1) T / Gs): every
-// CU reads the same number of tiles, whatever the lengths.  A unit inside one share is computed
+// Balanced persistent grid (batched decode).  Every unit -- (sequence, row
+// group, kv head) in that order -- takes kUnitLeadTiles lead positions (its
+// item's fixed cost) and then one position per 16-key tile of its key range
+// [t_lo, t_hi) of split_of; the units are laid end to end, T positions in
+// all, and workgroup b of the Gs = min(G, T) first of the G = gridDim.x
+// workgroups (one per CU) takes the contiguous share [b T / Gs, (b + 1) T /
+// Gs): every CU gets the same work, tiles plus item costs, whatever the
+// lengths.  A share computes the tiles among its positions; lead positions
+// alone make no item.  A unit inside one share is computed
 // whole and written directly.  A unit cut by share boundaries is computed
 // as one work item per share it meets; each item publishes a partial and
 // the last to arrive merges them in share order (fixed, so the result is
@@ -458,7 +461,7 @@ __device__ __forceinline__ void balanced_loop(const Params& p, unsigned char* ld
     if (L > 0 && M > 0) {
       for (int rg = 0; rg < p.row_groups; ++rg) {
         const SegSplit sp = split_of(p, L, M, rg);
-        if (sp.n_live > 0) n += sp.t_hi - sp.t_lo;
+        if (sp.n_live > 0) n += kUnitLeadTiles + sp.t_hi - sp.t_lo;
       }
     }
     sm_cnt[i] = n * p.num_kv_heads;
@@ -495,15 +498,16 @@ __device__ __forceinline__ void balanced_loop(const Params& p, unsigned char* ld
       for (int kvh = 0; kvh < p.num_kv_heads; ++kvh) zero(s, kvh, rg, M);
   }
   const int T = sm_pref[S];
-  // Shares of the first min(G, T) workgroups: each holds at least one tile,
-  // so every share a unit meets has an item that arrives.
+  // Shares of the first min(G, T) workgroups, each at least one position.
+  // A share meets a unit when it holds one of the unit's tiles (not only
+  // lead positions); each share a unit meets has an item that arrives.
   const int Gs = min(G, T);
   if (b >= Gs) return;
   const int start = int(int64_t(b) * T / Gs), end = int(int64_t(b + 1) * T / Gs);
-  // Share holding tile t: the largest b' with floor(b' T / Gs) <= t.
+  // Share holding position t: the largest b' with floor(b' T / Gs) <= t.
   auto owner = [&](int t) { return int((int64_t(t + 1) * Gs - 1) / T); };
   auto share_end = [&](int bb) { return int(int64_t(bb + 1) * T / Gs); };
-  // Sequence holding tile `start`: the last s with sm_pref[s] <= start.
+  // Sequence holding position `start`: the last s with sm_pref[s] <= start.
   int lo = 0, hi = S - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -514,19 +518,25 @@ __device__ __forceinline__ void balanced_loop(const Params& p, unsigned char* ld
     const int L = sm_len[s];
     const int M = L > 0 ? seq_queries(p, s).m : 0;
     if (M == 0) continue;
-    int ub = sm_pref[s];  // first tile of the unit being visited
+    int ub = sm_pref[s];  // first position of the unit being visited
     for (int rg = 0; rg < p.row_groups && pos < end; ++rg) {
       const SegSplit sp = split_of(p, L, M, rg);
       if (sp.n_live == 0) continue;
       const int nu = sp.t_hi - sp.t_lo;
-      for (int kvh = 0; kvh < p.num_kv_heads && pos < end; ++kvh, ub += nu) {
-        const int ue = ub + nu;
+      for (int kvh = 0; kvh < p.num_kv_heads && pos < end; ++kvh, ub += kUnitLeadTiles + nu) {
+        // Positions [ub, ub + lead) stand for the item's fixed cost; the
+        // unit's tiles are positions [rb, ue).
+        const int rb = ub + kUnitLeadTiles, ue = rb + nu;
         if (ue <= pos) continue;
-        const int f0 = max(ub, pos), f1 = min(ue, end);
-        const int b0 = owner(ub), b1 = owner(ue - 1);
+        const int f0 = max(rb, pos), f1 = min(ue, end);
+        if (f0 >= f1) {  // the share ends among the lead positions
+          pos = end;
+          break;
+        }
+        const int b0 = owner(rb), b1 = owner(ue - 1);
         Frag f;
-        f.ts = sp.t_lo + (f0 - ub);
-        f.te = sp.t_lo + (f1 - ub);
+        f.ts = sp.t_lo + (f0 - rb);
+        f.te = sp.t_lo + (f1 - rb);
         f.n_parts = b1 - b0 + 1;
         f.merge_slices = 1;
         f.slot = f1 == end ? b : G + b;

@@ -119,7 +119,7 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
   const int64_t seg_persist = std::max<int64_t>(4, (int64_t(3) << 20) / tile_bytes);
   // The dot and prefill families are built for one workgroup per item only.
   const bool can_persist = p.path == PAD_PATH_MFMA && sh.num_seqs <= kPersistMaxSeqs &&
-                           units * (ceil_div(table_keys, kTileKeys) + 1) < (int64_t(1) << 31) &&
+                           units * (ceil_div(table_keys, kTileKeys) + 1 + kUnitLeadTiles) < (int64_t(1) << 31) &&
                            units * kCtlWordStride * int64_t(sizeof(int32_t)) <= int64_t(kCounterBytes);
   if (sh.schedule == PAD_SCHED_PERSISTENT && !can_persist) return PAD_EUNSUPPORTED;
   p.persistent = sh.schedule == PAD_SCHED_PERSISTENT ||

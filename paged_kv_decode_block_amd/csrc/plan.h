@@ -63,6 +63,13 @@ constexpr size_t kCounterBytes = size_t(1) << 20;
 // Balanced persistent grid (batched decode): at most this many sequences
 // (its LDS tables).
 constexpr int kPersistMaxSeqs = 1024;
+// Balanced persistent grid: each unit also counts as this many tiles of
+// work when the batch is cut into equal shares, for the fixed cost of an
+// item (its first cold loads, combine, publish, arrival and merge) that a
+// share pays once per unit it meets.  Batch workload (64 sequences of
+// 512..16384 keys, head size 256), graph-timed: 229.4 us at 0, 225.9 at 3,
+// 223.2 at 6, 222.7 at 8, 219-221 from 10 to 24.
+constexpr int kUnitLeadTiles = 12;
 constexpr int64_t kLdsPerCu = 160 << 10;  // LDS bytes of a gfx950 CU
 
 // Waves per workgroup.  Four for every shape: on one bf16 sequence with

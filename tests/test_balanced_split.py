@@ -1,11 +1,14 @@
 """Host check of the balanced persistent grid's work split (no GPU).
 
-The device code (balanced_loop in csrc/decode_common.h) lays the 16-key
-tiles of every unit end to end and gives workgroup b of Gs = min(G, T) the
-share [b T / Gs, (b + 1) T / Gs).  This test restates that arithmetic and
-checks, over seeded batches, the properties the kernel relies on:
+The device code (balanced_loop in csrc/decode_common.h) lays every unit
+with tiles end to end as `lead` positions (the item's fixed cost) followed
+by one position per 16-key tile, and gives workgroup b of Gs = min(G, T)
+the share [b T / Gs, (b + 1) T / Gs) of the T positions.  This test
+restates that arithmetic and checks, over seeded batches and lead counts,
+the properties the kernel relies on:
 * every tile of every unit is computed by exactly one item;
-* every share holds at least one tile (so every counted item arrives);
+* every share holds at least one position, and a share meets a unit only
+  where it holds one of its tiles (so every counted item arrives);
 * a unit cut by share boundaries has one item per share it meets, and the
   count the items carry (n_parts) is that number;
 * the slots the items publish to are exactly the slots the merge reads, in
@@ -18,20 +21,20 @@ import numpy as np
 import pytest
 
 
-def split(unit_tiles, G):
-    """Items of the balanced split: (unit, t0, t1, n_parts, slot, first, last)."""
-    T = int(sum(unit_tiles))
+def split(unit_tiles, G, lead=0):
+    """Items of the balanced split: (unit, t0, t1, n_parts, slot, first, last, share)."""
+    span = [lead + int(t) if t > 0 else 0 for t in unit_tiles]
+    T = int(sum(span))
     Gs = min(G, T)
     items = []
     if T == 0:
         return items, Gs
     owner = lambda t: ((t + 1) * Gs - 1) // T  # noqa: E731
     share_end = lambda bb: (bb + 1) * T // Gs  # noqa: E731
-    pref = np.concatenate([[0], np.cumsum(unit_tiles)]).astype(np.int64)
+    pref = np.concatenate([[0], np.cumsum(span)]).astype(np.int64)
     for b in range(Gs):
         start, end = b * T // Gs, (b + 1) * T // Gs
-        assert end > start, "every share holds a tile"
-        # first unit holding tile `start`: the last u with pref[u] <= start and tiles
+        assert end > start, "every share holds a position"
         pos = start
         for u in range(len(unit_tiles)):
             ub, ue = int(pref[u]), int(pref[u + 1])
@@ -39,18 +42,22 @@ def split(unit_tiles, G):
                 continue
             if pos >= end:
                 break
-            f0, f1 = max(ub, pos), min(ue, end)
-            b0, b1 = owner(ub), owner(ue - 1)
+            rb = ub + lead  # first tile position
+            f0, f1 = max(rb, pos), min(ue, end)
+            if f0 >= f1:  # the share ends among the lead positions
+                break
+            b0, b1 = owner(rb), owner(ue - 1)
             n = b1 - b0 + 1
             slot = b if f1 == end else G + b
             last = b1 if ue == share_end(b1) else G + b1
-            items.append((u, f0 - ub, f1 - ub, n, slot, b0, last, b))
+            items.append((u, f0 - rb, f1 - rb, n, slot, b0, last, b))
             pos = f1
     return items, Gs
 
 
+@pytest.mark.parametrize("lead", [0, 1, 6, 40])
 @pytest.mark.parametrize("seed", range(40))
-def test_balanced_split_invariants(seed):
+def test_balanced_split_invariants(seed, lead):
     r = np.random.default_rng(seed)
     G = int(r.choice([1, 3, 8, 256]))
     U = int(r.integers(1, 300))
@@ -64,8 +71,8 @@ def test_balanced_split_invariants(seed):
         tiles[r.integers(0, U)] = int(r.integers(1, 5000))  # one long unit
     else:
         tiles = r.integers(30, 1100, U)
-    items, Gs = split(tiles, G)
-    T = int(tiles.sum())
+    items, Gs = split(tiles, G, lead)
+    T = int(sum(lead + int(t) for t in tiles if t > 0))
     # every tile of every unit exactly once
     cover = [np.zeros(int(t), dtype=np.int64) for t in tiles]
     for u, t0, t1, *_ in items:
@@ -97,7 +104,7 @@ def test_balanced_split_invariants(seed):
         if it[3] > 1:
             per_wg[it[7]] = per_wg.get(it[7], 0) + 1
     assert all(v <= 2 for v in per_wg.values())
-    # shares are equal to within one tile
+    # shares are equal to within one position
     if T:
         sizes = [(b + 1) * T // Gs - b * T // Gs for b in range(Gs)]
         assert max(sizes) - min(sizes) <= 1 and min(sizes) >= 1
