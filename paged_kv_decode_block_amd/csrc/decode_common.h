@@ -31,6 +31,13 @@ struct Mfma<__bf16> {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(x4, a), __builtin_bit_cast(x4, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint16_t bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x)); }
+  // Two values rounded to bf16 and packed (a in the low half): one
+  // conversion instruction for the pair.
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, b2));
+  }
 };
 
 template <>
@@ -44,6 +51,11 @@ struct Mfma<_Float16> {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(x4, a), __builtin_bit_cast(x4, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint16_t bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, h2));
+  }
 };
 
 constexpr float kNegInf = -__builtin_huge_valf();

@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "decode_common.h"
 #include "kernels.h"
@@ -72,7 +73,7 @@ struct PfShape {
   static constexpr int kTileElems = kKeys * kStride;
   static constexpr int kBufBytes = 2 * kTileElems * 2;  // the K and V rows of one tile
   static constexpr int kIdsOff = 2 * kBufBytes;         // after two buffers
-  static constexpr int kLoopBytes = kIdsOff + kPrefillMaxSegTiles * 4;
+  static constexpr int kLoopBytes = kIdsOff + kPrefillMaxSegTiles * 8;
   using CB = Combine<D, kRows / 16, 1>;
   static constexpr int kBytes = (kLoopBytes > CB::kBytes ? kLoopBytes : CB::kBytes) + 16;
   static constexpr int DS = D / 16;  // 16-element steps of QK^T
@@ -134,21 +135,31 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(Params p
   fr.ctl = p.ws_cnt + ((int64_t(s) * p.num_kv_heads + kvh) * p.row_groups + rg) * p.merge_slices * kCtlStride;
   const int ts = fr.ts, te = fr.te;
 
-  // The segment's block ids, one per 16-key tile (the planner keeps a
-  // segment within kPrefillMaxSegTiles of them).
+  // Where each 16-key tile of the segment starts: the element offset of
+  // its first key's K row in the kv head's cache (page and in-page token),
+  // once per tile here rather than per load (the planner keeps a segment
+  // within kPrefillMaxSegTiles tiles).
   const int32_t* table = p.block_table + int64_t(s) * p.max_blocks;
-  int* sm_ids = reinterpret_cast<int*>(lds + SH::kIdsOff);
-  for (int t = tid; t < te - ts; t += NT) sm_ids[t] = table[(t + ts) * 16 / p.page_size];
+  int64_t* sm_off = reinterpret_cast<int64_t*>(lds + SH::kIdsOff);
+  for (int t = tid; t < te - ts; t += NT) {
+    const int key = (t + ts) * 16;
+    sm_off[t] = int64_t(table[key / p.page_size]) * p.block_stride + int64_t(key % p.page_size) * p.token_stride;
+  }
 
   // This lane's query row: its B operand chunks (head-dim 16 st + 8 h ..
   // + 7 of step st), position and window start; rows past G*M see nothing.
+  // The scale's sign goes into the query rows (an exact sign flip), so
+  // the scores' exp2-domain values are x * |scale log2 e|: the largest raw
+  // score of a row gives the largest scaled one.
   const int r = row0 + slab * 32 + n;
+  const float sl2 = fabsf(p.scale_log2);
+  const int qsign = p.scale_log2 < 0.f ? int(0x80008000u) : 0;
   i32x4 qop[DS];
   if (r < rows) {
     const T* qrow = static_cast<const T*>(p.q) +
                     ((int64_t(sq.first) + r / p.group) * p.num_q_heads + kvh * p.group + r % p.group) * D + 8 * h;
 #pragma unroll
-    for (int st = 0; st < DS; ++st) qop[st] = *reinterpret_cast<const i32x4*>(qrow + 16 * st);
+    for (int st = 0; st < DS; ++st) qop[st] = *reinterpret_cast<const i32x4*>(qrow + 16 * st) ^ qsign;
   } else {
 #pragma unroll
     for (int st = 0; st < DS; ++st) qop[st] = i32x4{0, 0, 0, 0};
@@ -164,39 +175,46 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(Params p
   const int lo_max = p.window > 0 ? max(0, qpos_max - p.window + 1) : 0;
   const int key_lo = max(16 * ts, lo_min), key_hi = min(16 * te, L);
   const int full_lo = max(16 * ts, lo_max), full_hi = min(min(16 * te, L) - 1, qpos_min);
+  // This row's visible keys in the segment: [vis_lo, vis_hi), empty for a
+  // row past the query rows.
+  const int vis_lo = max(lo_r, key_lo), vis_hi = min(qpos + 1, key_hi);
+  const uint32_t vis_span = uint32_t(max(vis_hi - vis_lo, 0));
 
   const unsigned char* KVh =
       static_cast<const unsigned char*>(p.kv) + int64_t(kvh) * p.head_stride * int64_t(sizeof(T));
   auto kbuf = [&](int b) { return reinterpret_cast<uint16_t*>(lds + b * SH::kBufBytes); };
   // Chunk u of this thread in a tile: key kKeysPerU u + key_t of the tile,
   // its K row (part 0) or V row, 16 bytes at column chunk col.  A tile's
-  // four 16-key groups each lie in one page: their element offsets are
-  // wave-uniform (the block id of a group outside the segment is clamped
-  // to one inside it; such keys are zeroed when the tile is stored).
+  // four 16-key groups each lie in one page: their offsets are
+  // wave-uniform (a group outside the segment is clamped to one inside it;
+  // such keys are zeroed when the tile is stored), and a chunk sits at a
+  // fixed byte offset from its group's first K row.
   constexpr int kKeysPerU = NT / (D / 4);
   static_assert(kKeysPerU == 16 || kKeysPerU == 32, "a thread's chunk u covers one or two 16-key groups");
   const int key_t = tid / (D / 4), part = (tid / (D / 8)) & 1, col = tid % (D / 8);
+  const uint32_t chunk_off =
+      (uint32_t(key_t & 15) * uint32_t(p.token_stride) + uint32_t(part * D)) * uint32_t(sizeof(T)) + 16u * col;
   // Two register stages: a tile's loads go out two tiles ahead of its
   // products, every chunk loaded (a fixed count per tile keeps the
   // compiler's wait counts exact, so storing a tile waits only for its own
   // loads).
   i32x4 stage[2][SH::kPerThread];
   auto load_tile = [&](int kt, int sl) {
-    int64_t gbase[4];
+    const unsigned char* gbase[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int t16 = min(max(4 * kt + g, ts), te - 1);
-      const int blk = __builtin_amdgcn_readfirstlane(sm_ids[t16 - ts]);
-      gbase[g] = int64_t(blk) * p.block_stride + int64_t((16 * t16) % p.page_size) * p.token_stride;
+      const int64_t off = sm_off[t16 - ts];
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(int(uint32_t(uint64_t(off))));
+      const uint32_t hi = __builtin_amdgcn_readfirstlane(int(uint32_t(uint64_t(off) >> 32)));
+      gbase[g] = KVh + int64_t((uint64_t(hi) << 32) | lo) * int64_t(sizeof(T));
     }
 #pragma unroll
     for (int u = 0; u < SH::kPerThread; ++u) {
-      const int key = kKeysPerU * u + key_t;
       // the key's 16-key group: u (16 keys per u) or one of u's two groups
-      const int64_t gb =
+      const unsigned char* gb =
           kKeysPerU == 16 ? gbase[u & 3] : ((key_t & 16) ? gbase[(2 * u + 1) & 3] : gbase[(2 * u) & 3]);
-      stage[sl][u] = *reinterpret_cast<const i32x4*>(
-          KVh + (gb + int64_t(key & 15) * p.token_stride + part * D) * int64_t(sizeof(T)) + 16 * col);
+      stage[sl][u] = *reinterpret_cast<const i32x4*>(gb + chunk_off);
     }
   };
   // Keys outside [key_lo, key_hi) may hold anything (even NaN): zeros go to
@@ -249,41 +267,65 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(Params p
       for (int st = 0; st < DS; ++st) sc[j] = MM::mma(*reinterpret_cast<const i32x4*>(kr + 16 * st), qop[st], sc[j]);
     }
     // Value v of block kb is key key0 + 32 kb + 8 (v / 4) + 4 h + v % 4.
-    const bool edge = !(key0 >= full_lo && key0 + SH::kKeys - 1 <= full_hi);
-    float tmax = kNegInf;
-#pragma unroll
-    for (int j = 0; j < KB; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float x = sc[j][v] * p.scale_log2;
-        if (edge) {
-          const int key = key0 + 32 * (half * KB + j) + 8 * (v >> 2) + 4 * h + (v & 3);
-          if (key < lo_r || key > qpos || key < key_lo || key >= key_hi) x = kNegInf;
-        }
-        sc[j][v] = x;
-        tmax = fmaxf(tmax, x);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const bool move = tmax > m_run + kMaxSlack;
-    const float m_new = move ? tmax : m_run;
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = move ? fast_exp2(m_run - m_use) : 1.f;
-    float psum = 0.f;
+    // The online softmax; on tiles with a key some row may not see
+    // (wave-uniform), with those scores masked: -inf for the maximum and
+    // a zero weight whatever the scale.  p = 2^(x |scale log2 e| - m).
+    // The two variants are separate code, so the unmasked tiles run no
+    // mask arithmetic.
+    float alpha = 1.f, psum = 0.f;
+    bool moved = false;
     i32x4 pb[KB][2];
+    auto softmax = [&](auto masked_t) {
+      constexpr bool kMasked = decltype(masked_t)::value;
+      if constexpr (kMasked) {
+        // The row sees keys [vis_lo, vis_hi); relative to this lane's first
+        // key, a key is visible when its offset is below the span.
 #pragma unroll
-    for (int j = 0; j < KB; ++j)
+        for (int j = 0; j < KB; ++j) {
+          const int base = key0 + 32 * (half * KB + j) + 4 * h - vis_lo;
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(sc[j][8 * sub + 2 * e] - m_use);
-          const float p1 = fast_exp2(sc[j][8 * sub + 2 * e + 1] - m_use);
-          psum += p0 + p1;
-          pb[j][sub][e] = int(uint32_t(MF::bits(p0)) | (uint32_t(MF::bits(p1)) << 16));
+          for (int v = 0; v < 16; ++v)
+            if (uint32_t(base + 8 * (v >> 2) + (v & 3)) >= vis_span) sc[j][v] = kNegInf;
         }
+      }
+      float tmax = kNegInf;
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sc[j][v]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      tmax = tmax == kNegInf ? kNegInf : tmax * sl2;
+      const bool move = tmax > m_run + kMaxSlack;
+      const float m_new = move ? tmax : m_run;
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      alpha = move ? fast_exp2(m_run - m_use) : 1.f;
+      m_run = m_new;
+      moved = __builtin_amdgcn_ballot_w64(move) != 0;
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x0 = sc[j][8 * sub + 2 * e], x1 = sc[j][8 * sub + 2 * e + 1];
+            float p0 = fast_exp2(fmaf(x0, sl2, -m_use));
+            float p1 = fast_exp2(fmaf(x1, sl2, -m_use));
+            if constexpr (kMasked) {
+              p0 = x0 == kNegInf ? 0.f : p0;
+              p1 = x1 == kNegInf ? 0.f : p1;
+            }
+            psum += p0 + p1;
+            pb[j][sub][e] = int(MF::pack2(p0, p1));
+          }
+    };
+    const bool edge =
+        __builtin_amdgcn_readfirstlane(int(!(key0 >= full_lo && key0 + SH::kKeys - 1 <= full_hi))) != 0;
+    if (edge)
+      softmax(std::true_type{});
+    else
+      softmax(std::false_type{});
     l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+    if (moved) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db] *= alpha;
     }
