@@ -69,9 +69,15 @@ struct PfShape {
   static constexpr int KB = 2 / kHalves;   // 32-key blocks of a tile per wave
   static constexpr int kRows = kPrefillRows;   // query rows of a workgroup
   static constexpr int kKeys = kPrefillKeys;   // keys of an LDS tile
-  static constexpr int kStride = D + 8;        // elements per LDS row (16-byte pad: spreads the banks)
-  static constexpr int kTileElems = kKeys * kStride;
-  static constexpr int kBufBytes = 2 * kTileElems * 2;  // the K and V rows of one tile
+  // Elements per LDS row.  K rows are read 16 bytes per lane, 32
+  // consecutive rows at a time: a 4-dword pad puts them on distinct banks.
+  // V rows are read transposed, 8 bytes per lane from four consecutive
+  // rows and two 16-column groups: a 16-dword pad puts a 32-lane read on
+  // all 64 banks once.
+  static constexpr int kStride = D + 8;
+  static constexpr int kVStride = D + 32;
+  static constexpr int kTileElems = kKeys * kStride;  // the K rows; the V rows follow
+  static constexpr int kBufBytes = (kTileElems + kKeys * kVStride) * 2;  // the K and V rows of one tile
   static constexpr int kIdsOff = 2 * kBufBytes;         // after two buffers
   static constexpr int kLoopBytes = kIdsOff + kPrefillMaxSegTiles * 8;
   using CB = Combine<D, kRows / 16, 1>;
@@ -227,7 +233,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(Params p
       const int key = kKeysPerU * u + key_t;
       i32x4 v = stage[sl][u];
       if (!full && (key0 + key < key_lo || key0 + key >= key_hi)) v = i32x4{0, 0, 0, 0};
-      *reinterpret_cast<i32x4*>(kbuf(b) + part * SH::kTileElems + key * SH::kStride + 8 * col) = v;
+      *reinterpret_cast<i32x4*>(kbuf(b) + part * SH::kTileElems + key * (part ? SH::kVStride : SH::kStride) +
+                                8 * col) = v;
     }
   };
 
@@ -334,19 +341,19 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(Params p
     // + 8 + 0..3, two transposed reads (lane group g4 = lane / 16 addresses
     // rows 4 h + i / 4, columns 16 (g4 % 2) + 4 (i % 4) of the block).
     const int g4 = lane >> 4, i16 = lane & 15;
-    const uint16_t* vtr = vt_lds + (4 * h + (i16 >> 2)) * SH::kStride + 16 * (g4 & 1) + 4 * (i16 & 3);
+    const uint16_t* vtr = vt_lds + (4 * h + (i16 >> 2)) * SH::kVStride + 16 * (g4 & 1) + 4 * (i16 & 3);
 #pragma unroll
     for (int j = 0; j < KB; ++j)
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const uint16_t* a = vtr + (32 * (half * KB + j) + 16 * sub) * SH::kStride + 32 * db;
+          const uint16_t* a = vtr + (32 * (half * KB + j) + 16 * sub) * SH::kVStride + 32 * db;
           const uint64_t lo = __builtin_bit_cast(
               uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a)));
           const uint64_t hi = __builtin_bit_cast(
               uint64_t,
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a + 8 * SH::kStride)));
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a + 8 * SH::kVStride)));
           const i32x4 va = {int(uint32_t(lo)), int(uint32_t(lo >> 32)), int(uint32_t(hi)), int(uint32_t(hi >> 32))};
           acc[db] = MM::mma(va, pb[j][sub], acc[db]);
         }
