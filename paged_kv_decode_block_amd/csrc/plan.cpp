@@ -161,6 +161,19 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
     int64_t seg_target = std::max<int64_t>(4, std::min<int64_t>(8, (int64_t(64) << 10) / tile_bytes));
     if (span_tiles / seg_target < 16) seg_target = 4;
     if (span_tiles / seg_target < 16 && ceil_div(span_tiles, 2) <= 16) seg_target = 2;
+    const int64_t wg_rows = std::min(rows, p.row_tiles * 16);
+    // Strided key rows (NHD with several kv heads: consecutive keys of one
+    // head sit a token stride apart) make each tile's loads slower, and
+    // short spans gain from two-tile segments up to twice that count while
+    // a segment's partial stays within a quarter of its K/V bytes (a
+    // 512-key window, head size 256, fp16, 8/2 heads: M = 1, 4 rows, 10.07
+    // us in 7 segments against 8.90 in 17; M = 4, 16 rows, 11.4 in 7
+    // against 12.1 in 17).
+    const bool strided = sh.layout == PAD_NHD && sh.num_kv_heads > 1;
+    const bool two_tile = strided && seg_target > 2 && span_tiles / seg_target < 16 &&
+                          ceil_div(span_tiles, 2) <= 32 &&
+                          4 * wg_rows * (sh.head_size + 2) * int64_t(sizeof(float)) <= 2 * tile_bytes;
+    if (two_tile) seg_target = 2;
     // Where that still leaves 32 or more segments, a segment also keeps its
     // partial (wg_rows rows of D + 2 floats, written and read back) below a
     // sixth of its K/V bytes: wide heads with many live rows otherwise spend
@@ -169,11 +182,11 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
     // 21.3 us; 64 against 128 at 8k keys, 24.8 against 27.5 us).  Shorter
     // contexts keep the smaller segments (there 16 segments of 1k keys beat
     // 8, 15.5 against 18.0 us).
-    const int64_t wg_rows = std::min(rows, p.row_tiles * 16);
     const int64_t part_min = ceil_div(6 * wg_rows * (sh.head_size + 2) * int64_t(sizeof(float)), tile_bytes);
     if (part_min > seg_target && span_tiles / part_min >= 32) seg_target = part_min;
     const int64_t work = std::max<int64_t>(1, span_tiles / seg_target);
     nseg = std::min<int64_t>(fill, std::max<int64_t>(work, std::min<int64_t>(4, fill)));
+    if (two_tile) nseg = std::min<int64_t>(fill, ceil_div(span_tiles, 2));
     // A unit of at most 64 KiB of K/V runs as one segment: its loop is a
     // single round of loads, shorter than the split-KV epilogue (one bf16
     // sequence, 32/8 heads of 128, 128 keys: 6.4 us against 7.2 us at the
