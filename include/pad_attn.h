@@ -173,7 +173,12 @@ int32_t pad_abi_version(void);
 const char* pad_status_string(pad_status status);
 
 /* Plan a call for a device with `num_cus` compute units (> 0).  Pure host
- * computation; no GPU needed.  `window` >= 0 as in pad_decode_attn. */
+ * computation; no GPU needed.  `window` >= 0 as in pad_decode_attn.
+ * Logging: with the environment variable PAD_LOG set to anything but "" or
+ * "0" (read once per process), every plan the library makes -- here, for a
+ * workspace size and for each decode call -- is printed to stderr as one
+ * line "pad plan: <shape> -> <plan fields>", unless it equals the previous
+ * line printed on the same thread. */
 pad_status pad_decode_attn_plan(const pad_shape* shape, int32_t window, int32_t num_cus,
                                 pad_plan* plan);
 

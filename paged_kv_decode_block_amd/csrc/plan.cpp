@@ -2,6 +2,10 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
 
 namespace pad {
 namespace {
@@ -13,6 +17,42 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool known_head_size(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
+
+// Planner decisions go to stderr, one line per plan that differs from the
+// previous one logged on the calling thread, when the environment variable
+// PAD_LOG is set to anything but "" or "0" (read once per process).
+bool log_plans() {
+  static const bool on = [] {
+    const char* v = std::getenv("PAD_LOG");
+    return v != nullptr && v[0] != '\0' && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+const char* path_name(int path) {
+  switch (path) {
+    case PAD_PATH_MFMA: return "mfma";
+    case PAD_PATH_DOT: return "dot";
+    case PAD_PATH_PREFILL: return "prefill";
+  }
+  return "?";
+}
+
+void log_plan(const pad_shape& sh, int window, int num_cus, const Plan& p) {
+  char line[512];
+  std::snprintf(line, sizeof(line),
+                "pad plan: S=%d M=%d Hq=%d Hkv=%d D=%d page=%d max_seq_len=%d window=%d dtype=%d layout=%d cus=%d"
+                " -> path=%s rows=%d row_tiles=%d row_groups=%d waves=%d segments=%dx%d tiles grid=%dx%d"
+                " merge_slices=%d persistent=%d workspace=%zu\n",
+                sh.num_seqs, sh.query_len, sh.num_q_heads, sh.num_kv_heads, sh.head_size, sh.page_size,
+                sh.max_seq_len, window, sh.dtype, sh.layout, num_cus, path_name(p.path), p.rows, p.row_tiles,
+                p.row_groups, p.waves, p.nseg, p.seg_tiles, p.grid_x, p.grid_y, p.merge_slices, p.persistent,
+                p.ws_bytes);
+  thread_local std::string last;
+  if (last == line) return;
+  last = line;
+  std::fputs(line, stderr);
+}
 
 }  // namespace
 
@@ -324,6 +364,7 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
     p.merge_slices = 1;
   }
   *pl = p;
+  if (log_plans()) log_plan(sh, window, num_cus, p);
   return PAD_OK;
 }
 

@@ -597,3 +597,40 @@ def test_plan_prefill_family(M, head_size):
         b = plan(shape(num_seqs=16, num_q_heads=32, num_kv_heads=8, head_size=head_size, query_len=M,
                        max_blocks_per_seq=512))
         assert b["path"] == pad.PAD_PATH_PREFILL and b["persistent"] == 0
+
+
+def _plan_log(env_value):
+    """stderr of a child process that plans the same shape twice and a second shape once."""
+    import os
+    import subprocess
+    import sys
+
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import paged_kv_decode_block_amd as pad\n"
+        "a = pad.pad_shape(num_seqs=1, query_len=4, num_q_heads=32, num_kv_heads=8, head_size=128, page_size=16,\n"
+        "                  max_blocks_per_seq=2048, max_seq_len=32768, dtype=pad.PAD_BF16, layout=pad.PAD_HND)\n"
+        "b = pad.pad_shape(num_seqs=1, query_len=1, num_q_heads=32, num_kv_heads=8, head_size=128, page_size=16,\n"
+        "                  max_blocks_per_seq=2048, max_seq_len=32768, dtype=pad.PAD_BF16, layout=pad.PAD_HND)\n"
+        "pad.pad_decode_attn_plan(a, 0, num_cus=256)\n"
+        "pad.pad_decode_attn_plan(a, 0, num_cus=256)\n"
+        "pad.pad_decode_attn_plan(b, 0, num_cus=256)\n"
+    ) % os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ)
+    env.pop("PAD_LOG", None)
+    if env_value is not None:
+        env["PAD_LOG"] = env_value
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    return [l for l in r.stderr.splitlines() if l.startswith("pad plan:")]
+
+
+def test_plan_logging():
+    """PAD_LOG prints each new plan once (repeats of the previous line are
+    dropped); unset or "0" prints nothing."""
+    lines = _plan_log("1")
+    assert len(lines) == 2, lines
+    assert "M=4" in lines[0] and "M=1" in lines[1]
+    assert all("path=mfma" in l and "segments=" in l and "workspace=" in l for l in lines)
+    assert _plan_log(None) == []
+    assert _plan_log("0") == []
