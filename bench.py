@@ -164,12 +164,20 @@ def read_ceiling(case, nseg_hint: int) -> dict:
     }
 
 
+# Sources the decode kernel (both schedules) is built from or planned by,
+# with the headers they include; the prefill, cache-write, packed-store,
+# calibration and allocation-free sources are not among them.
+DECODE_SOURCES = ("decode_mfma.hip", "decode_common.h", "octave_dev.h", "kernels.h", "plan.h", "plan.cpp",
+                  "api.cpp", "entry.h", "launch.hip")
+
+
 def kernel_hash() -> str:
-    """Hash of every kernel and planner source and of the build script
-    (its compiler flags): a change to any of them makes the committed
-    traffic counters stale."""
+    """Hash of the decode kernel's sources (DECODE_SOURCES), the public
+    headers they include and the build script (its compiler flags): a
+    change to any of them makes the committed traffic counters stale."""
     h = hashlib.sha256()
-    paths = [os.path.join(CSRC, n) for n in sorted(os.listdir(CSRC))]
+    paths = [os.path.join(CSRC, n) for n in DECODE_SOURCES]
+    paths += [os.path.join(ROOT, "include", n) for n in ("pad_attn.h", "pad_octave.h")]
     paths.append(os.path.join(ROOT, "paged_kv_decode_block_amd", "build.py"))
     for path in paths:
         with open(path, "rb") as f:

@@ -68,3 +68,26 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode != 0
     assert "one GPU" in (res.stdout + res.stderr)
+
+
+def test_traffic_hash_covers_decode_includes():
+    """The sources the traffic counters' staleness hash covers include every
+    local file the decode kernel's translation units include, transitively."""
+    import os
+    import re
+
+    import bench
+
+    csrc = bench.CSRC
+    seen, todo = set(), ["decode_mfma.hip", "api.cpp", "plan.cpp", "launch.hip"]
+    while todo:
+        name = todo.pop()
+        if name in seen:
+            continue
+        seen.add(name)
+        with open(os.path.join(csrc, name)) as f:
+            for inc in re.findall(r'#include\s+"([^"]+)"', f.read()):
+                if "/" not in inc:
+                    todo.append(inc)
+    assert seen <= set(bench.DECODE_SOURCES), seen - set(bench.DECODE_SOURCES)
+    assert all(os.path.exists(os.path.join(csrc, n)) for n in bench.DECODE_SOURCES)
