@@ -100,7 +100,7 @@ typedef enum pad_layout { PAD_NHD = 0, PAD_HND = 1 } pad_layout;
  * split a segment's keys and are combined at the end.  DOT: per-head dot
  * products (G*M <= 4, head size <= 128).  PREFILL: prefill chunks (head
  * size 64 or 128, one workgroup per item): 128 query rows of a kv head per
- * workgroup share each 64-key tile through LDS (the prefill work items of
+ * workgroup share each 128-key tile through LDS (the prefill work items of
  * plan_prefill on the rocm_rdna_hip page); AUTO takes it for chunks of at
  * least 128 rows per kv head whose row blocks fill a quarter of the device,
  * over at least 1024 keys. */

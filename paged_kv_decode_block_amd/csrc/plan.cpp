@@ -168,12 +168,12 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
                       slots);
   // Prefill: about one workgroup per CU (one fits: 300 registers per
   // lane; 256 tokens over 4096 keys in 4 segments 56.8 us, in 8 81.2 us)
-  // over the units' row blocks, segments of at least 4 tiles (one 64-key
-  // LDS tile) and a multiple of 4 tiles.  Computed from the window-free
+  // over the units' row blocks, segments of at least one LDS tile
+  // (kPrefillKeys keys) and a multiple of one.  Computed from the window-free
   // span as well, so the workspace bound below covers every window.
   auto prefill_nseg = [&](int64_t tiles) {
     const int64_t want = ceil_div(slots, std::max<int64_t>(1, units));
-    return std::max<int64_t>(1, std::min(want, ceil_div(tiles, 4)));
+    return std::max<int64_t>(1, std::min(want, ceil_div(tiles, kPrefillKeys / kTileKeys)));
   };
   int64_t nseg;
   if (sh.num_segments > 0) {
@@ -237,7 +237,8 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
   nseg = std::min<int64_t>(nseg, kMaxSegments);
   nseg = std::max<int64_t>(1, nseg);
   p.seg_tiles = int(ceil_div(span_tiles, nseg));
-  if (p.path == PAD_PATH_PREFILL && sh.num_segments == 0) p.seg_tiles = int(ceil_div(p.seg_tiles, 4) * 4);
+  if (p.path == PAD_PATH_PREFILL && sh.num_segments == 0)
+    p.seg_tiles = int(ceil_div(p.seg_tiles, kPrefillKeys / kTileKeys) * (kPrefillKeys / kTileKeys));
   p.nseg = int(ceil_div(span_tiles, p.seg_tiles));
   // The row groups of one (kv head, segment) read the same tiles; the
   // kernel places them on one XCD (sharing its L2) when segments x kv

@@ -8,8 +8,8 @@
 // One workgroup serves one (sequence, kv head, 128-row block, key
 // segment): the kv head's G * M query rows are GQA-packed (row = token * G
 // + head) and cut into blocks of 128.  Its eight waves form four slabs of
-// 32 rows; the two waves of a slab take the two 32-key halves of every
-// 64-key tile (two independent waves per SIMD, so one's softmax overlaps
+// 32 rows; the two waves of a slab take the two 64-key halves of every
+// 128-key tile (two independent waves per SIMD, so one's softmax overlaps
 // the other's products) and are combined at the end.  Per tile, staged
 // once in LDS for all eight waves (double-buffered, its loads issued two
 // tiles ahead into registers), a wave
@@ -66,9 +66,10 @@ struct PfShape {
   static constexpr int NW = kPrefillWaves;
   static constexpr int kThreads = NW * 64;
   static constexpr int kHalves = NW / 4;   // waves per 32-row slab (key halves of a tile)
-  static constexpr int KB = 2 / kHalves;   // 32-key blocks of a tile per wave
   static constexpr int kRows = kPrefillRows;   // query rows of a workgroup
   static constexpr int kKeys = kPrefillKeys;   // keys of an LDS tile
+  static constexpr int kGroups = kKeys / 16;   // 16-key groups of a tile
+  static constexpr int KB = kKeys / 32 / kHalves;  // 32-key blocks of a tile per wave
   // Elements per LDS row.  K rows are read 16 bytes per lane, 32
   // consecutive rows at a time: a 4-dword pad puts them on distinct banks.
   // V rows are read transposed, 8 bytes per lane from four consecutive
@@ -206,10 +207,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(Params p
   // loads).
   i32x4 stage[2][SH::kPerThread];
   auto load_tile = [&](int kt, int sl) {
-    const unsigned char* gbase[4];
+    const unsigned char* gbase[SH::kGroups];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int t16 = min(max(4 * kt + g, ts), te - 1);
+    for (int g = 0; g < SH::kGroups; ++g) {
+      const int t16 = min(max(SH::kGroups * kt + g, ts), te - 1);
       const int64_t off = sm_off[t16 - ts];
       const uint32_t lo = __builtin_amdgcn_readfirstlane(int(uint32_t(uint64_t(off))));
       const uint32_t hi = __builtin_amdgcn_readfirstlane(int(uint32_t(uint64_t(off) >> 32)));
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(Params p
     for (int u = 0; u < SH::kPerThread; ++u) {
       // the key's 16-key group: u (16 keys per u) or one of u's two groups
       const unsigned char* gb =
-          kKeysPerU == 16 ? gbase[u & 3] : ((key_t & 16) ? gbase[(2 * u + 1) & 3] : gbase[(2 * u) & 3]);
+          kKeysPerU == 16 ? gbase[u] : gbase[2 * u + (key_t >> 4)];
       stage[sl][u] = *reinterpret_cast<const i32x4*>(gb + chunk_off);
     }
   };
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(Params p
     for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
 
   __syncthreads();  // the block ids
-  const int kt0 = ts / 4, kt1 = (te + 3) / 4;
+  const int kt0 = ts / SH::kGroups, kt1 = (te + SH::kGroups - 1) / SH::kGroups;
   load_tile(kt0, 0);
   store_tile(kt0, 0, 0);
   load_tile(min(kt0 + 1, kt1 - 1), 1);
