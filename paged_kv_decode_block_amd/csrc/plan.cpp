@@ -101,15 +101,20 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
   // chunks) the prefill family, whose workgroups share each K/V tile among
   // 128 rows.  The per-head dot-product family is used when asked for.
   // AUTO takes it where its 128-row blocks fill a quarter of the device
-  // without splitting the keys into many segments, over at least 1024 keys
-  // (16/8 heads of 128, bf16: 256 tokens over 4096 keys 56.8 against 65.3
-  // us, a 2048-token prompt 91 against 164 us; 64 tokens over 8192 keys
-  // 86.8 against 38.9 us and a 512-token prompt 26.5 against 22.5 us stay
-  // with the key-split family).
+  // and a kv head has at least 2^20 query rows x keys of work (32/8 heads
+  // of 128, bf16, graph-timed, prefill family against the key-split one:
+  // 256 tokens over 4096 keys 42 against 65 us, a 1024-token prompt 28.4
+  // against 56.6, 768 tokens 31.6 against 42.9, 640 tokens 27.4 against
+  // 36.6, 512 tokens over 384 keys of context 27.1 against 30.6; a
+  // 512-token prompt (2^20) ties at 23.1 / 23.3 and 256 tokens over 512
+  // keys (0.75 x 2^20) at 23.6; a 384-token prompt, 25.0 against 19.2, and
+  // short chunks over long contexts, whose row blocks do not fill the
+  // device (64 tokens over 8192 keys 86.8 against 38.9), stay with the
+  // key-split family).
   {
     const int64_t pf_units = int64_t(std::max(1, sh.num_seqs)) * sh.num_kv_heads * ceil_div(rows, kPrefillRows);
     const int64_t keys = sh.max_seq_len ? sh.max_seq_len : int64_t(sh.max_blocks_per_seq) * sh.page_size;
-    const bool pf_wins = rows >= kPrefillMinRows && 4 * pf_units >= num_cus && keys >= kPrefillMinKeys;
+    const bool pf_wins = rows >= kPrefillMinRows && 4 * pf_units >= num_cus && rows * keys >= kPrefillMinWork;
     if (sh.path == PAD_PATH_AUTO)
       p.path = prefill_ok && pf_wins ? PAD_PATH_PREFILL : PAD_PATH_MFMA;
     else

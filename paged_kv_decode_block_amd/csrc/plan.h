@@ -49,7 +49,7 @@ constexpr int kDotWaveCount = 4;
 // spans at most
 // kPrefillMaxSegTiles 16-key tiles (its block ids are staged in LDS).  The
 // planner picks the family for at least kPrefillMinRows rows per kv head
-// and kPrefillMinKeys keys (see make_plan).
+// and kPrefillMinWork query rows x keys per kv head (see make_plan).
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillRows = 128;
 // 128 keys per LDS tile (each wave two 32-key blocks per step, half the
@@ -59,7 +59,7 @@ constexpr int kPrefillRows = 128;
 constexpr int kPrefillKeys = 128;
 constexpr int kPrefillMaxSegTiles = 1024;
 constexpr int kPrefillMinRows = 128;
-constexpr int kPrefillMinKeys = 1024;
+constexpr int64_t kPrefillMinWork = int64_t(1) << 20;  // query rows x keys per kv head
 // Merge control words live in a fixed-size prefix of the workspace, so
 // calls of different shapes can share one workspace: partials never land
 // where any shape keeps control words, and every call leaves them zero.

@@ -571,8 +571,9 @@ def test_workspace_covers_every_window(window, nseg):
 def test_plan_prefill_family(M, head_size):
     """AUTO takes the prefill family (head sizes 64 and 128) for at least
     128 GQA-packed rows per kv head when its 128-row blocks fill a quarter
-    of the device, over at least 1024 keys: 128-row blocks of one workgroup
-    each, segments of a multiple of 4 tiles within the LDS id area, about
+    of the device, with at least 2^20 rows x keys per kv head: 128-row
+    blocks of one workgroup each, segments of a multiple of 8 16-key tiles
+    (one 128-key LDS tile) within the LDS id area, about
     one workgroup per CU; batches keep it on the grid schedule."""
     sh = shape(num_q_heads=32, num_kv_heads=8, head_size=head_size, query_len=M, max_blocks_per_seq=512)
     p = plan(sh)
@@ -583,7 +584,7 @@ def test_plan_prefill_family(M, head_size):
         assert p["row_tiles"] == 8 and p["row_groups"] == -(-rows // 128) and p["waves"] == 8
         assert p["persistent"] == 0
         assert p["segment_tiles"] <= 1024
-        assert p["num_segments"] == 1 or p["segment_tiles"] % 4 == 0
+        assert p["num_segments"] == 1 or p["segment_tiles"] % 8 == 0
         assert p["grid_x"] == p["num_segments"] * 8 * p["row_groups"]
         assert p["workspace_bytes"] >= 0
     else:
