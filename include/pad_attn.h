@@ -103,7 +103,7 @@ typedef enum pad_layout { PAD_NHD = 0, PAD_HND = 1 } pad_layout;
  * workgroup share each 128-key tile through LDS (the prefill work items of
  * plan_prefill on the rocm_rdna_hip page); AUTO takes it for chunks of at
  * least 128 rows per kv head whose row blocks fill a quarter of the device,
- * over at least 1024 keys. */
+ * with at least 2^20 query rows x keys per kv head. */
 typedef enum pad_path {
   PAD_PATH_AUTO = 0,
   PAD_PATH_MFMA = 1,
