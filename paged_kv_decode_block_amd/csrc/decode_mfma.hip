@@ -478,9 +478,10 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
 #pragma unroll
         for (int j = 0; j < 4; ++j) x[j] = sj[j] * p.scale_log2;
       }
+      // One wave-uniform branch per row tile, selects inside it.
+      if (edge) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (edge) {
+        for (int j = 0; j < 4; ++j) {
           const int key = key0 + 4 * g + j;
           if (key < lo_r[rt] || key > qpos_r[rt]) x[j] = kNegInf;
         }
