@@ -635,3 +635,44 @@ def test_plan_logging():
     assert all("path=mfma" in l and "segments=" in l and "workspace=" in l for l in lines)
     assert _plan_log(None) == []
     assert _plan_log("0") == []
+
+
+@pytest.mark.parametrize(
+    "M,keys,expect",
+    [
+        (256, 1023, pad.PAD_PATH_MFMA),  # 1024 rows x 1023 keys: just below 2^20
+        (256, 1024, pad.PAD_PATH_PREFILL),  # exactly 2^20
+        (256, 768, pad.PAD_PATH_MFMA),  # 256 tokens over 512 keys of context
+        (384, 384, pad.PAD_PATH_MFMA),  # a 384-token prompt
+        (512, 512, pad.PAD_PATH_PREFILL),  # a 512-token prompt
+        (96, 8192, pad.PAD_PATH_MFMA),  # enough work, but 24 row blocks leave the device idle
+        (1024, 4096, pad.PAD_PATH_PREFILL),
+    ],
+)
+def test_plan_prefill_work_rule(M, keys, expect):
+    """AUTO's prefill threshold: at least 2^20 query rows x keys per kv
+    head (32/8 heads: 4 rows per token), besides 128 rows and row blocks
+    for a quarter of the device; the key count is the shape's largest
+    sequence length."""
+    p = plan(shape(query_len=M, max_seq_len=keys, max_blocks_per_seq=1024))
+    assert p["path"] == expect, p
+
+
+def test_window_plan_strided_rows():
+    """A 512-key window over an NHD cache with two kv heads (strided key
+    rows): one query row per kv head's workgroup takes two-tile segments
+    (17 of them); four rows make the partial too large for that and keep
+    the longer segments, as does the head-major layout or one kv head."""
+    kw = dict(num_q_heads=8, num_kv_heads=2, head_size=256, dtype=pad.PAD_F16, max_seq_len=8192,
+              max_blocks_per_seq=512)
+    nhd1 = plan(shape(layout=pad.PAD_NHD, query_len=1, **kw), window=512)
+    assert (nhd1["num_segments"], nhd1["segment_tiles"]) == (17, 2)
+    nhd4 = plan(shape(layout=pad.PAD_NHD, query_len=4, **kw), window=512)
+    hnd1 = plan(shape(layout=pad.PAD_HND, query_len=1, **kw), window=512)
+    one = plan(shape(layout=pad.PAD_NHD, query_len=1, **dict(kw, num_q_heads=4, num_kv_heads=1)), window=512)
+    for p in (nhd4, hnd1, one):
+        assert p["segment_tiles"] > 2 and p["num_segments"] < 17, p
+        assert p["num_segments"] * p["segment_tiles"] * 16 >= 512 + 15
+    # without a window the span is long and keeps the usual segments
+    full = plan(shape(layout=pad.PAD_NHD, query_len=1, **kw))
+    assert full["segment_tiles"] >= 4

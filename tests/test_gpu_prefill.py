@@ -121,15 +121,10 @@ def test_prefill_bench_chunk_full():
     check(run_gpu(c), oracle_out(c), c.q.dtype, "prefill bench chunk")
 
 
-def test_prefill_2048_token_prompt():
-    """A 2048-token prompt (no earlier context) in one call: 8192 GQA-packed
-    rows per kv head, 64 row blocks.  Sampled tokens (the first, the last
-    and 62 spread between) of every head against the oracle's own
-    gather-and-softmax steps."""
-    spec = wl.CONFIGS[2]
-    M = 2048
-    c = wl.make_case(spec, [M], M, seed=8400, device=DEV)
-    say("prefill prompt: 2048 tokens, config 2 shapes")
+def _sampled_prompt_check(c, spec, M, window, what):
+    """Sampled tokens of a whole prompt (the first, the last and 62 spread
+    between) of every head against the oracle's own gather-and-softmax
+    steps: the full oracle is too slow at these sizes."""
     out = run_gpu(c)
     assert torch.isfinite(out).all()
     kv64, table, lens = wl.compact(c)
@@ -140,8 +135,41 @@ def test_prefill_2048_token_prompt():
     for kvh in range(spec.num_kv_heads):
         K_all, V_all = oracle.gather_kv(kv64, c.layout, table[0], kvh, range(M))
         for i, m in enumerate(toks):
-            lo, hi = oracle.key_bounds(M, M, m, 0)
+            lo, hi = oracle.key_bounds(M, M, m, window)
             for g in range(G):
                 h = kvh * G + g
                 ref[i, h] = oracle.attention._softmax_attend(q64[0, m, h], K_all[lo:hi + 1], V_all[lo:hi + 1], c.scale)
-    check(out[0, toks], ref, c.q.dtype, "2048-token prompt, sampled tokens")
+    check(out[0, toks], ref, c.q.dtype, what)
+
+
+def test_prefill_2048_token_prompt():
+    """A 2048-token prompt (no earlier context) in one call: 8192 GQA-packed
+    rows per kv head, 64 row blocks, on sampled tokens."""
+    spec = wl.CONFIGS[2]
+    M = 2048
+    c = wl.make_case(spec, [M], M, seed=8400, device=DEV)
+    say("prefill prompt: 2048 tokens, config 2 shapes")
+    _sampled_prompt_check(c, spec, M, 0, "2048-token prompt, sampled tokens")
+
+
+@pytest.mark.parametrize(
+    "spec,window",
+    [
+        (wl.Spec("bf16", 128, 32, 4, 16, wl.HND), 0),
+        (wl.Spec("fp16", 64, 16, 2, 32, wl.NHD, window=777), 777),
+    ],
+    ids=["bf16_d128_hnd", "fp16_d64_nhd_window"],
+)
+def test_prefill_largest_prompt(spec, window):
+    """The largest call the planner takes: a 4096-token prompt with eight
+    query heads per kv head, 32768 GQA-packed rows per kv head (256 row
+    blocks), through the automatic plan (the prefill family), on sampled
+    tokens; once with a sliding window over a token-major cache."""
+    M = 4096
+    c = wl.make_case(spec, [M], M, seed=8500 + spec.head_size, device=DEV, window=window)
+    sh = pad.make_shape(c.q, c.kv_cache, c.block_tables[0], c.layout)
+    p = pad.pad_decode_attn_plan(sh, window)
+    assert p["path"] == PREFILL and p["rows"] == 32768 and p["row_groups"] == 256, p
+    say(f"prefill prompt: 4096 tokens, {spec.dtype} D={spec.head_size} "
+        f"{spec.num_q_heads}/{spec.num_kv_heads} heads, window {window}")
+    _sampled_prompt_check(c, spec, M, window, f"4096-token prompt, window {window}, sampled tokens")
