@@ -38,13 +38,15 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of one MI355X
 POOL_BYTES = 512 << 20
 COPY_BYTES = 256 << 20  # --copy-calibration: bytes read (and written) per copy
 # Committed HBM-traffic counter runs, by (config, context, M) of the
-# workload they were taken on (MFMA family, automatic plan).
+# workload they were taken on (MFMA family, automatic plan; a packed
+# cache's runs by its format name in place of the config).
 TRAFFIC_FILES = {
     (2, 32768, 4): "traffic_decode_mfma_bf16_D128_Hq32_Hkv8_L32768_M4.json",
     (3, 16384, 4): "traffic_decode_mfma_fp16_D256_Hq8_Hkv2_NHD_W512_L16384_M4.json",
     (4, 32768, 1): "traffic_decode_mfma_bf16_D512_Hq16_Hkv2_L32768_M1.json",
     (4, 32768, 8): "traffic_decode_mfma_bf16_D512_Hq16_Hkv2_L32768_M8.json",
     (5, 16384, 4): "traffic_decode_mfma_persistent_bf16_D256_Hq16_Hkv2_P1056_batch64_M4.json",
+    ("octave_k3v4", 16384, 4): "traffic_decode_octave_k3v4_D256_Hq16_Hkv2_P1056_batch64_M4.json",
 }
 CSRC = os.path.join(ROOT, "paged_kv_decode_block_amd", "csrc")
 
@@ -269,7 +271,20 @@ def cpu_baseline(cfg: int, context: int, M: int, budget_s: float = 12.0) -> dict
     }
 
 
-def traffic_entry(cfg: int, context: int, M: int):
+def copy_calibration() -> None:
+    """Ten device copies of COPY_BYTES: a counter run's reference for
+    scaling the HBM byte counters of the kernels around it."""
+    import torch
+
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def traffic_entry(cfg, context: int, M: int):
     """Measured HBM bytes per launch from the committed counter runs of
     this workload, if there are any and they were taken on the current
     kernel source."""
@@ -466,6 +481,8 @@ def octave_main(args) -> int:
 
     ms = _event_time(call, args.warmup, args.steps)
     gbs = nbytes / (ms * 1e-3) / 1e9
+    if getattr(args, "copy_calibration", False):
+        copy_calibration()
     cpu = None
     if not args.no_cpu:
         from oracle import octave as oc
@@ -499,7 +516,7 @@ def octave_main(args) -> int:
                    "bytes_per_step": nbytes,
                    "bf16_cache_bytes_per_step": int(sum(L * Hkv * 2 * spec.head_size * 2 for L in lens if L > 0))},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_entry(args.octave, ctx, M)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -628,12 +645,7 @@ def main() -> int:
     print(f"[bench] timed {args.steps} steps: {ms * 1e3:.2f} us/step", file=sys.stderr, flush=True)
     gbs = nbytes / (ms * 1e-3) / 1e9
     if args.copy_calibration:
-        src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").normal_()
-        dst = torch.empty_like(src)
-        for _ in range(10):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration()
 
     ceiling = None
     if not args.no_ceiling:

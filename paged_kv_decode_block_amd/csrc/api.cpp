@@ -202,6 +202,7 @@ pad_status decode(const pad_shape* shape, const void* q, const int32_t* q_start,
   pr.merge_slices = p.merge_slices;
   pr.slot_rows = p.slot_rows;
   pr.persistent = p.persistent;
+  pr.unit_lead = p.unit_lead;
   pr.merge_wait_ticks = g_merge_wait_ticks.load();
   pr.scale_log2 = float(double(scale) * 1.4426950408889634);  // log2(e)
   const int rc = format ? pad::launch_decode_octave(p, pr, shape->dtype, format, stream)

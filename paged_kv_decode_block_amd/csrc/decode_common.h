@@ -436,13 +436,13 @@ __device__ __forceinline__ SegSplit split_of(const Params& p, int L, int M, int 
 }
 
 // Balanced persistent grid (batched decode).  Every unit -- (sequence, row
-// group, kv head) in that order -- takes kUnitLeadTiles lead positions (its
-// item's fixed cost) and then one position per 16-key tile of its key range
-// [t_lo, t_hi) of split_of; the units are laid end to end, T positions in
-// all, and workgroup b of the Gs = min(G, T) first of the G = gridDim.x
-// workgroups (one per CU) takes the contiguous share [b T / Gs, (b + 1) T /
-// Gs): every CU gets the same work, tiles plus item costs, whatever the
-// lengths.  A share computes the tiles among its positions; lead positions
+// group, kv head) in that order -- takes p.unit_lead lead positions (its
+// item's fixed cost, in tiles) and then one position per 16-key tile of its
+// key range [t_lo, t_hi) of split_of; the units are laid end to end, T
+// positions in all, and workgroup b of the Gs = min(G, T) first of the G =
+// gridDim.x workgroups (one per CU, or two for a packed cache) takes the
+// contiguous share [b T / Gs, (b + 1) T / Gs): every workgroup gets the same
+// work, tiles plus item costs, whatever the lengths.  A share computes the tiles among its positions; lead positions
 // alone make no item.  A unit inside one share is computed
 // whole and written directly.  A unit cut by share boundaries is computed
 // as one work item per share it meets; each item publishes a partial and
@@ -473,7 +473,7 @@ __device__ __forceinline__ void balanced_loop(const Params& p, unsigned char* ld
     if (L > 0 && M > 0) {
       for (int rg = 0; rg < p.row_groups; ++rg) {
         const SegSplit sp = split_of(p, L, M, rg);
-        if (sp.n_live > 0) n += kUnitLeadTiles + sp.t_hi - sp.t_lo;
+        if (sp.n_live > 0) n += p.unit_lead + sp.t_hi - sp.t_lo;
       }
     }
     sm_cnt[i] = n * p.num_kv_heads;
@@ -535,10 +535,10 @@ __device__ __forceinline__ void balanced_loop(const Params& p, unsigned char* ld
       const SegSplit sp = split_of(p, L, M, rg);
       if (sp.n_live == 0) continue;
       const int nu = sp.t_hi - sp.t_lo;
-      for (int kvh = 0; kvh < p.num_kv_heads && pos < end; ++kvh, ub += kUnitLeadTiles + nu) {
+      for (int kvh = 0; kvh < p.num_kv_heads && pos < end; ++kvh, ub += p.unit_lead + nu) {
         // Positions [ub, ub + lead) stand for the item's fixed cost; the
         // unit's tiles are positions [rb, ue).
-        const int rb = ub + kUnitLeadTiles, ue = rb + nu;
+        const int rb = ub + p.unit_lead, ue = rb + nu;
         if (ue <= pos) continue;
         const int f0 = max(rb, pos), f1 = min(ue, end);
         if (f0 >= f1) {  // the share ends among the lead positions

@@ -730,8 +730,11 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
 // for no kernel-argument fetch.  The other fields stay in the Params block; the
 // host keeps the three strides within 32 bits.  (One sequence of 32k
 // keys: 31.35 -> 31.03 us; 4k keys: 12.89 -> 12.65 us.)
+// A packed cache's kernels are held to two waves per SIMD (at most 256
+// registers per lane), so kPackedWgPerCu workgroups share a CU.
 template <typename T, int D, int RT, bool PERSIST, bool LEAN, int FMT = 0>
-__global__ __launch_bounds__((Shape<D, RT>::kThreads)) void decode_mfma_kernel(
+__global__ __launch_bounds__((Shape<D, RT>::kThreads))
+__attribute__((amdgpu_waves_per_eu(FMT != 0 ? kPackedWgPerCu : 1))) void decode_mfma_kernel(
     const int32_t* seq_lens, const int32_t* block_table, const void* kv, int32_t row_groups, int32_t num_kv_heads,
     int32_t max_blocks, int32_t seg_tiles, int32_t page_size, int32_t window, int32_t block_stride,
     int32_t head_stride, int32_t token_stride, Params params) {
@@ -1096,12 +1099,10 @@ int launch_dtype(const Plan& pl, const Params& pr, hipStream_t st) {
   return launch_d<T, D>(pl, pr, st);
 }
 #else
+// The planner gives a packed cache one row tile per wave.
 template <typename T, int FMT>
 int launch_octave_t(const Plan& pl, const Params& pr, hipStream_t st) {
-  switch (pl.row_tiles) {
-    case 1: return launch_t<T, kOctD, 1, FMT>(pl, pr, st);
-    case 2: return launch_t<T, kOctD, 2, FMT>(pl, pr, st);
-  }
+  if (pl.row_tiles == 1) return launch_t<T, kOctD, 1, FMT>(pl, pr, st);
   return int(hipErrorInvalidValue);
 }
 

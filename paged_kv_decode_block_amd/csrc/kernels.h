@@ -32,7 +32,8 @@ struct Params {
   int32_t merge_slices;       // slices of the merged output (merging workgroups)
   int32_t slot_rows;          // rows of one partial slot (see Plan::slot_rows)
   uint32_t merge_wait_ticks;  // helpers' wait bound (100 MHz real-time ticks)
-  int32_t persistent;         // 1: balanced persistent grid (one workgroup per CU)
+  int32_t persistent;         // 1: balanced persistent grid (one workgroup per CU, two for a packed cache)
+  int32_t unit_lead;          // balanced grid: lead positions per unit
   float scale_log2;           // scale * log2(e): logits are kept in the exp2 domain
   const uint32_t* k_signs;    // packed cache: sign bits of the K rotation [8]
   const uint32_t* v_signs;    // packed cache: sign bits of the V rotation [8]

@@ -43,11 +43,11 @@ void log_plan(const pad_shape& sh, int window, int num_cus, const Plan& p) {
   std::snprintf(line, sizeof(line),
                 "pad plan: S=%d M=%d Hq=%d Hkv=%d D=%d page=%d max_seq_len=%d window=%d dtype=%d layout=%d cus=%d"
                 " -> path=%s rows=%d row_tiles=%d row_groups=%d waves=%d segments=%dx%d tiles grid=%dx%d"
-                " merge_slices=%d persistent=%d workspace=%zu\n",
+                " merge_slices=%d persistent=%d lead=%d workspace=%zu\n",
                 sh.num_seqs, sh.query_len, sh.num_q_heads, sh.num_kv_heads, sh.head_size, sh.page_size,
                 sh.max_seq_len, window, sh.dtype, sh.layout, num_cus, path_name(p.path), p.rows, p.row_tiles,
                 p.row_groups, p.waves, p.nseg, p.seg_tiles, p.grid_x, p.grid_y, p.merge_slices, p.persistent,
-                p.ws_bytes);
+                p.unit_lead, p.ws_bytes);
   thread_local std::string last;
   if (last == line) return;
   last = line;
@@ -130,7 +130,9 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
     p.row_groups = int(ceil_div(rows, kPrefillRows));
     p.waves = kPrefillWaves;
   } else {
-    int rt = std::min(tiles_total, max_row_tiles(sh.head_size));
+    // A packed cache takes one row tile per wave, so two workgroups fit a
+    // CU (kPackedWgPerCu).
+    int rt = std::min(tiles_total, key_bytes > 0 ? 1 : max_row_tiles(sh.head_size));
     p.row_groups = int(ceil_div(tiles_total, rt));
     p.row_tiles = int(ceil_div(tiles_total, p.row_groups));
     p.waves = waves_for(sh.head_size, p.row_tiles);
@@ -146,8 +148,16 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
     span_tiles = std::min(all_tiles, ceil_div(int64_t(window) + sh.query_len - 1, kTileKeys) + 1);
 
   const int64_t units = int64_t(sh.num_seqs) * sh.num_kv_heads * p.row_groups;
-  // One workgroup per CU: its 4 waves keep enough loads in flight.
-  const int64_t slots = num_cus;
+  // One workgroup per CU: its 4 waves keep enough loads in flight; two
+  // for a packed cache, whose workgroups are smaller.  The grid
+  // schedule's segment fill still counts one per CU (grid_fill): a packed
+  // cache's shorter segments at two per CU cost more in partials and merges
+  // than the pairing gains (k3v4, 16/2 heads of 256, event-timed: one
+  // sequence of 32k keys at M = 1 20.4 against 26.6 us, at M = 4 27.5
+  // against 35.2; 8 sequences of 4k keys at M = 4 27.5 against 73.4).
+  const int64_t slots = int64_t(num_cus) * (key_bytes > 0 ? kPackedWgPerCu : 1);
+  const int64_t grid_fill = num_cus;
+  p.unit_lead = key_bytes > 0 ? kUnitLeadTilesPacked : kUnitLeadTiles;
   // K/V bytes of one 16-key tile of one kv head: two fp16/bf16 rows per key,
   // or the packed slot of a quantized cache.
   const int64_t tile_bytes = int64_t(kTileKeys) * (key_bytes > 0 ? key_bytes : 2 * sh.head_size * 2);
@@ -164,7 +174,7 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
   const int64_t seg_persist = std::max<int64_t>(4, (int64_t(3) << 20) / tile_bytes);
   // The dot and prefill families are built for one workgroup per item only.
   const bool can_persist = p.path == PAD_PATH_MFMA && sh.num_seqs <= kPersistMaxSeqs &&
-                           units * (ceil_div(table_keys, kTileKeys) + 1 + kUnitLeadTiles) < (int64_t(1) << 31) &&
+                           units * (ceil_div(table_keys, kTileKeys) + 1 + p.unit_lead) < (int64_t(1) << 31) &&
                            units * kCtlWordStride * int64_t(sizeof(int32_t)) <= int64_t(kCounterBytes);
   if (sh.schedule == PAD_SCHED_PERSISTENT && !can_persist) return PAD_EUNSUPPORTED;
   p.persistent = sh.schedule == PAD_SCHED_PERSISTENT ||
@@ -190,7 +200,7 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
   } else {
     // One full round of workgroups for a single sequence; two rounds when a
     // batch's lengths may differ, so short sequences leave no idle CUs.
-    const int64_t target = sh.num_seqs > 1 ? 2 * slots : slots;
+    const int64_t target = sh.num_seqs > 1 ? 2 * grid_fill : grid_fill;
     const int64_t fill = std::max<int64_t>(1, target / std::max<int64_t>(1, units));
     // About 64 KiB of K/V per segment, 4 to 8 tiles (two tiles per wave at
     // head size 128, one at 512), 4 tiles while that leaves fewer than 16
@@ -286,9 +296,9 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
   }
 
   if (p.persistent) {
-    // One workgroup per CU: the key-split and dot families fill a CU's
-    // registers (and, for the key-split combine, most of its LDS).
-    p.grid_x = num_cus;
+    // One workgroup per CU: the key-split family fills a CU's registers
+    // and most of its LDS (two per CU for a packed cache).
+    p.grid_x = int(slots);
     p.grid_y = 1;
   } else {
     p.grid_x = p.nseg * sh.num_kv_heads * p.row_groups;
@@ -317,7 +327,7 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
   } else if (p.path == PAD_PATH_PREFILL) {
     ws_nseg = prefill_nseg(all_tiles);
   } else {
-    const int64_t target = sh.num_seqs > 1 ? 2 * slots : slots;
+    const int64_t target = sh.num_seqs > 1 ? 2 * grid_fill : grid_fill;
     // A window-free span of at most 64 KiB per unit plans one segment
     // (and so does every window, which only shortens it).
     const bool one_seg = all_tiles * tile_bytes <= (int64_t(64) << 10);
@@ -330,7 +340,7 @@ pad_status make_plan(const pad_shape& sh, int window, int num_cus, Plan* pl, int
   const size_t S = size_t(sh.num_seqs), H = size_t(sh.num_kv_heads), D = size_t(sh.head_size);
   const size_t grid_rows = may_grid && ws_nseg > 1 ? S * H * size_t(ws_nseg) * size_t(rows) : 0;
   const size_t bal_slot_rows = size_t(std::min(rows, p.row_tiles * 16));
-  const size_t bal_rows = may_persist ? 2 * size_t(num_cus) * bal_slot_rows : 0;
+  const size_t bal_rows = may_persist ? 2 * size_t(slots) * bal_slot_rows : 0;
   auto bytes_for = [&](size_t r) { return r ? kCounterBytes + align_up(r * 2 * sizeof(float)) + align_up(r * D * sizeof(float)) : 0; };
   p.ws_bytes = std::max(bytes_for(grid_rows), bytes_for(bal_rows));
   p.ws_counters = 0;

@@ -74,6 +74,19 @@ constexpr int kPersistMaxSeqs = 1024;
 // 512..16384 keys, head size 256), graph-timed: 229.4 us at 0, 225.9 at 3,
 // 223.2 at 6, 222.7 at 8, 219-221 from 10 to 24.
 constexpr int kUnitLeadTiles = 12;
+// The same for a packed (quantized) cache: its 16-key tiles carry about a
+// quarter of the bytes, while an item's fixed cost does not shrink (it
+// adds the query rotation and the output's inverse rotation).  Batch
+// workload, k3v4 / k3v3 compact, event-timed: 12 lead tiles 155 / 152 us,
+// 24 142 / 141, 40 138 / 139, 64 135 / 134, 96 139 / 141, 140 147 / 146.
+constexpr int kUnitLeadTilesPacked = 64;
+// Workgroups per CU for a packed cache.  Its per-tile chain (loads,
+// unpack, products, softmax) is latency-bound at one wave per SIMD; with
+// one 16-row tile per wave a workgroup fits 256 registers per lane and 74
+// KiB of LDS, so two share a CU and one's chain overlaps the other's
+// (batch workload, k3v4: 193-199 us with two row tiles, one workgroup per
+// CU and 12 lead tiles; 155-160 us with one row tile, two per CU).
+constexpr int kPackedWgPerCu = 2;
 constexpr int64_t kLdsPerCu = 160 << 10;  // LDS bytes of a gfx950 CU
 
 // Waves per workgroup.  Four for every shape: on one bf16 sequence with
@@ -97,6 +110,7 @@ struct Plan {
   int lean;          // 1: the grid fills the device (single-copy tile loop)
   int grid_x, grid_y;
   int slot_rows;     // rows of one partial slot: G*M (grid) or row_tiles*16 (balanced grid)
+  int unit_lead;     // balanced grid: lead positions per unit (kUnitLeadTiles or kUnitLeadTilesPacked)
   // Workspace layout (byte offsets; all 256-byte aligned): the counter
   // prefix (kCounterBytes; per (unit, row group) merge_slices words, one
   // 128-byte line apart: the arrival counter, then one hand-over word per

@@ -676,3 +676,47 @@ def test_window_plan_strided_rows():
     # without a window the span is long and keeps the usual segments
     full = plan(shape(layout=pad.PAD_NHD, query_len=1, **kw))
     assert full["segment_tiles"] >= 4
+
+
+def _octave_plan_log(shapes):
+    """PAD_LOG lines of a child process that sizes the packed-cache (k3v4)
+    workspace of each shape (keyword dicts for pad_shape) and then the
+    plain one of the first, with 256 CUs (no device here)."""
+    import os
+    import subprocess
+    import sys
+
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import paged_kv_decode_block_amd as pad\n"
+        "for kw in %r:\n"
+        "    pad.pad_decode_attn_octave_workspace_size(pad.pad_shape(**kw), pad.OCTAVE_FORMATS['octave_k3v4'])\n"
+        "pad.pad_decode_attn_workspace_size(pad.pad_shape(**%r[0]))\n"
+    ) % (os.path.dirname(os.path.dirname(os.path.abspath(__file__))), shapes, shapes)
+    env = dict(os.environ, PAD_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    lines = [l for l in r.stderr.splitlines() if l.startswith("pad plan:")]
+    return [dict(kv.split("=", 1) for kv in l.split("->", 1)[1].split() if "=" in kv) for l in lines]
+
+
+def test_packed_cache_plans():
+    """A packed cache runs one 16-row tile per wave, so two workgroups share
+    a CU: the balanced grid has two workgroups per CU and 64 lead tiles per
+    unit (12 for the plain cache of the same batch); a single sequence on
+    the grid schedule fills the device counting one workgroup per CU."""
+    base = dict(num_q_heads=16, num_kv_heads=2, head_size=256, dtype=pad.PAD_BF16, layout=pad.PAD_HND,
+                num_segments=0, path=0, schedule=0)
+    batch = dict(base, num_seqs=65, query_len=4, page_size=1056, max_blocks_per_seq=16, max_seq_len=16384)
+    single = dict(base, num_seqs=1, query_len=4, page_size=32, max_blocks_per_seq=1024, max_seq_len=32768)
+    one_row = dict(single, query_len=1)
+    pb, ps, p1, plain = _octave_plan_log([batch, single, one_row])
+    assert pb["persistent"] == "1" and pb["grid"] == "512x1" and pb["lead"] == "64", pb
+    assert pb["row_tiles"] == "1" and pb["row_groups"] == "2", pb
+    assert plain["persistent"] == "1" and plain["grid"] == "256x1" and plain["lead"] == "12", plain
+    assert plain["row_tiles"] == "2" and plain["row_groups"] == "1", plain
+    for p, rg in ((ps, 2), (p1, 1)):
+        assert p["persistent"] == "0" and p["row_tiles"] == "1" and p["row_groups"] == str(rg), p
+        nseg = int(p["segments"].split("x")[0])
+        gx, gy = (int(v) for v in p["grid"].split("x"))
+        assert gx * gy == nseg * 2 * rg <= 256, p
