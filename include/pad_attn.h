@@ -121,8 +121,9 @@ typedef enum pad_path {
 typedef enum pad_schedule {  /* the dot family runs on the grid schedule only */
   PAD_SCHED_AUTO = 0,
   PAD_SCHED_GRID = 1,        /* one workgroup per (sequence, kv head, segment)  */
-  PAD_SCHED_PERSISTENT = 2,  /* one workgroup per CU, each taking an equal
-                                contiguous share of the batch's 16-key tiles   */
+  PAD_SCHED_PERSISTENT = 2,  /* one workgroup per CU (two for a packed cache,
+                                pad_octave.h), each taking an equal contiguous
+                                share of the batch's 16-key tiles              */
 } pad_schedule;
 
 /* Shape of one call.  Every field is host data. */

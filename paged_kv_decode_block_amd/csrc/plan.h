@@ -72,7 +72,10 @@ constexpr int kPersistMaxSeqs = 1024;
 // item (its first cold loads, combine, publish, arrival and merge) that a
 // share pays once per unit it meets.  Batch workload (64 sequences of
 // 512..16384 keys, head size 256), graph-timed: 229.4 us at 0, 225.9 at 3,
-// 223.2 at 6, 222.7 at 8, 219-221 from 10 to 24.
+// 223.2 at 6, 222.7 at 8, 219-221 from 10 to 24.  The same batch at other
+// head sizes (M = 4) keeps 12: 32/8 heads of 128 389.3 us against 394.4 /
+// 390.4 / 395.3 at 6 / 24 / 48; 16/2 heads of 512 736.5 against 738.4 /
+// 744.8 / 756.2.
 constexpr int kUnitLeadTiles = 12;
 // The same for a packed (quantized) cache: its 16-key tiles carry about a
 // quarter of the bytes, while an item's fixed cost does not shrink (it
@@ -106,7 +109,7 @@ struct Plan {
   int seg_tiles;     // planned tiles per segment
   int merge_slices;  // slices the merged output is cut into (1..kMaxSlices)
   int ws_nseg;       // segment slots the workspace holds (>= nseg, the same for every window)
-  int persistent;    // 1: one workgroup per CU takes an equal share of the batch's tiles
+  int persistent;    // 1: one workgroup per CU (two for a packed cache) takes an equal share of the batch's tiles
   int lean;          // 1: the grid fills the device (single-copy tile loop)
   int grid_x, grid_y;
   int slot_rows;     // rows of one partial slot: G*M (grid) or row_tiles*16 (balanced grid)
