@@ -55,11 +55,11 @@ def split(unit_tiles, G, lead=0):
     return items, Gs
 
 
-@pytest.mark.parametrize("lead", [0, 1, 6, 40])
+@pytest.mark.parametrize("lead", [0, 1, 6, 12, 40, 64])
 @pytest.mark.parametrize("seed", range(40))
 def test_balanced_split_invariants(seed, lead):
     r = np.random.default_rng(seed)
-    G = int(r.choice([1, 3, 8, 256]))
+    G = int(r.choice([1, 3, 8, 256, 512]))
     U = int(r.integers(1, 300))
     kind = seed % 4
     if kind == 0:
