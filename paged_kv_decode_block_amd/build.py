@@ -32,7 +32,10 @@ MFMA_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
 # head size, in parallel.
 SOURCES = [("decode_mfma.hip", f"decode_mfma_d{d}", [f"-DPAD_HEAD_SIZE={d}", *MFMA_FLAGS]) for d in (64, 128, 256, 512)] + [
     # the packed (quantized) cache's kernels: a further build at head size 256
-    ("decode_mfma.hip", "decode_octave_d256", ["-DPAD_HEAD_SIZE=256", "-DPAD_OCTAVE=1", *MFMA_FLAGS]),
+    # (a missed two-waves-per-SIMD register target is an error: two of its
+    # workgroups must fit one CU)
+    ("decode_mfma.hip", "decode_octave_d256", ["-DPAD_HEAD_SIZE=256", "-DPAD_OCTAVE=1", "-Werror=pass-failed",
+                                               *MFMA_FLAGS]),
     # the prefill kernels (head sizes 64 and 128)
     ("prefill_mfma.hip", "prefill_mfma", [*MFMA_FLAGS]),
 ] + [

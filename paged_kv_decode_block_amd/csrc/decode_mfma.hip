@@ -113,6 +113,8 @@ __device__ __forceinline__ void decode_unit(const Params& p, unsigned char* lds,
   using SH = Shape<D, RT, LEAN>;
   constexpr int NW = SH::NW, KC = SH::KC, DT = SH::DT;
   static_assert(FMT == 0 || D == kOctD, "packed formats are built for head size 256");
+  static_assert(FMT == 0 || SH::kBytes * kPackedWgPerCu <= kLdsPerCu,
+                "kPackedWgPerCu packed-cache workgroups share one CU's LDS");
   // Tiles in flight beyond the one computed: a packed tile carries a
   // quarter of the bytes of a bf16 one in a few registers per lane, so the
   // packed path keeps a deeper ring.
