@@ -7,7 +7,7 @@
  * (so the loads cannot be removed), and write one int32 to `sink` only when
  * that XOR hits a fixed 32-bit value (practically never).
  *
- * Source: ROCm/vllm pull request 1330, "Summary" -- the kernel is judged
+ * Source: ROCm/vllm pull request 1330, "Summary" -- the kernel is treated
  * as an HBM-bound stream and reported as a fraction of peak bandwidth; the
  * gather kernel below walks pages exactly as the attention kernel does
  * (same block table, same key range per query window), so its rate is the
