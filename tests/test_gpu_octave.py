@@ -107,6 +107,40 @@ def test_decode_batch_workload_shapes():
     check(out[pick], _oracle(c, packed, 1, sk, sv, seqs=pick), c.q.dtype, "octave batch (5 sequences)")
 
 
+@pytest.mark.parametrize("fmt", [1, 3])
+def test_decode_batch_poisoned_workspace(fmt):
+    """The balanced persistent grid at two workgroups per CU on a 64-sequence
+    batch (lengths 512..3000, 16/2 heads of 256, page 1056, M=4) with an
+    explicit workspace whose partial area is NaN-filled before every call:
+    three calls give the same bits, the control words are left zero, and
+    eight sequences (the longest among them) match the oracle."""
+    g = torch.Generator().manual_seed(78 + fmt)
+    lens = torch.randint(512, 3001, (64,), generator=g).tolist() + [0]
+    c, packed, kw_, vw_, sk, sv = _packed_case(fmt, "bf16", wl.HND, lens, 4, 16, 2, 1056, 4300 + fmt)
+    q = c.q.to(DEV)
+    cache = torch.from_numpy(packed).to(DEV)
+    bt, sl = c.block_tables[0].to(DEV), c.seq_lens.to(DEV)
+    shape = pad._octave_shape(q, cache, bt, c.layout, fmt)
+    need = pad.pad_decode_attn_octave_workspace_size(shape, fmt)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    pad.pad_decode_attn_workspace_init(ws)
+    say(f"octave batch, {NAMES[fmt]}: 64 + 1 padded, workspace {need} B poisoned before each call")
+    outs = []
+    for _ in range(3):
+        ws[1 << 20:].fill_(0xFF)
+        out = torch.full_like(q, float("nan"))
+        pad.pad_decode_attn_octave(q, cache, bt, sl, kw_.to(DEV), vw_.to(DEV), c.scale, out, fmt, layout=c.layout,
+                                   workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(out)
+        assert int(ws[: 1 << 20].view(torch.int32).abs().sum()) == 0, "control words must be left zero"
+    assert all(torch.equal(outs[0], o) for o in outs[1:]), "repeated calls must give the same bits"
+    assert torch.all(outs[0][64] == 0)
+    longest = int(np.argmax(lens[:64]))
+    pick = sorted({0, 9, 21, 33, 42, 55, 63, longest})
+    check(outs[0][pick], _oracle(c, packed, fmt, sk, sv, seqs=pick), c.q.dtype, f"octave batch {NAMES[fmt]}")
+
+
 def _ambiguous(x, step):
     r = x / np.where(step > 0, step, 1.0)
     return np.abs(r - np.round(r)) < 1e-4
