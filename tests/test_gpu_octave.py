@@ -141,6 +141,50 @@ def test_decode_batch_poisoned_workspace(fmt):
     check(outs[0][pick], _oracle(c, packed, fmt, sk, sv, seqs=pick), c.q.dtype, f"octave batch {NAMES[fmt]}")
 
 
+def test_graph_replay_packed():
+    """A packed-cache (k3v4) call on the balanced grid (two workgroups per
+    CU) captured in a HIP graph and replayed 20 times, with eager calls on
+    the grid schedule through the same workspace between replays: every
+    replay gives the eager call's bits, and the control words end zero."""
+    g = torch.Generator().manual_seed(91)
+    lens = torch.randint(512, 2001, (16,), generator=g).tolist() + [0]
+    c, packed, kw_, vw_, sk, sv = _packed_case(1, "bf16", wl.HND, lens, 4, 16, 2, 544, 4400)
+    q = c.q.to(DEV)
+    cache = torch.from_numpy(packed).to(DEV)
+    bt, sl, ks, vs = c.block_tables[0].to(DEV), c.seq_lens.to(DEV), kw_.to(DEV), vw_.to(DEV)
+    need = max(pad.pad_decode_attn_octave_workspace_size(pad._octave_shape(q, cache, bt, c.layout, 1, schedule=sch), 1)
+               for sch in (pad.PAD_SCHED_PERSISTENT, pad.PAD_SCHED_GRID))
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    pad.pad_decode_attn_workspace_init(ws)
+
+    def call(out, sch):
+        pad.pad_decode_attn_octave(q, cache, bt, sl, ks, vs, c.scale, out, 1, layout=c.layout, workspace=ws,
+                                   schedule=sch)
+        return out
+
+    say("octave graph replay: 16 + 1 padded sequences, k3v4 bf16, persistent schedule captured")
+    eager = call(torch.empty_like(q), pad.PAD_SCHED_PERSISTENT)
+    grid_ref = call(torch.empty_like(q), pad.PAD_SCHED_GRID)
+    torch.cuda.synchronize()
+    static_out = torch.zeros_like(q)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(static_out, pad.PAD_SCHED_PERSISTENT)
+    for it in range(20):
+        static_out.fill_(float("nan"))
+        graph.replay()
+        if it % 5 == 0:
+            other = call(torch.empty_like(q), pad.PAD_SCHED_GRID)  # eager work between replays
+            torch.cuda.synchronize()
+            assert torch.equal(other, grid_ref), f"eager grid call {it} changed"
+        torch.cuda.synchronize()
+        assert torch.equal(static_out, eager), f"replay {it} differs from the eager result"
+    assert int(ws[: 1 << 20].view(torch.int32).abs().sum()) == 0, "control words must be left zero"
+    pick = [0, 5, 11, 15]
+    check(static_out[pick], _oracle(c, packed, 1, sk, sv, seqs=pick), c.q.dtype, "octave graph replay")
+    assert torch.all(static_out[16] == 0)
+
+
 def _ambiguous(x, step):
     r = x / np.where(step > 0, step, 1.0)
     return np.abs(r - np.round(r)) < 1e-4
