@@ -173,3 +173,38 @@ def test_prefill_largest_prompt(spec, window):
     say(f"prefill prompt: 4096 tokens, {spec.dtype} D={spec.head_size} "
         f"{spec.num_q_heads}/{spec.num_kv_heads} heads, window {window}")
     _sampled_prompt_check(c, spec, M, window, f"4096-token prompt, window {window}, sampled tokens")
+
+
+def test_prefill_graph_replay():
+    """A prefill-family call (96 tokens over a 1904-key context, forced
+    segments, so its split-KV merge runs) captured in a HIP graph and
+    replayed 20 times, with eager decode calls through the same workspace
+    between replays: every replay gives the eager call's bits, and the
+    control words end zero."""
+    spec = wl.CONFIGS[2]
+    c = wl.make_case(spec, [2000], 96, seed=8600, device=DEV, instances=2)
+    d = wl.make_case(spec, [3000], 4, seed=8601, device=DEV)
+    need = max(pad.pad_decode_attn_workspace_size(pad.make_shape(x.q, x.kv_cache, x.block_tables[0], x.layout,
+                                                                 num_segments=n, path=p))
+               for x, n, p in ((c, 3, PREFILL), (d, 0, 0)))
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    pad.pad_decode_attn_workspace_init(ws)
+    say("prefill graph replay: 96 tokens over 1904 keys, config 2 shapes, 3 segments")
+    eager = run_gpu(c, 0, workspace=ws, path=PREFILL, num_segments=3)
+    dref = run_gpu(d, workspace=ws)
+    torch.cuda.synchronize()
+    static_out = torch.zeros_like(c.q)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_gpu(c, 0, workspace=ws, out=static_out, path=PREFILL, num_segments=3)
+    for it in range(20):
+        static_out.fill_(float("nan"))
+        g.replay()
+        if it % 5 == 0:
+            other = run_gpu(d, workspace=ws)  # eager work between replays
+            torch.cuda.synchronize()
+            assert torch.equal(other, dref), f"eager decode call {it} changed"
+        torch.cuda.synchronize()
+        assert torch.equal(static_out, eager), f"replay {it} differs from the eager result"
+    assert int(ws[: 1 << 20].view(torch.int32).abs().sum()) == 0, "control words must be left zero"
+    check(static_out, oracle_out(c), c.q.dtype, "prefill graph replay")
