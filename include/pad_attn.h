@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define PAD_ABI_VERSION 7
+#define PAD_ABI_VERSION 8
 
 typedef enum pad_status {
   PAD_OK = 0,
@@ -220,7 +220,7 @@ pad_status pad_decode_attn(const pad_shape* shape, const void* q, const void* kv
  * RocmOctaveMetadataBuilder._fill_query_maps on the octave page).
  * q_start is a device int32 array of num_seqs + 1 entries, read only on
  * the device (no host synchronisation; the call can be captured in a HIP
- * graph).  shape->query_len is the host bound on every M_s (1..256; it sizes
+ * graph).  shape->query_len is the host bound on every M_s (1..4096; it sizes
  * the plan and the workspace like a uniform call of that M).  Contract on
  * the device values: q_start non-decreasing, q_start[0] >= 0, M_s <=
  * query_len, and q/out hold at least q_start[num_seqs] rows; a count

@@ -99,6 +99,22 @@ pad_status pad_decode_attn_octave(const pad_shape* shape, int32_t format, const 
                                   const uint32_t* v_signs, float scale, void* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* pad_decode_attn_octave with a query count per sequence: the per-request
+ * query maps of RocmOctaveMetadataBuilder._fill_query_maps on the octave
+ * page, given as offsets.  q and out are packed [T, num_q_heads, 256] rows;
+ * sequence s owns rows q_start[s] .. q_start[s + 1] - 1, its M_s query
+ * tokens at positions L_s - M_s + m.  q_start: device int32 [num_seqs + 1],
+ * 4-byte aligned, read only on the device; shape->query_len bounds every
+ * M_s; the device-value contract and the clamping are those of
+ * pad_decode_attn_varlen (pad_attn.h).  Every other argument, the
+ * workspace rules and the errors as pad_decode_attn_octave (PAD_EINVAL for
+ * a missing or misaligned q_start). */
+pad_status pad_decode_attn_octave_varlen(const pad_shape* shape, int32_t format, const void* q,
+                                         const int32_t* q_start, const void* cache, const int32_t* block_table,
+                                         const int32_t* seq_lens, const uint32_t* k_signs, const uint32_t* v_signs,
+                                         float scale, void* out, void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,7 @@ __all__ = [
     "PAD_NOALLOC_SCRATCH_BYTES", "pad_decode_attn_noalloc",
     "PAD_KV_OCTAVE_K3V4", "PAD_KV_OCTAVE_K3V3", "PAD_KV_OCTAVE_K3V3_COMPACT", "OCTAVE_FORMATS",
     "pad_octave_cache_shape", "pad_octave_slot_bytes", "pad_octave_cache_write",
-    "pad_decode_attn_octave_workspace_size", "pad_decode_attn_octave",
+    "pad_decode_attn_octave_workspace_size", "pad_decode_attn_octave", "pad_decode_attn_octave_varlen",
     "PAD_F16", "PAD_BF16", "PAD_NHD", "PAD_HND",
     "PAD_PATH_AUTO", "PAD_PATH_MFMA", "PAD_PATH_DOT", "PAD_PATH_PREFILL",
     "PAD_SCHED_AUTO", "PAD_SCHED_GRID", "PAD_SCHED_PERSISTENT",
@@ -151,6 +151,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         P(pad_shape), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
         ctypes.c_void_p,
+    ]
+    L.pad_decode_attn_octave_varlen.restype = ctypes.c_int
+    L.pad_decode_attn_octave_varlen.argtypes = [
+        P(pad_shape), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_size_t, ctypes.c_void_p,
     ]
     L.pad_calib_gather_read.restype = ctypes.c_int
     L.pad_calib_gather_read.argtypes = [
@@ -600,6 +606,22 @@ def pad_decode_attn_octave_workspace_size(shape: pad_shape, fmt: int) -> int:
     return int(n.value)
 
 
+def _octave_workspace(device, shape: pad_shape, fmt: int, stream) -> torch.Tensor | None:
+    """The default packed-cache workspace of (device, stream): grown and
+    zeroed on that stream when a shape needs more."""
+    key = (device.index, _stream_ptr(stream), "octave")
+    ws_obj = _default_ws.get(key)
+    if ws_obj is None:
+        ws_obj = _default_ws[key] = Workspace(device)
+    need = pad_decode_attn_octave_workspace_size(shape, fmt)
+    if need and (ws_obj.buf is None or ws_obj.buf.numel() < need):
+        buf = torch.empty(need, dtype=torch.uint8, device=device)
+        _record_on(buf, stream)
+        pad_decode_attn_workspace_init(buf, stream)
+        ws_obj.buf = buf
+    return ws_obj.buf
+
+
 def pad_decode_attn_octave(q: torch.Tensor, cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
                            k_signs: torch.Tensor, v_signs: torch.Tensor, scale: float, out: torch.Tensor, fmt: int, *,
                            layout: int = PAD_HND, workspace: torch.Tensor | None = None, max_seq_len: int = 0,
@@ -615,20 +637,7 @@ def pad_decode_attn_octave(q: torch.Tensor, cache: torch.Tensor, block_table: to
         raise ValueError("out must match q's shape and dtype")
     shape = _octave_shape(q, cache, block_table, layout, fmt, max_seq_len=max_seq_len, num_segments=num_segments,
                           path=path, schedule=schedule)
-    if workspace is None:
-        key = (q.device.index, _stream_ptr(stream), "octave")
-        ws_obj = _default_ws.get(key)
-        if ws_obj is None:
-            ws_obj = _default_ws[key] = Workspace(q.device)
-        need = pad_decode_attn_octave_workspace_size(shape, fmt)
-        if need and (ws_obj.buf is None or ws_obj.buf.numel() < need):
-            buf = torch.empty(need, dtype=torch.uint8, device=q.device)
-            _record_on(buf, stream)
-            pad_decode_attn_workspace_init(buf, stream)
-            ws_obj.buf = buf
-        ws = ws_obj.buf
-    else:
-        ws = workspace
+    ws = _octave_workspace(q.device, shape, fmt, stream) if workspace is None else workspace
     ws_ptr = ws.data_ptr() if ws is not None else 0
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
@@ -636,4 +645,39 @@ def pad_decode_attn_octave(q: torch.Tensor, cache: torch.Tensor, block_table: to
         ctypes.byref(shape), int(fmt), ptr(q), ptr(cache), ptr(block_table), ptr(seq_lens), ptr(k_signs), ptr(v_signs),
         ctypes.c_float(scale), ptr(out), ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes),
         ctypes.c_void_p(_stream_ptr(stream))), "pad_decode_attn_octave")
+    return out
+
+
+def pad_decode_attn_octave_varlen(q: torch.Tensor, q_start: torch.Tensor, cache: torch.Tensor,
+                                  block_table: torch.Tensor, seq_lens: torch.Tensor, k_signs: torch.Tensor,
+                                  v_signs: torch.Tensor, scale: float, out: torch.Tensor, fmt: int, *,
+                                  max_query_len: int = 8, layout: int = PAD_HND, workspace: torch.Tensor | None = None,
+                                  max_seq_len: int = 0, num_segments: int = 0, path: int = PAD_PATH_AUTO,
+                                  schedule: int = PAD_SCHED_AUTO, stream=None) -> torch.Tensor:
+    """Packed-cache decode with a query count per sequence
+    (include/pad_octave.h): ``q`` and ``out`` are packed ``[T, Hq, 256]``;
+    sequence ``s`` owns rows ``q_start[s] .. q_start[s + 1] - 1``
+    (``q_start``: device int32, ``S + 1`` entries, never read on the host);
+    ``max_query_len`` bounds every per-sequence count."""
+    _require_device(q=q, q_start=q_start, cache=cache, block_table=block_table, seq_lens=seq_lens, k_signs=k_signs,
+                    v_signs=v_signs, out=out)
+    if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must be packed [T, Hq, D] tensors of one dtype")
+    S = block_table.shape[0]
+    if q_start.dtype != torch.int32 or q_start.shape != (S + 1,):
+        raise ValueError("q_start must be int32 with one entry per sequence plus one")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or seq_lens.shape != (S,):
+        raise ValueError("block_table and seq_lens must be int32, one row / entry per sequence")
+    T, Hq, D = q.shape
+    q_like = torch.empty((S, max_query_len, Hq, D), dtype=q.dtype, device="meta")
+    shape = _octave_shape(q_like, cache, block_table, layout, fmt, max_seq_len=max_seq_len, num_segments=num_segments,
+                          path=path, schedule=schedule)
+    ws = _octave_workspace(q.device, shape, fmt, stream) if workspace is None else workspace
+    ws_ptr = ws.data_ptr() if ws is not None else 0
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    _check(lib.pad_decode_attn_octave_varlen(
+        ctypes.byref(shape), int(fmt), ptr(q), ptr(q_start), ptr(cache), ptr(block_table), ptr(seq_lens), ptr(k_signs),
+        ptr(v_signs), ctypes.c_float(scale), ptr(out), ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes),
+        ctypes.c_void_p(_stream_ptr(stream))), "pad_decode_attn_octave_varlen")
     return out

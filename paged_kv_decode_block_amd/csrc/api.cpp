@@ -267,4 +267,16 @@ pad_status pad_decode_attn_octave(const pad_shape* shape, int32_t format, const 
                 format, k_signs, v_signs);
 }
 
+pad_status pad_decode_attn_octave_varlen(const pad_shape* shape, int32_t format, const void* q,
+                                         const int32_t* q_start, const void* cache, const int32_t* block_table,
+                                         const int32_t* seq_lens, const uint32_t* k_signs, const uint32_t* v_signs,
+                                         float scale, void* out, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  if (!shape) return PAD_EINVAL;
+  if (format < PAD_KV_OCTAVE_K3V4 || format > PAD_KV_OCTAVE_K3V3_COMPACT) return PAD_EINVAL;
+  if (shape->num_seqs > 0 && (!q_start || !aligned(q_start, 4))) return PAD_EINVAL;
+  return decode(shape, q, q_start, cache, block_table, seq_lens, scale, 0, out, workspace, workspace_bytes, stream,
+                format, k_signs, v_signs);
+}
+
 }  // extern "C"

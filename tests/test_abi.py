@@ -537,6 +537,23 @@ def test_octave_validation():
     # span, never below the control prefix
     assert pad.pad_decode_attn_octave_workspace_size(split, 1) >= 1 << 20
 
+    def dec_v(sh, fmt=1, q=0x1000, qs=0x1800, cache=0x2000, bt=0x3000, sl=0x4000, ks=0x5000, vs=0x6000, out=0x7000):
+        return L.pad_decode_attn_octave_varlen(ctypes.byref(sh), fmt, P(q), P(qs), P(cache), P(bt), P(sl), P(ks),
+                                               P(vs), ctypes.c_float(0.1), P(out), P(0), ctypes.c_size_t(0), None)
+
+    # the per-sequence-count entry: q_start required and 4-byte aligned,
+    # the format and the rest checked as above
+    assert dec_v(shape(**base), qs=0) == pad.PAD_EINVAL
+    assert dec_v(shape(**base), qs=0x1802) == pad.PAD_EINVAL
+    assert dec_v(shape(**base), fmt=0) == pad.PAD_EINVAL
+    assert dec_v(shape(**base), ks=0) == pad.PAD_EINVAL
+    assert dec_v(shape(num_q_heads=16, num_kv_heads=2, head_size=128)) == pad.PAD_EUNSUPPORTED
+    assert dec_v(shape(num_seqs=0, **base), q=0, qs=0, cache=0, bt=0, sl=0, ks=0, vs=0, out=0) == pad.PAD_OK
+    assert dec_v(split) == pad.PAD_EWORKSPACE
+    assert L.pad_decode_attn_octave_varlen(None, 1, P(0x1000), P(0x1800), P(0x2000), P(0x3000), P(0x4000),
+                                           P(0x5000), P(0x6000), ctypes.c_float(0.1), P(0x7000), P(0),
+                                           ctypes.c_size_t(0), None) == pad.PAD_EINVAL
+
     def wr(fmt=1, head_size=256, tokens=4, key=0x1000, ks=0x2000, cache=0x3000):
         sh = pad.pad_octave_cache_shape(num_tokens=tokens, num_kv_heads=2, head_size=head_size, page_size=16,
                                         num_blocks=4, dtype=pad.PAD_BF16, layout=pad.PAD_HND, format=fmt)

@@ -185,6 +185,52 @@ def test_graph_replay_packed():
     assert torch.all(static_out[16] == 0)
 
 
+VARLEN_CASES = [
+    # fmt, dtype, layout, lens, counts, schedule
+    (1, "bf16", wl.HND, [1500, 40, 0, 900, 2600, 3], [1, 4, 2, 0, 3, 4], pad.PAD_SCHED_AUTO),
+    (3, "fp16", wl.NHD, [700, 1200, 64], [2, 1, 4], pad.PAD_SCHED_PERSISTENT),
+    (2, "bf16", wl.HND, [2000, 33, 900], [4, 2, 1], pad.PAD_SCHED_GRID),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=[f"v{i}" for i in range(len(VARLEN_CASES))])
+def test_decode_varlen_matches_oracle(case):
+    """A query count per sequence over a packed cache
+    (pad_decode_attn_octave_varlen): sequence s owns its packed rows and its
+    M_s tokens sit at the last M_s positions; each sequence against the
+    oracle's own call with M_s tokens.  A count of 0 skips the sequence, a
+    padded sequence gets zero rows, L < M rows see no key, and the three
+    leading rows no sequence owns are left untouched."""
+    fmt, dt, layout, lens, counts, sched = case
+    mmax = max(counts)
+    say(f"octave varlen: {NAMES[fmt]} {dt} layout={layout} lens={lens} counts={counts} schedule={sched}")
+    c, packed, kw_, vw_, sk, sv = _packed_case(fmt, dt, layout, lens, mmax, 16, 2, 32, 9500 + fmt + len(lens))
+    lead = 3
+    rows = [c.q[s, :m] for s, m in enumerate(counts)]
+    q_packed = torch.cat([torch.zeros((lead,) + tuple(c.q.shape[2:]), dtype=c.q.dtype)] + rows).to(DEV)
+    starts = np.concatenate([[lead], lead + np.cumsum(counts)]).astype(np.int32)
+    out = torch.full_like(q_packed, float("nan"))
+    pad.pad_decode_attn_octave_varlen(q_packed, torch.from_numpy(starts).to(DEV), torch.from_numpy(packed).to(DEV),
+                                      c.block_tables[0].to(DEV), c.seq_lens.to(DEV), kw_.to(DEV), vw_.to(DEV),
+                                      c.scale, out, fmt, max_query_len=mmax, layout=layout, schedule=sched)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[:lead]).all(), "rows no sequence owns are left untouched"
+    bt = c.block_tables[0].numpy()
+    for s, (L, m) in enumerate(zip(lens, counts)):
+        if m == 0:
+            continue
+        got = out[starts[s]:starts[s + 1]]
+        if L == 0:
+            assert torch.all(got == 0), "padded sequence must be zero"
+            continue
+        used = np.unique(bt[s])
+        table = np.searchsorted(used, bt[s])[None, :]
+        q64 = c.q[s:s + 1, :m].to(torch.float64).numpy()
+        with np.errstate(invalid="ignore"):
+            ref = oc.decode_attention_quant(q64, packed[used], table, [L], c.scale, layout, NAMES[fmt], sk, sv)
+        check(got[None], ref, c.q.dtype, f"octave varlen seq {s} (L={L}, M={m})")
+
+
 def _ambiguous(x, step):
     r = x / np.where(step > 0, step, 1.0)
     return np.abs(r - np.round(r)) < 1e-4
