@@ -79,6 +79,8 @@ CASES = [
     (2, "bf16", wl.HND, [2500], 2, 16, 2, 32, {"num_segments": 17}),
     (3, "fp16", wl.HND, [4000, 900, 0, 2000], 4, 16, 2, 544, {"schedule": pad.PAD_SCHED_PERSISTENT}),
     (1, "bf16", wl.HND, [4000, 900, 0, 2000], 4, 16, 2, 544, {"schedule": pad.PAD_SCHED_GRID, "num_segments": 5}),
+    (1, "bf16", wl.HND, [1200, 30], 40, 16, 2, 32, {}),                # a 40-token chunk: 320 rows, 20 row groups
+    (3, "fp16", wl.NHD, [2500], 24, 8, 2, 16, {"schedule": pad.PAD_SCHED_PERSISTENT}),
 ]
 
 
