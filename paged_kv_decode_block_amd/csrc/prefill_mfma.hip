@@ -341,6 +341,13 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(Params p
     // (column d, half h) is V of keys 32 kb + 16 sub + 4 h + 0..3 and
     // + 8 + 0..3, two transposed reads (lane group g4 = lane / 16 addresses
     // rows 4 h + i / 4, columns 16 (g4 % 2) + 4 (i % 4) of the block).
+    // The wave issuing its PV products runs at a raised priority, so the
+    // other wave of its SIMD fills the gaps with its softmax (medians of six
+    // graph-timed runs on two boxes, TFLOP/s: chunk 463 / 442 against 458 /
+    // 438, 2048-token prompt 612 / 594 against 611 / 586, 4096-token prompt
+    // 763 / 728 against 750 / 723; raised for the QK^T products too:
+    // slower; for the softmax instead: no gain).
+    __builtin_amdgcn_s_setprio(1);
     const int g4 = lane >> 4, i16 = lane & 15;
     const uint16_t* vtr = vt_lds + (4 * h + (i16 >> 2)) * SH::kVStride + 16 * (g4 & 1) + 4 * (i16 & 3);
 #pragma unroll
@@ -358,6 +365,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(Params p
           const i32x4 va = {int(uint32_t(lo)), int(uint32_t(lo >> 32)), int(uint32_t(hi)), int(uint32_t(hi >> 32))};
           acc[db] = MM::mma(va, pb[j][sub], acc[db]);
         }
+    __builtin_amdgcn_s_setprio(0);
     if (kt + 1 < kt1) store_tile(kt + 1, b ^ 1, b ^ 1);
     __syncthreads();
   };
