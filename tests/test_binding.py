@@ -117,3 +117,51 @@ def test_explicit_workspace_is_passed_through(fake):
     pad.pad_decode_attn(q, kv, bt, lens, 0.125, 0, out, workspace=ws, stream=FakeStream(5))
     assert fake.events == [("decode", 5, ws.data_ptr(), 8192)]
     assert ctypes.sizeof(ctypes.c_void_p) == 8
+
+
+def test_packed_cache_default_workspace(fake):
+    """The packed-cache calls share one default workspace per (device,
+    stream), apart from the plain decode's, zeroed on the launch stream
+    and passed to both the uniform and the per-sequence-count entries."""
+    calls = []
+
+    def slot_bytes(fmt, head_size, n_ref):
+        n_ref._obj.value = 240
+        return pad.PAD_OK
+
+    def octave_ws(shape_ref, fmt, n_ref):
+        n_ref._obj.value = 2048
+        return pad.PAD_OK
+
+    def octave(shape, fmt, q, cache, bt, lens, ks, vs, scale, out, ws, ws_bytes, stream):
+        calls.append(("octave", stream.value, ws.value, ws_bytes.value))
+        return pad.PAD_OK
+
+    def octave_varlen(shape, fmt, q, qs, cache, bt, lens, ks, vs, scale, out, ws, ws_bytes, stream):
+        calls.append(("varlen", stream.value, ws.value, ws_bytes.value))
+        return pad.PAD_OK
+
+    fake.pad_octave_slot_bytes = slot_bytes
+    fake.pad_decode_attn_octave_workspace_size = octave_ws
+    fake.pad_decode_attn_octave = octave
+    fake.pad_decode_attn_octave_varlen = octave_varlen
+    S, M, Hq, Hkv, D, P = 2, 4, 16, 2, 256, 16
+    q = torch.zeros((S, M, Hq, D), dtype=torch.bfloat16)
+    cache = torch.zeros((8, Hkv, P, 240), dtype=torch.uint8)
+    bt = torch.zeros((S, 4), dtype=torch.int32)
+    lens = torch.ones(S, dtype=torch.int32)
+    signs = torch.zeros(8, dtype=torch.int32)
+    s = FakeStream(0x5150)
+    pad.pad_decode_attn_octave(q, cache, bt, lens, signs, signs, 0.1, torch.empty_like(q), 1, stream=s)
+    qp = torch.zeros((5, Hq, D), dtype=torch.bfloat16)
+    q_start = torch.tensor([0, 2, 5], dtype=torch.int32)
+    pad.pad_decode_attn_octave_varlen(qp, q_start, cache, bt, lens, signs, signs, 0.1, torch.empty_like(qp), 1,
+                                      max_query_len=M, stream=s)
+    (init,) = [e for e in fake.events if e[0] == "init"]
+    assert init[1] == 0x5150 and init[3] == 2048
+    assert calls == [("octave", 0x5150, init[2], 2048), ("varlen", 0x5150, init[2], 2048)]
+    # the plain decode on the same stream gets a workspace of its own
+    q2, kv2, bt2, lens2, out2 = _tensors()
+    pad.pad_decode_attn(q2, kv2, bt2, lens2, 0.125, 0, out2, stream=s)
+    decode = [e for e in fake.events if e[0] == "decode"]
+    assert decode and decode[0][2] != init[2]
